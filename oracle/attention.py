@@ -1,0 +1,131 @@
+"""Paged decode, rolling-buffer decode, chunked prefill and the split merge.
+
+Test infrastructure only (see the package docstring).  Everything is fp64.
+
+What is computed is the textbook definition of scaled dot-product attention,
+``softmax(scale * q k^T) v``, with the keys and values fetched through a block
+table ("PagedAttention in mistral.rs": the cache is cut into fixed-size token
+blocks and each sequence reaches its blocks through a table).  The paged
+method is exact up to rounding order, so the oracle is the definition.
+
+Readings where the pages are silent (each listed in the design notes):
+
+* Query head h reads KV head ``h // (Hq // Hkv)`` (contiguous groups).
+* ``context_lens[b]`` counts the token being decoded: the writer stores it
+  first, then attention reads it (write-then-attend, as the "Update" post of
+  mistral.rs discussion 46 orders the two operations).
+* An empty context gives an all-zero output.
+* Rolling buffer ("Rolling buffer cache", llama.cpp discussion 3581, opening
+  post): position i sits at ring slot i mod W; a W-slot ring written before
+  attending holds positions i-W+1 .. i, so the query attends to W keys.  The
+  ring is read in slot order; softmax does not depend on key order.
+* Chunked prefill: query j of a chunk of C tokens appended to a context of
+  total length ctx sits at absolute position ctx - C + j and sees keys
+  0 .. ctx - C + j (causal).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .cache import bits_to_f64, gather_f64
+
+
+def softmax_attend(q, k, v, scale: float):
+    """softmax(scale * k q) weighted sum of v, for one query vector.
+
+    q: ``[D]``; k, v: ``[L, D]``; returns ``[D]`` (zeros when L == 0).
+    """
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[1], dtype=np.float64)
+    s = scale * (k @ q)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return (p @ v) / np.sum(p)
+
+
+def decode(query_bits, act_fmt: str, key_cache, value_cache, cache_fmt: str,
+           block_tables, context_lens, scale: float, k_scale: float = 1.0,
+           v_scale: float = 1.0, window: int = 0):
+    """Paged decode: one query token per sequence.
+
+    query_bits: ``[B, Hq, D]`` activation bits.  Pools ``[NB, Hkv, BS, D]``.
+    block_tables: ``[B, MBPS]``; context_lens: ``[B]``.
+    window == 0: attend to logical rows 0..L-1 with L = context_lens[b].
+    window  > 0: the table addresses a ring of ``window`` rows; attend to ring
+    rows 0..min(L, window)-1.
+    Returns fp64 ``[B, Hq, D]``.
+    """
+    q = bits_to_f64(query_bits, act_fmt)
+    B, Hq, D = q.shape
+    Hkv = key_cache.shape[1]
+    group = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        if window > 0:
+            L = min(L, window)
+        k = gather_f64(key_cache, block_tables[b], L, cache_fmt, k_scale)
+        v = gather_f64(value_cache, block_tables[b], L, cache_fmt, v_scale)
+        for h in range(Hq):
+            g = h // group
+            out[b, h] = softmax_attend(q[b, h], k[:, g, :], v[:, g, :], scale)
+    return out
+
+
+def prefill_chunk(query_bits, act_fmt: str, cu_q_lens, key_cache, value_cache,
+                  cache_fmt: str, block_tables, context_lens, scale: float,
+                  k_scale: float = 1.0, v_scale: float = 1.0):
+    """Chunked prefill with a causal mask over prefix + chunk.
+
+    query_bits: ``[total_q, Hq, D]`` packed; sequence b owns rows
+    ``cu_q_lens[b] .. cu_q_lens[b+1]-1``.  context_lens[b] includes the chunk.
+    Returns fp64 ``[total_q, Hq, D]``.
+    """
+    q = bits_to_f64(query_bits, act_fmt)
+    total, Hq, D = q.shape
+    Hkv = key_cache.shape[1]
+    group = Hq // Hkv
+    out = np.zeros((total, Hq, D), dtype=np.float64)
+    B = len(cu_q_lens) - 1
+    for b in range(B):
+        q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        C = q1 - q0
+        ctx = int(context_lens[b])
+        k = gather_f64(key_cache, block_tables[b], ctx, cache_fmt, k_scale)
+        v = gather_f64(value_cache, block_tables[b], ctx, cache_fmt, v_scale)
+        for j in range(C):
+            i = ctx - C + j  # absolute position of this query
+            for h in range(Hq):
+                g = h // group
+                out[q0 + j, h] = softmax_attend(q[q0 + j, h], k[: i + 1, g, :],
+                                                v[: i + 1, g, :], scale)
+    return out
+
+
+def partial(q, k, v, scale: float):
+    """Unnormalised partial result of one key partition.
+
+    Returns (m, l, o): m = max score, l = sum of exp(s - m),
+    o = sum of exp(s - m) * v.  An empty partition gives (-inf, 0, 0).
+    """
+    if k.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(v.shape[1], dtype=np.float64)
+    s = scale * (k @ q)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return m, np.sum(p), p @ v
+
+
+def merge(parts):
+    """Combine partition partials (m_p, l_p, o_p) into the attention output.
+
+    M = max m_p; w_p = exp(m_p - M); out = sum w_p o_p / sum w_p l_p.
+    """
+    live = [(m, l, o) for (m, l, o) in parts if np.isfinite(m)]
+    if not live:
+        return np.zeros_like(parts[0][2])
+    M = max(m for m, _, _ in live)
+    num = sum(np.exp(m - M) * o for m, _, o in live)
+    den = sum(np.exp(m - M) * l for m, l, _ in live)
+    return num / den
