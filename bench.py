@@ -1,0 +1,382 @@
+#!/usr/bin/env python3
+"""Paged KV-cache benchmark on one MI355X.
+
+Default workload: Mistral-7B-shaped paged decode (32 query / 8 KV heads,
+head_dim 128, bf16, 32 sequences with context lengths uniform in
+[512, 4096], block size 32, shuffled pool).  One step = the slot writer for
+the 32 new tokens plus the paged decode over all 32 sequences, all inputs
+resident in HBM.  The pool is replicated so that consecutive steps read
+different copies and the working set (>= 2 GB) cannot sit in the 256 MB
+last-level cache.
+
+Prints ONE JSON line.  ``value`` is the KV-read bandwidth of the whole step
+(algorithmic K/V bytes the decode must read / step time).  ``roofline``
+reports the decode alone (both of its kernels) against the 8 TB/s HBM peak,
+timed with HIP events on the launch stream.  ``cpu_baseline`` times the CPU
+oracle on the same inputs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode: KV-read GB/s (% of HBM peak) and decode tokens/s, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="mistral_decode",
+                    choices=["mistral_decode", "fp8_decode", "sliding_decode", "tiny_decode",
+                             "prefix_prefill"])
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for 2 GB)")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0,
+                    help="instead: time a plain device copy of this many GiB (counter scaling)")
+    return ap.parse_args()
+
+
+def _workload(name):
+    from paged_kv_cache_175_amd import workloads as W
+    return {"mistral_decode": W.mistral_decode, "fp8_decode": W.fp8_decode,
+            "sliding_decode": W.sliding_decode, "tiny_decode": W.tiny_decode,
+            "prefix_prefill": W.prefix_prefill}[name]()
+
+
+def _act_tensor(bits, act, torch):
+    import numpy as np
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[act]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dt).cuda()
+
+
+def _cpu_info():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+# --------------------------------------------------------------------------- decode
+
+
+def bench_decode(wl, a, torch):
+    import numpy as np
+    from paged_kv_cache_175_amd import ops, pool
+
+    dev = torch.device("cuda", 0)
+    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
+    cache_dt = torch.uint8 if wl.cache == "e4m3" else {"bf16": torch.bfloat16,
+                                                        "f16": torch.float16}[wl.cache]
+    elem = 1 if wl.cache == "e4m3" else 2
+    pool_bytes = 2 * math.prod(shape) * elem
+    R = a.replicas or max(1, math.ceil(2e9 / pool_bytes))
+
+    kc0 = torch.zeros(shape, dtype=cache_dt, device=dev)
+    vc0 = torch.zeros_like(kc0)
+    # Cached tokens through the HIP writer, slots from the host block manager.
+    ks, vs, sl = [], [], []
+    for b in range(wl.B):
+        n = wl.cached_k[b].shape[0]
+        if n:
+            pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+            sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+            ks.append(wl.cached_k[b])
+            vs.append(wl.cached_v[b])
+    if sl:
+        ops.reshape_and_cache(_act_tensor(np.concatenate(ks), wl.act, torch),
+                              _act_tensor(np.concatenate(vs), wl.act, torch), kc0, vc0,
+                              torch.from_numpy(np.concatenate(sl).astype(np.int32)).to(dev),
+                              wl.k_scale, wl.v_scale)
+    del ks, vs, sl
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    q0 = _act_tensor(wl.query, wl.act, torch)
+    qs = [q0] + [q0.clone() for _ in range(R - 1)]
+    new_k = _act_tensor(wl.new_k, wl.act, torch)
+    new_v = _act_tensor(wl.new_v, wl.act, torch)
+    new_slots = torch.from_numpy(np.array(
+        [pool.slots_from_table(wl.block_tables[b], [wl.new_pos[b]], wl.BS, wl.window)[0]
+         for b in range(wl.B)], dtype=np.int32)).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    max_len = int(wl.context_lens.max())
+    need = ops.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, max_len, wl.window,
+                                      a.partition_tokens)
+    ws = ops.alloc_workspace(need, dev)
+    out = torch.empty_like(q0)
+
+    writes, decodes = [], []
+    for r in range(R):
+        kc, vc = pools[r]
+        writes.append(ops.prepare_reshape_and_cache(new_k, new_v, kc, vc, new_slots,
+                                                    wl.k_scale, wl.v_scale))
+        decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
+                                          wl.k_scale, wl.v_scale, wl.window,
+                                          a.partition_tokens))
+
+    kv_tokens = wl.kv_read_tokens()
+    kv_bytes = kv_tokens * wl.Hkv * wl.D * elem * 2
+    write_bytes = wl.B * wl.Hkv * wl.D * (2 * 2 + 2 * elem)   # read K,V act; write K,V cache
+    qo_bytes = 2 * wl.B * wl.Hq * wl.D * 2
+
+    for i in range(a.warmup):
+        writes[i % R]()
+        decodes[i % R]()
+    torch.cuda.synchronize()
+
+    K = a.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        writes[i % R]()
+        ev[i][0].record()
+        decodes[i % R]()
+        ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    dec_avg_s = sum(dec_ms) / K * 1e-3
+    step_s = total_ms / K * 1e-3
+
+    achieved = kv_bytes / dec_avg_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(kv_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.cache != "e4m3" else "e4m3->bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+            "head_dim": wl.D, "block_size": wl.BS, "act_dtype": wl.act,
+            "cache_dtype": wl.cache, "window": wl.window, "seed": wl.meta["seed"],
+            "context_tokens_read": kv_tokens, "max_context_len": max_len,
+            "new_tokens_written": wl.B, "pool_blocks": wl.pool_blocks, "replicas": R,
+            "partition_tokens": a.partition_tokens or "auto",
+        },
+        "tokens_per_s": round(wl.B / step_s, 1),
+        "decode_tokens_per_s": round(wl.B / dec_avg_s, 1),
+        "decode_us": round(dec_avg_s * 1e6, 3),
+        "decode_us_p10_p90": [round(float(x) * 1e3, 3) for x in
+                              np.percentile(np.array(dec_ms), [10, 90])],
+        "step_us": round(step_s * 1e6, 3),
+        "wall_us_per_step": round(wall / K * 1e6, 3),
+        "kv_bytes_per_step": kv_bytes,
+        "other_bytes_per_step": write_bytes + qo_bytes,
+        "roofline": {
+            "kernel": "pa_decode (split-context pass 1 + merge pass 2)",
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    return res, (wl, kv_bytes)
+
+
+def cpu_baseline_decode(wl, kv_bytes, seconds):
+    """The CPU oracle on the same inputs: untimed pool population, then timed
+    repetitions of (writer for the new tokens + decode of every sequence)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import attention as o_attn
+    from oracle import cache as o_cache
+    from oracle import pool as o_pool
+
+    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
+    dt = np.uint8 if wl.cache == "e4m3" else np.uint16
+    kc = np.zeros(shape, dt)
+    vc = np.zeros(shape, dt)
+
+    def row(pos):
+        return o_pool.ring_index(int(pos), wl.window) if wl.window else int(pos)
+
+    for b in range(wl.B):
+        n = wl.cached_k[b].shape[0]
+        slots = [o_cache.slot_of(wl.block_tables[b], row(wl.cached_pos0[b] + t), wl.BS)
+                 for t in range(n)]
+        o_cache.reshape_and_cache(wl.cached_k[b], wl.cached_v[b], kc, vc, np.array(slots),
+                                  wl.act, wl.cache, wl.k_scale, wl.v_scale)
+    new_slots = np.array([o_cache.slot_of(wl.block_tables[b], row(wl.new_pos[b]), wl.BS)
+                          for b in range(wl.B)])
+
+    def step():
+        o_cache.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, new_slots, wl.act, wl.cache,
+                                  wl.k_scale, wl.v_scale)
+        o_attn.decode(wl.query, wl.act, kc, vc, wl.cache, wl.block_tables, wl.context_lens,
+                      wl.scale, wl.k_scale, wl.v_scale, wl.window)
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        reps, t = 0, 0.0
+        while reps == 0 or t < seconds:
+            t0 = time.perf_counter()
+            step()
+            t += time.perf_counter() - t0
+            reps += 1
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    per = t / reps
+    return {
+        "value": round(kv_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "tokens_per_s": round(wl.B / per, 3), "seconds_per_step": round(per, 4),
+        "sample": f"full workload ({wl.B} sequences, {wl.kv_read_tokens()} tokens per KV head): "
+                  f"writer + fp64 decode, {reps} repetitions in {t:.1f} s, single thread",
+        "cpu_model": _cpu_info(), "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+# --------------------------------------------------------------------------- prefill
+
+
+def bench_prefill(wl, a, torch):
+    import numpy as np
+    from paged_kv_cache_175_amd import ops, pool
+
+    dev = torch.device("cuda", 0)
+    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    sl = pool.slots_from_table(wl.block_tables[0], np.arange(wl.prefix_len), wl.BS)
+    ops.reshape_and_cache(_act_tensor(wl.prefix_k, wl.act, torch),
+                          _act_tensor(wl.prefix_v, wl.act, torch), kc, vc,
+                          torch.from_numpy(sl).to(dev))
+    ck = _act_tensor(np.concatenate(wl.chunk_k), wl.act, torch)
+    cv = _act_tensor(np.concatenate(wl.chunk_v), wl.act, torch)
+    chunk_slots = torch.from_numpy(np.concatenate([
+        pool.slots_from_table(wl.block_tables[b],
+                              np.arange(wl.prefix_len, wl.prefix_len + int(wl.chunk_lens[b])),
+                              wl.BS) for b in range(wl.B)])).to(dev)
+    q = _act_tensor(wl.query, wl.act, torch)
+    out = torch.empty_like(q)
+    write = ops.prepare_reshape_and_cache(ck, cv, kc, vc, chunk_slots)
+    run = ops.prepare_prefill_chunk(q, torch.from_numpy(wl.cu_q_lens).to(dev), kc, vc,
+                                    torch.from_numpy(wl.block_tables).to(dev),
+                                    torch.from_numpy(wl.context_lens).to(dev),
+                                    int(wl.chunk_lens.max()), wl.scale, out)
+    for _ in range(a.warmup):
+        write()
+        run()
+    torch.cuda.synchronize()
+    K = a.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        write()
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    step_s = t0.elapsed_time(t1) / K * 1e-3
+    pre_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) / K * 1e-3
+    flops = wl.flops()
+    tf = flops / pre_s / 1e12
+    return {
+        "metric": "chunked prefill over shared prefix: attention TFLOP/s, 1 MI355X",
+        "value": round(flops / step_s / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": a.warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "prefix_len": wl.prefix_len,
+                   "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS},
+        "prefill_us": round(pre_s * 1e6, 3), "step_us": round(step_s * 1e6, 3),
+        "tokens_per_s": round(wl.total_q / step_s, 1),
+        "roofline": {"kernel": "pa_prefill_chunk", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops},
+    }
+
+
+def calibrate_copy(gib, a, torch):
+    n = int(gib * (1 << 30))
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(a.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(a.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    s = t0.elapsed_time(t1) / a.steps * 1e-3
+    return {"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+            "us_per_copy": round(s * 1e6, 2), "GBps_read_plus_write": round(2 * n / s / 1e9, 1)}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by sequence or KV head, but no "
+                                   "multi-GPU code is built)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if a.calibrate_copy > 0:
+        print(json.dumps(calibrate_copy(a.calibrate_copy, a, torch)))
+        return
+    wl = _workload(a.config)
+    if a.config == "prefix_prefill":
+        res = bench_prefill(wl, a, torch)
+    else:
+        res, (wl, kv_bytes) = bench_decode(wl, a, torch)
+        if a.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_decode(wl, kv_bytes, a.cpu_seconds)
+        from paged_kv_cache_175_amd import pool
+        cfg = pool.PagedKVConfig(cache_dtype="f8e4m3" if wl.cache == "e4m3" else "auto",
+                                 window=wl.window)
+        res["describe"] = pool.describe(cfg, 1, wl.kv_read_tokens())
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache attention library for MI355X (gfx950).
+ *
+ * What it computes (pages cited by title and section):
+ *
+ *  - "PagedAttention in mistral.rs", opening section: the KV cache is cut into
+ *    fixed-size blocks of tokens (default 32) taken from a pool allocated up
+ *    front; each sequence reaches its blocks through a table.  Attention over
+ *    such a cache for one new query token per sequence is pa_decode().
+ *  - same page, section "KV Cache Quantization": the cache may hold FP8
+ *    (E4M3) instead of the activation type; the slot writer quantises on
+ *    write and the attention kernels dequantise on read.
+ *  - "Optimization plans" (mistral.rs discussion 46), "Update" post: the slot
+ *    writer reshape_and_cache stores each new token's K and V into its cache
+ *    slot before attention runs; pa_reshape_and_cache() is that writer.
+ *  - "Rolling buffer cache" (llama.cpp discussion 3581), opening post: with a
+ *    sliding window of W tokens the cache is a ring of W rows and position i
+ *    lives in row i mod W; pa_decode() with window > 0 reads such a ring.
+ *  - same page "PagedAttention in mistral.rs", sections "Prefix caching" and
+ *    "FlashAttention V2/V3 + PagedAttention": prompt (prefill) tokens attend
+ *    causally over cached blocks that may be shared between sequences;
+ *    pa_prefill_chunk() is that causal attention over a block table.
+ *  - "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build: the pages are
+ *    head-major, which fixes the layout below.
+ *
+ * Conventions for every entry point:
+ *
+ *  - Pointers named *_cache, key, value, query, out, slot_mapping,
+ *    block_tables, context_lens, cu_q_lens and workspace are DEVICE pointers
+ *    owned by the caller.  The library allocates nothing and keeps no state
+ *    between calls.
+ *  - Cache pools are [num_blocks][num_kv_heads][block_size][head_dim],
+ *    row-major; one (block, head) page is a contiguous run of
+ *    block_size * head_dim elements.  Activations are row-major.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *    stream).  The library never synchronises.
+ *  - Errors are returned as pa_status; nothing is thrown and nothing aborts.
+ *    Arguments the host can see are checked before anything is launched.
+ *    Device data (table entries, lengths, slots) is NOT checked: the caller
+ *    contracts below must hold, or the kernels read or write out of bounds.
+ *  - Supported now: block_size 32; head_dim 64 or 128 for decode, 64, 96 or
+ *    128 for prefill; act dtype PA_F16 or PA_BF16; cache dtype equal to the
+ *    act dtype or PA_F8E4M3; Hq/Hkv between 1 and 16 (decode: at most 8).
+ *    Anything else returns PA_ERR_UNSUPPORTED.
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F8E4M3 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* a host-visible argument is malformed             */
+  PA_ERR_UNSUPPORTED = 2, /* well-formed but not built (shape, dtype)          */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required        */
+  PA_ERR_HIP = 4          /* a HIP runtime call or launch failed               */
+} pa_status;
+
+/* Human-readable name of a status code.  Never NULL. */
+const char* pa_status_string(pa_status s);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_reshape_and_cache -- write T new tokens into the cache pools.
+ *
+ * key, value      [T][Hkv][D] in act_dtype.
+ * key_cache,
+ * value_cache     [NB][Hkv][BS][D] in cache_dtype, updated in place.
+ * slot_mapping    [T] int32.  Token n goes to block slot_mapping[n] / BS,
+ *                 row slot_mapping[n] % BS, for every KV head.  A negative
+ *                 slot skips the token.  Caller contract: non-negative slots
+ *                 are < NB*BS and unique within one call.
+ * cache_dtype     act_dtype (bit copy) or PA_F8E4M3: code =
+ *                 E4M3(fp32(x) / scale) with IEEE fp32 division, round to
+ *                 nearest even, saturation to +-448, NaN -> 0x7F|sign,
+ *                 scale = k_scale for keys and v_scale for values (must be
+ *                 finite and > 0).
+ * Every byte of the pools outside the written rows is left unchanged.
+ * T == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int32_t* slot_mapping, int32_t T,
+                               int32_t Hkv, int32_t D, int32_t BS, int32_t NB,
+                               pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
+                               float v_scale, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- bytes of scratch pa_decode needs for this
+ * shape.  Same arguments as pa_decode (partition_tokens 0 = automatic).
+ * Returns 0 when the call needs no workspace, and (size_t)-1 when the
+ * arguments are invalid.
+ */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_context_len, int32_t window,
+                                 int32_t partition_tokens);
+
+/*
+ * pa_decode -- one query token per sequence attends over its cached tokens.
+ *
+ * out             [B][Hq][D] act_dtype, written.
+ * query           [B][Hq][D] act_dtype.
+ * block_tables    [B][MBPS] int32: logical block j of sequence b lives in
+ *                 physical block block_tables[b*MBPS + j].
+ * context_lens    [B] int32: tokens of sequence b, the decoded token included
+ *                 (write it with pa_reshape_and_cache first).
+ * window == 0     full cache: rows 0..L-1 with L = context_lens[b].
+ * window  > 0     rolling buffer of `window` rows (window % BS == 0,
+ *                 window <= MBPS*BS); rows 0..min(L, window)-1 are read, in
+ *                 any order (softmax does not depend on key order).
+ * max_context_len host-side upper bound of context_lens (sizes the split).
+ * softmax_scale   multiplies q.k before the softmax.
+ * k_scale,v_scale dequantisation scales of an E4M3 cache (ignored otherwise).
+ * partition_tokens tokens per split-context partition, a multiple of BS; 0
+ *                 lets the library choose.  Results do not depend on it
+ *                 beyond rounding.
+ * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
+ *                 (may be NULL when that is 0).
+ * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV
+ * head h / (Hq/Hkv); an empty context gives zeros.  Caller contract: table
+ * entries read (logical blocks < ceil(L/BS)) lie in [0, NB);
+ * context_lens[b] <= max_context_len and (window == 0) <= MBPS*BS.
+ */
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                    int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                    float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                    float k_scale, float v_scale, int32_t window,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * pa_prefill_chunk -- causal attention of a chunk of new tokens per sequence
+ * over everything cached for it (shared prefix blocks included).
+ *
+ * out, query      [total_q][Hq][D] act_dtype, sequences packed back to back.
+ * cu_q_lens       [B+1] int32 prefix sums of the chunk lengths C_b.
+ * context_lens    [B] int32: cached tokens of sequence b, chunk included (the
+ *                 chunk must already be written with pa_reshape_and_cache).
+ * Query j of sequence b sits at absolute position context_lens[b] - C_b + j
+ * and attends to positions 0 .. that position.
+ * max_chunk_len   host-side upper bound of C_b (sizes the grid).
+ * Caller contract: C_b <= context_lens[b]; table entries for logical blocks
+ * < ceil(context_lens[b]/BS) lie in [0, NB).
+ */
+pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_lens,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                           int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                           pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
+                           float v_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

@@ -1,0 +1,58 @@
+// launch.hpp -- internal interface between the C ABI (pa_api.cpp) and the
+// kernel translation units.  Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct CacheWriteArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const int32_t* slot_mapping;
+  int T, Hkv, D, BS;
+  int act, cache;  // Fmt codes
+  float k_scale, v_scale;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int B, Hkv, G, D, MBPS, window, part_tok, NP;
+  int act, cache;  // Fmt codes
+  float softmax_scale, k_scale, v_scale;
+  float* ws_m;  // [B*Hq*NP]
+  float* ws_l;  // [B*Hq*NP]
+  float* ws_o;  // [B*Hq*NP*D]
+};
+
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  const int32_t* cu_q_lens;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int B, Hq, Hkv, D, MBPS, max_chunk;
+  int act, cache;
+  float softmax_scale, k_scale, v_scale;
+};
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+
+bool decode_supported(int D, int G, int act, int cache);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+bool prefill_supported(int D, int G, int act, int cache);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace pa

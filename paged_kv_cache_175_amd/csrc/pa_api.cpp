@@ -1,0 +1,280 @@
+// pa_api.cpp -- the C ABI declared in include/pa.h: argument checks, the
+// split-context plan and workspace layout, and dispatch to the kernels.
+//
+// Nothing here allocates device memory or synchronises; every launch goes to
+// the caller's stream.  All host-visible arguments are checked before the
+// first launch, so an error status means nothing ran.
+
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+pa_status fail(pa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status fail(pa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pa_status ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+pa_status hip_fail(hipError_t e, const char* where) {
+  return fail(PA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int fmt_of(pa_dtype d) { return static_cast<int>(d); }
+
+bool act_ok(pa_dtype a) { return a == PA_F16 || a == PA_BF16; }
+
+bool cache_ok(pa_dtype act, pa_dtype cache) { return cache == act || cache == PA_F8E4M3; }
+
+size_t elem_bytes(pa_dtype d) { return d == PA_F8E4M3 ? 1 : 2; }
+
+constexpr int kBlock = 32;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Split-context plan: tokens per partition and the number of partitions for
+// the longest sequence.  Partitions are whole pages.  The automatic choice
+// starts at 4 pages and doubles while the launch would exceed ~4096 waves,
+// which keeps every CU of the MI355X (256 CUs) busy with several waves while
+// bounding the partial-result traffic to a few percent of the K/V stream.
+struct Plan {
+  int part_tok;
+  int NP;
+};
+
+bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, Plan* p) {
+  int L = max_len;
+  if (window > 0 && window < L) L = window;
+  if (L < 1) L = 1;
+  int part = partition_tokens;
+  if (part == 0) {
+    const long long pages = (L + kBlock - 1) / kBlock;
+    long long pp = 4;
+    while (pp < pages && (long long)B * Hkv * ((pages + pp - 1) / pp) > 4096) pp *= 2;
+    part = (int)(pp * kBlock);
+  }
+  if (part <= 0 || part % kBlock != 0) return false;
+  p->part_tok = part;
+  p->NP = (L + part - 1) / part;
+  return true;
+}
+
+size_t workspace_for(int B, int Hq, int D, const Plan& p) {
+  if (p.NP <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * p.NP;
+  return 2 * round_up(rows * sizeof(float), kAlign) + round_up(rows * D * sizeof(float), kAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID: return "PA_ERR_INVALID";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int32_t* slot_mapping, int32_t T,
+                               int32_t Hkv, int32_t D, int32_t BS, int32_t NB,
+                               pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
+                               float v_scale, void* stream) {
+  if (T < 0) return fail(PA_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (Hkv < 1 || D < 1 || NB < 1 || BS < 1)
+    return fail(PA_ERR_INVALID, "Hkv, D, BS and NB must be positive");
+  if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
+  if (D % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if ((long long)NB * BS >= (1LL << 31)) return fail(PA_ERR_INVALID, "NB*BS must be < 2^31");
+  if (cache_dtype == PA_F8E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_INVALID, "E4M3 scales must be finite and > 0");
+  if (T == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16))
+    return fail(PA_ERR_INVALID, "key/value must be 16-byte aligned");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
+    return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
+  pa::CacheWriteArgs a{key,  value, key_cache, value_cache, slot_mapping, T,
+                       Hkv,  D,     BS,        fmt_of(act_dtype), fmt_of(cache_dtype),
+                       k_scale, v_scale};
+  hipError_t e = pa::launch_cache_write(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
+  return ok();
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_context_len, int32_t window,
+                                 int32_t partition_tokens) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || max_context_len < 0 || window < 0 ||
+      partition_tokens < 0)
+    return (size_t)-1;
+  Plan p;
+  if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, &p)) return (size_t)-1;
+  return workspace_for(B, Hq, D, p);
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                    int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                    float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                    float k_scale, float v_scale, int32_t window,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || MBPS < 1 || max_context_len < 0)
+    return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_context_len out of range");
+  if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
+  const int G = Hq / Hkv;
+  if (!pa::decode_supported(D, G, fmt_of(act_dtype), fmt_of(cache_dtype)))
+    return fail(PA_ERR_UNSUPPORTED, "decode supports head_dim 64/128 and Hq/Hkv in {1,2,4,8}");
+  if (!std::isfinite(softmax_scale)) return fail(PA_ERR_INVALID, "softmax_scale must be finite");
+  if (cache_dtype == PA_F8E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_INVALID, "E4M3 scales must be finite and > 0");
+  if (window < 0) return fail(PA_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && (window % BS != 0 || window > (long long)MBPS * BS))
+    return fail(PA_ERR_INVALID, "window must be a multiple of block_size and <= MBPS*block_size");
+  if (window == 0 && max_context_len > (long long)MBPS * BS)
+    return fail(PA_ERR_INVALID, "max_context_len exceeds MBPS*block_size");
+  if (partition_tokens < 0 || partition_tokens % BS != 0)
+    return fail(PA_ERR_INVALID, "partition_tokens must be a non-negative multiple of block_size");
+  if (B == 0) return ok();
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16))
+    return fail(PA_ERR_INVALID, "out/query must be 16-byte aligned");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
+    return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
+  if ((long long)B * Hq > 0x7fffffffLL / D) return fail(PA_ERR_UNSUPPORTED, "B*Hq*D too large");
+  Plan p;
+  if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, &p))
+    return fail(PA_ERR_INVALID, "bad partition size");
+  if (p.NP > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", p.NP);
+  const size_t need = workspace_for(B, Hq, D, p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (need > 0 && !aligned(workspace, kAlign))
+    return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.D = D;
+  a.MBPS = MBPS;
+  a.window = window;
+  a.part_tok = p.part_tok;
+  a.NP = p.NP;
+  a.act = fmt_of(act_dtype);
+  a.cache = fmt_of(cache_dtype);
+  a.softmax_scale = softmax_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if (need > 0) {
+    const size_t rows = (size_t)B * Hq * p.NP;
+    char* w = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(w);
+    a.ws_l = reinterpret_cast<float*>(w + round_up(rows * sizeof(float), kAlign));
+    a.ws_o = reinterpret_cast<float*>(w + 2 * round_up(rows * sizeof(float), kAlign));
+  }
+  hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_lens,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                           int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                           pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
+                           float v_scale, void* stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || MBPS < 1 || max_chunk_len < 0)
+    return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_chunk_len out of range");
+  if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
+  if (!pa::prefill_supported(D, Hq / Hkv, fmt_of(act_dtype), fmt_of(cache_dtype)))
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports head_dim 64/96/128 and Hq/Hkv <= 16");
+  if (!std::isfinite(softmax_scale)) return fail(PA_ERR_INVALID, "softmax_scale must be finite");
+  if (cache_dtype == PA_F8E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_INVALID, "E4M3 scales must be finite and > 0");
+  if (B == 0 || max_chunk_len == 0) return ok();
+  if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16))
+    return fail(PA_ERR_INVALID, "out/query must be 16-byte aligned");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
+    return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
+  if ((long long)B > 65535 || Hq > 65535) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.query = query;
+  a.cu_q_lens = cu_q_lens;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.MBPS = MBPS;
+  a.max_chunk = max_chunk_len;
+  a.act = fmt_of(act_dtype);
+  a.cache = fmt_of(cache_dtype);
+  a.softmax_scale = softmax_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+"""Python binding of the paged KV-cache ops (thin marshalling over the C ABI).
+
+Tensors are torch tensors on the GPU; torch provides device memory and the
+current stream, nothing else.  Every op runs in the HIP kernels of
+``libpagedkv.so``; there is no fallback path.
+
+Cache dtypes follow the page "PagedAttention in mistral.rs", section "KV
+Cache Quantization": ``"auto"`` stores the activation dtype, ``"f8e4m3"``
+stores E4M3 codes (held in ``torch.uint8`` tensors) with per-tensor fp32
+scales for K and V.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PagedKVError  # noqa: F401  (re-export)
+
+_ACT = {torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
+
+
+def _act_code(t: torch.Tensor) -> int:
+    try:
+        return _ACT[t.dtype]
+    except KeyError:
+        raise TypeError(f"activation dtype must be float16 or bfloat16, got {t.dtype}") from None
+
+
+def _cache_code(cache: torch.Tensor, act: torch.dtype) -> int:
+    if cache.dtype == torch.uint8 or cache.dtype == getattr(torch, "float8_e4m3fn", None):
+        return _lib.PA_F8E4M3
+    if cache.dtype != act:
+        raise TypeError(f"cache dtype {cache.dtype} must equal the activation dtype {act} "
+                        "or be uint8 (E4M3 codes)")
+    return _ACT[act]
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _i32(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise TypeError(f"index tensors must be int32, got {t.dtype}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def cache_dtype_name(cache: torch.Tensor) -> str:
+    return "f8e4m3" if cache.dtype in (torch.uint8,) else "auto"
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Write ``key``/``value`` ``[T, Hkv, D]`` into the pools at ``slot_mapping``.
+
+    Pools are ``[NB, Hkv, BS, D]``; a negative slot skips its token.
+    """
+    _dev(key, value, key_cache, value_cache, slot_mapping)
+    _i32(slot_mapping)
+    if key.shape != value.shape or key.dim() != 3:
+        raise ValueError("key and value must both be [T, Hkv, D]")
+    T, Hkv, D = key.shape
+    if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
+        raise ValueError("caches must both be [NB, Hkv, BS, D]")
+    NB, Hc, BS, Dc = key_cache.shape
+    if (Hc, Dc) != (Hkv, D) or slot_mapping.numel() != T:
+        raise ValueError("shape mismatch between tokens, caches and slot_mapping")
+    act = _act_code(key)
+    cache = _cache_code(key_cache, key.dtype)
+    lib = _lib.load()
+    _lib.check(lib.pa_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, Hkv, D, BS, NB, act, cache, float(k_scale), float(v_scale),
+        _stream()))
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: int,
+                           window: int = 0, partition_tokens: int = 0) -> int:
+    n = _lib.load().pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window,
+                                              partition_tokens)
+    if n == (1 << 64) - 1:
+        raise PagedKVError(_lib.PA_ERR_INVALID, "invalid workspace query")
+    return int(n)
+
+
+def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+           softmax_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+           window: int = 0, partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode attention; returns ``out`` ``[B, Hq, D]``.
+
+    ``workspace`` (uint8, >= :func:`decode_workspace_bytes`) is allocated here
+    when not given.
+    """
+    _dev(query, key_cache, value_cache, block_tables, context_lens)
+    _i32(block_tables, context_lens)
+    B, Hq, D = query.shape
+    NB, Hkv, BS, Dc = key_cache.shape
+    if Dc != D or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes do not match the query")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, MBPS] and context_lens [B]")
+    MBPS = block_tables.shape[1]
+    act = _act_code(query)
+    cache = _cache_code(key_cache, query.dtype)
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens)
+    if workspace is None:
+        workspace = alloc_workspace(need, query.device)
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.pa_decode(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+        int(max_context_len), float(softmax_scale), act, cache, float(k_scale),
+        float(v_scale), int(window), int(partition_tokens), ws_ptr, ws_bytes, _stream()))
+    return out
+
+
+def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch.Tensor,
+                  value_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, max_chunk_len: int, softmax_scale: float,
+                  k_scale: float = 1.0, v_scale: float = 1.0,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal chunked prefill over the paged cache; returns ``out`` ``[total_q, Hq, D]``."""
+    _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
+    _i32(cu_q_lens, block_tables, context_lens)
+    total_q, Hq, D = query.shape
+    NB, Hkv, BS, Dc = key_cache.shape
+    B = context_lens.numel()
+    if Dc != D or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes do not match the query")
+    if cu_q_lens.numel() != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_q_lens must be [B+1] and block_tables [B, MBPS]")
+    MBPS = block_tables.shape[1]
+    act = _act_code(query)
+    cache = _cache_code(key_cache, query.dtype)
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    lib = _lib.load()
+    _lib.check(lib.pa_prefill_chunk(
+        out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
+        value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv,
+        D, BS, MBPS, int(max_chunk_len), float(softmax_scale), act, cache, float(k_scale),
+        float(v_scale), _stream()))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Prepared calls: all marshalling done once, so that a tight loop (or a HIP
+# graph capture) pays only the ctypes call.  The returned callables launch on
+# the stream that was current when they were prepared.
+
+
+def prepare_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+                              k_scale: float = 1.0, v_scale: float = 1.0):
+    _dev(key, value, key_cache, value_cache, slot_mapping)
+    _i32(slot_mapping)
+    T, Hkv, D = key.shape
+    NB, _, BS, _ = key_cache.shape
+    lib = _lib.load()
+    args = (key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            slot_mapping.data_ptr(), T, Hkv, D, BS, NB, _act_code(key),
+            _cache_code(key_cache, key.dtype), float(k_scale), float(v_scale), _stream())
+    fn = lib.pa_reshape_and_cache
+
+    def call():
+        _lib.check(fn(*args))
+    return call
+
+
+def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
+                   max_context_len: int, softmax_scale: float, out, workspace=None,
+                   k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
+                   partition_tokens: int = 0):
+    _dev(query, key_cache, value_cache, block_tables, context_lens, out)
+    _i32(block_tables, context_lens)
+    B, Hq, D = query.shape
+    NB, Hkv, BS, _ = key_cache.shape
+    MBPS = block_tables.shape[1]
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise PagedKVError(_lib.PA_ERR_WORKSPACE, f"workspace needs {need} bytes")
+    lib = _lib.load()
+    args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+            int(max_context_len), float(softmax_scale), _act_code(query),
+            _cache_code(key_cache, query.dtype), float(k_scale), float(v_scale), int(window),
+            int(partition_tokens), 0 if workspace is None else workspace.data_ptr(), ws_bytes,
+            _stream())
+    fn = lib.pa_decode
+
+    def call():
+        _lib.check(fn(*args))
+    return call
+
+
+def prepare_prefill_chunk(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens,
+                          max_chunk_len: int, softmax_scale: float, out,
+                          k_scale: float = 1.0, v_scale: float = 1.0):
+    _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens, out)
+    _i32(cu_q_lens, block_tables, context_lens)
+    total_q, Hq, D = query.shape
+    NB, Hkv, BS, _ = key_cache.shape
+    B = context_lens.numel()
+    MBPS = block_tables.shape[1]
+    lib = _lib.load()
+    args = (out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
+            value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv,
+            D, BS, MBPS, int(max_chunk_len), float(softmax_scale), _act_code(query),
+            _cache_code(key_cache, query.dtype), float(k_scale), float(v_scale), _stream())
+    fn = lib.pa_prefill_chunk
+
+    def call():
+        _lib.check(fn(*args))
+    return call

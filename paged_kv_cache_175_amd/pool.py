@@ -1,0 +1,238 @@
+"""Host-side block manager: pool sizing, block allocation, block tables and
+slot mappings (full cache and rolling buffer), shared prefix blocks.
+
+What the pages fix ("PagedAttention in mistral.rs"):
+
+* the pool has two inputs, a GPU memory budget in MB and a block size in
+  tokens (default 32); the budget may also be a fraction of GPU memory or,
+  in the Rust API, a context size in tokens;
+* the pool is allocated up front, which is why an oversized budget shows up
+  as an out-of-memory error;
+* an F8E4M3 cache about halves the memory of an FP16 one;
+* prefix caching reuses cached prefix KV across requests.
+
+"Rolling buffer cache" (llama.cpp discussion 3581, opening post): with a
+window of W tokens the cache is a ring of W rows; position i goes to row
+i mod W, overwriting older positions.
+
+Sizing reading (the pages give no formula): one block of one layer holds K
+and V of ``block_size`` tokens for every KV head; the block count is the
+budget divided by (block bytes x layers), rounded down, with MB read as MiB.
+
+Everything here is plain integer bookkeeping on the host.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+DEFAULT_BLOCK_SIZE = 32
+CACHE_DTYPES = ("auto", "f8e4m3")
+MIB = 1 << 20
+
+
+@dataclass(frozen=True)
+class PagedKVConfig:
+    """Pool configuration, mirroring the pages' knobs.
+
+    Exactly one of ``gpu_mem_mb`` (budget in MiB), ``gpu_mem_usage``
+    (fraction of free device memory) or ``context_size`` (tokens per
+    sequence-slot of the pool) sets the size.
+    """
+
+    block_size: int = DEFAULT_BLOCK_SIZE
+    cache_dtype: str = "auto"
+    gpu_mem_mb: Optional[int] = None
+    gpu_mem_usage: Optional[float] = None
+    context_size: Optional[int] = None
+    window: int = 0
+
+    def __post_init__(self):
+        if self.block_size <= 0:
+            raise ValueError("block_size must be positive")
+        if self.cache_dtype not in CACHE_DTYPES:
+            raise ValueError(f"cache_dtype must be one of {CACHE_DTYPES}")
+        given = [x is not None for x in (self.gpu_mem_mb, self.gpu_mem_usage, self.context_size)]
+        if sum(given) > 1:
+            raise ValueError("give at most one of gpu_mem_mb, gpu_mem_usage, context_size")
+        if self.gpu_mem_usage is not None and not 0 < self.gpu_mem_usage <= 1:
+            raise ValueError("gpu_mem_usage must be in (0, 1]")
+        if self.window < 0 or (self.window and self.window % self.block_size):
+            raise ValueError("window must be a non-negative multiple of block_size")
+
+
+def element_bytes(cache_dtype: str, act_bytes: int = 2) -> int:
+    return 1 if cache_dtype == "f8e4m3" else act_bytes
+
+
+def bytes_per_block(cfg: PagedKVConfig, num_kv_heads: int, head_dim: int,
+                    num_layers: int = 1, act_bytes: int = 2) -> int:
+    """Device bytes of one block across all layers, K and V together."""
+    return (2 * cfg.block_size * num_kv_heads * head_dim
+            * element_bytes(cfg.cache_dtype, act_bytes) * num_layers)
+
+
+def num_blocks(cfg: PagedKVConfig, num_kv_heads: int, head_dim: int, num_layers: int = 1,
+               act_bytes: int = 2, free_bytes: Optional[int] = None) -> int:
+    """Blocks the configured budget buys (same count in every layer)."""
+    per = bytes_per_block(cfg, num_kv_heads, head_dim, num_layers, act_bytes)
+    if cfg.context_size is not None:
+        return math.ceil(cfg.context_size / cfg.block_size)
+    if cfg.gpu_mem_mb is not None:
+        return (cfg.gpu_mem_mb * MIB) // per
+    if cfg.gpu_mem_usage is not None:
+        if free_bytes is None:
+            raise ValueError("gpu_mem_usage needs the free device memory")
+        return int(cfg.gpu_mem_usage * free_bytes) // per
+    raise ValueError("no pool size configured")
+
+
+class OutOfBlocks(RuntimeError):
+    pass
+
+
+class BlockAllocator:
+    """Free list of physical block ids with reference counts.
+
+    A block shared by several sequences (a cached prefix) is freed when its
+    last holder releases it.
+    """
+
+    def __init__(self, num_blocks: int, order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0:
+            raise ValueError("num_blocks must be positive")
+        self.num_blocks = num_blocks
+        ids = list(range(num_blocks)) if order is None else [int(i) for i in order]
+        if sorted(ids) != list(range(num_blocks)):
+            raise ValueError("order must be a permutation of the block ids")
+        self._free: List[int] = ids[::-1]          # pop() hands out ids in `order`
+        self._ref = np.zeros(num_blocks, dtype=np.int64)
+
+    @property
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def allocate(self) -> int:
+        if not self._free:
+            raise OutOfBlocks("KV block pool exhausted")
+        blk = self._free.pop()
+        self._ref[blk] = 1
+        return blk
+
+    def share(self, blk: int) -> int:
+        if self._ref[blk] <= 0:
+            raise ValueError(f"block {blk} is not allocated")
+        self._ref[blk] += 1
+        return blk
+
+    def release(self, blk: int) -> None:
+        if self._ref[blk] <= 0:
+            raise ValueError(f"block {blk} is not allocated")
+        self._ref[blk] -= 1
+        if self._ref[blk] == 0:
+            self._free.append(blk)
+
+    def refcount(self, blk: int) -> int:
+        return int(self._ref[blk])
+
+
+class SequenceBlocks:
+    """Blocks of one sequence: logical block j -> physical block ``blocks[j]``.
+
+    Full cache: position p lives in logical row p.  Rolling buffer (window W):
+    position p lives in ring row p mod W, and the sequence owns exactly W/BS
+    blocks once it has reached W tokens.
+    """
+
+    def __init__(self, allocator: BlockAllocator, block_size: int, window: int = 0):
+        self.alloc = allocator
+        self.bs = block_size
+        self.window = window
+        self.blocks: List[int] = []
+        self.num_tokens = 0
+
+    def _row(self, pos: int) -> int:
+        return pos % self.window if self.window else pos
+
+    def _ensure_row(self, row: int) -> None:
+        while row // self.bs >= len(self.blocks):
+            self.blocks.append(self.alloc.allocate())
+
+    def slot(self, pos: int) -> int:
+        """Flat cache slot of absolute position ``pos`` (must be resident)."""
+        row = self._row(pos)
+        return self.blocks[row // self.bs] * self.bs + row % self.bs
+
+    def append(self, n: int = 1) -> List[int]:
+        """Reserve the next ``n`` positions; returns their slots."""
+        out = []
+        for _ in range(n):
+            pos = self.num_tokens
+            self._ensure_row(self._row(pos))
+            self.num_tokens += 1
+            out.append(self.slot(pos))
+        return out
+
+    def share_prefix(self, other: "SequenceBlocks", num_tokens: int) -> None:
+        """Start this (empty) sequence with ``other``'s first ``num_tokens``
+        positions, sharing whole blocks (``num_tokens`` must be whole blocks)."""
+        if self.blocks or self.num_tokens:
+            raise ValueError("share_prefix needs an empty sequence")
+        if self.window or other.window:
+            raise ValueError("shared prefixes are for full caches")
+        if num_tokens % self.bs or num_tokens > other.num_tokens:
+            raise ValueError("prefix must be whole, resident blocks")
+        for blk in other.blocks[: num_tokens // self.bs]:
+            self.blocks.append(self.alloc.share(blk))
+        self.num_tokens = num_tokens
+
+    def context_len(self) -> int:
+        return self.num_tokens
+
+    def release(self) -> None:
+        for blk in self.blocks:
+            self.alloc.release(blk)
+        self.blocks = []
+        self.num_tokens = 0
+
+
+def block_table_array(seqs: Sequence[SequenceBlocks], max_blocks: Optional[int] = None,
+                      pad: int = 0) -> np.ndarray:
+    """``[B, MBPS]`` int32 block tables, padded with ``pad``."""
+    mbps = max_blocks or max(1, max(len(s.blocks) for s in seqs))
+    bt = np.full((len(seqs), mbps), pad, dtype=np.int32)
+    for b, s in enumerate(seqs):
+        if len(s.blocks) > mbps:
+            raise ValueError("sequence has more blocks than max_blocks")
+        bt[b, : len(s.blocks)] = s.blocks
+    return bt
+
+
+def slots_from_table(block_table_row: np.ndarray, positions: np.ndarray, block_size: int,
+                     window: int = 0) -> np.ndarray:
+    """Vectorised slot mapping of absolute positions through one table row."""
+    pos = np.asarray(positions, dtype=np.int64)
+    rows = pos % window if window else pos
+    phys = np.asarray(block_table_row, dtype=np.int64)[rows // block_size]
+    return (phys * block_size + rows % block_size).astype(np.int32)
+
+
+def describe(cfg: PagedKVConfig, num_layers: int, cached_tokens: int) -> Dict[str, object]:
+    """Cache description in the shape of a trace record (dtype, block size,
+    page key, prefix cache, counts), as the libmir-metal trace builder reports."""
+    return {
+        "dtype": "f8e4m3" if cfg.cache_dtype == "f8e4m3" else "auto",
+        "quant_mode": "per-tensor fp32 scale" if cfg.cache_dtype == "f8e4m3" else "none",
+        "decode_attention": "paged split-context decode (HIP, gfx950)",
+        "block_size": cfg.block_size,
+        "physical_page_key": "layer + sequence; head-major pages"
+        + ("; rolling ring" if cfg.window else ""),
+        "paged_attention": True,
+        "entry_count": num_layers,
+        "cached_tokens": cached_tokens,
+        "resident_token_slots": cached_tokens,
+    }

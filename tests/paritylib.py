@@ -1,0 +1,188 @@
+"""Shared helpers of the GPU parity tests: run a workload through the HIP path
+and through the oracle, each with its own code, from the same seeded inputs.
+
+HIP side: slots from the product's host block manager
+(``paged_kv_cache_175_amd.pool``), writes with ``ops.reshape_and_cache``,
+attention with ``ops.decode`` / ``ops.prefill_chunk``.
+Oracle side: slots from ``oracle.cache.slot_of`` / ``oracle.pool.ring_index``,
+writes with ``oracle.cache.reshape_and_cache``, attention with
+``oracle.attention``.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attention as o_attn
+from oracle import cache as o_cache
+from oracle import pool as o_pool
+from paged_kv_cache_175_amd import ops, pool
+from paged_kv_cache_175_amd.workloads import DecodeWorkload, PrefillWorkload
+
+NAN16 = {"bf16": 0x7FC0, "f16": 0x7E00}
+NAN_E4M3 = 0x7F
+TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16}
+TOL = {"bf16": 1e-2, "f16": 1e-2, "e4m3": 2e-2}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------- HIP side
+
+
+def _act_tensor(bits: np.ndarray, act: str, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_ACT[act])
+    return t.to(device)
+
+
+def gpu_pools(wl, device="cuda"):
+    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
+    if wl.cache == "e4m3":
+        kc = torch.full(shape, NAN_E4M3, dtype=torch.uint8, device=device)
+    else:
+        kc = torch.full(shape, NAN16[wl.cache], dtype=torch.int16, device=device)
+        kc = kc.view(TORCH_ACT[wl.cache])
+    return kc, kc.clone()
+
+
+def _gpu_write(wl, kc, vc, k_bits, v_bits, slots, device="cuda"):
+    if len(slots) == 0:
+        return
+    ops.reshape_and_cache(_act_tensor(k_bits, wl.act, device), _act_tensor(v_bits, wl.act, device),
+                          kc, vc, torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(device),
+                          wl.k_scale, wl.v_scale)
+
+
+def hip_decode_setup(wl: DecodeWorkload, device="cuda"):
+    """Pools written through the HIP writer: cached tokens, then the new ones."""
+    kc, vc = gpu_pools(wl, device)
+    ks, vs, sl = [], [], []
+    for b in range(wl.B):
+        n = wl.cached_k[b].shape[0]
+        if n:
+            pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+            sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+            ks.append(wl.cached_k[b])
+            vs.append(wl.cached_v[b])
+    if sl:
+        _gpu_write(wl, kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(sl), device)
+    new_slots = np.array([pool.slots_from_table(wl.block_tables[b], [wl.new_pos[b]], wl.BS,
+                                                wl.window)[0] for b in range(wl.B)], np.int32)
+    _gpu_write(wl, kc, vc, wl.new_k, wl.new_v, new_slots, device)
+    return kc, vc
+
+
+def hip_decode(wl: DecodeWorkload, kc, vc, partition_tokens=0, device="cuda"):
+    q = _act_tensor(wl.query, wl.act, device)
+    bt = torch.from_numpy(wl.block_tables).to(device)
+    cl = torch.from_numpy(wl.context_lens).to(device)
+    out = ops.decode(q, kc, vc, bt, cl, int(wl.context_lens.max(initial=0)), wl.scale,
+                     wl.k_scale, wl.v_scale, wl.window, partition_tokens)
+    return out
+
+
+def hip_prefill_setup(wl: PrefillWorkload, device="cuda"):
+    kc, vc = gpu_pools(wl, device)
+    # Shared prefix once (its blocks are the same in every table).
+    pos = np.arange(wl.prefix_len)
+    sl = pool.slots_from_table(wl.block_tables[0], pos, wl.BS)
+    _gpu_write(wl, kc, vc, wl.prefix_k, wl.prefix_v, sl, device)
+    # Then every chunk into its private blocks.
+    ks, vs, sls = [], [], []
+    for b in range(wl.B):
+        C = int(wl.chunk_lens[b])
+        pos = np.arange(wl.prefix_len, wl.prefix_len + C)
+        sls.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS))
+        ks.append(wl.chunk_k[b])
+        vs.append(wl.chunk_v[b])
+    _gpu_write(wl, kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(sls), device)
+    return kc, vc
+
+
+def hip_prefill(wl: PrefillWorkload, kc, vc, device="cuda"):
+    q = _act_tensor(wl.query, wl.act, device)
+    return ops.prefill_chunk(q, torch.from_numpy(wl.cu_q_lens).to(device), kc, vc,
+                             torch.from_numpy(wl.block_tables).to(device),
+                             torch.from_numpy(wl.context_lens).to(device),
+                             int(wl.chunk_lens.max()), wl.scale, wl.k_scale, wl.v_scale)
+
+
+def pool_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# --------------------------------------------------------------------------- oracle side
+
+
+def oracle_pools(wl):
+    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
+    if wl.cache == "e4m3":
+        return np.full(shape, NAN_E4M3, np.uint8), np.full(shape, NAN_E4M3, np.uint8)
+    return np.full(shape, NAN16[wl.cache], np.uint16), np.full(shape, NAN16[wl.cache], np.uint16)
+
+
+def _oracle_row(wl, pos):
+    return o_pool.ring_index(int(pos), wl.window) if wl.window else int(pos)
+
+
+def oracle_decode_setup(wl: DecodeWorkload, seqs=None):
+    kc, vc = oracle_pools(wl)
+    seqs = range(wl.B) if seqs is None else seqs
+    for b in seqs:
+        n = wl.cached_k[b].shape[0]
+        slots = [o_cache.slot_of(wl.block_tables[b], _oracle_row(wl, wl.cached_pos0[b] + t), wl.BS)
+                 for t in range(n)]
+        o_cache.reshape_and_cache(wl.cached_k[b], wl.cached_v[b], kc, vc, np.array(slots, np.int64),
+                                  wl.act, wl.cache, wl.k_scale, wl.v_scale)
+    for b in seqs:
+        s = o_cache.slot_of(wl.block_tables[b], _oracle_row(wl, wl.new_pos[b]), wl.BS)
+        o_cache.reshape_and_cache(wl.new_k[b:b + 1], wl.new_v[b:b + 1], kc, vc, np.array([s]),
+                                  wl.act, wl.cache, wl.k_scale, wl.v_scale)
+    return kc, vc
+
+
+def oracle_decode(wl: DecodeWorkload, kc, vc, seqs=None):
+    seqs = list(range(wl.B)) if seqs is None else list(seqs)
+    return o_attn.decode(wl.query[seqs], wl.act, kc, vc, wl.cache, wl.block_tables[seqs],
+                         wl.context_lens[seqs], wl.scale, wl.k_scale, wl.v_scale, wl.window)
+
+
+def oracle_prefill_setup(wl: PrefillWorkload):
+    kc, vc = oracle_pools(wl)
+    slots = [o_cache.slot_of(wl.block_tables[0], t, wl.BS) for t in range(wl.prefix_len)]
+    o_cache.reshape_and_cache(wl.prefix_k, wl.prefix_v, kc, vc, np.array(slots, np.int64),
+                              wl.act, wl.cache, wl.k_scale, wl.v_scale)
+    for b in range(wl.B):
+        C = int(wl.chunk_lens[b])
+        slots = [o_cache.slot_of(wl.block_tables[b], wl.prefix_len + t, wl.BS) for t in range(C)]
+        o_cache.reshape_and_cache(wl.chunk_k[b], wl.chunk_v[b], kc, vc, np.array(slots, np.int64),
+                                  wl.act, wl.cache, wl.k_scale, wl.v_scale)
+    return kc, vc
+
+
+def oracle_prefill(wl: PrefillWorkload, kc, vc):
+    return o_attn.prefill_chunk(wl.query, wl.act, wl.cu_q_lens, kc, vc, wl.cache,
+                                wl.block_tables, wl.context_lens, wl.scale, wl.k_scale,
+                                wl.v_scale)
+
+
+def max_abs(a: np.ndarray, b: np.ndarray) -> float:
+    if a.size == 0:
+        return 0.0
+    d = np.abs(a - b)
+    if np.isnan(d).any():
+        return float("nan")
+    return float(d.max())
