@@ -16,10 +16,10 @@
  *  - "Rolling buffer cache" (llama.cpp discussion 3581), opening post: with a
  *    sliding window of W tokens the cache is a ring of W rows and position i
  *    lives in row i mod W; pa_decode() with window > 0 reads such a ring.
- *  - same page "PagedAttention in mistral.rs", sections "Prefix caching" and
- *    "FlashAttention V2/V3 + PagedAttention": prompt (prefill) tokens attend
- *    causally over cached blocks that may be shared between sequences;
- *    pa_prefill_chunk() is that causal attention over a block table.
+ *  - same page, the prefix-caching note and section "FlashAttention V2/V3 +
+ *    PagedAttention": prompt (prefill) tokens attend causally over cached
+ *    blocks that may be shared between sequences; pa_prefill_chunk() is that
+ *    causal attention over a block table.
  *  - "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build: the pages are
  *    head-major, which fixes the layout below.
  *
@@ -29,19 +29,24 @@
  *    block_tables, context_lens, cu_q_lens and workspace are DEVICE pointers
  *    owned by the caller.  The library allocates nothing and keeps no state
  *    between calls.
- *  - Cache pools are [num_blocks][num_kv_heads][block_size][head_dim],
- *    row-major; one (block, head) page is a contiguous run of
- *    block_size * head_dim elements.  Activations are row-major.
+ *  - Cache pools are head-major: one (block, KV head) page is a contiguous
+ *    run of block_size * head_dim elements, pages ordered [num_blocks]
+ *    [num_kv_heads].  Inside a page (t = row 0..block_size-1, d = 0..D-1):
+ *      key page   [D/8][block_size][8]  element (t, d) at ((d/8)*BS + t)*8 + d%8
+ *      value page [D][block_size]       element (t, d) at d*BS + t
+ *    (so the key pool is [NB][Hkv][D/8][BS][8] and the value pool
+ *    [NB][Hkv][D][BS]).  Both layouts make the attention kernels' matrix-core
+ *    operands single 16-byte loads.  Activations are row-major.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
  *    stream).  The library never synchronises.
  *  - Errors are returned as pa_status; nothing is thrown and nothing aborts.
  *    Arguments the host can see are checked before anything is launched.
  *    Device data (table entries, lengths, slots) is NOT checked: the caller
  *    contracts below must hold, or the kernels read or write out of bounds.
- *  - Supported now: block_size 32; head_dim 64 or 128 for decode, 64, 96 or
- *    128 for prefill; act dtype PA_F16 or PA_BF16; cache dtype equal to the
- *    act dtype or PA_F8E4M3; Hq/Hkv between 1 and 16 (decode: at most 8).
- *    Anything else returns PA_ERR_UNSUPPORTED.
+ *  - Supported now: block_size 32; head_dim 64, 96 or 128; act dtype PA_F16
+ *    or PA_BF16; cache dtype equal to the act dtype or PA_F8E4M3; Hq/Hkv in
+ *    {1, 2, 4, 8, 16} for decode and 1..16 for prefill.  Anything else
+ *    returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PAGED_KV_PA_H
 #define PAGED_KV_PA_H
@@ -74,7 +79,7 @@ const char* pa_last_error(void);
  *
  * key, value      [T][Hkv][D] in act_dtype.
  * key_cache,
- * value_cache     [NB][Hkv][BS][D] in cache_dtype, updated in place.
+ * value_cache     pools in cache_dtype (layout above), updated in place.
  * slot_mapping    [T] int32.  Token n goes to block slot_mapping[n] / BS,
  *                 row slot_mapping[n] % BS, for every KV head.  A negative
  *                 slot skips the token.  Caller contract: non-negative slots
@@ -120,8 +125,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * softmax_scale   multiplies q.k before the softmax.
  * k_scale,v_scale dequantisation scales of an E4M3 cache (ignored otherwise).
  * partition_tokens tokens per split-context partition, a multiple of BS; 0
- *                 lets the library choose.  Results do not depend on it
- *                 beyond rounding.
+ *                 lets the library choose; values above 64*BS act as 64*BS.
+ *                 Results do not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0).
  * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV

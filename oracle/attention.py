@@ -49,7 +49,7 @@ def decode(query_bits, act_fmt: str, key_cache, value_cache, cache_fmt: str,
            v_scale: float = 1.0, window: int = 0):
     """Paged decode: one query token per sequence.
 
-    query_bits: ``[B, Hq, D]`` activation bits.  Pools ``[NB, Hkv, BS, D]``.
+    query_bits: ``[B, Hq, D]`` activation bits.  Pools as in :mod:`oracle.cache`.
     block_tables: ``[B, MBPS]``; context_lens: ``[B]``.
     window == 0: attend to logical rows 0..L-1 with L = context_lens[b].
     window  > 0: the table addresses a ring of ``window`` rows; attend to ring
@@ -65,8 +65,8 @@ def decode(query_bits, act_fmt: str, key_cache, value_cache, cache_fmt: str,
         L = int(context_lens[b])
         if window > 0:
             L = min(L, window)
-        k = gather_f64(key_cache, block_tables[b], L, cache_fmt, k_scale)
-        v = gather_f64(value_cache, block_tables[b], L, cache_fmt, v_scale)
+        k, v = gather_f64(key_cache, value_cache, block_tables[b], L, cache_fmt, k_scale,
+                          v_scale)
         for h in range(Hq):
             g = h // group
             out[b, h] = softmax_attend(q[b, h], k[:, g, :], v[:, g, :], scale)
@@ -92,8 +92,8 @@ def prefill_chunk(query_bits, act_fmt: str, cu_q_lens, key_cache, value_cache,
         q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
         C = q1 - q0
         ctx = int(context_lens[b])
-        k = gather_f64(key_cache, block_tables[b], ctx, cache_fmt, k_scale)
-        v = gather_f64(value_cache, block_tables[b], ctx, cache_fmt, v_scale)
+        k, v = gather_f64(key_cache, value_cache, block_tables[b], ctx, cache_fmt, k_scale,
+                          v_scale)
         for j in range(C):
             i = ctx - C + j  # absolute position of this query
             for h in range(Hq):

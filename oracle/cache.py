@@ -2,10 +2,18 @@
 
 Test infrastructure only (see the package docstring).
 
-Layout (a reading of the head-major pages named in "libmir-metal 0.2.0,
-src/native/trace/kv.rs", ``fn build``): each cache pool is
-``[num_blocks, num_kv_heads, block_size, head_dim]``, so one (block, head)
-page is a contiguous run of ``block_size * head_dim`` elements.
+Layout.  The pages only say the pages are head-major ("libmir-metal 0.2.0,
+src/native/trace/kv.rs", ``fn build``); the byte layout inside a
+(block, head) page is fixed by the library's ABI, and the oracle stores
+exactly those bytes so that writes can be compared one for one:
+
+* key pool   ``[num_blocks][num_kv_heads][head_dim/8][block_size][8]``:
+  row t, dimension d of a page sits at ``((d // 8) * block_size + t) * 8 + d % 8``;
+* value pool ``[num_blocks][num_kv_heads][head_dim][block_size]``: row t,
+  dimension d sits at ``d * block_size + t`` (the page is stored transposed).
+
+The helpers :func:`put_row` / :func:`get_row` are the only places that know
+this layout; everything else works with logical rows ``[num_kv_heads, D]``.
 
 Element formats, all held as raw bits so that writes can be compared byte for
 byte:
@@ -45,6 +53,38 @@ def storage_dtype(fmt: str):
     return np.uint8 if fmt == "e4m3" else np.uint16
 
 
+def empty_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                fmt: str, fill: int = 0):
+    """Key and value pools in their physical layouts, every element = ``fill``."""
+    if head_dim % 8:
+        raise ValueError("head_dim must be a multiple of 8")
+    dt = storage_dtype(fmt)
+    k = np.full((num_blocks, num_kv_heads, head_dim // 8, block_size, 8), fill, dtype=dt)
+    v = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=dt)
+    return k, v
+
+
+def pool_geometry(key_cache):
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a key pool."""
+    nb, hkv, d8, bs, _ = key_cache.shape
+    return nb, hkv, bs, d8 * 8
+
+
+def put_row(key_cache, value_cache, blk: int, off: int, k_row, v_row) -> None:
+    """Store one token's K and V rows ``[Hkv, D]`` at (block, row)."""
+    hkv, d8 = key_cache.shape[1], key_cache.shape[2]
+    key_cache[blk, :, :, off, :] = np.asarray(k_row).reshape(hkv, d8, 8)
+    value_cache[blk, :, :, off] = np.asarray(v_row)
+
+
+def get_row(key_cache, value_cache, blk: int, off: int):
+    """One token's stored K and V rows ``[Hkv, D]`` at (block, row)."""
+    hkv, d8 = key_cache.shape[1], key_cache.shape[2]
+    k = key_cache[blk, :, :, off, :].reshape(hkv, d8 * 8)
+    v = value_cache[blk, :, :, off]
+    return k, v
+
+
 def slot_of(block_table_row, logical_index: int, block_size: int) -> int:
     """Flat slot holding logical cache index ``logical_index`` of a sequence.
 
@@ -72,35 +112,41 @@ def reshape_and_cache(key_bits, value_bits, key_cache, value_cache, slot_mapping
     """Write tokens into the pools in place.
 
     key_bits, value_bits: ``[T, Hkv, D]`` activation bits.
-    key_cache, value_cache: ``[NB, Hkv, BS, D]`` storage arrays, updated.
+    key_cache, value_cache: pools from :func:`empty_pools`, updated.
     slot_mapping: ``[T]`` ints; ``s >= 0`` writes to block ``s // BS``, row
     ``s % BS``; ``s < 0`` is skipped.
     """
-    bs = key_cache.shape[2]
+    bs = pool_geometry(key_cache)[2]
     slots = np.asarray(slot_mapping).reshape(-1)
     for n, s in enumerate(slots):
         s = int(s)
         if s < 0:
             continue
-        blk, off = s // bs, s % bs
-        key_cache[blk, :, off, :] = encode_tokens(key_bits[n], act_fmt, cache_fmt, k_scale)
-        value_cache[blk, :, off, :] = encode_tokens(value_bits[n], act_fmt, cache_fmt, v_scale)
+        put_row(key_cache, value_cache, s // bs, s % bs,
+                encode_tokens(key_bits[n], act_fmt, cache_fmt, k_scale),
+                encode_tokens(value_bits[n], act_fmt, cache_fmt, v_scale))
 
 
-def gather_f64(cache, block_table_row, length: int, fmt: str, scale: float = 1.0):
-    """Logical rows 0..length-1 of one sequence as fp64 ``[length, Hkv, D]``.
+def gather_f64(key_cache, value_cache, block_table_row, length: int, fmt: str,
+               k_scale: float = 1.0, v_scale: float = 1.0):
+    """Logical rows 0..length-1 of one sequence as fp64 K and V ``[length, Hkv, D]``.
 
     Walks the block table token by token; for E4M3 the code values are
-    multiplied by the scale in fp64.
+    multiplied by the scales in fp64.
     """
-    bs = cache.shape[2]
-    rows = []
+    _, hkv, bs, d = pool_geometry(key_cache)
+    ks, vs = [], []
     for t in range(length):
         phys = int(block_table_row[t // bs])
-        rows.append(cache[phys, :, t % bs, :])
-    if not rows:
-        return np.zeros((0, cache.shape[1], cache.shape[3]), dtype=np.float64)
-    vals = bits_to_f64(np.stack(rows), fmt)
+        k, v = get_row(key_cache, value_cache, phys, t % bs)
+        ks.append(k)
+        vs.append(v)
+    if not ks:
+        z = np.zeros((0, hkv, d), dtype=np.float64)
+        return z, z.copy()
+    kv = bits_to_f64(np.stack(ks), fmt)
+    vv = bits_to_f64(np.stack(vs), fmt)
     if fmt == "e4m3":
-        vals = vals * np.float64(np.float32(scale))
-    return vals
+        kv = kv * np.float64(np.float32(k_scale))
+        vv = vv * np.float64(np.float32(v_scale))
+    return kv, vv

@@ -1,9 +1,18 @@
-// common.hpp -- element formats, E4M3 codec and wave helpers for gfx950.
+// common.hpp -- element formats, page layout, E4M3 codec and wave helpers
+// shared by the gfx950 kernels.
 //
 // Element formats of the paged cache ("PagedAttention in mistral.rs",
 // section "KV Cache Quantization"): the cache holds either the activation
 // type (fp16 / bf16) or FP8 E4M3.  E4M3 here is the OCP "FN" variant: bias 7,
 // largest finite magnitude 448, no infinities, NaN = S.1111.111.
+//
+// Page layout (one (block, KV head) page of BS = 32 tokens, head-major as in
+// "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build):
+//   K page [D/8][BS][8]: element (t, d) at ((d/8)*BS + t)*8 + d%8
+//   V page [D][BS]     : element (t, d) at d*BS + t   (stored transposed)
+// With these layouts both MFMA B operands of decode (K for S = Q K^T with the
+// head dimension as the reduction axis, V for O = P V with tokens as the
+// reduction axis) are single 16-byte (8-byte for E4M3) loads per lane.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,12 +22,20 @@ namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum Fmt { FMT_F16 = 0, FMT_BF16 = 1, FMT_E4M3 = 2 };
+
+constexpr int kPage = 32;  // tokens per block (page)
+
+// Offsets (in elements) inside one (block, head) page.
+__device__ __forceinline__ int k_page_off(int t, int d) { return ((d >> 3) * kPage + t) * 8 + (d & 7); }
+__device__ __forceinline__ int v_page_off(int t, int d) { return d * kPage + t; }
 
 // ---------------------------------------------------------------------------
 // 16-bit activation formats <-> fp32.
@@ -66,6 +83,35 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return f32_to_16<F>(a) | (f32_to_16<F>(b) << 16);
 }
 
+// fp32 -> 16-bit with the hardware converter (round to nearest even); for
+// finite values only (softmax probabilities).
+template <int F>
+__device__ __forceinline__ uint16_t cvt16(float x);
+template <>
+__device__ __forceinline__ uint16_t cvt16<FMT_BF16>(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+template <>
+__device__ __forceinline__ uint16_t cvt16<FMT_F16>(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources: a descriptor over [base, base + bytes) for buffer loads.
+// Loads at offsets past `bytes` return zero instead of touching memory.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+
 // ---------------------------------------------------------------------------
 // E4M3 encode: code of t = fp32(x) / fp32(scale).
 //
@@ -99,31 +145,118 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x, float scale) {
   return e4m3_encode_t(__fdiv_rn(x, scale));
 }
 
-// E4M3 -> fp32 for the two codes in the low (HI = false) or high half of w.  Every E4M3
-// value is exactly representable in fp32, bf16 and fp16.
+// E4M3 -> fp32 for the two codes in the low (HI = false) or high half of w.
+// Every E4M3 value is exactly representable in fp32, bf16 and fp16.
 template <bool HI>
 __device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
 }
 
+// E4M3 -> two packed 16-bit values of format F (exact; unit scale).
+template <int F, bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_16(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t e4m3x2_to_16<FMT_BF16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t e4m3x2_to_16<FMT_BF16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t e4m3x2_to_16<FMT_F16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t e4m3x2_to_16<FMT_F16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+// Eight E4M3 codes (two words) -> eight 16-bit values (four words).
+template <int F>
+__device__ __forceinline__ u32x4 e4m3x8_to_16(u32x2 c) {
+  return u32x4{e4m3x2_to_16<F, false>(c[0]), e4m3x2_to_16<F, true>(c[0]),
+               e4m3x2_to_16<F, false>(c[1]), e4m3x2_to_16<F, true>(c[1])};
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers (64 lanes).
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
+// DPP lane permutations inside a row of 16 lanes.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
 
-// Max / sum over the 16 lanes of a row (lanes 16r .. 16r+15), by xor-shuffles
-// that stay inside the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// max(v, v of the DPP-selected lane) as one v_max_f32_dpp.  Written as
+// inline assembly because the compiler otherwise splits it into a DPP move,
+// a NaN-quieting max and the max.  The leading s_nop covers the two wait
+// states a DPP read needs after a VALU write of its source; the inputs here
+// are finite or -inf, never NaN.
+#define PA_DPP_MAX(v, CTRL)                                                                  \
+  do {                                                                                       \
+    float r_;                                                                                \
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf" \
+                 : "=&v"(r_)                                                                 \
+                 : "v"(v));                                                                  \
+    v = r_;                                                                                  \
+  } while (0)
+
+// Max / sum over the 16 lanes of a row (lanes 16r .. 16r+15), all in DPP:
+// swap neighbours, swap pairs, mirror halves of 8, mirror the row of 16.
 __device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  PA_DPP_MAX(v, "quad_perm:[1,0,3,2]");
+  PA_DPP_MAX(v, "quad_perm:[2,3,0,1]");
+  PA_DPP_MAX(v, "row_half_mirror");
+  PA_DPP_MAX(v, "row_mirror");
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
   return v;
 }
 
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Max / sum over all 64 lanes, result uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// MFMA 16x16x32 with 16-bit inputs, fp32 accumulate.
+template <int AF>
+struct Mfma;
+template <>
+struct Mfma<FMT_BF16> {
+  typedef bf16x8 vec;
+  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<FMT_F16> {
+  typedef f16x8 vec;
+  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 }  // namespace pa

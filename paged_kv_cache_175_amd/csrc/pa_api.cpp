@@ -49,12 +49,13 @@ bool cache_ok(pa_dtype act, pa_dtype cache) { return cache == act || cache == PA
 size_t elem_bytes(pa_dtype d) { return d == PA_F8E4M3 ? 1 : 2; }
 
 constexpr int kBlock = 32;
+constexpr int kMaxPartition = 64 * kBlock;  // a partition's pages fit one wave's lanes
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Split-context plan: tokens per partition and the number of partitions for
-// the longest sequence.  Partitions are whole pages.  The automatic choice
+// the longest sequence.  Partitions are whole pages, at most 64 of them.  The automatic choice
 // starts at 4 pages and doubles while the launch would exceed ~4096 waves,
 // which keeps every CU of the MI355X (256 CUs) busy with several waves while
 // bounding the partial-result traffic to a few percent of the K/V stream.
@@ -75,6 +76,7 @@ bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, Pl
     part = (int)(pp * kBlock);
   }
   if (part <= 0 || part % kBlock != 0) return false;
+  if (part > kMaxPartition) part = kMaxPartition;
   p->part_tok = part;
   p->NP = (L + part - 1) / part;
   return true;
@@ -163,7 +165,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
   const int G = Hq / Hkv;
   if (!pa::decode_supported(D, G, fmt_of(act_dtype), fmt_of(cache_dtype)))
-    return fail(PA_ERR_UNSUPPORTED, "decode supports head_dim 64/128 and Hq/Hkv in {1,2,4,8}");
+    return fail(PA_ERR_UNSUPPORTED, "decode supports head_dim 64/96/128 and Hq/Hkv in {1,2,4,8,16}");
   if (!std::isfinite(softmax_scale)) return fail(PA_ERR_INVALID, "softmax_scale must be finite");
   if (cache_dtype == PA_F8E4M3 &&
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))

@@ -8,23 +8,21 @@
 // addresses a W-row ring ("Rolling buffer cache", llama.cpp discussion 3581,
 // opening post) and min(L, W) rows are read.
 //
-// Work split.  One 64-lane wave owns (sequence b, KV head g, partition p),
-// where a partition is `part_tok` consecutive tokens (a multiple of the
-// 32-token page).  The wave streams its pages one at a time:
+// Work split.  One 64-lane wave owns (sequence b, KV head g, partition p), a
+// partition being `part_tok` consecutive tokens (whole 32-token pages).  The
+// wave keeps the G query heads of the group as the rows of 16x16 MFMA tiles
+// (rows G..15 are zero) and streams its pages, prefetching page n+1 into a
+// second register buffer while it computes page n:
 //
-//   * S = Q_g K^T on MFMA (v_mfma_f32_16x16x32, bf16 or f16): the G query
-//     heads of the group are the 16-row A operand (zero rows pad G up to 16),
-//     the page's 32 tokens are two 16-column B tiles.  K is loaded straight
-//     into the B-operand layout: lane i reads token (i%16 [+16]) and the
-//     8-element chunk (i/16 + 4j) of the head dimension.
-//   * Online softmax on the 16x32 score tile: each lane of row 0 holds the
-//     scores of one token column for four heads, so the per-head page max and
-//     sum are 16-lane row reductions.  Scores are kept in log2 units
-//     (scale * log2(e) folded in) so exp is a single v_exp_f32.
-//   * O += P V on the vector ALU: V is read fully coalesced (lane i reads
-//     8 elements of token i/(D/8) + (64/(D/8))*s), the probabilities travel
-//     through 32*G floats of LDS, and each lane keeps G x 8 fp32 partial
-//     outputs for its chunk of the head dimension.
+//   * S = Q K^T: two 16x16x32 tiles of 16 tokens, D/32 k-steps each.  The K
+//     page layout [D/8][32][8] makes every B operand one 16-byte load
+//     (8 bytes for E4M3).
+//   * Online softmax in log2 units (scale * log2 e folded in): each MFMA
+//     output row is one head, so the per-head page max and sum are 16-lane
+//     row reductions done entirely in DPP.
+//   * P goes through 1 KiB of LDS into the MFMA A-operand layout (the only
+//     transpose), and O += P V runs as D/16 16x16x32 MFMAs whose B operands
+//     are single loads from the transposed V page [D][32].
 //
 // A partition either writes the normalised output (when it is the only one
 // of its sequence) or its unnormalised (m, l, o) to the workspace; a second
@@ -38,20 +36,11 @@ namespace pa {
 
 namespace {
 
-constexpr int BS = 32;          // tokens per page
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int PROW = kPage + 8;  // LDS row of P (16-bit elements), padded
+constexpr float kRescaleSlack = 8.f;  // log2 units a row max may grow before rescaling
 
-template <int CF>
-struct CacheElem {
-  static constexpr int bytes = 2;
-};
-template <>
-struct CacheElem<FMT_E4M3> {
-  static constexpr int bytes = 1;
-};
-
-// The 8 cache elements a lane needs, as raw words: 4 words for 16-bit
-// formats, 2 words for E4M3.
+// Eight cache elements: 16 bytes for 16-bit formats, 8 bytes for E4M3.
 template <int CF>
 struct Raw8 {
   u32x4 w;
@@ -62,71 +51,46 @@ struct Raw8<FMT_E4M3> {
 };
 
 template <int CF>
-__device__ __forceinline__ Raw8<CF> load8(const uint8_t* p) {
-  Raw8<CF> r;
+__device__ __forceinline__ Raw8<CF> load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  Raw8<CF> x;
   if constexpr (CF == FMT_E4M3) {
-    r.w = *reinterpret_cast<const u32x2*>(p);
+    x.w = buf_load8(r, voff, soff);
   } else {
-    r.w = *reinterpret_cast<const u32x4*>(p);
+    x.w = buf_load16(r, voff, soff);
   }
-  return r;
+  return x;
 }
 
-// Widen 8 cache elements to fp32.
-template <int CF>
-__device__ __forceinline__ void widen8(const Raw8<CF>& r, float (&x)[8]) {
-  if constexpr (CF == FMT_E4M3) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      f32x2 a = e4m3x2_to_f32<false>(r.w[w]);
-      f32x2 b = e4m3x2_to_f32<true>(r.w[w]);
-      x[4 * w + 0] = a[0];
-      x[4 * w + 1] = a[1];
-      x[4 * w + 2] = b[0];
-      x[4 * w + 3] = b[1];
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      x[2 * w + 0] = lo16_to_f32<CF>(r.w[w]);
-      x[2 * w + 1] = hi16_to_f32<CF>(r.w[w]);
-    }
-  }
-}
-
-// MFMA operand type for an activation format.
-template <int AF>
-struct Mfma;
-template <>
-struct Mfma<FMT_BF16> {
-  typedef bf16x8 vec;
-  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct Mfma<FMT_F16> {
-  typedef f16x8 vec;
-  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-// 8 cache elements as an MFMA operand in the activation format.  For a
-// 16-bit cache the bits are used as they are; E4M3 values are exact in both
-// bf16 and fp16, so the widened fp32 values convert without rounding.
+// Eight cache elements as an MFMA operand in the activation format.  E4M3
+// values are exact in bf16 and fp16, so the widening is exact.
 template <int CF, int AF>
 __device__ __forceinline__ typename Mfma<AF>::vec as_operand(const Raw8<CF>& r) {
-  u32x4 w;
   if constexpr (CF == FMT_E4M3) {
-    float x[8];
-    widen8<CF>(r, x);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = pack2<AF>(x[2 * k], x[2 * k + 1]);
+    return __builtin_bit_cast(typename Mfma<AF>::vec, e4m3x8_to_16<AF>(r.w));
   } else {
-    w = r.w;
+    return __builtin_bit_cast(typename Mfma<AF>::vec, r.w);
   }
-  return __builtin_bit_cast(typename Mfma<AF>::vec, w);
+}
+
+// Registers of one page.  16-bit caches: K operand of token tile tt and
+// k-step j is one 16-byte load (token col + 16 tt).  E4M3: one 16-byte load
+// per k-step holds the 8-byte chunks of tokens 2 col and 2 col + 1, which are
+// column col of token tiles 0 and 1.
+template <int D, int CF>
+struct PageRegs {
+  Raw8<CF> k[2][D / 32];   // [token tile][k-step]
+  Raw8<CF> v[D / 16];      // [output tile]
+};
+template <int D>
+struct PageRegs<D, FMT_E4M3> {
+  u32x4 k[D / 32];         // [k-step]: tile 0 in words 0-1, tile 1 in words 2-3
+  Raw8<FMT_E4M3> v[D / 16];
+};
+
+// Token of a page held in MFMA column `col` of token tile `tt`.
+template <int CF>
+__device__ __forceinline__ int tile_token(int tt, int col) {
+  return CF == FMT_E4M3 ? 2 * col + tt : col + 16 * tt;
 }
 
 template <int D, int G, int CF, int AF>
@@ -137,23 +101,18 @@ __global__ __launch_bounds__(64) void decode_pass1(
     int Hkv, int MBPS, int window, int part_tok, int NP, float qk_scale_log2,
     float v_scale, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o) {
-  static_assert(D % 32 == 0 && (D == 64 || D == 128), "head_dim");
-  static_assert(G >= 1 && G <= 8, "group");
-  constexpr int EB = CacheElem<CF>::bytes;
-  constexpr int KSTEPS = D / 32;        // MFMA k-steps per token tile
-  constexpr int CPR = D / 8;            // 8-element chunks per token row
-  constexpr int TPI = 64 / CPR;         // tokens per V load instruction
-  constexpr int VLOADS = BS / TPI;      // V load instructions per page
-  constexpr int HROWS = (G + 3) / 4;    // MFMA output rows of 16 lanes holding heads
+  static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
+  static_assert(G >= 1 && G <= 16, "group");
+  constexpr int EB = (CF == FMT_E4M3) ? 1 : 2;
+  constexpr int KSTEPS = D / 32;
+  constexpr int NT = D / 16;
   typedef typename Mfma<AF>::vec vec;
 
-  __shared__ float p_lds[BS * G];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lds[16 * PROW];
 
   const int lane = threadIdx.x;
-  const int col = lane & 15;            // MFMA: token column / A row (head)
-  const int r4 = lane >> 4;             // MFMA: k-group / output row group
-  const int vc = lane % CPR;            // V chunk owned by this lane
-  const int vq = lane / CPR;            // V token sub-index
+  const int col = lane & 15;
+  const int r4 = lane >> 4;
 
   const int p = blockIdx.x;
   const int g = blockIdx.y;
@@ -167,10 +126,7 @@ __global__ __launch_bounds__(64) void decode_pass1(
   if (L <= 0) {
     // Empty context: zeros, written once by partition 0.
     if (p == 0) {
-      for (int h = 0; h < G; ++h) {
-        uint16_t* o = out + ((size_t)b * Hq + g * G + h) * D;
-        for (int d = lane; d < D; d += 64) o[d] = 0;
-      }
+      for (int i = lane; i < G * D; i += 64) out[((size_t)b * Hq + g * G) * D + i] = 0;
     }
     return;
   }
@@ -178,10 +134,11 @@ __global__ __launch_bounds__(64) void decode_pass1(
 
   const int t0 = p * part_tok;
   const int t1 = min(L, t0 + part_tok);
-  const int pg0 = t0 / BS;
-  const int pg1 = (t1 + BS - 1) / BS;
+  const int pg0 = t0 / kPage;
+  const int pg1 = (t1 + kPage - 1) / kPage;
 
-  // Q as the MFMA A operand: row = head (col < G), k chunk (r4 + 4j).
+  // Q as the A operand: row = head `col` of the group (zero when col >= G),
+  // k-group r4 of k-step j = head-dimension chunk (r4 + 4j).
   vec qa[KSTEPS];
   {
     const uint16_t* qrow = query + ((size_t)b * Hq + g * G + (col < G ? col : 0)) * D;
@@ -193,158 +150,201 @@ __global__ __launch_bounds__(64) void decode_pass1(
     }
   }
 
+  const size_t page_elems = (size_t)kPage * D;
+  const int32_t* bt = block_tables + (size_t)b * MBPS;
+
+  // Per-lane byte offsets inside a page (loop invariant).  K operand of
+  // k-step j, token tile tt: chunk (r4 + 4j), token tile_token(tt, col); V
+  // operand of output tile n: dim 16n + col, tokens 8 r4 .. 8 r4 + 7.
+  const int k_lane = ((r4 * kPage + tile_token<CF>(0, col)) * 8) * EB;
+  const int v_lane = (col * kPage + 8 * r4) * EB;
+  constexpr int K_J = 4 * kPage * 8 * EB;    // byte step between k-steps
+  constexpr int K_TT = 16 * 8 * EB;          // byte step between token tiles (16-bit)
+  constexpr int V_N = 16 * kPage * EB;       // byte step between output tiles
+  constexpr uint32_t PAGE_BYTES = (uint32_t)kPage * D * EB;
+
+  // Physical blocks of this partition, lane i holding page pg0 + i (a
+  // partition spans at most 64 pages), so the page loop never waits on a
+  // block-table load.
+  const int npg = pg1 - pg0;
+  const int bt_lane = bt[pg0 + (lane < npg ? lane : 0)];
+
+  auto load_page = [&](int pg, PageRegs<D, CF>& P) {
+    const int phys = __builtin_amdgcn_readlane(bt_lane, pg - pg0);
+    const size_t base = ((size_t)phys * Hkv + g) * page_elems * EB;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, PAGE_BYTES);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(value_cache + base, PAGE_BYTES);
+    if constexpr (CF == FMT_E4M3) {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) P.k[j] = buf_load16(kr, k_lane, j * K_J);
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) P.k[tt][j] = load8<CF>(kr, k_lane, j * K_J + tt * K_TT);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) P.v[n] = load8<CF>(vr, v_lane, n * V_N);
+  };
+
+  // K operand of token tile tt, k-step j.
+  auto k_operand = [&](const PageRegs<D, CF>& P, int tt, int j) -> vec {
+    if constexpr (CF == FMT_E4M3) {
+      Raw8<CF> r;
+      r.w = tt == 0 ? u32x2{P.k[j][0], P.k[j][1]} : u32x2{P.k[j][2], P.k[j][3]};
+      return as_operand<CF, AF>(r);
+    } else {
+      return as_operand<CF, AF>(P.k[tt][j]);
+    }
+  };
+
   float m_run[4], l_run[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     m_run[r] = -INFINITY;
     l_run[r] = 0.f;
   }
-  float acc[G][8];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t page_elems = (size_t)BS * D;
-  const int32_t* bt = block_tables + (size_t)b * MBPS;
-
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const int phys = bt[pg];
-    const size_t page_off = ((size_t)phys * Hkv + g) * page_elems;
-    const uint8_t* kp = key_cache + page_off * EB;
-    const uint8_t* vp = value_cache + page_off * EB;
-
-    // Issue every load of the page up front.
-    Raw8<CF> kr[2][KSTEPS];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int j = 0; j < KSTEPS; ++j)
-        kr[tt][j] = load8<CF>(kp + ((size_t)(col + 16 * tt) * D + 8 * (r4 + 4 * j)) * EB);
-    Raw8<CF> vr[VLOADS];
-#pragma unroll
-    for (int s = 0; s < VLOADS; ++s)
-      vr[s] = load8<CF>(vp + ((size_t)(vq + TPI * s) * D + 8 * vc) * EB);
-
-    // S = Q K^T for tokens [16tt, 16tt+16) of the page.
-    f32x4 sacc[2];
+  auto compute_page = [&](const PageRegs<D, CF>& P, int pg) {
+    // S = Q K^T; lane (r4, col) gets heads 4*r4 + r, tokens tok0 and tok1.
+    f32x4 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j)
-        sacc[tt] = Mfma<AF>::mma(qa[j], as_operand<CF, AF>(kr[tt][j]), sacc[tt]);
+      for (int j = 0; j < KSTEPS; ++j) s[tt] = Mfma<AF>::mma(qa[j], k_operand(P, tt, j), s[tt]);
     }
-
-    // Online softmax.  Lane (r4, col) holds heads 4*r4 + r for token col (+16).
-    const int base = pg * BS;
-    float alpha[4];
+    const int base = pg * kPage;
+    const int tok0 = tile_token<CF>(0, col);
+    const int tok1 = tile_token<CF>(1, col);
+    const bool live0 = base + tok0 < t1;
+    const bool live1 = base + tok1 < t1;
+    float sc[4][2], pm[4];
+    bool grow = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float s0 = sacc[0][r] * qk_scale_log2;
-      float s1 = sacc[1][r] * qk_scale_log2;
-      if (base + col >= t1) s0 = -INFINITY;
-      if (base + col + 16 >= t1) s1 = -INFINITY;
-      const float pm = row16_max(fmaxf(s0, s1));
-      const float m_new = fmaxf(m_run[r], pm);
-      alpha[r] = fast_exp2(m_run[r] - m_new);
-      const float e0 = fast_exp2(s0 - m_new);
-      const float e1 = fast_exp2(s1 - m_new);
-      l_run[r] = l_run[r] * alpha[r] + row16_sum(e0 + e1);
-      m_run[r] = m_new;
-      const int h = 4 * r4 + r;
-      if (r4 < HROWS && h < G) {
-        p_lds[col * G + h] = e0;
-        p_lds[(col + 16) * G + h] = e1;
+      sc[r][0] = live0 ? s[0][r] * qk_scale_log2 : -INFINITY;
+      sc[r][1] = live1 ? s[1][r] * qk_scale_log2 : -INFINITY;
+      pm[r] = row16_max(fmaxf(sc[r][0], sc[r][1]));
+      grow |= pm[r] > m_run[r] + kRescaleSlack;
+    }
+    // The running reference max only moves when some row's page max exceeds
+    // it by more than kRescaleSlack (log2 units); otherwise probabilities are
+    // taken against the old reference (they stay below 2^kRescaleSlack) and
+    // the output needs no rescaling.  The test is wave-uniform.
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m_new = fmaxf(m_run[r], pm[r]);
+        const float alpha = fast_exp2(m_run[r] - m_new);
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n][r] *= alpha;
+        m_run[r] = m_new;
       }
     }
-    __syncthreads();
-
-    // Rescale the running output, then accumulate P V.
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[h & 3]), 16 * (h >> 2)));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-    }
-    // Rows past the end of the context may hold anything (NaN included):
-    // their probabilities are 0, but 0 * NaN is NaN, so their values are
-    // zeroed on the (uniform) last, partial page.
-    const bool partial_page = base + BS > t1;
-#pragma unroll
-    for (int s = 0; s < VLOADS; ++s) {
-      float x[8];
-      widen8<CF>(vr[s], x);
-      const int tok = vq + TPI * s;
-      if (partial_page && base + tok >= t1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const float e0 = fast_exp2(sc[r][0] - m_run[r]);
+      const float e1 = fast_exp2(sc[r][1] - m_run[r]);
+      l_run[r] += row16_sum(e0 + e1);
+      if constexpr (CF == FMT_E4M3) {
+        // Tokens 2 col and 2 col + 1: one 32-bit store.
+        *reinterpret_cast<uint32_t*>(&p_lds[(4 * r4 + r) * PROW + tok0]) =
+            (uint32_t)cvt16<AF>(e0) | ((uint32_t)cvt16<AF>(e1) << 16);
+      } else {
+        p_lds[(4 * r4 + r) * PROW + tok0] = cvt16<AF>(e0);
+        p_lds[(4 * r4 + r) * PROW + tok1] = cvt16<AF>(e1);
       }
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = p_lds[tok * G + h];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // A operand: P[head col][tokens 8*r4 .. 8*r4 + 7].
+    const vec pa = *reinterpret_cast<const vec*>(&p_lds[col * PROW + 8 * r4]);
+    // Rows past the context end may hold anything (NaN included); their
+    // probabilities are 0, but 0 * NaN is NaN, so those V values are zeroed
+    // on the (uniform) last partial page.
+    const bool partial = base + kPage > t1;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      vec vb = as_operand<CF, AF>(P.v[n]);
+      if (partial) {
+        u32x4 w = __builtin_bit_cast(u32x4, vb);
+        const int tok = base + 8 * r4;  // this lane holds tokens tok .. tok + 7
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (tok + 2 * e < t1) ? 0xffffu : 0u;
+          const uint32_t hi = (tok + 2 * e + 1 < t1) ? 0xffff0000u : 0u;
+          w[e] &= (lo | hi);
+        }
+        vb = __builtin_bit_cast(vec, w);
+      }
+      acc[n] = Mfma<AF>::mma(pa, vb, acc[n]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  // Two register buffers: page pg is computed while page pg + 1 loads.  The
+  // prefetch past the last page re-reads the last page (an L2 hit) so that
+  // no load sits behind a branch.
+  PageRegs<D, CF> A, Bf;
+  load_page(pg0, A);
+  for (int pg = pg0;;) {
+    load_page(min(pg + 1, pg1 - 1), Bf);
+    compute_page(A, pg);
+    if (++pg >= pg1) break;
+    load_page(min(pg + 1, pg1 - 1), A);
+    compute_page(Bf, pg);
+    if (++pg >= pg1) break;
   }
 
-  // Sum the partial outputs of the lanes that share a chunk.
-#pragma unroll
-  for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
-
-  // Per-head running max / sum, uniform across the wave.
-  float mh[G], lh[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mh[h] = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_run[h & 3]), 16 * (h >> 2)));
-    lh[h] = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_run[h & 3]), 16 * (h >> 2)));
-  }
-
-  // Lane (vq, vc) writes heads h = vq, vq + TPI, ... of chunk vc.
+  // Lane (r4, col) holds O[head 4*r4 + r][dim 16n + col].
   if (nparts == 1) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if ((h % TPI) != vq) continue;
-      const float inv = v_scale / lh[h];
-      u32x4 w;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * r4 + r;
+      if (h >= G) continue;
+      const float inv = v_scale / l_run[r];
+      uint16_t* o = out + ((size_t)b * Hq + g * G + h) * D + col;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = pack2<AF>(acc[h][2 * k] * inv, acc[h][2 * k + 1] * inv);
-      *reinterpret_cast<u32x4*>(out + ((size_t)b * Hq + g * G + h) * D + 8 * vc) = w;
+      for (int n = 0; n < NT; ++n) o[16 * n] = static_cast<uint16_t>(f32_to_16<AF>(acc[n][r] * inv));
     }
   } else {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if ((h % TPI) != vq) continue;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * r4 + r;
+      if (h >= G) continue;
       const size_t row = ((size_t)b * Hq + g * G + h) * NP + p;
-      f32x4* o = reinterpret_cast<f32x4*>(ws_o + row * D + 8 * vc);
-      o[0] = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-      o[1] = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-      if (vc == 0) {
-        ws_m[row] = mh[h];
-        ws_l[row] = lh[h];
+      float* o = ws_o + row * D + col;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[16 * n] = acc[n][r];
+      if (col == 0) {
+        ws_m[row] = m_run[r];
+        ws_l[row] = l_run[r];
       }
     }
   }
 }
 
-// Merge the partitions of each (sequence, query head).
+// Merge the partitions of one (sequence, query head): one wave.  Partitions
+// are taken 16 at a time with every load of a group issued before any use, so
+// a group costs one memory round trip; the running max is rescaled between
+// groups.
+constexpr int kMergeGroup = 16;
+
 template <int D, int AF>
 __global__ __launch_bounds__(64) void decode_pass2(
     uint16_t* __restrict__ out, const int32_t* __restrict__ context_lens, int Hq, int window,
     int part_tok, int NP, float v_scale, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const float* __restrict__ ws_o) {
-  constexpr int DPT = D / 64;  // dims per lane
+  constexpr int DPT = (D + 63) / 64;  // dims per lane
+  const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   int L = context_lens[b];
@@ -352,24 +352,48 @@ __global__ __launch_bounds__(64) void decode_pass2(
   const int nparts = (L + part_tok - 1) / part_tok;
   if (nparts <= 1) return;  // written by pass 1
   const size_t row = ((size_t)b * Hq + h) * NP;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_m[row + p]);
-  float num[DPT];
+  int dk[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) dk[k] = min(lane + 64 * k, D - 1);
+
+  float M = -INFINITY, den = 0.f, num[DPT];
 #pragma unroll
   for (int k = 0; k < DPT; ++k) num[k] = 0.f;
-  float den = 0.f;
-  const int d0 = threadIdx.x * DPT;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(ws_m[row + p] - M);
-    den = fmaf(w, ws_l[row + p], den);
-    const float* o = ws_o + (row + p) * D + d0;
+  for (int p0 = 0; p0 < nparts; p0 += kMergeGroup) {
+    const int n = min(kMergeGroup, nparts - p0);
+    float mp[kMergeGroup], lp[kMergeGroup], op[kMergeGroup][DPT];
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) num[k] = fmaf(w, o[k], num[k]);
+    for (int i = 0; i < kMergeGroup; ++i) {
+      const size_t r = row + p0 + min(i, n - 1);
+      mp[i] = ws_m[r];
+      lp[i] = ws_l[r];
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) op[i][k] = ws_o[r * D + dk[k]];
+    }
+    float Mg = M;
+#pragma unroll
+    for (int i = 0; i < kMergeGroup; ++i)
+      if (i < n) Mg = fmaxf(Mg, mp[i]);
+    const float f = fast_exp2(M - Mg);
+    den *= f;
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) num[k] *= f;
+#pragma unroll
+    for (int i = 0; i < kMergeGroup; ++i) {
+      const float w = i < n ? fast_exp2(mp[i] - Mg) : 0.f;
+      den = fmaf(w, lp[i], den);
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) num[k] = fmaf(w, op[i][k], num[k]);
+    }
+    M = Mg;
   }
   const float inv = v_scale / den;
-  uint16_t* dst = out + ((size_t)b * Hq + h) * D + d0;
+  uint16_t* dst = out + ((size_t)b * Hq + h) * D;
 #pragma unroll
-  for (int k = 0; k < DPT; ++k) dst[k] = static_cast<uint16_t>(f32_to_16<AF>(num[k] * inv));
+  for (int k = 0; k < DPT; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) dst[d] = static_cast<uint16_t>(f32_to_16<AF>(num[k] * inv));
+  }
 }
 
 template <int D, int G, int CF, int AF>
@@ -409,6 +433,7 @@ hipError_t launch_group(const DecodeArgs& a, hipStream_t s) {
     case 2: return launch_fmt<D, 2>(a, s);
     case 4: return launch_fmt<D, 4>(a, s);
     case 8: return launch_fmt<D, 8>(a, s);
+    case 16: return launch_fmt<D, 16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -416,8 +441,8 @@ hipError_t launch_group(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 bool decode_supported(int D, int G, int act, int cache) {
-  if (D != 64 && D != 128) return false;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  if (D != 64 && D != 96 && D != 128) return false;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
   if (act != FMT_BF16 && act != FMT_F16) return false;
   return cache == act || cache == FMT_E4M3;
 }
@@ -425,6 +450,7 @@ bool decode_supported(int D, int G, int act, int cache) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   switch (a.D) {
     case 64: return launch_group<64>(a, s);
+    case 96: return launch_group<96>(a, s);
     case 128: return launch_group<128>(a, s);
     default: return hipErrorInvalidValue;
   }

@@ -14,10 +14,11 @@
 // The workgroup walks the key pages of the sequence (32 tokens each) up to
 // the last position its queries can see:
 //
-//   * the 256 threads stage the page in LDS: K row-major [32][D], V
-//     transposed [D][32] (so that both MFMA operands are 16-byte LDS reads);
-//     rows at or past the context end are zeroed, and E4M3 codes are widened
-//     to the activation format (exactly) on the way in;
+//   * the 256 threads copy the page into LDS as K [32][D] and V [D][32] (the
+//     cache pages are K [D/8][32][8] and V [D][32], so both copies move
+//     16-byte chunks and both MFMA operands become 16-byte LDS reads); rows
+//     at or past the context end are zeroed, and E4M3 codes are widened to
+//     the activation format (exactly) on the way in;
 //   * each wave: S = Q K^T (v_mfma_f32_16x16x32), causal mask, online softmax
 //     in log2 units, P rounded to the activation format and passed through
 //     LDS into the A-operand layout, O += P V.
@@ -34,23 +35,6 @@ constexpr int QT = 128;          // queries per workgroup
 constexpr int QW = 32;           // queries per wave
 constexpr float LOG2E_P = 1.4426950408889634f;
 
-template <int AF>
-struct MfmaP;
-template <>
-struct MfmaP<FMT_BF16> {
-  typedef bf16x8 vec;
-  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct MfmaP<FMT_F16> {
-  typedef f16x8 vec;
-  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
 template <int D, int CF, int AF>
 __global__ __launch_bounds__(256) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
@@ -64,7 +48,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   constexpr int VROW = BS + 8;          // padded LDS row of transposed V
   constexpr int EB = (CF == FMT_E4M3) ? 1 : 2;
   constexpr int CPR = D / 8;            // 8-element chunks per token row
-  typedef typename MfmaP<AF>::vec vec;
+  typedef typename Mfma<AF>::vec vec;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[BS * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VROW];
@@ -137,40 +121,43 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const size_t page_off = ((size_t)phys * Hkv + g) * (size_t)BS * D;
     const int base = pg * BS;
 
-    // Stage K (row-major) and V (transposed) of the page.
+    // Stage K (row-major [32][D]) and V (transposed [D][32]) of the page in
+    // LDS.  Cache pages are K [D/8][32][8] and V [D][32], so both copies are
+    // 8-element chunks.  Rows at or past the context end are zeroed.
     for (int c = tid; c < BS * CPR; c += 256) {
-      const int t = c / CPR;
-      const int d0 = (c - t * CPR) * 8;
-      const size_t src = (page_off + (size_t)t * D + d0) * EB;
-      u32x4 kw, vw;
+      // K chunk: token t, dims 8*dc .. 8*dc + 7.
+      const int t = c % BS;
+      const int dc = c / BS;
+      u32x4 kw = u32x4{0u, 0u, 0u, 0u};
       if (base + t < ctx) {
+        const size_t src = (page_off + (size_t)(dc * BS + t) * 8) * EB;
         if constexpr (CF == FMT_E4M3) {
-          const u32x2 kr = *reinterpret_cast<const u32x2*>(key_cache + src);
-          const u32x2 vr = *reinterpret_cast<const u32x2*>(value_cache + src);
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            f32x2 a = e4m3x2_to_f32<false>(kr[w]), bb = e4m3x2_to_f32<true>(kr[w]);
-            kw[2 * w] = pack2<AF>(a[0], a[1]);
-            kw[2 * w + 1] = pack2<AF>(bb[0], bb[1]);
-            a = e4m3x2_to_f32<false>(vr[w]);
-            bb = e4m3x2_to_f32<true>(vr[w]);
-            vw[2 * w] = pack2<AF>(a[0], a[1]);
-            vw[2 * w + 1] = pack2<AF>(bb[0], bb[1]);
-          }
+          kw = e4m3x8_to_16<AF>(*reinterpret_cast<const u32x2*>(key_cache + src));
         } else {
           kw = *reinterpret_cast<const u32x4*>(key_cache + src);
-          vw = *reinterpret_cast<const u32x4*>(value_cache + src);
         }
+      }
+      *reinterpret_cast<u32x4*>(&k_lds[t * KROW + 8 * dc]) = kw;
+      // V chunk: dim d, tokens 8*tq .. 8*tq + 7.
+      const int d = c / 4;
+      const int tq = c % 4;
+      const size_t vsrc = (page_off + (size_t)d * BS + 8 * tq) * EB;
+      u32x4 vw;
+      if constexpr (CF == FMT_E4M3) {
+        vw = e4m3x8_to_16<AF>(*reinterpret_cast<const u32x2*>(value_cache + vsrc));
       } else {
-        kw = u32x4{0u, 0u, 0u, 0u};
-        vw = u32x4{0u, 0u, 0u, 0u};
+        vw = *reinterpret_cast<const u32x4*>(value_cache + vsrc);
       }
-      *reinterpret_cast<u32x4*>(&k_lds[t * KROW + d0]) = kw;
+      const int tok = base + 8 * tq;
+      if (tok + 8 > ctx) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        v_lds[(d0 + 2 * w) * VROW + t] = (uint16_t)(vw[w] & 0xffffu);
-        v_lds[(d0 + 2 * w + 1) * VROW + t] = (uint16_t)(vw[w] >> 16);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (tok + 2 * e < ctx) ? 0xffffu : 0u;
+          const uint32_t hi = (tok + 2 * e + 1 < ctx) ? 0xffff0000u : 0u;
+          vw[e] &= (lo | hi);
+        }
       }
+      *reinterpret_cast<u32x4*>(&v_lds[d * VROW + 8 * tq]) = vw;
     }
     __syncthreads();
 
@@ -188,7 +175,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           s_acc[mt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s)
-            s_acc[mt][tt] = MfmaP<AF>::mma(qa[mt][s], kb[s], s_acc[mt][tt]);
+            s_acc[mt][tt] = Mfma<AF>::mma(qa[mt][s], kb[s], s_acc[mt][tt]);
         }
       }
 
@@ -231,7 +218,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const vec vb = *reinterpret_cast<const vec*>(&v_lds[(16 * n + col) * VROW + 8 * r4]);
-          o_acc[mt][n] = MfmaP<AF>::mma(pa, vb, o_acc[mt][n]);
+          o_acc[mt][n] = Mfma<AF>::mma(pa, vb, o_acc[mt][n]);
         }
       }
     }

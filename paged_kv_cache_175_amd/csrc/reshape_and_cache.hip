@@ -3,14 +3,15 @@
 // Stores each new token's K and V rows into the cache slot named by its slot
 // number ("Optimization plans", mistral.rs discussion 46, "Update" post,
 // names this operation reshape_and_cache): block slot / 32, row slot % 32, for
-// every KV head of a head-major pool [NB][Hkv][32][D].  A negative slot skips
-// the token.  With an E4M3 cache each element is quantised on the way in
-// ("PagedAttention in mistral.rs", section "KV Cache Quantization").
+// every KV head.  A negative slot skips the token.  With an E4M3 cache each
+// element is quantised on the way in ("PagedAttention in mistral.rs",
+// section "KV Cache Quantization").
 //
-// One thread moves 8 elements (16 bytes of a 16-bit activation).  Threads are
-// laid out token-major, so the reads of the packed [T][Hkv][D] inputs are
-// fully coalesced and each thread's write is one 16-byte (or, for E4M3,
-// 8-byte) store inside a contiguous head row of D elements.
+// One thread moves one 8-element chunk of one (token, head): a 16-byte read
+// of K and of V from the packed [T][Hkv][D] inputs (threads token-major, so
+// reads are fully coalesced), one 16-byte (8-byte for E4M3) store of the K
+// chunk into the page's [D/8][32][8] layout, and eight 2-byte (1-byte) stores
+// of V into the transposed [D][32] page.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,8 +22,9 @@ template <int AF, int CF>
 __global__ __launch_bounds__(256) void cache_write(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
-    const int32_t* __restrict__ slot_mapping, int T, int Hkv, int D, int BS,
-    float k_scale, float v_scale) {
+    const int32_t* __restrict__ slot_mapping, int T, int Hkv, int D, float k_scale,
+    float v_scale) {
+  constexpr int EB = (CF == FMT_E4M3) ? 1 : 2;
   const int chunks_per_row = D / 8;
   const long long per_token = (long long)Hkv * chunks_per_row;
   const long long total = (long long)T * per_token;
@@ -34,33 +36,41 @@ __global__ __launch_bounds__(256) void cache_write(
     const int c = rem - h * chunks_per_row;
     const int slot = slot_mapping[n];
     if (slot < 0) continue;
-    const int blk = slot / BS;
-    const int off = slot - blk * BS;
+    const int blk = slot / kPage;
+    const int off = slot - blk * kPage;
     const size_t src = ((size_t)n * Hkv + h) * D + 8 * c;
-    const size_t dst = (((size_t)blk * Hkv + h) * BS + off) * D + 8 * c;
+    const size_t page = ((size_t)blk * Hkv + h) * (size_t)kPage * D;
+    const size_t kdst = (page + k_page_off(off, 8 * c)) * EB;
     const u32x4 kw = *reinterpret_cast<const u32x4*>(key + src);
     const u32x4 vw = *reinterpret_cast<const u32x4*>(value + src);
     if constexpr (CF == FMT_E4M3) {
-      u32x2 kq, vq;
+      u32x2 kq;
+      uint32_t vb[8];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        uint32_t kb = 0, vb = 0;
+        uint32_t kb = 0;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const uint32_t kx = kw[2 * w + k], vx = vw[2 * w + k];
           kb |= e4m3_encode(lo16_to_f32<AF>(kx), k_scale) << (16 * k);
           kb |= e4m3_encode(hi16_to_f32<AF>(kx), k_scale) << (16 * k + 8);
-          vb |= e4m3_encode(lo16_to_f32<AF>(vx), v_scale) << (16 * k);
-          vb |= e4m3_encode(hi16_to_f32<AF>(vx), v_scale) << (16 * k + 8);
+          vb[4 * w + 2 * k] = e4m3_encode(lo16_to_f32<AF>(vx), v_scale);
+          vb[4 * w + 2 * k + 1] = e4m3_encode(hi16_to_f32<AF>(vx), v_scale);
         }
         kq[w] = kb;
-        vq[w] = vb;
       }
-      *reinterpret_cast<u32x2*>(key_cache + dst) = kq;
-      *reinterpret_cast<u32x2*>(value_cache + dst) = vq;
+      *reinterpret_cast<u32x2*>(key_cache + kdst) = kq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        value_cache[page + v_page_off(off, 8 * c + e)] = static_cast<uint8_t>(vb[e]);
     } else {
-      *reinterpret_cast<u32x4*>(key_cache + dst * 2) = kw;
-      *reinterpret_cast<u32x4*>(value_cache + dst * 2) = vw;
+      *reinterpret_cast<u32x4*>(key_cache + kdst) = kw;
+      uint16_t* vdst = reinterpret_cast<uint16_t*>(value_cache);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vdst[page + v_page_off(off, 8 * c + 2 * w)] = static_cast<uint16_t>(vw[w] & 0xffffu);
+        vdst[page + v_page_off(off, 8 * c + 2 * w + 1)] = static_cast<uint16_t>(vw[w] >> 16);
+      }
     }
   }
 }
@@ -80,7 +90,7 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
   uint8_t* vc = (uint8_t*)a.value_cache;
 #define PA_LAUNCH(AF, CF)                                                                  \
   hipLaunchKernelGGL((cache_write<AF, CF>), grid, dim3(threads), 0, s, k, v, kc, vc,        \
-                     a.slot_mapping, a.T, a.Hkv, a.D, a.BS, a.k_scale, a.v_scale)
+                     a.slot_mapping, a.T, a.Hkv, a.D, a.k_scale, a.v_scale)
   if (a.act == FMT_BF16 && a.cache == FMT_BF16) PA_LAUNCH(FMT_BF16, FMT_BF16);
   else if (a.act == FMT_F16 && a.cache == FMT_F16) PA_LAUNCH(FMT_F16, FMT_F16);
   else if (a.act == FMT_BF16 && a.cache == FMT_E4M3) PA_LAUNCH(FMT_BF16, FMT_E4M3);

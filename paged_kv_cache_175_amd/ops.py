@@ -60,21 +60,49 @@ def cache_dtype_name(cache: torch.Tensor) -> str:
     return "f8e4m3" if cache.dtype in (torch.uint8,) else "auto"
 
 
+def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 32):
+    """Shapes of the key and value pools.
+
+    Key pages are ``[head_dim/8][block_size][8]`` and value pages are stored
+    transposed, ``[head_dim][block_size]`` (the layout of include/pa.h).
+    """
+    if head_dim % 8:
+        raise ValueError("head_dim must be a multiple of 8")
+    return ((num_blocks, num_kv_heads, head_dim // 8, block_size, 8),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def alloc_pools(num_blocks: int, num_kv_heads: int, head_dim: int, act_dtype: torch.dtype,
+                cache_dtype: str = "auto", device="cuda", block_size: int = 32):
+    """Allocate (uninitialised) key and value pools up front."""
+    ks, vs = pool_shapes(num_blocks, num_kv_heads, head_dim, block_size)
+    dt = torch.uint8 if cache_dtype == "f8e4m3" else act_dtype
+    return (torch.empty(ks, dtype=dt, device=device), torch.empty(vs, dtype=dt, device=device))
+
+
+def _pool_geometry(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    """(NB, Hkv, BS, D) of a pair of pools; raises on malformed shapes."""
+    if key_cache.dim() != 5 or key_cache.shape[4] != 8 or value_cache.dim() != 4:
+        raise ValueError("key_cache must be [NB, Hkv, D/8, BS, 8] and value_cache [NB, Hkv, D, BS]")
+    NB, Hkv, D8, BS, _ = key_cache.shape
+    if tuple(value_cache.shape) != (NB, Hkv, D8 * 8, BS) or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache does not match key_cache")
+    return NB, Hkv, BS, D8 * 8
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                       value_cache: torch.Tensor, slot_mapping: torch.Tensor,
                       k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Write ``key``/``value`` ``[T, Hkv, D]`` into the pools at ``slot_mapping``.
 
-    Pools are ``[NB, Hkv, BS, D]``; a negative slot skips its token.
+    Pools as from :func:`alloc_pools`; a negative slot skips its token.
     """
     _dev(key, value, key_cache, value_cache, slot_mapping)
     _i32(slot_mapping)
     if key.shape != value.shape or key.dim() != 3:
         raise ValueError("key and value must both be [T, Hkv, D]")
     T, Hkv, D = key.shape
-    if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
-        raise ValueError("caches must both be [NB, Hkv, BS, D]")
-    NB, Hc, BS, Dc = key_cache.shape
+    NB, Hc, BS, Dc = _pool_geometry(key_cache, value_cache)
     if (Hc, Dc) != (Hkv, D) or slot_mapping.numel() != T:
         raise ValueError("shape mismatch between tokens, caches and slot_mapping")
     act = _act_code(key)
@@ -114,8 +142,8 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     _dev(query, key_cache, value_cache, block_tables, context_lens)
     _i32(block_tables, context_lens)
     B, Hq, D = query.shape
-    NB, Hkv, BS, Dc = key_cache.shape
-    if Dc != D or value_cache.shape != key_cache.shape:
+    NB, Hkv, BS, Dc = _pool_geometry(key_cache, value_cache)
+    if Dc != D:
         raise ValueError("cache shapes do not match the query")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables must be [B, MBPS] and context_lens [B]")
@@ -148,9 +176,9 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
     _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
     _i32(cu_q_lens, block_tables, context_lens)
     total_q, Hq, D = query.shape
-    NB, Hkv, BS, Dc = key_cache.shape
+    NB, Hkv, BS, Dc = _pool_geometry(key_cache, value_cache)
     B = context_lens.numel()
-    if Dc != D or value_cache.shape != key_cache.shape:
+    if Dc != D:
         raise ValueError("cache shapes do not match the query")
     if cu_q_lens.numel() != B + 1 or block_tables.shape[0] != B:
         raise ValueError("cu_q_lens must be [B+1] and block_tables [B, MBPS]")
@@ -180,7 +208,7 @@ def prepare_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
     _dev(key, value, key_cache, value_cache, slot_mapping)
     _i32(slot_mapping)
     T, Hkv, D = key.shape
-    NB, _, BS, _ = key_cache.shape
+    NB, _, BS, _ = _pool_geometry(key_cache, value_cache)
     lib = _lib.load()
     args = (key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
             slot_mapping.data_ptr(), T, Hkv, D, BS, NB, _act_code(key),
@@ -199,7 +227,7 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
     _dev(query, key_cache, value_cache, block_tables, context_lens, out)
     _i32(block_tables, context_lens)
     B, Hq, D = query.shape
-    NB, Hkv, BS, _ = key_cache.shape
+    NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
     MBPS = block_tables.shape[1]
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -225,7 +253,7 @@ def prepare_prefill_chunk(query, cu_q_lens, key_cache, value_cache, block_tables
     _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens, out)
     _i32(cu_q_lens, block_tables, context_lens)
     total_q, Hq, D = query.shape
-    NB, Hkv, BS, _ = key_cache.shape
+    NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
     B = context_lens.numel()
     MBPS = block_tables.shape[1]
     lib = _lib.load()

@@ -42,13 +42,16 @@ def _act_tensor(bits: np.ndarray, act: str, device="cuda") -> torch.Tensor:
 
 
 def gpu_pools(wl, device="cuda"):
-    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
+    kshape, vshape = ops.pool_shapes(wl.pool_blocks, wl.Hkv, wl.D, wl.BS)
     if wl.cache == "e4m3":
-        kc = torch.full(shape, NAN_E4M3, dtype=torch.uint8, device=device)
+        kc = torch.full(kshape, NAN_E4M3, dtype=torch.uint8, device=device)
+        vc = torch.full(vshape, NAN_E4M3, dtype=torch.uint8, device=device)
     else:
-        kc = torch.full(shape, NAN16[wl.cache], dtype=torch.int16, device=device)
+        kc = torch.full(kshape, NAN16[wl.cache], dtype=torch.int16, device=device)
+        vc = torch.full(vshape, NAN16[wl.cache], dtype=torch.int16, device=device)
         kc = kc.view(TORCH_ACT[wl.cache])
-    return kc, kc.clone()
+        vc = vc.view(TORCH_ACT[wl.cache])
+    return kc, vc
 
 
 def _gpu_write(wl, kc, vc, k_bits, v_bits, slots, device="cuda"):
@@ -128,10 +131,8 @@ def out_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def oracle_pools(wl):
-    shape = (wl.pool_blocks, wl.Hkv, wl.BS, wl.D)
-    if wl.cache == "e4m3":
-        return np.full(shape, NAN_E4M3, np.uint8), np.full(shape, NAN_E4M3, np.uint8)
-    return np.full(shape, NAN16[wl.cache], np.uint16), np.full(shape, NAN16[wl.cache], np.uint16)
+    fill = NAN_E4M3 if wl.cache == "e4m3" else NAN16[wl.cache]
+    return o_cache.empty_pools(wl.pool_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, fill)
 
 
 def _oracle_row(wl, pos):

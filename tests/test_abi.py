@@ -81,7 +81,8 @@ def _decode(**kw):
     (dict(Hq=7), _lib.PA_ERR_INVALID),                    # Hq not a multiple of Hkv
     (dict(BS=16), _lib.PA_ERR_UNSUPPORTED),
     (dict(D=80), _lib.PA_ERR_UNSUPPORTED),
-    (dict(Hq=32, Hkv=2), _lib.PA_ERR_UNSUPPORTED),       # group 16 > 8
+    (dict(Hq=64, Hkv=2), _lib.PA_ERR_UNSUPPORTED),       # group 32 > 16
+    (dict(Hq=6, Hkv=2), _lib.PA_ERR_UNSUPPORTED),        # group 3
     (dict(act=_lib.PA_F8E4M3), _lib.PA_ERR_UNSUPPORTED),
     (dict(cache=_lib.PA_F16), _lib.PA_ERR_UNSUPPORTED),   # f16 cache with bf16 act
     (dict(cache=_lib.PA_F8E4M3, ks=0.0), _lib.PA_ERR_INVALID),

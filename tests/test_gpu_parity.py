@@ -114,15 +114,19 @@ def test_e4m3_encode_exhaustive(act, scale):
     k = bits.reshape(T, Hkv, D)
     v = bits[::-1].copy().reshape(T, Hkv, D)
     NB = T // BS
-    kc = torch.full((NB, Hkv, BS, D), 0x7F, dtype=torch.uint8, device="cuda")
-    vc = kc.clone()
+    ks, vs = ops.pool_shapes(NB, Hkv, D, BS)
+    kc = torch.full(ks, 0x7F, dtype=torch.uint8, device="cuda")
+    vc = torch.full(vs, 0x7F, dtype=torch.uint8, device="cuda")
     slots = torch.arange(T, dtype=torch.int32, device="cuda")
     ops.reshape_and_cache(P._act_tensor(k, act), P._act_tensor(v, act), kc, vc, slots, scale, scale)
     torch.cuda.synchronize()
-    from oracle.cache import bits_to_f64
-    for name, src, dst in (("key", k, kc), ("value", v, vc)):
-        x32 = bits_to_f64(src, act).astype(np.float32)
-        want = o_e4m3.encode(x32, scale).reshape(NB, BS, Hkv, D).transpose(0, 2, 1, 3)
+    from oracle.cache import bits_to_f64, empty_pools, put_row
+    wk, wv = empty_pools(NB, Hkv, BS, D, "e4m3", 0x7F)
+    ek = o_e4m3.encode(bits_to_f64(k, act).astype(np.float32), scale)
+    ev = o_e4m3.encode(bits_to_f64(v, act).astype(np.float32), scale)
+    for n in range(T):
+        put_row(wk, wv, n // BS, n % BS, ek[n], ev[n])
+    for name, want, dst in (("key", wk, kc), ("value", wv, vc)):
         got = P.pool_bits(dst)
         bad = np.argwhere(got != want)
         assert bad.size == 0, f"{name}: {len(bad)} codes differ, first {bad[:3]}"
@@ -133,11 +137,13 @@ def test_e4m3_decode_all_codes():
     output is the code's value (exact in bf16); NaN codes give NaN."""
     P.say("[decode] all 256 E4M3 codes")
     Hkv, D, BS = 1, 128, 32
-    kc = torch.zeros((3, Hkv, BS, D), dtype=torch.uint8, device="cuda")
-    vc = torch.zeros_like(kc)
+    ks, vs = ops.pool_shapes(3, Hkv, D, BS)
+    kc = torch.zeros(ks, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(vs, dtype=torch.uint8, device="cuda")
     codes = np.arange(256, dtype=np.uint8).reshape(2, D)
-    vc[0, 0, 0] = torch.from_numpy(codes[0]).cuda()
-    vc[1, 0, 0] = torch.from_numpy(codes[1]).cuda()
+    # Token 0 of blocks 0 and 1 (value pages are [D][BS]).
+    vc[0, 0, :, 0] = torch.from_numpy(codes[0]).cuda()
+    vc[1, 0, :, 0] = torch.from_numpy(codes[1]).cuda()
     q = torch.randn(2, 1, D, device="cuda").to(torch.bfloat16)
     bt = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
     cl = torch.tensor([1, 1], dtype=torch.int32, device="cuda")

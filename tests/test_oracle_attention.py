@@ -53,8 +53,7 @@ def _contiguous_setup(rng, lens, Hq, Hkv, D, BS, act):
     B = len(lens)
     nbps = max(-(-l // BS) for l in lens)
     NB = B * nbps
-    kc = np.full((NB, Hkv, BS, D), NAN_BITS[act], dtype=np.uint16)
-    vc = kc.copy()
+    kc, vc = cache.empty_pools(NB, Hkv, BS, D, act, NAN_BITS[act])
     bt = np.arange(NB, dtype=np.int32).reshape(B, nbps)
     dense_k, dense_v = [], []
     for b, L in enumerate(lens):
@@ -63,8 +62,7 @@ def _contiguous_setup(rng, lens, Hq, Hkv, D, BS, act):
         dense_k.append(k)
         dense_v.append(v)
         for t in range(L):
-            kc[bt[b, t // BS], :, t % BS, :] = k[t]
-            vc[bt[b, t // BS], :, t % BS, :] = v[t]
+            cache.put_row(kc, vc, bt[b, t // BS], t % BS, k[t], v[t])
     return kc, vc, bt, dense_k, dense_v
 
 
@@ -138,10 +136,10 @@ def test_p3_closed_forms():
     outz = attention.decode(qz, act, kc, vc, act, bt, np.array([1, 6]), 0.5)
     np.testing.assert_allclose(outz[1, 0], _f64(dv[1][:, 0], act).mean(0), atol=1e-14)
     # Equal keys: uniform weights as well.
-    kc_eq = kc.copy()
+    kc_eq, vc_eq = kc.copy(), vc.copy()
     for t in range(6):
-        kc_eq[bt[1, t // BS], :, t % BS, :] = dk[1][0]
-    oute = attention.decode(q, act, kc_eq, vc, act, bt, np.array([1, 6]), 0.5)
+        cache.put_row(kc_eq, vc_eq, bt[1, t // BS], t % BS, dk[1][0], dv[1][t])
+    oute = attention.decode(q, act, kc_eq, vc_eq, act, bt, np.array([1, 6]), 0.5)
     np.testing.assert_allclose(oute[1, 1], _f64(dv[1][:, 0], act).mean(0), atol=1e-14)
     # Empty context: zeros.
     out0 = attention.decode(q, act, kc, vc, act, bt, np.array([0, 6]), 0.5)
@@ -157,8 +155,7 @@ def test_p5_ring_equals_window_mask(W, BS, i):
     NB = nblk + 3
     phys = rng.permutation(NB)[:nblk].astype(np.int32)
     bt = phys[None, :]
-    kc = np.full((NB, Hkv, BS, D), NAN_BITS[act], dtype=np.uint16)
-    vc = kc.copy()
+    kc, vc = cache.empty_pools(NB, Hkv, BS, D, act, NAN_BITS[act])
     ks = _bits(rng, (i + 1, Hkv, D), act)
     vs = _bits(rng, (i + 1, Hkv, D), act)
     # Write every position 0..i through its ring row, overwriting older ones.
@@ -200,9 +197,7 @@ def test_p6_split_merge_equals_single_pass(cuts):
 def test_p7_writer_touches_only_written_slots(cache_fmt):
     rng = np.random.default_rng(7)
     act, Hkv, D, BS, NB, T = "bf16", 3, 8, 4, 6, 9
-    st_dtype = cache.storage_dtype(cache_fmt)
-    kc = np.full((NB, Hkv, BS, D), NAN_BITS[cache_fmt], dtype=st_dtype)
-    vc = kc.copy()
+    kc, vc = cache.empty_pools(NB, Hkv, BS, D, cache_fmt, NAN_BITS[cache_fmt])
     slots = rng.permutation(NB * BS)[:T].astype(np.int32)
     slots[2] = -1
     k = _bits(rng, (T, Hkv, D), act)
@@ -214,17 +209,26 @@ def test_p7_writer_touches_only_written_slots(cache_fmt):
         if s < 0:
             continue
         written[s // BS, s % BS] = True
+        kr, vr = cache.get_row(kc, vc, s // BS, s % BS)
         if cache_fmt == act:
-            assert np.array_equal(kc[s // BS, :, s % BS], k[n])
-            assert np.array_equal(vc[s // BS, :, s % BS], v[n])
+            assert np.array_equal(kr, k[n])
+            assert np.array_equal(vr, v[n])
         else:
             # Read-back through the decoder lands within half an E4M3 step.
-            back = e4m3.decode(kc[s // BS, :, s % BS], ks)
+            back = e4m3.decode(kr, ks)
             x = _f64(k[n], act)
             assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) / 16, 2.0 ** -10 * ks))
-    untouched = ~written
-    assert np.all(kc.transpose(0, 2, 1, 3)[untouched] == NAN_BITS[cache_fmt])
-    assert np.all(vc.transpose(0, 2, 1, 3)[untouched] == NAN_BITS[cache_fmt])
+    for blk, off in np.argwhere(~written):
+        kr, vr = cache.get_row(kc, vc, blk, off)
+        assert np.all(kr == NAN_BITS[cache_fmt]) and np.all(vr == NAN_BITS[cache_fmt])
+    # The two layouts put a row's elements where the ABI says.
+    blk, off = int(slots[0]) // BS, int(slots[0]) % BS
+    flat_k = kc[blk, 1].reshape(-1)
+    flat_v = vc[blk, 1].reshape(-1)
+    kr, vr = cache.get_row(kc, vc, blk, off)
+    for d in range(D):
+        assert flat_k[((d // 8) * BS + off) * 8 + d % 8] == kr[1, d]
+        assert flat_v[d * BS + off] == vr[1, d]
 
 
 # --- P9: brute force against scalar loops that never see a block table -----
@@ -247,7 +251,7 @@ def test_p9_brute_force_decode(data):
     Hkv = data.draw(st.integers(1, 2))
     G = data.draw(st.sampled_from([1, 2, 3]))
     Hq = Hkv * G
-    D = data.draw(st.integers(1, 8))
+    D = data.draw(st.sampled_from([8, 16, 24]))
     BS = data.draw(st.sampled_from([2, 4]))
     lens = [data.draw(st.integers(0, 11)) for _ in range(B)]
     seed = data.draw(st.integers(0, 2 ** 31 - 1))
@@ -256,16 +260,14 @@ def test_p9_brute_force_decode(data):
     NB = B * mbps + 2
     perm = rng.permutation(NB).astype(np.int32)
     bt = perm[: B * mbps].reshape(B, mbps)
-    kc = np.full((NB, Hkv, BS, D), NAN_BITS["bf16"], dtype=np.uint16)
-    vc = kc.copy()
+    kc, vc = cache.empty_pools(NB, Hkv, BS, D, "bf16", NAN_BITS["bf16"])
     seqs = []
     for b, L in enumerate(lens):
         k = _bits(rng, (L, Hkv, D), "bf16")
         v = _bits(rng, (L, Hkv, D), "bf16")
         seqs.append((k, v))
         for t in range(L):
-            kc[bt[b, t // BS], :, t % BS] = k[t]
-            vc[bt[b, t // BS], :, t % BS] = v[t]
+            cache.put_row(kc, vc, bt[b, t // BS], t % BS, k[t], v[t])
     q = _bits(rng, (B, Hq, D), "bf16")
     scale = 0.7
     out = attention.decode(q, "bf16", kc, vc, "bf16", bt, np.array(lens), scale)
@@ -286,7 +288,7 @@ def test_p9_brute_force_prefill(data):
     Hkv = data.draw(st.integers(1, 2))
     G = data.draw(st.sampled_from([1, 2]))
     Hq = Hkv * G
-    D = data.draw(st.integers(1, 6))
+    D = data.draw(st.sampled_from([8, 16]))
     BS = data.draw(st.sampled_from([2, 4]))
     chunks = [data.draw(st.integers(1, 5)) for _ in range(B)]
     prefix = [data.draw(st.integers(0, 7)) for _ in range(B)]
@@ -296,16 +298,14 @@ def test_p9_brute_force_prefill(data):
     NB = B * mbps + 1
     perm = rng.permutation(NB).astype(np.int32)
     bt = perm[: B * mbps].reshape(B, mbps)
-    kc = np.full((NB, Hkv, BS, D), NAN_BITS["f16"], dtype=np.uint16)
-    vc = kc.copy()
+    kc, vc = cache.empty_pools(NB, Hkv, BS, D, "f16", NAN_BITS["f16"])
     seqs = []
     for b, L in enumerate(ctx):
         k = _bits(rng, (L, Hkv, D), "f16")
         v = _bits(rng, (L, Hkv, D), "f16")
         seqs.append((k, v))
         for t in range(L):
-            kc[bt[b, t // BS], :, t % BS] = k[t]
-            vc[bt[b, t // BS], :, t % BS] = v[t]
+            cache.put_row(kc, vc, bt[b, t // BS], t % BS, k[t], v[t])
     cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     q = _bits(rng, (int(cu[-1]), Hq, D), "f16")
     out = attention.prefill_chunk(q, "f16", cu, kc, vc, "f16", bt, np.array(ctx), 0.6)
@@ -327,8 +327,7 @@ def test_fp8_decode_uses_scaled_codes():
     act, Hq, Hkv, D, BS = "bf16", 4, 2, 16, 4
     lens = [9, 4]
     NB = 8
-    kc = np.full((NB, Hkv, BS, D), 0x7F, dtype=np.uint8)
-    vc = kc.copy()
+    kc, vc = cache.empty_pools(NB, Hkv, BS, D, "e4m3", 0x7F)
     bt = np.array([[5, 2, 7], [0, 6, 6]], dtype=np.int32)
     ks, vs = 0.011, 0.013
     dense = []
