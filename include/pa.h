@@ -124,9 +124,11 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * max_context_len host-side upper bound of context_lens (sizes the split).
  * softmax_scale   multiplies q.k before the softmax.
  * k_scale,v_scale dequantisation scales of an E4M3 cache (ignored otherwise).
- * partition_tokens tokens per split-context partition, a multiple of BS; 0
- *                 lets the library choose; values above 64*BS act as 64*BS.
- *                 Results do not depend on it beyond rounding.
+ * partition_tokens split size hint, a multiple of BS: > 0 splits every
+ *                 sequence into ceil(max_len / partition_tokens) parts whose
+ *                 partial results are merged (max_len = max_context_len,
+ *                 capped at window); 0 lets the library choose.  Results do
+ *                 not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0).
  * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV

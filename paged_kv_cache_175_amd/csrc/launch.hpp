@@ -26,12 +26,14 @@ struct DecodeArgs {
   const void* value_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  int B, Hkv, G, D, MBPS, window, part_tok, NP;
+  int B, Hkv, G, D, MBPS, window;
+  int S;  // splits per (sequence, KV head)
+  int W;  // waves per workgroup (4 or 8)
   int act, cache;  // Fmt codes
   float softmax_scale, k_scale, v_scale;
-  float* ws_m;  // [B*Hq*NP]
-  float* ws_l;  // [B*Hq*NP]
-  float* ws_o;  // [B*Hq*NP*D]
+  float* ws_m;  // [B*Hq*S]
+  float* ws_l;  // [B*Hq*S]
+  float* ws_o;  // [B*Hq*S*D]
 };
 
 struct PrefillArgs {

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "launch.hpp"
 
@@ -49,42 +50,49 @@ bool cache_ok(pa_dtype act, pa_dtype cache) { return cache == act || cache == PA
 size_t elem_bytes(pa_dtype d) { return d == PA_F8E4M3 ? 1 : 2; }
 
 constexpr int kBlock = 32;
-constexpr int kMaxPartition = 64 * kBlock;  // a partition's pages fit one wave's lanes
+constexpr long long kTargetWaves = 2048;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split-context plan: tokens per partition and the number of partitions for
-// the longest sequence.  Partitions are whole pages, at most 64 of them.  The automatic choice
-// starts at 4 pages and doubles while the launch would exceed ~4096 waves,
-// which keeps every CU of the MI355X (256 CUs) busy with several waves while
-// bounding the partial-result traffic to a few percent of the K/V stream.
+// Split-context plan.  A workgroup of W waves handles one split of the pages
+// of one (sequence, KV head).  The automatic choice aims at ~2048 resident
+// waves (8 per CU on the 256 CUs of an MI355X): W = 8 while B * Hkv <= 256,
+// else W = 4; S splits per sequence so that B * Hkv * S * W ~ 2048, but with
+// at least two pages per wave on the longest sequence.  A wave holds the
+// block-table entries of its pages in one register, so a split spans at most
+// 64 * W pages.  partition_tokens > 0 forces S = ceil(len / partition_tokens).
 struct Plan {
-  int part_tok;
-  int NP;
+  int S;
+  int W;
 };
 
 bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, Plan* p) {
-  int L = max_len;
+  long long L = max_len;
   if (window > 0 && window < L) L = window;
   if (L < 1) L = 1;
-  int part = partition_tokens;
-  if (part == 0) {
-    const long long pages = (L + kBlock - 1) / kBlock;
-    long long pp = 4;
-    while (pp < pages && (long long)B * Hkv * ((pages + pp - 1) / pp) > 4096) pp *= 2;
-    part = (int)(pp * kBlock);
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0) return false;
+  const long long pages = (L + kBlock - 1) / kBlock;
+  const long long pairs = (long long)B * Hkv;
+  const int W = pairs > 256 ? 4 : 8;
+  long long S;
+  if (partition_tokens > 0) {
+    S = (L + partition_tokens - 1) / partition_tokens;
+  } else {
+    S = pairs > 0 ? kTargetWaves / (pairs * W) : 1;
+    S = std::min(S, pages / (2 * W));
+    S = std::max(S, 1LL);
   }
-  if (part <= 0 || part % kBlock != 0) return false;
-  if (part > kMaxPartition) part = kMaxPartition;
-  p->part_tok = part;
-  p->NP = (L + part - 1) / part;
+  S = std::max(S, (pages + 64LL * W - 1) / (64LL * W));
+  if (S > 65535) return false;
+  p->S = (int)S;
+  p->W = W;
   return true;
 }
 
 size_t workspace_for(int B, int Hq, int D, const Plan& p) {
-  if (p.NP <= 1) return 0;
-  const size_t rows = (size_t)B * Hq * p.NP;
+  if (p.S <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * p.S;
   return 2 * round_up(rows * sizeof(float), kAlign) + round_up(rows * D * sizeof(float), kAlign);
 }
 
@@ -188,7 +196,6 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
   Plan p;
   if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, &p))
     return fail(PA_ERR_INVALID, "bad partition size");
-  if (p.NP > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", p.NP);
   const size_t need = workspace_for(B, Hq, D, p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
@@ -208,15 +215,15 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
   a.D = D;
   a.MBPS = MBPS;
   a.window = window;
-  a.part_tok = p.part_tok;
-  a.NP = p.NP;
+  a.S = p.S;
+  a.W = p.W;
   a.act = fmt_of(act_dtype);
   a.cache = fmt_of(cache_dtype);
   a.softmax_scale = softmax_scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
-    const size_t rows = (size_t)B * Hq * p.NP;
+    const size_t rows = (size_t)B * Hq * p.S;
     char* w = static_cast<char*>(workspace);
     a.ws_m = reinterpret_cast<float*>(w);
     a.ws_l = reinterpret_cast<float*>(w + round_up(rows * sizeof(float), kAlign));
