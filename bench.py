@@ -51,6 +51,40 @@ def _args():
     return ap.parse_args()
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources, to tie recorded counter data to a build."""
+    import hashlib
+    d = os.path.join(ROOT, "paged_kv_cache_175_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config: str, kernel_prefix: str):
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    total = 0.0
+    found = False
+    for k, v in t.get("configs", {}).get(config, {}).items():
+        if k.startswith(kernel_prefix):
+            total += v["fetch_bytes"] + v["write_bytes"]
+            found = True
+    return round(total) if found else None
+
+
 def _workload(name):
     from paged_kv_cache_175_amd import workloads as W
     return {"mistral_decode": W.mistral_decode, "fp8_decode": W.fp8_decode,
@@ -197,9 +231,10 @@ def bench_decode(wl, a, torch):
         "kv_bytes_per_step": kv_bytes,
         "other_bytes_per_step": write_bytes + qo_bytes,
         "roofline": {
-            "kernel": "pa_decode (split-context pass 1 + merge pass 2)",
+            "kernel": "pa_decode (decode_split, plus decode_merge when a sequence is split)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(wl.name, "decode_"),
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
@@ -322,7 +357,8 @@ def bench_prefill(wl, a, torch):
         "tokens_per_s": round(wl.total_q / step_s, 1),
         "roofline": {"kernel": "pa_prefill_chunk", "bound": "mfma", "achieved": round(tf, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(wl.name, "prefill_"),
                      "algorithmic_flops_per_launch": flops},
     }
 
