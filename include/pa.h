@@ -89,6 +89,7 @@ const char* pa_last_error(void);
  *                 nearest even, saturation to +-448, NaN -> 0x7F|sign,
  *                 scale = k_scale for keys and v_scale for values (must be
  *                 finite and > 0).
+ * D must be a multiple of 8 and at most 512.
  * Every byte of the pools outside the written rows is left unchanged.
  * T == 0 is a no-op returning PA_OK.
  */

@@ -125,7 +125,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
   if (!cache_ok(act_dtype, cache_dtype))
     return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
-  if (D % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (D % 8 != 0 || D > 512)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8, at most 512");
   if ((long long)NB * BS >= (1LL << 31)) return fail(PA_ERR_INVALID, "NB*BS must be < 2^31");
   if (cache_dtype == PA_F8E4M3 &&
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))

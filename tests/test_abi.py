@@ -133,6 +133,7 @@ def test_workspace_query():
     (dict(T=-1), _lib.PA_ERR_INVALID),
     (dict(BS=64), _lib.PA_ERR_UNSUPPORTED),
     (dict(D=36), _lib.PA_ERR_UNSUPPORTED),
+    (dict(D=1024), _lib.PA_ERR_UNSUPPORTED),
     (dict(cache=_lib.PA_F8E4M3, ks=-1.0), _lib.PA_ERR_INVALID),
     (dict(key=0), _lib.PA_ERR_INVALID),
     (dict(kc=FAKE + 4), _lib.PA_ERR_INVALID),
