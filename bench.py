@@ -44,6 +44,8 @@ def _args():
                              "prefix_prefill"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for 2 GB)")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--separate-write", action="store_true",
+                    help="time pa_reshape_and_cache + pa_decode instead of pa_decode_append")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
@@ -159,14 +161,24 @@ def bench_decode(wl, a, torch):
     ws = ops.alloc_workspace(need, dev)
     out = torch.empty_like(q0)
 
+    # One step: store the 32 new tokens and attend.  Default: the fused
+    # pa_decode_append (one launch); --separate-write: pa_reshape_and_cache
+    # then pa_decode.
     writes, decodes = [], []
     for r in range(R):
         kc, vc = pools[r]
-        writes.append(ops.prepare_reshape_and_cache(new_k, new_v, kc, vc, new_slots,
-                                                    wl.k_scale, wl.v_scale))
-        decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
-                                          wl.k_scale, wl.v_scale, wl.window,
-                                          a.partition_tokens))
+        if a.separate_write:
+            writes.append(ops.prepare_reshape_and_cache(new_k, new_v, kc, vc, new_slots,
+                                                        wl.k_scale, wl.v_scale))
+            decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
+                                              wl.k_scale, wl.v_scale, wl.window,
+                                              a.partition_tokens))
+        else:
+            writes.append(lambda: None)
+            decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
+                                              wl.k_scale, wl.v_scale, wl.window,
+                                              a.partition_tokens, new_key=new_k,
+                                              new_value=new_v))
 
     kv_tokens = wl.kv_read_tokens()
     kv_bytes = kv_tokens * wl.Hkv * wl.D * elem * 2
@@ -178,9 +190,8 @@ def bench_decode(wl, a, torch):
         decodes[i % R]()
     torch.cuda.synchronize()
 
+    # Timed region 1: K back-to-back steps between two events (step time).
     K = a.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -188,16 +199,24 @@ def bench_decode(wl, a, torch):
     t_start.record()
     for i in range(K):
         writes[i % R]()
-        ev[i][0].record()
         decodes[i % R]()
-        ev[i][1].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+    step_s = total_ms / K * 1e-3
+    # Timed region 2: the same K steps with an event pair around every decode
+    # launch (its duration on the launch stream, for the roofline).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        writes[i % R]()
+        ev[i][0].record()
+        decodes[i % R]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
     dec_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     dec_avg_s = sum(dec_ms) / K * 1e-3
-    step_s = total_ms / K * 1e-3
 
     achieved = kv_bytes / dec_avg_s / 1e9
     res = {
@@ -220,6 +239,8 @@ def bench_decode(wl, a, torch):
             "context_tokens_read": kv_tokens, "max_context_len": max_len,
             "new_tokens_written": wl.B, "pool_blocks": wl.pool_blocks, "replicas": R,
             "partition_tokens": a.partition_tokens or "auto",
+            "step": "pa_reshape_and_cache + pa_decode" if a.separate_write
+                    else "pa_decode_append (write + decode in one launch)",
         },
         "tokens_per_s": round(wl.B / step_s, 1),
         "decode_tokens_per_s": round(wl.B / dec_avg_s, 1),
@@ -231,7 +252,8 @@ def bench_decode(wl, a, torch):
         "kv_bytes_per_step": kv_bytes,
         "other_bytes_per_step": write_bytes + qo_bytes,
         "roofline": {
-            "kernel": "pa_decode (decode_split, plus decode_merge when a sequence is split)",
+            "kernel": ("pa_decode" if a.separate_write else "pa_decode_append")
+                      + " (decode_split, plus decode_merge when a sequence is split)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(wl.name, "decode_"),
@@ -329,19 +351,23 @@ def bench_prefill(wl, a, torch):
         run()
     torch.cuda.synchronize()
     K = a.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(K):
         write()
-        ev[i][0].record()
         run()
-        ev[i][1].record()
     t1.record()
     torch.cuda.synchronize()
     step_s = t0.elapsed_time(t1) / K * 1e-3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        write()
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
     pre_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) / K * 1e-3
     flops = wl.flops()
     tf = flops / pre_s / 1e12

@@ -147,6 +147,29 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     void* stream);
 
 /*
+ * pa_decode_append -- pa_reshape_and_cache of the decoded token followed by
+ * pa_decode, in one launch.
+ *
+ * key, value      [B][Hkv][D] act_dtype: K and V of each sequence's decoded
+ *                 token.  Its cache row is context_lens[b] - 1 (window == 0)
+ *                 or (context_lens[b] - 1) % window (rolling buffer), in the
+ *                 block that block_tables names for that row; it is stored
+ *                 exactly as pa_reshape_and_cache stores it (E4M3 with
+ *                 k_scale / v_scale for an FP8 cache) and is part of the
+ *                 attention of this call.
+ * All other arguments, outputs and errors are those of pa_decode.  Caller
+ * contract: context_lens[b] >= 1 (a sequence with 0 gets zeros and no write).
+ */
+pa_status pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                           void* key_cache, void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                           float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, int32_t window,
+                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * pa_prefill_chunk -- causal attention of a chunk of new tokens per sequence
  * over everything cached for it (shared prefix blocks included).
  *

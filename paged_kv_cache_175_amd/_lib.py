@@ -36,6 +36,9 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_append": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+        ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _vp]),

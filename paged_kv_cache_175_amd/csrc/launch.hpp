@@ -34,6 +34,8 @@ struct DecodeArgs {
   float* ws_m;  // [B*Hq*S]
   float* ws_l;  // [B*Hq*S]
   float* ws_o;  // [B*Hq*S*D]
+  const void* new_key;    // append mode: [B][Hkv][D] act, or null
+  const void* new_value;
 };
 
 struct PrefillArgs {

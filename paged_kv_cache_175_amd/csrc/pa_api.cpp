@@ -157,14 +157,19 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   return workspace_for(B, Hq, D, p);
 }
 
-pa_status pa_decode(void* out, const void* query, const void* key_cache,
-                    const void* value_cache, const int32_t* block_tables,
-                    const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                    int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
-                    float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
-                    float k_scale, float v_scale, int32_t window,
-                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_decode_append share everything but the appended row.
+pa_status decode_common(void* out, const void* query, const void* new_key,
+                        const void* new_value, const void* key_cache, const void* value_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                        int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_t MBPS,
+                        int32_t max_context_len, float softmax_scale, pa_dtype act_dtype,
+                        pa_dtype cache_dtype, float k_scale, float v_scale, int32_t window,
+                        int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || MBPS < 1 || max_context_len < 0)
     return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_context_len out of range");
   if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
@@ -230,9 +235,47 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
     a.ws_l = reinterpret_cast<float*>(w + round_up(rows * sizeof(float), kAlign));
     a.ws_o = reinterpret_cast<float*>(w + 2 * round_up(rows * sizeof(float), kAlign));
   }
+  a.new_key = new_key;
+  a.new_value = new_value;
   hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                    int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                    float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                    float k_scale, float v_scale, int32_t window,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                       context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len, softmax_scale,
+                       act_dtype, cache_dtype, k_scale, v_scale, window, partition_tokens,
+                       workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                           void* key_cache, void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                           float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, int32_t window,
+                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (B > 0 && (key == nullptr || value == nullptr))
+    return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!aligned(key, 2) || !aligned(value, 2))
+    return fail(PA_ERR_INVALID, "key/value must be 2-byte aligned");
+  return decode_common(out, query, key, value, key_cache, value_cache, block_tables,
+                       context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len, softmax_scale,
+                       act_dtype, cache_dtype, k_scale, v_scale, window, partition_tokens,
+                       workspace, workspace_bytes, stream);
 }
 
 pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_lens,

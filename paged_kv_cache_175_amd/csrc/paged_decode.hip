@@ -25,6 +25,9 @@
 //     and O += P V runs as D/16 MFMAs whose B operands are single loads from
 //     the transposed V page [D][32].
 //
+// Append mode (pa_decode_append) also stores the decoded token's K/V into its
+// cache row in the same launch; the wave reading that row takes it from LDS.
+//
 // The W partial results of a workgroup are combined through LDS.  When a
 // sequence is one split (S == 1, the usual case once B * Hkv workgroups fill
 // the GPU) that is the output; otherwise each split writes (m, l, o) to the
@@ -98,10 +101,12 @@ __device__ __forceinline__ int tile_token(int tt, int col) {
 template <int D, int G, int CF, int AF, int W>
 __global__ __launch_bounds__(64 * W) void decode_split(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
-    const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
+    uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int Hkv, int MBPS, int window, int S, float qk_scale_log2, float v_scale,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+    const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
+    float k_enc_scale, float v_enc_scale) {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
   constexpr int EB = (CF == FMT_E4M3) ? 1 : 2;
@@ -113,6 +118,8 @@ __global__ __launch_bounds__(64 * W) void decode_split(
   __shared__ float m_lds[W][G];
   __shared__ float l_lds[W][G];
   __shared__ __attribute__((aligned(16))) float o_lds[W][G][D];
+  __shared__ __attribute__((aligned(16))) uint16_t newk_lds[D];
+  __shared__ __attribute__((aligned(16))) uint16_t newv_lds[D];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -142,6 +149,45 @@ __global__ __launch_bounds__(64 * W) void decode_split(
   const int pa = (int)((long long)s * P / S);
   const int pb = (int)((long long)(s + 1) * P / S);
   const int npg = pb - pa > wave ? (pb - pa - wave + W - 1) / W : 0;  // <= 64 (host plan)
+
+  // Append mode: the decoded token's K/V (new_key / new_value [B][Hkv][D])
+  // belong in cache row r_new (the last position, or its ring row).  The
+  // split that owns that row's page stores it (E4M3-encoded when the cache
+  // is FP8) and stages the stored values in LDS; the one wave that reads the
+  // page patches the row into its MFMA operands, so nothing in this launch
+  // depends on the store becoming visible.
+  int row_new = -1, k_new = -1, w_new = -1;
+  if (new_key != nullptr) {
+    const int ctx = context_lens[b];
+    const int r_new = window > 0 ? (ctx - 1) % window : ctx - 1;
+    const int pg_new = r_new / kPage;
+    if (pg_new >= pa && pg_new < pb) {
+      row_new = r_new - pg_new * kPage;
+      w_new = (pg_new - pa) % W;
+      k_new = (pg_new - pa) / W;
+      const int phys = block_tables[(size_t)b * MBPS + pg_new];
+      const size_t page = ((size_t)phys * Hkv + g) * (size_t)kPage * D;
+      const size_t src = ((size_t)b * Hkv + g) * D;
+      for (int d = threadIdx.x; d < D; d += 64 * W) {
+        const uint16_t kx = new_key[src + d];
+        const uint16_t vx = new_value[src + d];
+        if constexpr (CF == FMT_E4M3) {
+          const uint32_t kq = e4m3_encode(lo16_to_f32<AF>(kx), k_enc_scale);
+          const uint32_t vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
+          key_cache[page + k_page_off(row_new, d)] = static_cast<uint8_t>(kq);
+          value_cache[page + v_page_off(row_new, d)] = static_cast<uint8_t>(vq);
+          newk_lds[d] = static_cast<uint16_t>(e4m3x2_to_16<AF, false>(kq) & 0xffffu);
+          newv_lds[d] = static_cast<uint16_t>(e4m3x2_to_16<AF, false>(vq) & 0xffffu);
+        } else {
+          reinterpret_cast<uint16_t*>(key_cache)[page + k_page_off(row_new, d)] = kx;
+          reinterpret_cast<uint16_t*>(value_cache)[page + v_page_off(row_new, d)] = vx;
+          newk_lds[d] = kx;
+          newv_lds[d] = vx;
+        }
+      }
+    }
+  }
+  __syncthreads();
 
   float m_run[4], l_run[4];
 #pragma unroll
@@ -213,13 +259,20 @@ __global__ __launch_bounds__(64 * W) void decode_split(
     };
 
     auto compute_page = [&](const PageRegs<D, CF>& Pg, int k) {
+      // Is this the page holding the appended row?  (Wave-uniform.)
+      const bool patch = wave == w_new && k == k_new;
       // S = Q K^T; lane (r4, col) gets heads 4*r4 + r, tokens tok0 and tok1.
       f32x4 sc4[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         sc4[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) sc4[tt] = Mfma<AF>::mma(qa[j], k_operand(Pg, tt, j), sc4[tt]);
+        for (int j = 0; j < KSTEPS; ++j) {
+          vec kop = k_operand(Pg, tt, j);
+          if (patch && tile_token<CF>(tt, col) == row_new)
+            kop = *reinterpret_cast<const vec*>(&newk_lds[8 * (r4 + 4 * j)]);
+          sc4[tt] = Mfma<AF>::mma(qa[j], kop, sc4[tt]);
+        }
       }
       const int base = (pa + wave + W * k) * kPage;
       const int tok0 = tile_token<CF>(0, col);
@@ -286,6 +339,18 @@ __global__ __launch_bounds__(64 * W) void decode_split(
             const uint32_t lo = (tok + 2 * e < L) ? 0xffffu : 0u;
             const uint32_t hi = (tok + 2 * e + 1 < L) ? 0xffff0000u : 0u;
             w[e] &= (lo | hi);
+          }
+          vb = __builtin_bit_cast(vec, w);
+        }
+        if (patch && r4 == (row_new >> 3)) {
+          // Element row_new % 8 of this lane's 8 tokens is the appended row.
+          u32x4 w = __builtin_bit_cast(u32x4, vb);
+          const uint32_t x = newv_lds[16 * n + col];
+          const int e = row_new & 7;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (q == (e >> 1))
+              w[q] = (e & 1) ? ((w[q] & 0xffffu) | (x << 16)) : ((w[q] & 0xffff0000u) | x);
           }
           vb = __builtin_bit_cast(vec, w);
         }
@@ -426,14 +491,18 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.S, a.Hkv, a.B);
   if (a.W == 8) {
     hipLaunchKernelGGL((decode_split<D, G, CF, AF, 8>), grid, dim3(512), 0, stream,
-                       (uint16_t*)a.out, (const uint16_t*)a.query, (const uint8_t*)a.key_cache,
-                       (const uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
-                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o);
+                       (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
+                       (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
+                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
+                       a.v_scale);
   } else if (a.W == 4) {
     hipLaunchKernelGGL((decode_split<D, G, CF, AF, 4>), grid, dim3(256), 0, stream,
-                       (uint16_t*)a.out, (const uint16_t*)a.query, (const uint8_t*)a.key_cache,
-                       (const uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
-                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o);
+                       (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
+                       (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
+                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
+                       a.v_scale);
   } else {
     return hipErrorInvalidValue;
   }

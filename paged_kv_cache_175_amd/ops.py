@@ -133,11 +133,14 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
            block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
            softmax_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
            window: int = 0, partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, new_key: Optional[torch.Tensor] = None,
+           new_value: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged decode attention; returns ``out`` ``[B, Hq, D]``.
 
     ``workspace`` (uint8, >= :func:`decode_workspace_bytes`) is allocated here
-    when not given.
+    when not given.  With ``new_key`` / ``new_value`` (``[B, Hkv, D]``) the
+    decoded token is first stored into its cache row in the same launch
+    (``pa_decode_append``).
     """
     _dev(query, key_cache, value_cache, block_tables, context_lens)
     _i32(block_tables, context_lens)
@@ -159,12 +162,27 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = _lib.load()
-    _lib.check(lib.pa_decode(
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
-        int(max_context_len), float(softmax_scale), act, cache, float(k_scale),
-        float(v_scale), int(window), int(partition_tokens), ws_ptr, ws_bytes, _stream()))
+    tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+            int(max_context_len), float(softmax_scale), act, cache, float(k_scale),
+            float(v_scale), int(window), int(partition_tokens), ws_ptr, ws_bytes, _stream())
+    if new_key is None:
+        _lib.check(lib.pa_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                                 value_cache.data_ptr(), *tail))
+    else:
+        _check_new_token(new_key, new_value, query, Hkv, D)
+        _lib.check(lib.pa_decode_append(out.data_ptr(), query.data_ptr(), new_key.data_ptr(),
+                                        new_value.data_ptr(), key_cache.data_ptr(),
+                                        value_cache.data_ptr(), *tail))
     return out
+
+
+def _check_new_token(new_key, new_value, query, Hkv, D):
+    _dev(new_key, new_value)
+    B = query.shape[0]
+    if new_value is None or new_key.shape != (B, Hkv, D) or new_value.shape != (B, Hkv, D):
+        raise ValueError("new_key / new_value must both be [B, Hkv, D]")
+    if new_key.dtype != query.dtype or new_value.dtype != query.dtype:
+        raise TypeError("new_key / new_value must have the activation dtype")
 
 
 def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch.Tensor,
@@ -223,7 +241,7 @@ def prepare_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
 def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
                    max_context_len: int, softmax_scale: float, out, workspace=None,
                    k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
-                   partition_tokens: int = 0):
+                   partition_tokens: int = 0, new_key=None, new_value=None):
     _dev(query, key_cache, value_cache, block_tables, context_lens, out)
     _i32(block_tables, context_lens)
     B, Hq, D = query.shape
@@ -234,13 +252,20 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
     if ws_bytes < need:
         raise PagedKVError(_lib.PA_ERR_WORKSPACE, f"workspace needs {need} bytes")
     lib = _lib.load()
-    args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-            block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+    tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
             int(max_context_len), float(softmax_scale), _act_code(query),
             _cache_code(key_cache, query.dtype), float(k_scale), float(v_scale), int(window),
             int(partition_tokens), 0 if workspace is None else workspace.data_ptr(), ws_bytes,
             _stream())
-    fn = lib.pa_decode
+    if new_key is None:
+        args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                value_cache.data_ptr()) + tail
+        fn = lib.pa_decode
+    else:
+        _check_new_token(new_key, new_value, query, Hkv, D)
+        args = (out.data_ptr(), query.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
+                key_cache.data_ptr(), value_cache.data_ptr()) + tail
+        fn = lib.pa_decode_append
 
     def call():
         _lib.check(fn(*args))

@@ -81,6 +81,32 @@ def hip_decode_setup(wl: DecodeWorkload, device="cuda"):
     return kc, vc
 
 
+def hip_decode_append_setup(wl: DecodeWorkload, device="cuda"):
+    """Pools holding only the cached tokens; the new ones go in with the decode."""
+    kc, vc = gpu_pools(wl, device)
+    ks, vs, sl = [], [], []
+    for b in range(wl.B):
+        n = wl.cached_k[b].shape[0]
+        if n:
+            pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+            sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+            ks.append(wl.cached_k[b])
+            vs.append(wl.cached_v[b])
+    if sl:
+        _gpu_write(wl, kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(sl), device)
+    return kc, vc
+
+
+def hip_decode_append(wl: DecodeWorkload, kc, vc, partition_tokens=0, device="cuda"):
+    q = _act_tensor(wl.query, wl.act, device)
+    bt = torch.from_numpy(wl.block_tables).to(device)
+    cl = torch.from_numpy(wl.context_lens).to(device)
+    return ops.decode(q, kc, vc, bt, cl, int(wl.context_lens.max(initial=0)), wl.scale,
+                      wl.k_scale, wl.v_scale, wl.window, partition_tokens,
+                      new_key=_act_tensor(wl.new_k, wl.act, device),
+                      new_value=_act_tensor(wl.new_v, wl.act, device))
+
+
 def hip_decode(wl: DecodeWorkload, kc, vc, partition_tokens=0, device="cuda"):
     q = _act_tensor(wl.query, wl.act, device)
     bt = torch.from_numpy(wl.block_tables).to(device)

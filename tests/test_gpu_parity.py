@@ -63,6 +63,34 @@ def test_decode_parity(name):
     _check_decode(DECODE_CASES[name]())
 
 
+def _check_decode_append(wl, partition_tokens=0):
+    """Fused write + decode: same pool bytes and outputs as the oracle's
+    writer followed by its decode."""
+    P.say(f"[decode_append] {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} act={wl.act} "
+          f"cache={wl.cache} W={wl.window} part={partition_tokens}")
+    kc, vc = P.hip_decode_append_setup(wl)
+    out = P.hip_decode_append(wl, kc, vc, partition_tokens)
+    torch.cuda.synchronize()
+    okc, ovc = P.oracle_decode_setup(wl)
+    assert np.array_equal(P.pool_bits(kc), okc), "key pool bytes differ"
+    assert np.array_equal(P.pool_bits(vc), ovc), "value pool bytes differ"
+    ref = P.oracle_decode(wl, okc, ovc)
+    err = P.max_abs(P.out_f64(out), ref)
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL[wl.cache], f"max-abs error {err} > {P.TOL[wl.cache]}"
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_decode_append_parity(name):
+    _check_decode_append(DECODE_CASES[name]())
+
+
+@pytest.mark.parametrize("part", [32, 96, 512])
+def test_decode_append_forced_splits(part):
+    _check_decode_append(DECODE_CASES["mistral_small"](), partition_tokens=part)
+    _check_decode_append(DECODE_CASES["sliding_fp8"](), partition_tokens=part)
+
+
 @pytest.mark.parametrize("part", [32, 64, 96, 160, 512, 4096])
 def test_decode_forced_splits(part):
     _check_decode(DECODE_CASES["mistral_small"](), partition_tokens=part)
