@@ -53,30 +53,39 @@ def _args():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources, to tie recorded counter data to a build."""
+# Sources whose change alters a kernel's memory traffic: the kernel file plus
+# the shared device helpers and the host planner that picks its grid.
+_KERNEL_SOURCES = {
+    "decode_": ("paged_decode.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
+    "prefill_": ("paged_prefill.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
+}
+
+
+def kernel_source_hash(kernel_prefix: str) -> str:
+    """sha256 over the HIP sources a kernel family is built from, to tie
+    recorded counter data to a build of that kernel."""
     import hashlib
     d = os.path.join(ROOT, "paged_kv_cache_175_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+    for f in _KERNEL_SOURCES[kernel_prefix]:
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
 def recorded_traffic(config: str, kernel_prefix: str):
     """HBM bytes per launch of the dominant kernel, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
-    kernel sources; else None."""
+    sources of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != kernel_source_hash():
+    hashes = t.get("source_sha256")
+    if not isinstance(hashes, dict) or hashes.get(kernel_prefix) != kernel_source_hash(kernel_prefix):
         return None
     total = 0.0
     found = False
@@ -205,18 +214,18 @@ def bench_decode(wl, a, torch):
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     step_s = total_ms / K * 1e-3
-    # Timed region 2: the same K steps with an event pair around every decode
-    # launch (its duration on the launch stream, for the roofline).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    # Timed region 2: K back-to-back launches of the decode kernel alone
+    # between two events on its launch stream: its average launch duration,
+    # for the roofline.  (With the fused write this is region 1 again; with
+    # --separate-write the writer is left out.)
+    d_start = torch.cuda.Event(enable_timing=True)
+    d_end = torch.cuda.Event(enable_timing=True)
+    d_start.record()
     for i in range(K):
-        writes[i % R]()
-        ev[i][0].record()
         decodes[i % R]()
-        ev[i][1].record()
+    d_end.record()
     torch.cuda.synchronize()
-    dec_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    dec_avg_s = sum(dec_ms) / K * 1e-3
+    dec_avg_s = d_start.elapsed_time(d_end) / K * 1e-3
 
     achieved = kv_bytes / dec_avg_s / 1e9
     res = {
@@ -245,8 +254,6 @@ def bench_decode(wl, a, torch):
         "tokens_per_s": round(wl.B / step_s, 1),
         "decode_tokens_per_s": round(wl.B / dec_avg_s, 1),
         "decode_us": round(dec_avg_s * 1e6, 3),
-        "decode_us_p10_p90": [round(float(x) * 1e3, 3) for x in
-                              np.percentile(np.array(dec_ms), [10, 90])],
         "step_us": round(step_s * 1e6, 3),
         "wall_us_per_step": round(wall / K * 1e6, 3),
         "kv_bytes_per_step": kv_bytes,
@@ -360,15 +367,15 @@ def bench_prefill(wl, a, torch):
     t1.record()
     torch.cuda.synchronize()
     step_s = t0.elapsed_time(t1) / K * 1e-3
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    # Kernel duration: K back-to-back prefill launches between two events.
+    t2 = torch.cuda.Event(enable_timing=True)
+    t3 = torch.cuda.Event(enable_timing=True)
+    t2.record()
     for i in range(K):
-        write()
-        ev[i][0].record()
         run()
-        ev[i][1].record()
+    t3.record()
     torch.cuda.synchronize()
-    pre_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) / K * 1e-3
+    pre_s = t2.elapsed_time(t3) / K * 1e-3
     flops = wl.flops()
     tf = flops / pre_s / 1e12
     return {
