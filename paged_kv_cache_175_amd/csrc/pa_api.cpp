@@ -305,7 +305,9 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_len
     return fail(PA_ERR_INVALID, "out/query must be 16-byte aligned");
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
     return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
-  if ((long long)B > 65535 || Hq > 65535) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  // Query rows (position, head) of one sequence and the flat grid must fit in int32.
+  if ((long long)max_chunk_len * Hq * B > 0x7fffff00LL)
+    return fail(PA_ERR_UNSUPPORTED, "max_chunk_len * Hq * B too large");
   pa::PrefillArgs a{};
   a.out = out;
   a.query = query;

@@ -9,20 +9,54 @@
 // ("PagedAttention in mistral.rs": prefix caching works with the paged cache,
 // and prefill runs as a separate attention kernel when FlashAttention is on).
 //
-// Work split.  A workgroup of 4 waves owns 128 consecutive queries of one
-// (sequence, query head); each wave owns 32 of them as two 16-row MFMA tiles.
-// The workgroup walks the key pages of the sequence (32 tokens each) up to
-// the last position its queries can see:
+// Work split.  The query rows of one (sequence, KV head) are the pairs
+// (position j, head h in the KV head's group), numbered row = j * G + h, so a
+// staged K/V page serves all G query heads that read it.  A workgroup of 4
+// waves owns 64 * NQ consecutive rows; each wave owns NQ tiles of 16 rows.
+// The workgroup walks the sequence's key pages (32 tokens each) up to the last
+// position its rows can see.  Pages of a 16-bit cache go from global memory
+// straight into LDS (global_load_lds_dwordx4, no registers), two pages ahead
+// of the one being computed, through three LDS buffers and one barrier a
+// page.  E4M3 pages are widened to the activation format on the way, so they
+// pass through registers, one page ahead, through two buffers.
 //
-//   * the 256 threads copy the page into LDS as K [32][D] and V [D][32] (the
-//     cache pages are K [D/8][32][8] and V [D][32], so both copies move
-//     16-byte chunks and both MFMA operands become 16-byte LDS reads); rows
-//     at or past the context end are zeroed, and E4M3 codes are widened to
-//     the activation format (exactly) on the way in;
-//   * each wave: S = Q K^T (v_mfma_f32_16x16x32), causal mask, online softmax
-//     in log2 units, P rounded to the activation format and passed through
-//     LDS into the A-operand layout, O += P V.
-// The output is O / l, rounded to the activation format.
+// Per wave and page, everything is computed transposed so that the
+// probabilities never leave registers:
+//   S^T = K Q^T   (v_mfma_f32_16x16x32; K from LDS as the A operand, Q held
+//                  in registers as the B operand).  The two 16-key A tiles of
+//                  a page take the keys with bit 2 clear and set: tile kt row
+//                  x is key 8 * (x / 4) + 4 * kt + x % 4.  Lane l then holds,
+//                  for query column l % 16, the eight consecutive keys
+//                  8 * (l / 16) .. 8 * (l / 16) + 7;
+//   P^T = exp2(S^T * c - m), rounded to the activation format: those eight
+//                  values per lane are exactly a B operand over the page's
+//                  keys in natural order;
+//   O^T += V^T P^T (A operand = V^T: eight consecutive tokens of one head
+//                  dimension, one 16-byte LDS read).
+// LDS pages keep the cache's chunk layout (K [D/8][32][8], V [D][32]) with the
+// 16-byte chunks of each row XOR-swizzled so that both operand reads are free
+// of bank conflicts.
+// The running sum l of each query comes out of the same MFMAs: one more
+// O^T tile whose V^T rows are all ones gives sum_k P[k][q] in every row, so
+// l is accumulated from the rounded P that also weights V, and is rescaled
+// with O.  The running maximum m is only raised when a new score exceeds it
+// by more than 2^8 (any lane, checked with a ballot), so the cross-lane
+// maximum and the rescale of O run on a few pages only.  Probabilities
+// therefore stay below 2^8, which fp32 accumulation and the 16-bit P operand
+// both hold without loss of relative precision.
+//
+// Rows at or past the context end in a sequence's last page hold stale data.
+// Their scores are always masked (every query sits before the context end),
+// and on that page the V operand is zeroed there, so no Inf or NaN reaches
+// the accumulators through a zero probability.
+//
+// Workgroup order: workgroups are dispatched to the 8 XCDs round-robin, so
+// the flat workgroup id is remapped to give each XCD a contiguous range of
+// (KV head, sequence, row tile) items.  The workgroups that read one KV
+// head's shared prefix pages then run on one XCD, close in time, and hit in
+// its L2.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -31,224 +65,389 @@ namespace pa {
 namespace {
 
 constexpr int BS = 32;
-constexpr int QT = 128;          // queries per workgroup
-constexpr int QW = 32;           // queries per wave
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;
 constexpr float LOG2E_P = 1.4426950408889634f;
+// Scores (in log2 units) may exceed the running maximum by this much before
+// the maximum is raised.
+constexpr float kSlack = 8.0f;
 
-template <int D, int CF, int AF>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), mask, 64));
+}
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Four 16-bit values of an activation format (hardware conversion, round to
+// nearest even).
+template <int AF>
+struct Vec4;
+template <>
+struct Vec4<FMT_BF16> {
+  typedef __bf16 type __attribute__((ext_vector_type(4)));
+};
+template <>
+struct Vec4<FMT_F16> {
+  typedef _Float16 type __attribute__((ext_vector_type(4)));
+};
+
+// LDS chunk slots (16-byte chunks, in chunk units within one page).  Both
+// maps are involutions on the row index bits they touch, so the same
+// functions map a slot back to its cache chunk.
+__device__ __forceinline__ int k_slot(int dc, int t) { return dc * BS + (t ^ (((t >> 3) & 1) << 2)); }
+__device__ __forceinline__ int v_slot(int d, int tq) { return d * 4 + (tq ^ ((d >> 1) & 3)); }
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that does not wait for outstanding global loads (a
+// __syncthreads would drain the LDS-direct loads still in flight for later
+// pages).  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int CF, int AF, int NQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const int32_t* __restrict__ cu_q_lens, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int Hq, int Hkv, int MBPS,
-    float qk_scale_log2, float v_scale) {
-  constexpr int KSTEPS = D / 32;
-  constexpr int NT = D / 16;            // 16-wide output column tiles
-  constexpr int KROW = D + 8;           // padded LDS row of K (elements)
-  constexpr int VROW = BS + 8;          // padded LDS row of transposed V
-  constexpr int EB = (CF == FMT_E4M3) ? 1 : 2;
-  constexpr int CPR = D / 8;            // 8-element chunks per token row
+    const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int B, int MBPS,
+    int row_tiles, float qk_scale_log2, float v_scale) {
+  constexpr int KS = D / 32;              // k-steps of S^T (32 head dims each)
+  constexpr int NT = D / 16;              // 16-dim tiles of O^T
+  constexpr int PAGE = BS * D;            // elements of one K (or V) page
+  constexpr bool kDma = CF != FMT_E4M3;
+  constexpr int NBUF = kDma ? 3 : 2;
+  constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
+  constexpr int NCH = PAGE / 8;           // 8-element chunks per page (K or V)
+  constexpr int RW = 16 * NQ * kWaves;    // rows per workgroup
+  // LDS-direct loads: 64 chunks (1 KiB) per wave instruction; the K and V
+  // pages together are D / 8 such units, D / 32 per wave.
+  constexpr int UPW = D / 32;
+  // Register staging (E4M3): chunks per thread.
+  constexpr int ST = (NCH + kThreads - 1) / kThreads;
   typedef typename Mfma<AF>::vec vec;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BS * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VROW];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds[4][QW * (BS + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF][PAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NBUF][PAGE];
+
+  // --- which (KV head, sequence, row tile) this workgroup owns -----------
+  const int n_items = row_tiles * Hkv * B;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= n_items) return;
+  const int x = item % row_tiles;
+  const int b = (item / row_tiles) % B;
+  const int g = item / (row_tiles * B);
+
+  const int q_begin = cu_q_lens[b];
+  const int C = cu_q_lens[b + 1] - q_begin;
+  const int rows = C * G;
+  if (x * RW >= rows) return;
+  const int ctx = context_lens[b];
+  const int first_pos = ctx - C;               // absolute position of query 0
+  const int last_row_wg = min(rows, x * RW + RW) - 1;
+  const int npages = (first_pos + last_row_wg / G) / BS + 1;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int col = lane & 15;
-  const int r4 = lane >> 4;
+  const int q4 = lane >> 4;
 
-  const int tile = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int G = Hq / Hkv;
-  const int g = h / G;
+  const int row0 = x * RW + wave * 16 * NQ;    // first row of this wave
+  const bool wave_live = row0 < rows;
+  const int pos_lo = first_pos + row0 / G;                              // earliest query
+  const int pos_hi = first_pos + min(rows - 1, row0 + 16 * NQ - 1) / G;  // latest query
 
-  const int q_begin = cu_q_lens[b];
-  const int C = cu_q_lens[b + 1] - q_begin;
-  if (tile * QT >= C) return;
-  const int ctx = context_lens[b];
-  const int first_pos = ctx - C;                    // absolute position of query 0
-  const int j_wave = tile * QT + wave * QW;         // first query of this wave
-  const int j_last_wg = min(C, tile * QT + QT) - 1;
-  const int last_pos_wg = first_pos + j_last_wg;
-  const int npages = last_pos_wg / BS + 1;
-
-  // Q of this wave as A operands: tile mt, row 16mt + col, k chunk r4 + 4j.
-  vec qa[2][KSTEPS];
+  // Q^T operands and the query position of each tile column this lane holds.
+  vec qb[NQ][KS];
+  int qpos[NQ];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int j = j_wave + 16 * mt + col;
-    const bool live = j < C;
-    const uint16_t* qrow = query + ((size_t)(q_begin + (live ? j : 0)) * Hq + h) * D;
+  for (int t = 0; t < NQ; ++t) {
+    const int r = row0 + 16 * t + col;
+    const bool live = r < rows;
+    const int j = live ? r / G : C - 1;
+    const int hq = g * G + (live ? r - j * G : 0);
+    qpos[t] = first_pos + j;
+    const uint16_t* qrow = query + ((size_t)(q_begin + j) * Hq + hq) * D;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * (r4 + 4 * s));
+    for (int s = 0; s < KS; ++s) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * q4);
       if (!live) w = u32x4{0u, 0u, 0u, 0u};
-      qa[mt][s] = __builtin_bit_cast(vec, w);
+      qb[t][s] = __builtin_bit_cast(vec, w);
     }
   }
 
-  float m_run[2][4], l_run[2][4];
-  f32x4 o_acc[2][NT];
+  // o_acc[NT] is the all-ones tile: every row holds the running sum l.
+  float m_run[NQ];
+  f32x4 o_acc[NT + 1][NQ];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int t = 0; t < NQ; ++t) {
+    m_run[t] = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m_run[mt][r] = -INFINITY;
-      l_run[mt][r] = 0.f;
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) o_acc[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n <= NT; ++n) o_acc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const vec ones = __builtin_convertvector(f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, vec);
 
-  // Absolute positions of the rows this lane holds in the S/O layout.
-  int row_pos[2][4];
+  // Operand offsets (elements) inside a staged page.  K: chunk row
+  // (4s + q4), key row 8 * (col / 4) + 4 * kt + col % 4.  V: head dim
+  // 16n + col, token chunk q4.
+  int k_off[2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) row_pos[mt][r] = first_pos + j_wave + 16 * mt + 4 * r4 + r;
-  const int wave_last_pos = first_pos + min(C - 1, j_wave + QW - 1);
-  const bool wave_live = j_wave < C;
+  for (int kt = 0; kt < 2; ++kt) k_off[kt] = k_slot(q4, 8 * (col >> 2) + 4 * kt + (col & 3)) * 8;
+  const int v_off = v_slot(col, q4) * 8;       // + 16 * 4 * 8 * n (the swizzle ignores d / 16)
 
+  // --- page staging ------------------------------------------------------
   const int32_t* bt = block_tables + (size_t)b * MBPS;
-  uint16_t* pw = p_lds[wave];
+  int bt_reg = lane < npages ? bt[lane] : 0;   // physical blocks of pages 0..63
+  const size_t head_off = (size_t)g * PAGE;
+  const size_t blk_stride = (size_t)Hkv * PAGE;
+  auto phys_of = [&](int q) {
+    if ((q & 63) == 0 && q > 0) bt_reg = q + lane < npages ? bt[q + lane] : 0;
+    return __builtin_amdgcn_readlane(bt_reg, q & 63);
+  };
 
-  for (int pg = 0; pg < npages; ++pg) {
-    const int phys = bt[pg];
-    const size_t page_off = ((size_t)phys * Hkv + g) * (size_t)BS * D;
-    const int base = pg * BS;
-
-    // Stage K (row-major [32][D]) and V (transposed [D][32]) of the page in
-    // LDS.  Cache pages are K [D/8][32][8] and V [D][32], so both copies are
-    // 8-element chunks.  Rows at or past the context end are zeroed.
-    for (int c = tid; c < BS * CPR; c += 256) {
-      // K chunk: token t, dims 8*dc .. 8*dc + 7.
-      const int t = c % BS;
-      const int dc = c / BS;
-      u32x4 kw = u32x4{0u, 0u, 0u, 0u};
-      if (base + t < ctx) {
-        const size_t src = (page_off + (size_t)(dc * BS + t) * 8) * EB;
-        if constexpr (CF == FMT_E4M3) {
-          kw = e4m3x8_to_16<AF>(*reinterpret_cast<const u32x2*>(key_cache + src));
-        } else {
-          kw = *reinterpret_cast<const u32x4*>(key_cache + src);
-        }
-      }
-      *reinterpret_cast<u32x4*>(&k_lds[t * KROW + 8 * dc]) = kw;
-      // V chunk: dim d, tokens 8*tq .. 8*tq + 7.
-      const int d = c / 4;
-      const int tq = c % 4;
-      const size_t vsrc = (page_off + (size_t)d * BS + 8 * tq) * EB;
-      u32x4 vw;
-      if constexpr (CF == FMT_E4M3) {
-        vw = e4m3x8_to_16<AF>(*reinterpret_cast<const u32x2*>(value_cache + vsrc));
-      } else {
-        vw = *reinterpret_cast<const u32x4*>(value_cache + vsrc);
-      }
-      const int tok = base + 8 * tq;
-      if (tok + 8 > ctx) {
+  // LDS-direct path: source byte offset (inside a page) of this lane's chunk
+  // in each of the wave's units.
+  int dma_src[UPW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (tok + 2 * e < ctx) ? 0xffffu : 0u;
-          const uint32_t hi = (tok + 2 * e + 1 < ctx) ? 0xffff0000u : 0u;
-          vw[e] &= (lo | hi);
-        }
-      }
-      *reinterpret_cast<u32x4*>(&v_lds[d * VROW + 8 * tq]) = vw;
+  for (int i = 0; i < UPW; ++i) {
+    const int u = wave * UPW + i;
+    if (u < D / 16) {
+      const int s = u * 64 + lane;             // K slot
+      dma_src[i] = k_slot(s >> 5, s & 31) * 16;
+    } else {
+      const int s = (u - D / 16) * 64 + lane;  // V slot
+      dma_src[i] = v_slot(s >> 2, s & 3) * 16;
     }
+  }
+  auto dma_page = [&](int phys, int buf) {
+    const size_t page = ((size_t)phys * blk_stride + head_off) * EB;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int u = wave * UPW + i;
+      const bool is_k = u < D / 16;
+      const uint8_t* src = (is_k ? key_cache : value_cache) + page + dma_src[i];
+      uint16_t* dst = is_k ? &k_lds[buf][u * 512] : &v_lds[buf][(u - D / 16) * 512];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                       0);
+    }
+  };
+
+  // Register path (E4M3): chunk c of the K page is (d / 8, t) = (c / 32,
+  // c % 32) and chunk c of the V page is (d, t / 8) = (c / 4, c % 4).
+  u32x2 kreg[kDma ? 1 : ST], vreg[kDma ? 1 : ST];
+  auto load_regs = [&](int phys) {
+    const size_t page = ((size_t)phys * blk_stride + head_off) * EB;
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+      const int c = tid + i * kThreads;
+      if (NCH % kThreads == 0 || c < NCH) {
+        kreg[i] = *reinterpret_cast<const u32x2*>(key_cache + page + (size_t)c * 8);
+        vreg[i] = *reinterpret_cast<const u32x2*>(value_cache + page + (size_t)c * 8);
+      }
+    }
+  };
+  auto store_regs = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+      const int c = tid + i * kThreads;
+      if (NCH % kThreads == 0 || c < NCH) {
+        *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c >> 5, c & 31) * 8]) =
+            e4m3x8_to_16<AF>(kreg[i]);
+        *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(c >> 2, c & 3) * 8]) =
+            e4m3x8_to_16<AF>(vreg[i]);
+      }
+    }
+  };
+
+  if constexpr (kDma) {
+    dma_page(phys_of(0), 0);
+    if (npages > 1) {
+      dma_page(phys_of(1), 1);
+      wait_vmcnt<UPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+  } else {
+    load_regs(phys_of(0));
+    store_regs(0);
     __syncthreads();
+  }
 
-    if (wave_live && base <= wave_last_pos) {
-      // S = Q K^T for the two 16-token tiles of the page.
-      f32x4 s_acc[2][2];
+  int cur = 0;
+  for (int p = 0; p < npages; ++p) {
+    const int base = p * BS;
+    if constexpr (kDma) {
+      if (p + 2 < npages) dma_page(phys_of(p + 2), cur == 0 ? 2 : cur - 1);
+    } else {
+      if (p + 1 < npages) load_regs(phys_of(p + 1));
+    }
+
+    if (wave_live && base <= pos_hi) {
+      auto page = [&](auto masked) {
+      const uint16_t* kb = k_lds[cur];
+      const uint16_t* vb = v_lds[cur];
+      // S^T = K Q^T: the two 16-key tiles of the page.
+      f32x4 s_acc[2][NQ];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        vec kb[KSTEPS];
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          kb[s] = *reinterpret_cast<const vec*>(&k_lds[(16 * tt + col) * KROW + 8 * (r4 + 4 * s)]);
+        for (int t = 0; t < NQ; ++t) s_acc[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          s_acc[mt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KS; ++s) {
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s)
-            s_acc[mt][tt] = Mfma<AF>::mma(qa[mt][s], kb[s], s_acc[mt][tt]);
+        for (int kt = 0; kt < 2; ++kt) {
+          const vec ka = *reinterpret_cast<const vec*>(&kb[k_off[kt] + s * 4 * BS * 8]);
+#pragma unroll
+          for (int t = 0; t < NQ; ++t) s_acc[kt][t] = Mfma<AF>::mma(ka, qb[t][s], s_acc[kt][t]);
         }
       }
 
-      // Causal mask + online softmax; lane holds rows (mt, 4*r4 + r), token col (+16).
-      float alpha[2][4];
+      // Scores in log2 units, the causal mask, and P.  Lane element
+      // (kt, r) is key base + 8 * q4 + 4 * kt + r.  The mask is needed only
+      // where the page reaches past the earliest query of the wave; the two
+      // cases are separate instantiations so that the common, unmasked one
+      // sees only products (canonical floats) and its maxima need no NaN
+      // quieting.
+      vec pb[NQ];
+      {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+        for (int t = 0; t < NQ; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lim = min(row_pos[mt][r], ctx - 1);
-          float s0 = s_acc[mt][0][r] * qk_scale_log2;
-          float s1 = s_acc[mt][1][r] * qk_scale_log2;
-          if (base + col > lim) s0 = -INFINITY;
-          if (base + col + 16 > lim) s1 = -INFINITY;
-          const float pm = row16_max(fmaxf(s0, s1));
-          const float m_new = fmaxf(m_run[mt][r], pm);
-          // m_new is finite: key 0 is visible to every query.
-          alpha[mt][r] = fast_exp2(m_run[mt][r] - m_new);
-          const float e0 = fast_exp2(s0 - m_new);
-          const float e1 = fast_exp2(s1 - m_new);
-          l_run[mt][r] = l_run[mt][r] * alpha[mt][r] + row16_sum(e0 + e1);
-          m_run[mt][r] = m_new;
-          const int q = 16 * mt + 4 * r4 + r;
-          pw[q * (BS + 8) + col] = (uint16_t)f32_to_16<AF>(e0);
-          pw[q * (BS + 8) + col + 16] = (uint16_t)f32_to_16<AF>(e1);
+          for (int kt = 0; kt < 2; ++kt) s_acc[kt][t] *= qk_scale_log2;
+        if constexpr (decltype(masked)::value) {
+#pragma unroll
+          for (int t = 0; t < NQ; ++t)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (base + 8 * q4 + 4 * kt + r > qpos[t]) s_acc[kt][t][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+          const float lmax = fmaxf(fmaxf(fmaxf(s_acc[0][t][0], s_acc[0][t][1]),
+                                         fmaxf(s_acc[0][t][2], s_acc[0][t][3])),
+                                   fmaxf(fmaxf(s_acc[1][t][0], s_acc[1][t][1]),
+                                         fmaxf(s_acc[1][t][2], s_acc[1][t][3])));
+          if (__builtin_amdgcn_ballot_w64(lmax > m_run[t] + kSlack) != 0) {
+            // Raise the maximum of every query of this tile to its maximum
+            // over the four lanes that hold it (and never lower it).
+            float cm = fmaxf(lmax, shfl_xor_f(lmax, 16));
+            cm = fmaxf(cm, shfl_xor_f(cm, 32));
+            const float m_new = fmaxf(m_run[t], cm);
+            const float alpha = fast_exp2(m_run[t] - m_new);
+#pragma unroll
+            for (int n = 0; n <= NT; ++n) o_acc[n][t] *= alpha;
+            m_run[t] = m_new;
+          }
+          f32x8 pv;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[4 * kt + r] = fast_exp2(s_acc[kt][t][r] - m_run[t]);
+          pb[t] = __builtin_convertvector(pv, vec);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
-      // O = alpha * O + P V.
+      // O^T += V^T P^T; on the sequence's last page, tokens at or past the
+      // context end are zeroed in the V operand.
+      {
+        u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
+        if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o_acc[mt][n][r] *= alpha[mt][r];
-        const vec pa = *reinterpret_cast<const vec*>(&pw[(16 * mt + col) * (BS + 8) + 8 * r4]);
+          for (int e = 0; e < 4; ++e) {
+            const int tok = base + 8 * q4 + 2 * e;
+            keep[e] = (tok < ctx ? 0xffffu : 0u) | (tok + 1 < ctx ? 0xffff0000u : 0u);
+          }
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const vec vb = *reinterpret_cast<const vec*>(&v_lds[(16 * n + col) * VROW + 8 * r4]);
-          o_acc[mt][n] = Mfma<AF>::mma(pa, vb, o_acc[mt][n]);
+          u32x4 vw = *reinterpret_cast<const u32x4*>(&vb[v_off + n * 16 * 4 * 8]);
+          if constexpr (decltype(masked)::value) vw &= keep;
+          const vec va = __builtin_bit_cast(vec, vw);
+#pragma unroll
+          for (int t = 0; t < NQ; ++t) o_acc[n][t] = Mfma<AF>::mma(va, pb[t], o_acc[n][t]);
         }
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
+      }
+      };
+      if (base + BS - 1 > pos_lo) {
+        page(std::true_type{});
+      } else {
+        page(std::false_type{});
       }
     }
-    __syncthreads();
+    if constexpr (kDma) {
+      // This wave's share of page p + 1 has landed (page p + 2 may still be
+      // in flight); the barrier publishes every wave's share and retires
+      // buffer `cur` for reuse.
+      if (p + 2 < npages) {
+        wait_vmcnt<UPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      cur = cur == NBUF - 1 ? 0 : cur + 1;
+    } else {
+      if (p + 1 < npages) store_regs(cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
+    }
   }
 
   if (!wave_live) return;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int t = 0; t < NQ; ++t) {
+    const int r = row0 + 16 * t + col;
+    if (r >= rows) continue;
+    const int j = r / G;
+    const int hq = g * G + r - j * G;
+    const float inv = v_scale / o_acc[NT][t][0];
+    uint16_t* dst = out + ((size_t)(q_begin + j) * Hq + hq) * D + 4 * q4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j_wave + 16 * mt + 4 * r4 + r;
-      if (j >= C) continue;
-      const float inv = v_scale / l_run[mt][r];
-      uint16_t* dst = out + ((size_t)(q_begin + j) * Hq + h) * D;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) dst[16 * n + col] = (uint16_t)f32_to_16<AF>(o_acc[mt][n][r] * inv);
+    for (int n = 0; n < NT; ++n) {
+      const f32x4 o = o_acc[n][t] * inv;
+      *reinterpret_cast<u32x2*>(dst + 16 * n) =
+          __builtin_bit_cast(u32x2, __builtin_convertvector(o, typename Vec4<AF>::type));
     }
   }
 }
 
+template <int D>
+constexpr int query_tiles() {
+  return D <= 96 ? 4 : 2;
+}
+
 template <int D, int CF, int AF>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
+  constexpr int NQ = query_tiles<D>();
+  constexpr int RW = 16 * NQ * kWaves;
+  const int G = a.Hq / a.Hkv;
+  const long long row_tiles = ((long long)a.max_chunk * G + RW - 1) / RW;
+  const long long items = row_tiles * a.Hkv * a.B;
+  const long long per_xcd = (items + kXcds - 1) / kXcds;
+  if (per_xcd * kXcds > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float qk = a.softmax_scale * (CF == FMT_E4M3 ? a.k_scale : 1.f) * LOG2E_P;
   const float vs = CF == FMT_E4M3 ? a.v_scale : 1.f;
-  dim3 grid((a.max_chunk + QT - 1) / QT, a.Hq, a.B);
-  hipLaunchKernelGGL((prefill_kernel<D, CF, AF>), grid, dim3(256), 0, s, (uint16_t*)a.out,
-                     (const uint16_t*)a.query, a.cu_q_lens, (const uint8_t*)a.key_cache,
-                     (const uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hq,
-                     a.Hkv, a.MBPS, qk, vs);
+  hipLaunchKernelGGL((prefill_kernel<D, CF, AF, NQ>), dim3((unsigned)(per_xcd * kXcds)),
+                     dim3(kThreads), 0, s, (uint16_t*)a.out, (const uint16_t*)a.query,
+                     a.cu_q_lens, (const uint8_t*)a.key_cache, (const uint8_t*)a.value_cache,
+                     a.block_tables, a.context_lens, a.Hq, a.Hkv, G, a.B, a.MBPS,
+                     (int)row_tiles, qk, vs);
   return hipGetLastError();
 }
 
@@ -274,7 +473,7 @@ bool prefill_supported(int D, int G, int act, int cache) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  if (a.max_chunk <= 0) return hipSuccess;
+  if (a.max_chunk <= 0 || a.B <= 0) return hipSuccess;
   switch (a.D) {
     case 64: return launch_d<64>(a, s);
     case 96: return launch_d<96>(a, s);

@@ -196,6 +196,18 @@ PREFILL_CASES = {
                                                  chunk_range=(30, 170)),
     "no_prefix": lambda: W.prefill_workload("no_prefix", 25, B=2, Hq=4, Hkv=2, D=128,
                                             act="bf16", prefix_len=0, chunk_range=(1, 260)),
+    # Chunks spanning several 256-row workgroup tiles, ragged at both ends.
+    "long_chunk_d96": lambda: W.prefill_workload("long_chunk_d96", 26, B=2, Hq=2, Hkv=2, D=96,
+                                                 act="bf16", prefix_len=160,
+                                                 chunk_range=(300, 600)),
+    # Group sizes 3, 8 and 16 (rows interleave positions and heads).
+    "gqa3_d96": lambda: W.prefill_workload("gqa3_d96", 27, B=2, Hq=6, Hkv=2, D=96, act="bf16",
+                                           prefix_len=64, chunk_range=(20, 150)),
+    "gqa8_d64": lambda: W.prefill_workload("gqa8_d64", 28, B=2, Hq=16, Hkv=2, D=64, act="bf16",
+                                           prefix_len=32, chunk_range=(40, 120)),
+    "gqa16_f16_fp8_d128": lambda: W.prefill_workload("gqa16_f16_fp8_d128", 29, B=2, Hq=16,
+                                                     Hkv=1, D=128, act="f16", cache="e4m3",
+                                                     prefix_len=96, chunk_range=(10, 90)),
 }
 
 
