@@ -226,6 +226,17 @@ def bench_decode(wl, a, torch):
     d_end.record()
     torch.cuda.synchronize()
     dec_avg_s = d_start.elapsed_time(d_end) / K * 1e-3
+    # Timed region 3: an event pair around each decode launch, for the spread
+    # of single-launch times (each includes the event overhead, a few us).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        writes[i % R]()
+        ev[i][0].record()
+        decodes[i % R]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    launch_us = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
 
     achieved = kv_bytes / dec_avg_s / 1e9
     res = {
@@ -254,6 +265,8 @@ def bench_decode(wl, a, torch):
         "tokens_per_s": round(wl.B / step_s, 1),
         "decode_tokens_per_s": round(wl.B / dec_avg_s, 1),
         "decode_us": round(dec_avg_s * 1e6, 3),
+        "decode_launch_us_p10_p50_p90": [round(float(x), 3) for x in
+                                         np.percentile(launch_us, [10, 50, 90])],
         "step_us": round(step_s * 1e6, 3),
         "wall_us_per_step": round(wall / K * 1e6, 3),
         "kv_bytes_per_step": kv_bytes,
