@@ -12,18 +12,23 @@
 // pages of (sequence b, KV head g); its waves take the split's pages
 // round-robin, so they stream neighbouring pages side by side, and each wave
 // prefetches its next page into a second register buffer while it computes
-// the current one.  Per wave and page:
+// the current one.  Per wave and page everything is computed transposed, so
+// the probabilities never leave registers:
 //
-//   * S = Q K^T: the G query heads of the group are the rows of 16x16x32
-//     MFMA tiles (rows G..15 are zero), the page's 32 tokens two 16-column
-//     tiles, D/32 k-steps.  The K page layout [D/8][32][8] makes every B
-//     operand one 16-byte load (one 16-byte load covers two tokens for E4M3).
-//   * Online softmax in log2 units (scale * log2 e folded in): each MFMA
-//     output row is one head, so the per-head page max and sum are 16-lane
-//     row reductions done entirely in DPP; the reference max moves lazily.
-//   * P goes through 1 KiB of the wave's LDS into the MFMA A-operand layout,
-//     and O += P V runs as D/16 MFMAs whose B operands are single loads from
-//     the transposed V page [D][32].
+//   * S^T = K Q^T (v_mfma_f32_16x16x32): the page's 32 keys are two 16-row
+//     A tiles, tile kt row x being key 2x + kt; the G query heads of the
+//     group are the B columns (columns G..15 are zero); D/32 k-steps.  The K
+//     page layout [D/8][32][8] makes each A operand one 16-byte load (one
+//     16-byte load holds both tiles' chunks for E4M3).  Lane (q, col) then
+//     holds, for head col, the eight consecutive keys 8q .. 8q + 7.
+//   * Softmax in log2 units (scale * log2 e folded in) with a lazily moved
+//     reference max: only when some score exceeds it by more than 2^8 (a
+//     ballot) is the max taken across the four lanes of a head and O
+//     rescaled, so a page normally needs no cross-lane reduction at all.
+//   * O^T += V^T P^T: the eight probabilities of a lane are exactly its B
+//     operand; the A operands are single loads from the transposed V page
+//     [D][32] (dimension 16n + col, tokens 8q .. 8q + 7).  One more MFMA
+//     against an all-ones A tile accumulates the running sum l.
 //
 // Append mode (pa_decode_append) also stores the decoded token's K/V into its
 // cache row in the same launch; the wave reading that row takes it from LDS.
@@ -42,7 +47,6 @@ namespace pa {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int PROW = kPage + 8;  // LDS row of P (16-bit elements), padded
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may grow before rescaling
 
 // Eight cache elements: 16 bytes for 16-bit formats, 8 bytes for E4M3.
@@ -77,13 +81,13 @@ __device__ __forceinline__ typename Mfma<AF>::vec as_operand(const Raw8<CF>& r) 
   }
 }
 
-// Registers of one page.  16-bit caches: K operand of token tile tt and
-// k-step j is one 16-byte load (token col + 16 tt).  E4M3: one 16-byte load
-// per k-step holds the 8-byte chunks of tokens 2 col and 2 col + 1, which are
-// column col of token tiles 0 and 1.
+// Registers of one page.  16-bit caches: K operand of key tile kt and k-step
+// j is one 16-byte load (key 2 col + kt).  E4M3: one 16-byte load per k-step
+// holds the 8-byte chunks of keys 2 col and 2 col + 1, which are row col of
+// key tiles 0 and 1.
 template <int D, int CF>
 struct PageRegs {
-  Raw8<CF> k[2][D / 32];   // [token tile][k-step]
+  Raw8<CF> k[2][D / 32];   // [key tile][k-step]
   Raw8<CF> v[D / 16];      // [output tile]
 };
 template <int D>
@@ -92,14 +96,14 @@ struct PageRegs<D, FMT_E4M3> {
   Raw8<FMT_E4M3> v[D / 16];
 };
 
-// Token of a page held in MFMA column `col` of token tile `tt`.
-template <int CF>
-__device__ __forceinline__ int tile_token(int tt, int col) {
-  return CF == FMT_E4M3 ? 2 * col + tt : col + 16 * tt;
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), mask, 64));
 }
 
 template <int D, int G, int CF, int AF, int W>
-__global__ __launch_bounds__(64 * W) void decode_split(
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_split(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -114,18 +118,21 @@ __global__ __launch_bounds__(64 * W) void decode_split(
   constexpr int NT = D / 16;
   typedef typename Mfma<AF>::vec vec;
 
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds_all[W][16 * PROW];
   __shared__ float m_lds[W][G];
   __shared__ float l_lds[W][G];
   __shared__ __attribute__((aligned(16))) float o_lds[W][G][D];
   __shared__ __attribute__((aligned(16))) uint16_t newk_lds[D];
   __shared__ __attribute__((aligned(16))) uint16_t newv_lds[D];
 
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform across the wave; saying so keeps everything
+  // derived from it (page counts, prefetch indices) in scalar registers.
+  // A vector temporary there can be allocated to a register that an
+  // in-flight page load targets, which forces a wait for every outstanding
+  // load before the next page's loads are issued.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
-  const int r4 = lane >> 4;
-  uint16_t* p_lds = p_lds_all[wave];
+  const int q4 = lane >> 4;
 
   const int s = blockIdx.x;
   const int g = blockIdx.y;
@@ -153,9 +160,9 @@ __global__ __launch_bounds__(64 * W) void decode_split(
   // Append mode: the decoded token's K/V (new_key / new_value [B][Hkv][D])
   // belong in cache row r_new (the last position, or its ring row).  The
   // split that owns that row's page stores it (E4M3-encoded when the cache
-  // is FP8) and stages the stored values in LDS; the one wave that reads the
-  // page patches the row into its MFMA operands, so nothing in this launch
-  // depends on the store becoming visible.
+  // is FP8) and stages the stored cache elements in LDS; the one wave that
+  // reads the page patches the row into its page registers, so nothing in
+  // this launch depends on the store becoming visible.
   int row_new = -1, k_new = -1, w_new = -1;
   if (new_key != nullptr) {
     const int ctx = context_lens[b];
@@ -176,8 +183,8 @@ __global__ __launch_bounds__(64 * W) void decode_split(
           const uint32_t vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
           key_cache[page + k_page_off(row_new, d)] = static_cast<uint8_t>(kq);
           value_cache[page + v_page_off(row_new, d)] = static_cast<uint8_t>(vq);
-          newk_lds[d] = static_cast<uint16_t>(e4m3x2_to_16<AF, false>(kq) & 0xffffu);
-          newv_lds[d] = static_cast<uint16_t>(e4m3x2_to_16<AF, false>(vq) & 0xffffu);
+          newk_lds[d] = static_cast<uint16_t>(kq);
+          newv_lds[d] = static_cast<uint16_t>(vq);
         } else {
           reinterpret_cast<uint16_t*>(key_cache)[page + k_page_off(row_new, d)] = kx;
           reinterpret_cast<uint16_t*>(value_cache)[page + v_page_off(row_new, d)] = vx;
@@ -189,29 +196,26 @@ __global__ __launch_bounds__(64 * W) void decode_split(
   }
   __syncthreads();
 
-  float m_run[4], l_run[4];
+  // o_acc[NT] is the all-ones tile: every row holds the running sum l.
+  float m_run = -INFINITY;
+  f32x4 o_acc[NT + 1];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
-  f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n <= NT; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (npg > 0) {
-    // Q as the A operand: row = head `col` of the group (zero when col >= G),
-    // k-group r4 of k-step j = head-dimension chunk (r4 + 4j).
-    vec qa[KSTEPS];
+    // Q^T as the B operand: column = head `col` of the group (zero when
+    // col >= G), k-group q4 of k-step j = head-dimension chunk (q4 + 4j).
+    vec qb[KSTEPS];
     {
       const uint16_t* qrow = query + ((size_t)b * Hq + g * G + (col < G ? col : 0)) * D;
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
-        u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * (r4 + 4 * j));
+        u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * (q4 + 4 * j));
         if (col >= G) w = u32x4{0u, 0u, 0u, 0u};
-        qa[j] = __builtin_bit_cast(vec, w);
+        qb[j] = __builtin_bit_cast(vec, w);
       }
     }
+    const vec ones = __builtin_convertvector(f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, vec);
 
     const size_t page_elems = (size_t)kPage * D;
     const int32_t* bt = block_tables + (size_t)b * MBPS;
@@ -220,12 +224,12 @@ __global__ __launch_bounds__(64 * W) void decode_split(
     const int bt_lane = bt[pa + wave + W * (lane < npg ? lane : 0)];
 
     // Per-lane byte offsets inside a page (loop invariant).  K operand of
-    // k-step j, token tile tt: chunk (r4 + 4j), token tile_token(tt, col); V
-    // operand of output tile n: dim 16n + col, tokens 8 r4 .. 8 r4 + 7.
-    const int k_lane = ((r4 * kPage + tile_token<CF>(0, col)) * 8) * EB;
-    const int v_lane = (col * kPage + 8 * r4) * EB;
+    // k-step j, key tile kt: chunk (q4 + 4j), key 2 col + kt; V operand of
+    // output tile n: dim 16n + col, tokens 8 q4 .. 8 q4 + 7.
+    const int k_lane = ((q4 * kPage + 2 * col) * 8) * EB;
+    const int v_lane = (col * kPage + 8 * q4) * EB;
     constexpr int K_J = 4 * kPage * 8 * EB;    // byte step between k-steps
-    constexpr int K_TT = 16 * 8 * EB;          // byte step between token tiles (16-bit)
+    constexpr int K_KT = 8 * EB;               // byte step between key tiles (16-bit)
     constexpr int V_N = 16 * kPage * EB;       // byte step between output tiles
     constexpr uint32_t PAGE_BYTES = (uint32_t)kPage * D * EB;
 
@@ -239,126 +243,135 @@ __global__ __launch_bounds__(64 * W) void decode_split(
         for (int j = 0; j < KSTEPS; ++j) Pg.k[j] = buf_load16(kr, k_lane, j * K_J);
       } else {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) Pg.k[tt][j] = load8<CF>(kr, k_lane, j * K_J + tt * K_TT);
+          for (int j = 0; j < KSTEPS; ++j) Pg.k[kt][j] = load8<CF>(kr, k_lane, j * K_J + kt * K_KT);
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) Pg.v[n] = load8<CF>(vr, v_lane, n * V_N);
     };
 
-    // K operand of token tile tt, k-step j.
-    auto k_operand = [&](const PageRegs<D, CF>& Pg, int tt, int j) -> vec {
+    // K operand of key tile kt, k-step j.
+    auto k_operand = [&](const PageRegs<D, CF>& Pg, int kt, int j) -> vec {
       if constexpr (CF == FMT_E4M3) {
         Raw8<CF> r;
-        r.w = tt == 0 ? u32x2{Pg.k[j][0], Pg.k[j][1]} : u32x2{Pg.k[j][2], Pg.k[j][3]};
+        r.w = kt == 0 ? u32x2{Pg.k[j][0], Pg.k[j][1]} : u32x2{Pg.k[j][2], Pg.k[j][3]};
         return as_operand<CF, AF>(r);
       } else {
-        return as_operand<CF, AF>(Pg.k[tt][j]);
+        return as_operand<CF, AF>(Pg.k[kt][j]);
       }
     };
 
-    auto compute_page = [&](const PageRegs<D, CF>& Pg, int k) {
-      // Is this the page holding the appended row?  (Wave-uniform.)
-      const bool patch = wave == w_new && k == k_new;
-      // S = Q K^T; lane (r4, col) gets heads 4*r4 + r, tokens tok0 and tok1.
-      f32x4 sc4[2];
+    // Set element e (0..7, any lane-varying value) of a lane's eight
+    // consecutive cache elements.  Register arrays are only ever indexed by
+    // constants (a runtime index would move them to scratch memory).
+    auto set_elem = [&](auto& raw, int e, uint32_t x) {
+      constexpr int EPW = (CF == FMT_E4M3) ? 4 : 2;   // elements per word
+      constexpr int BITS = 32 / EPW;
+      constexpr uint32_t EMASK = (1u << BITS) - 1u;
+      const int sh = BITS * (e % EPW);
+      const uint32_t keep = ~(EMASK << sh);
+      const uint32_t put = (x & EMASK) << sh;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sc4[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) {
-          vec kop = k_operand(Pg, tt, j);
-          if (patch && tile_token<CF>(tt, col) == row_new)
-            kop = *reinterpret_cast<const vec*>(&newk_lds[8 * (r4 + 4 * j)]);
-          sc4[tt] = Mfma<AF>::mma(qa[j], kop, sc4[tt]);
-        }
-      }
+      for (int w = 0; w < 8 / EPW; ++w)
+        if (w == e / EPW) raw[w] = (raw[w] & keep) | put;
+    };
+
+    auto compute_page = [&](PageRegs<D, CF>& Pg, int k) {
       const int base = (pa + wave + W * k) * kPage;
-      const int tok0 = tile_token<CF>(0, col);
-      const int tok1 = tile_token<CF>(1, col);
-      const bool live0 = base + tok0 < L;
-      const bool live1 = base + tok1 < L;
-      float sc[4][2], pm[4];
-      bool grow = false;
+      // The page holding the appended row (a wave-uniform test): put the row
+      // into the page registers.  Key row_new is row row_new / 2 of key tile
+      // row_new % 2; in V it is element row_new % 8 of lane group
+      // row_new / 8.
+      if (wave == w_new && k == k_new) {
+        const int kt_new = row_new & 1;
+        if (col == (row_new >> 1)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sc[r][0] = live0 ? sc4[0][r] * qk_scale_log2 : -INFINITY;
-        sc[r][1] = live1 ? sc4[1][r] * qk_scale_log2 : -INFINITY;
-        pm[r] = row16_max(fmaxf(sc[r][0], sc[r][1]));
-        grow |= pm[r] > m_run[r] + kRescaleSlack;
-      }
-      // The running reference max only moves when some row's page max
-      // exceeds it by more than kRescaleSlack (log2 units); otherwise
-      // probabilities are taken against the old reference (they stay below
-      // 2^kRescaleSlack) and the output needs no rescaling.  The test is
-      // wave-uniform.
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          for (int j = 0; j < KSTEPS; ++j) {
+            const u32x4 nk = *reinterpret_cast<const u32x4*>(&newk_lds[8 * (q4 + 4 * j)]);
+            if constexpr (CF == FMT_E4M3) {
+              // The codes were staged one per 16-bit slot: pack eight into
+              // two words.
+              u32x2 c;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float m_new = fmaxf(m_run[r], pm[r]);
-          const float alpha = fast_exp2(m_run[r] - m_new);
-          l_run[r] *= alpha;
+              for (int w = 0; w < 2; ++w)
+                c[w] = (nk[2 * w] & 0xffu) | ((nk[2 * w] >> 8) & 0xff00u) |
+                       ((nk[2 * w + 1] & 0xffu) << 16) | ((nk[2 * w + 1] << 8) & 0xff000000u);
+              if (kt_new == 0) {
+                Pg.k[j][0] = c[0];
+                Pg.k[j][1] = c[1];
+              } else {
+                Pg.k[j][2] = c[0];
+                Pg.k[j][3] = c[1];
+              }
+            } else {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n][r] *= alpha;
-          m_run[r] = m_new;
+              for (int kt = 0; kt < 2; ++kt)
+                if (kt == kt_new) Pg.k[kt][j].w = nk;
+            }
+          }
+        }
+        if (q4 == (row_new >> 3)) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) set_elem(Pg.v[n].w, row_new & 7, newv_lds[16 * n + col]);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e0 = fast_exp2(sc[r][0] - m_run[r]);
-        const float e1 = fast_exp2(sc[r][1] - m_run[r]);
-        l_run[r] += row16_sum(e0 + e1);
-        if constexpr (CF == FMT_E4M3) {
-          // Tokens 2 col and 2 col + 1: one 32-bit store.
-          *reinterpret_cast<uint32_t*>(&p_lds[(4 * r4 + r) * PROW + tok0]) =
-              (uint32_t)cvt16<AF>(e0) | ((uint32_t)cvt16<AF>(e1) << 16);
-        } else {
-          p_lds[(4 * r4 + r) * PROW + tok0] = cvt16<AF>(e0);
-          p_lds[(4 * r4 + r) * PROW + tok1] = cvt16<AF>(e1);
-        }
-      }
-      // Only this wave touches its P buffer: a wave-local ordering point.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // A operand: P[head col][tokens 8*r4 .. 8*r4 + 7].
-      const vec pa_op = *reinterpret_cast<const vec*>(&p_lds[col * PROW + 8 * r4]);
-      // Rows past the context end may hold anything (NaN included); their
-      // probabilities are 0, but 0 * NaN is NaN, so those V values are
-      // zeroed on the (uniform) last partial page.
+      // Rows past the context end may hold anything (NaN included): their
+      // scores are masked below, and their V elements are zeroed here, since
+      // a zero probability times NaN is still NaN.  (A wave-uniform test.)
       const bool partial = base + kPage > L;
+      if (partial) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        vec vb = as_operand<CF, AF>(Pg.v[n]);
-        if (partial) {
-          u32x4 w = __builtin_bit_cast(u32x4, vb);
-          const int tok = base + 8 * r4;  // this lane holds tokens tok .. tok + 7
+        for (int e = 0; e < 8; ++e) {
+          if (base + 8 * q4 + e >= L) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = (tok + 2 * e < L) ? 0xffffu : 0u;
-            const uint32_t hi = (tok + 2 * e + 1 < L) ? 0xffff0000u : 0u;
-            w[e] &= (lo | hi);
+            for (int n = 0; n < NT; ++n) set_elem(Pg.v[n].w, e, 0u);
           }
-          vb = __builtin_bit_cast(vec, w);
         }
-        if (patch && r4 == (row_new >> 3)) {
-          // Element row_new % 8 of this lane's 8 tokens is the appended row.
-          u32x4 w = __builtin_bit_cast(u32x4, vb);
-          const uint32_t x = newv_lds[16 * n + col];
-          const int e = row_new & 7;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q == (e >> 1))
-              w[q] = (e & 1) ? ((w[q] & 0xffffu) | (x << 16)) : ((w[q] & 0xffff0000u) | x);
-          }
-          vb = __builtin_bit_cast(vec, w);
-        }
-        acc[n] = Mfma<AF>::mma(pa_op, vb, acc[n]);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // S^T = K Q^T; element (kt, r) of lane (q4, col) is key 8 q4 + 2r + kt.
+      f32x4 st[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) st[kt] = Mfma<AF>::mma(k_operand(Pg, kt, j), qb[j], st[kt]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) st[kt] *= qk_scale_log2;
+      if (partial) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (base + 8 * q4 + 2 * r + kt >= L) st[kt][r] = -INFINITY;
+      }
+      const float lmax = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                               fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
+      // The reference max only moves when some score exceeds it by more than
+      // kRescaleSlack (log2 units); it is then raised to the max over the
+      // four lanes that hold each head, so all of a head's lanes agree.
+      if (__builtin_amdgcn_ballot_w64(lmax > m_run + kRescaleSlack) != 0) {
+        float cm = fmaxf(lmax, shfl_xor_f(lmax, 16));
+        cm = fmaxf(cm, shfl_xor_f(cm, 32));
+        const float m_new = fmaxf(m_run, cm);
+        const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int n = 0; n <= NT; ++n) o_acc[n] *= alpha;
+        m_run = m_new;
+      }
+      f32x8 pv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) pv[2 * r + kt] = fast_exp2(st[kt][r] - m_run);
+      const vec pb = __builtin_convertvector(pv, vec);
+
+      // O^T += V^T P^T, and l += 1^T P^T.
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o_acc[n] = Mfma<AF>::mma(as_operand<CF, AF>(Pg.v[n]), pb, o_acc[n]);
+      o_acc[NT] = Mfma<AF>::mma(ones, pb, o_acc[NT]);
     };
 
     // Two register buffers: page k is computed while page k + 1 loads.  The
@@ -376,18 +389,17 @@ __global__ __launch_bounds__(64 * W) void decode_split(
     }
   }
 
-  // Combine the W waves through LDS.  Lane (r4, col) holds O[head 4*r4 + r]
-  // [dim 16n + col]; waves without pages contribute (-inf, 0, 0).
+  // Combine the W waves through LDS.  Lane (q4, col) holds O[head col]
+  // [dim 16n + 4 q4 + r] and l in every row of the ones tile; waves without
+  // pages contribute (-inf, 0, 0).
+  if (col < G) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * r4 + r;
-    if (h < G) {
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) o_lds[wave][h][16 * n + col] = acc[n][r];
-      if (col == 0) {
-        m_lds[wave][h] = m_run[r];
-        l_lds[wave][h] = l_run[r];
-      }
+      for (int r = 0; r < 4; ++r) o_lds[wave][col][16 * n + 4 * q4 + r] = o_acc[n][r];
+    if (q4 == 0) {
+      m_lds[wave][col] = m_run;
+      l_lds[wave][col] = o_acc[NT][0];
     }
   }
   __syncthreads();
