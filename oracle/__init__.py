@@ -16,7 +16,8 @@ Sources (the pages this restates, cited by title and section):
 * "Optimization plans" (mistral.rs discussion 46), the "Update" post: the
   cache slot writer ``reshape_and_cache`` runs before paged attention.
 * "libmir-metal 0.2.0, src/native/trace/kv.rs", ``fn build``: head-major
-  pages; sliding layers keep a bounded ring.
+  pages; sliding layers keep a bounded ring; a quantised cache holds packed
+  INT8 pages with per-token/head FP32 scales, dequantised inside attention.
 * "Rolling buffer cache" (llama.cpp discussion 3581), opening post: a cache of
   fixed size W holds timestep i at slot i mod W; KerfuffleV2's reply states the
   sliding-window span of a token.
@@ -24,6 +25,7 @@ Sources (the pages this restates, cited by title and section):
 Modules:
 
 * :mod:`oracle.e4m3`     -- OCP E4M3 ("FN") table, brute-force RNE encoder.
+* :mod:`oracle.int8`     -- symmetric per-(token, head) int8 codes, fp32 scales.
 * :mod:`oracle.cache`    -- slot arithmetic and the cache writer.
 * :mod:`oracle.attention` -- paged decode, rolling-buffer decode, chunked
   prefill, split-context merge.

@@ -54,6 +54,8 @@ def decode(query_bits, act_fmt: str, key_cache, value_cache, cache_fmt: str,
     window == 0: attend to logical rows 0..L-1 with L = context_lens[b].
     window  > 0: the table addresses a ring of ``window`` rows; attend to ring
     rows 0..min(L, window)-1.
+    k_scale / v_scale: per-tensor scales of an E4M3 cache, or the per-row
+    scale pools of an int8 cache (see :mod:`oracle.cache`).
     Returns fp64 ``[B, Hq, D]``.
     """
     q = bits_to_f64(query_bits, act_fmt)

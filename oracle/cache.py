@@ -20,7 +20,12 @@ byte:
 
 * ``"f16"``  -- IEEE binary16, stored as uint16 bits;
 * ``"bf16"`` -- bfloat16 (the top half of an fp32), stored as uint16 bits;
-* ``"e4m3"`` -- OCP E4M3 codes, stored as uint8 (see :mod:`oracle.e4m3`).
+* ``"e4m3"`` -- OCP E4M3 codes, stored as uint8 (see :mod:`oracle.e4m3`);
+* ``"int8"`` -- symmetric per-(token, KV head) int8 codes, stored as int8,
+  with one fp32 scale per (block, head, row) in separate scale pools
+  ``[num_blocks][num_kv_heads][block_size]`` (see :mod:`oracle.int8`).
+  For this format the ``k_scale`` / ``v_scale`` arguments below are those
+  scale pools instead of per-tensor floats.
 
 The writer is the cache-slot operation the "Optimization plans" discussion
 (mistral.rs discussion 46, "Update" post) calls ``reshape_and_cache``: token n
@@ -34,6 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import e4m3
+from . import int8
 
 
 def bits_to_f64(bits, fmt: str) -> np.ndarray:
@@ -46,11 +52,20 @@ def bits_to_f64(bits, fmt: str) -> np.ndarray:
         return wide.view(np.float32).astype(np.float64)
     if fmt == "e4m3":
         return e4m3.decode(bits, 1.0)
+    if fmt == "int8":
+        return bits.astype(np.int8).astype(np.float64)
     raise ValueError(f"unknown format {fmt!r}")
 
 
 def storage_dtype(fmt: str):
-    return np.uint8 if fmt == "e4m3" else np.uint16
+    return {"e4m3": np.uint8, "int8": np.int8}.get(fmt, np.uint16)
+
+
+def empty_scale_pools(num_blocks: int, num_kv_heads: int, block_size: int,
+                      fill: float = 0.0):
+    """Per-row fp32 scale pools of an int8 cache (K and V)."""
+    k = np.full((num_blocks, num_kv_heads, block_size), fill, dtype=np.float32)
+    return k, k.copy()
 
 
 def empty_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
@@ -107,14 +122,15 @@ def encode_tokens(x_bits, act_fmt: str, cache_fmt: str, scale: float):
 
 
 def reshape_and_cache(key_bits, value_bits, key_cache, value_cache, slot_mapping,
-                      act_fmt: str, cache_fmt: str, k_scale: float = 1.0,
-                      v_scale: float = 1.0) -> None:
+                      act_fmt: str, cache_fmt: str, k_scale=1.0, v_scale=1.0) -> None:
     """Write tokens into the pools in place.
 
     key_bits, value_bits: ``[T, Hkv, D]`` activation bits.
     key_cache, value_cache: pools from :func:`empty_pools`, updated.
     slot_mapping: ``[T]`` ints; ``s >= 0`` writes to block ``s // BS``, row
     ``s % BS``; ``s < 0`` is skipped.
+    cache_fmt "int8": k_scale / v_scale are the scale pools, updated with one
+    scale per written (row, head).
     """
     bs = pool_geometry(key_cache)[2]
     slots = np.asarray(slot_mapping).reshape(-1)
@@ -122,28 +138,42 @@ def reshape_and_cache(key_bits, value_bits, key_cache, value_cache, slot_mapping
         s = int(s)
         if s < 0:
             continue
-        put_row(key_cache, value_cache, s // bs, s % bs,
+        blk, off = s // bs, s % bs
+        if cache_fmt == "int8":
+            kc, ksc = int8.quantize_rows(bits_to_f64(key_bits[n], act_fmt).astype(np.float32))
+            vc, vsc = int8.quantize_rows(bits_to_f64(value_bits[n], act_fmt).astype(np.float32))
+            put_row(key_cache, value_cache, blk, off, kc, vc)
+            k_scale[blk, :, off] = ksc
+            v_scale[blk, :, off] = vsc
+            continue
+        put_row(key_cache, value_cache, blk, off,
                 encode_tokens(key_bits[n], act_fmt, cache_fmt, k_scale),
                 encode_tokens(value_bits[n], act_fmt, cache_fmt, v_scale))
 
 
 def gather_f64(key_cache, value_cache, block_table_row, length: int, fmt: str,
-               k_scale: float = 1.0, v_scale: float = 1.0):
+               k_scale=1.0, v_scale=1.0):
     """Logical rows 0..length-1 of one sequence as fp64 K and V ``[length, Hkv, D]``.
 
     Walks the block table token by token; for E4M3 the code values are
-    multiplied by the scales in fp64.
+    multiplied by the per-tensor scales in fp64, for int8 by each row's own
+    scale (``k_scale`` / ``v_scale`` are then the scale pools).
     """
     _, hkv, bs, d = pool_geometry(key_cache)
-    ks, vs = [], []
+    ks, vs, kss, vss = [], [], [], []
     for t in range(length):
         phys = int(block_table_row[t // bs])
         k, v = get_row(key_cache, value_cache, phys, t % bs)
         ks.append(k)
         vs.append(v)
+        if fmt == "int8":
+            kss.append(k_scale[phys, :, t % bs])
+            vss.append(v_scale[phys, :, t % bs])
     if not ks:
         z = np.zeros((0, hkv, d), dtype=np.float64)
         return z, z.copy()
+    if fmt == "int8":
+        return int8.decode(np.stack(ks), np.stack(kss)), int8.decode(np.stack(vs), np.stack(vss))
     kv = bits_to_f64(np.stack(ks), fmt)
     vv = bits_to_f64(np.stack(vs), fmt)
     if fmt == "e4m3":
