@@ -40,8 +40,8 @@ def _args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mistral_decode",
-                    choices=["mistral_decode", "fp8_decode", "sliding_decode", "tiny_decode",
-                             "prefix_prefill"])
+                    choices=["mistral_decode", "fp8_decode", "int8_decode", "sliding_decode",
+                             "tiny_decode", "prefix_prefill"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for 2 GB)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--separate-write", action="store_true",
@@ -99,6 +99,7 @@ def recorded_traffic(config: str, kernel_prefix: str):
 def _workload(name):
     from paged_kv_cache_175_amd import workloads as W
     return {"mistral_decode": W.mistral_decode, "fp8_decode": W.fp8_decode,
+            "int8_decode": W.int8_decode,
             "sliding_decode": W.sliding_decode, "tiny_decode": W.tiny_decode,
             "prefix_prefill": W.prefix_prefill}[name]()
 
@@ -131,14 +132,17 @@ def bench_decode(wl, a, torch):
 
     dev = torch.device("cuda", 0)
     kshape, vshape = ops.pool_shapes(wl.pool_blocks, wl.Hkv, wl.D, wl.BS)
-    cache_dt = torch.uint8 if wl.cache == "e4m3" else {"bf16": torch.bfloat16,
-                                                        "f16": torch.float16}[wl.cache]
-    elem = 1 if wl.cache == "e4m3" else 2
-    pool_bytes = 2 * math.prod(kshape) * elem
+    i8 = wl.cache == "int8"
+    cache_dt = {"e4m3": torch.uint8, "int8": torch.int8, "bf16": torch.bfloat16,
+                "f16": torch.float16}[wl.cache]
+    elem = 1 if wl.cache in ("e4m3", "int8") else 2
+    row_extra = 4 if i8 else 0          # an INT8 row also carries its fp32 scale
+    pool_bytes = 2 * (math.prod(kshape) * elem + wl.pool_blocks * wl.Hkv * wl.BS * row_extra)
     R = a.replicas or max(1, math.ceil(2e9 / pool_bytes))
 
     kc0 = torch.zeros(kshape, dtype=cache_dt, device=dev)
     vc0 = torch.zeros(vshape, dtype=cache_dt, device=dev)
+    ksc0, vsc0 = ops.alloc_scale_pools(wl.pool_blocks, wl.Hkv, dev) if i8 else (None, None)
     # Cached tokens through the HIP writer, slots from the host block manager.
     ks, vs, sl = [], [], []
     for b in range(wl.B):
@@ -152,9 +156,11 @@ def bench_decode(wl, a, torch):
         ops.reshape_and_cache(_act_tensor(np.concatenate(ks), wl.act, torch),
                               _act_tensor(np.concatenate(vs), wl.act, torch), kc0, vc0,
                               torch.from_numpy(np.concatenate(sl).astype(np.int32)).to(dev),
-                              wl.k_scale, wl.v_scale)
+                              wl.k_scale, wl.v_scale, key_scales=ksc0, value_scales=vsc0)
     del ks, vs, sl
-    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    clone = lambda t: None if t is None else t.clone()  # noqa: E731
+    pools = [(kc0, vc0, ksc0, vsc0)] + [(kc0.clone(), vc0.clone(), clone(ksc0), clone(vsc0))
+                                        for _ in range(R - 1)]
     q0 = _act_tensor(wl.query, wl.act, torch)
     qs = [q0] + [q0.clone() for _ in range(R - 1)]
     new_k = _act_tensor(wl.new_k, wl.act, torch)
@@ -170,18 +176,21 @@ def bench_decode(wl, a, torch):
     ws = ops.alloc_workspace(need, dev)
     out = torch.empty_like(q0)
 
-    # One step: store the 32 new tokens and attend.  Default: the fused
-    # pa_decode_append (one launch); --separate-write: pa_reshape_and_cache
-    # then pa_decode.
+    # One step: store the new tokens and attend.  Default: the fused
+    # pa_decode_append (one launch); --separate-write (and an INT8 cache, which
+    # has no fused entry): pa_reshape_and_cache then pa_decode.
+    separate = a.separate_write or i8
     writes, decodes = [], []
     for r in range(R):
-        kc, vc = pools[r]
-        if a.separate_write:
+        kc, vc, ksc, vsc = pools[r]
+        if separate:
             writes.append(ops.prepare_reshape_and_cache(new_k, new_v, kc, vc, new_slots,
-                                                        wl.k_scale, wl.v_scale))
+                                                        wl.k_scale, wl.v_scale,
+                                                        key_scales=ksc, value_scales=vsc))
             decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
                                               wl.k_scale, wl.v_scale, wl.window,
-                                              a.partition_tokens))
+                                              a.partition_tokens, key_scales=ksc,
+                                              value_scales=vsc))
         else:
             writes.append(lambda: None)
             decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
@@ -190,8 +199,9 @@ def bench_decode(wl, a, torch):
                                               new_value=new_v))
 
     kv_tokens = wl.kv_read_tokens()
-    kv_bytes = kv_tokens * wl.Hkv * wl.D * elem * 2
-    write_bytes = wl.B * wl.Hkv * wl.D * (2 * 2 + 2 * elem)   # read K,V act; write K,V cache
+    kv_bytes = kv_tokens * wl.Hkv * (wl.D * elem + row_extra) * 2
+    # read K,V act; write K,V cache (and their scales)
+    write_bytes = wl.B * wl.Hkv * (wl.D * (2 * 2 + 2 * elem) + 2 * row_extra)
     qo_bytes = 2 * wl.B * wl.Hq * wl.D * 2
 
     for i in range(a.warmup):
@@ -250,7 +260,7 @@ def bench_decode(wl, a, torch):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.cache != "e4m3" else "e4m3->bf16",
+        "dtype": {"e4m3": "e4m3->bf16", "int8": "i8->bf16"}.get(wl.cache, "bf16"),
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
@@ -259,7 +269,7 @@ def bench_decode(wl, a, torch):
             "context_tokens_read": kv_tokens, "max_context_len": max_len,
             "new_tokens_written": wl.B, "pool_blocks": wl.pool_blocks, "replicas": R,
             "partition_tokens": a.partition_tokens or "auto",
-            "step": "pa_reshape_and_cache + pa_decode" if a.separate_write
+            "step": "pa_reshape_and_cache + pa_decode" if separate
                     else "pa_decode_append (write + decode in one launch)",
         },
         "tokens_per_s": round(wl.B / step_s, 1),
@@ -272,7 +282,7 @@ def bench_decode(wl, a, torch):
         "kv_bytes_per_step": kv_bytes,
         "other_bytes_per_step": write_bytes + qo_bytes,
         "roofline": {
-            "kernel": ("pa_decode" if a.separate_write else "pa_decode_append")
+            "kernel": ("pa_decode" if separate else "pa_decode_append")
                       + " (decode_split, plus decode_merge when a sequence is split)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -296,6 +306,9 @@ def cpu_baseline_decode(wl, kv_bytes, seconds):
     from oracle import pool as o_pool
 
     kc, vc = o_cache.empty_pools(wl.pool_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, 0)
+    ks, vs = wl.k_scale, wl.v_scale
+    if wl.cache == "int8":
+        ks, vs = o_cache.empty_scale_pools(wl.pool_blocks, wl.Hkv, wl.BS)
 
     def row(pos):
         return o_pool.ring_index(int(pos), wl.window) if wl.window else int(pos)
@@ -305,15 +318,15 @@ def cpu_baseline_decode(wl, kv_bytes, seconds):
         slots = [o_cache.slot_of(wl.block_tables[b], row(wl.cached_pos0[b] + t), wl.BS)
                  for t in range(n)]
         o_cache.reshape_and_cache(wl.cached_k[b], wl.cached_v[b], kc, vc, np.array(slots),
-                                  wl.act, wl.cache, wl.k_scale, wl.v_scale)
+                                  wl.act, wl.cache, ks, vs)
     new_slots = np.array([o_cache.slot_of(wl.block_tables[b], row(wl.new_pos[b]), wl.BS)
                           for b in range(wl.B)])
 
     def step():
         o_cache.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, new_slots, wl.act, wl.cache,
-                                  wl.k_scale, wl.v_scale)
+                                  ks, vs)
         o_attn.decode(wl.query, wl.act, kc, vc, wl.cache, wl.block_tables, wl.context_lens,
-                      wl.scale, wl.k_scale, wl.v_scale, wl.window)
+                      wl.scale, ks, vs, wl.window)
 
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:

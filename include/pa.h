@@ -21,7 +21,9 @@
  *    blocks that may be shared between sequences; pa_prefill_chunk() is that
  *    causal attention over a block table.
  *  - "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build: the pages are
- *    head-major, which fixes the layout below.
+ *    head-major, which fixes the layout below; a quantised cache keeps packed
+ *    INT8 pages with one FP32 scale per token and head and dequantises inside
+ *    paged attention for prefill and decode: the *_i8 entry points.
  *
  * Conventions for every entry point:
  *
@@ -46,7 +48,15 @@
  *  - Supported now: block_size 32; head_dim 64, 96 or 128; act dtype PA_F16
  *    or PA_BF16; cache dtype equal to the act dtype or PA_F8E4M3; Hq/Hkv in
  *    {1, 2, 4, 8, 16} for decode and 1..16 for prefill.  Anything else
- *    returns PA_ERR_UNSUPPORTED.
+ *    returns PA_ERR_UNSUPPORTED.  PA_I8 is accepted only by the *_i8 entry
+ *    points (which take the scale pools).
+ *  - INT8 caches: int8 pools in the layout above plus two fp32 scale pools
+ *    key_scales, value_scales [NB][Hkv][BS] (one scale per cached row and
+ *    KV head), device memory owned by the caller.  A row x of D values is
+ *    stored as scale = fp32(max|x|) / 127 (IEEE division) and codes
+ *    clamp(round-half-even(fp32(x) / scale), -127, 127) (IEEE division; a
+ *    zero row has scale 0 and zero codes); it stands for code * scale.
+ *    Inputs must be finite.
  */
 #ifndef PAGED_KV_PA_H
 #define PAGED_KV_PA_H
@@ -58,7 +68,7 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F8E4M3 = 2 } pa_dtype;
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F8E4M3 = 2, PA_I8 = 3 } pa_dtype;
 
 typedef enum {
   PA_OK = 0,
@@ -98,6 +108,22 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
                                int32_t Hkv, int32_t D, int32_t BS, int32_t NB,
                                pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
                                float v_scale, void* stream);
+
+/*
+ * pa_reshape_and_cache_i8 -- pa_reshape_and_cache into an INT8 cache.
+ *
+ * key_cache, value_cache  int8 pools (layout above), updated in place.
+ * key_scales, value_scales fp32 [NB][Hkv][BS], updated: the scale of every
+ *                 written (row, KV head).
+ * Everything else as pa_reshape_and_cache (act_dtype PA_F16 or PA_BF16).
+ * Every byte of the pools and every scale outside the written rows is left
+ * unchanged.
+ */
+pa_status pa_reshape_and_cache_i8(const void* key, const void* value, int8_t* key_cache,
+                                  int8_t* value_cache, float* key_scales, float* value_scales,
+                                  const int32_t* slot_mapping, int32_t T, int32_t Hkv,
+                                  int32_t D, int32_t BS, int32_t NB, pa_dtype act_dtype,
+                                  void* stream);
 
 /*
  * pa_decode_workspace_bytes -- bytes of scratch pa_decode needs for this
@@ -170,6 +196,24 @@ pa_status pa_decode_append(void* out, const void* query, const void* key, const 
                            void* stream);
 
 /*
+ * pa_decode_i8 -- pa_decode over an INT8 cache: key k_t = code * key scale
+ * of row t, value v_t likewise, dequantised inside the kernel.
+ *
+ * key_scales, value_scales fp32 [NB][Hkv][BS], 16-byte aligned (written by
+ *                 pa_reshape_and_cache_i8).
+ * Same workspace (pa_decode_workspace_bytes), arguments, outputs and errors
+ * as pa_decode with cache dtype PA_I8 (no k_scale / v_scale).
+ */
+pa_status pa_decode_i8(void* out, const void* query, const int8_t* key_cache,
+                       const int8_t* value_cache, const float* key_scales,
+                       const float* value_scales, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                       float softmax_scale, pa_dtype act_dtype, int32_t window,
+                       int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * pa_prefill_chunk -- causal attention of a chunk of new tokens per sequence
  * over everything cached for it (shared prefix blocks included).
  *
@@ -190,6 +234,19 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_len
                            int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
                            pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
                            float v_scale, void* stream);
+
+/*
+ * pa_prefill_chunk_i8 -- pa_prefill_chunk over an INT8 cache (scales as in
+ * pa_decode_i8, 4-byte aligned).  Same arguments, outputs and errors as
+ * pa_prefill_chunk with cache dtype PA_I8.
+ */
+pa_status pa_prefill_chunk_i8(void* out, const void* query, const int32_t* cu_q_lens,
+                              const int8_t* key_cache, const int8_t* value_cache,
+                              const float* key_scales, const float* value_scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                              int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                              pa_dtype act_dtype, void* stream);
 
 #ifdef __cplusplus
 }

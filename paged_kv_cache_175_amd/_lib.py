@@ -14,7 +14,7 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
-PA_F16, PA_BF16, PA_F8E4M3 = 0, 1, 2
+PA_F16, PA_BF16, PA_F8E4M3, PA_I8 = 0, 1, 2, 3
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 STATUS_NAMES = {
     PA_OK: "PA_OK",
@@ -32,6 +32,8 @@ SIGNATURES = {
     "pa_reshape_and_cache": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int,
         _f32, _f32, _vp]),
+    "pa_reshape_and_cache_i8": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
@@ -39,6 +41,12 @@ SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_i8": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+        ctypes.c_int, _i32, _i32, _vp, _sz, _vp]),
+    "pa_prefill_chunk_i8": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+        _f32, ctypes.c_int, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _vp]),

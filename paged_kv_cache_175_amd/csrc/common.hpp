@@ -4,7 +4,9 @@
 // Element formats of the paged cache ("PagedAttention in mistral.rs",
 // section "KV Cache Quantization"): the cache holds either the activation
 // type (fp16 / bf16) or FP8 E4M3.  E4M3 here is the OCP "FN" variant: bias 7,
-// largest finite magnitude 448, no infinities, NaN = S.1111.111.
+// largest finite magnitude 448, no infinities, NaN = S.1111.111.  A third
+// option ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build) packs INT8
+// codes with one fp32 scale per (token, KV head), kept beside the pages.
 //
 // Page layout (one (block, KV head) page of BS = 32 tokens, head-major as in
 // "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build):
@@ -29,7 +31,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Fmt { FMT_F16 = 0, FMT_BF16 = 1, FMT_E4M3 = 2 };
+enum Fmt { FMT_F16 = 0, FMT_BF16 = 1, FMT_E4M3 = 2, FMT_I8 = 3 };
+
+// One byte per cached element.
+constexpr bool byte_fmt(int f) { return f == FMT_E4M3 || f == FMT_I8; }
 
 constexpr int kPage = 32;  // tokens per block (page)
 
@@ -177,6 +182,36 @@ template <int F>
 __device__ __forceinline__ u32x4 e4m3x8_to_16(u32x2 c) {
   return u32x4{e4m3x2_to_16<F, false>(c[0]), e4m3x2_to_16<F, true>(c[0]),
                e4m3x2_to_16<F, false>(c[1]), e4m3x2_to_16<F, true>(c[1])};
+}
+
+// Eight int8 codes (two words, code i in byte i) -> eight 16-bit values of
+// format F.  |code| <= 128 has at most 8 significant bits, so fp32 and then
+// bf16 / fp16 hold it exactly.
+template <int F>
+__device__ __forceinline__ u32x4 i8x8_to_16(u32x2 c) {
+  typedef float f32x8_t __attribute__((ext_vector_type(8)));
+  f32x8_t f;
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f[4 * w + i] = static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(c[w] >> (8 * i))));
+  if constexpr (F == FMT_BF16) {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(f, v8));
+  } else {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(f, v8));
+  }
+}
+
+// INT8 code of t = x / scale: round half to even, clamped to +-127; a zero
+// scale (an all-zero row) gives 0.
+__device__ __forceinline__ uint32_t i8_encode(float x, float scale) {
+  if (scale == 0.f) return 0u;
+  const float q = __builtin_rintf(__fdiv_rn(x, scale));
+  const float c = fminf(fmaxf(q, -127.f), 127.f);
+  return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c)));
 }
 
 // ---------------------------------------------------------------------------

@@ -17,6 +17,8 @@ struct CacheWriteArgs {
   int T, Hkv, D, BS;
   int act, cache;  // Fmt codes
   float k_scale, v_scale;
+  float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32, written per row
+  float* value_scales;
 };
 
 struct DecodeArgs {
@@ -36,6 +38,8 @@ struct DecodeArgs {
   float* ws_o;  // [B*Hq*S*D]
   const void* new_key;    // append mode: [B][Hkv][D] act, or null
   const void* new_value;
+  const float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32
+  const float* value_scales;
 };
 
 struct PrefillArgs {
@@ -49,6 +53,8 @@ struct PrefillArgs {
   int B, Hq, Hkv, D, MBPS, max_chunk;
   int act, cache;
   float softmax_scale, k_scale, v_scale;
+  const float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32
+  const float* value_scales;
 };
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);

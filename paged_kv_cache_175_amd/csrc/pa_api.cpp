@@ -113,17 +113,19 @@ const char* pa_status_string(pa_status s) {
 
 const char* pa_last_error(void) { return g_last_error; }
 
-pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
-                               void* value_cache, const int32_t* slot_mapping, int32_t T,
-                               int32_t Hkv, int32_t D, int32_t BS, int32_t NB,
-                               pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
-                               float v_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status cache_write_common(const void* key, const void* value, void* key_cache,
+                             void* value_cache, float* key_scales, float* value_scales,
+                             const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                             int32_t BS, int32_t NB, pa_dtype act_dtype, pa_dtype cache_dtype,
+                             float k_scale, float v_scale, void* stream) {
   if (T < 0) return fail(PA_ERR_INVALID, "T must be >= 0 (got %d)", T);
   if (Hkv < 1 || D < 1 || NB < 1 || BS < 1)
     return fail(PA_ERR_INVALID, "Hkv, D, BS and NB must be positive");
   if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
-  if (!cache_ok(act_dtype, cache_dtype))
-    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
   if (D % 8 != 0 || D > 512)
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8, at most 512");
@@ -134,16 +136,46 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
   if (T == 0) return ok();
   if (!key || !value || !key_cache || !value_cache || !slot_mapping)
     return fail(PA_ERR_INVALID, "null pointer argument");
+  if (cache_dtype == PA_I8 && (!key_scales || !value_scales))
+    return fail(PA_ERR_INVALID, "null scale pool");
   if (!aligned(key, 16) || !aligned(value, 16))
     return fail(PA_ERR_INVALID, "key/value must be 16-byte aligned");
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
     return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
+  if (!aligned(key_scales, 4) || !aligned(value_scales, 4))
+    return fail(PA_ERR_INVALID, "scale pools must be 4-byte aligned");
   pa::CacheWriteArgs a{key,  value, key_cache, value_cache, slot_mapping, T,
                        Hkv,  D,     BS,        fmt_of(act_dtype), fmt_of(cache_dtype),
-                       k_scale, v_scale};
+                       k_scale, v_scale, key_scales, value_scales};
   hipError_t e = pa::launch_cache_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int32_t* slot_mapping, int32_t T,
+                               int32_t Hkv, int32_t D, int32_t BS, int32_t NB,
+                               pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
+                               float v_scale, void* stream) {
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  return cache_write_common(key, value, key_cache, value_cache, nullptr, nullptr, slot_mapping,
+                            T, Hkv, D, BS, NB, act_dtype, cache_dtype, k_scale, v_scale,
+                            stream);
+}
+
+pa_status pa_reshape_and_cache_i8(const void* key, const void* value, int8_t* key_cache,
+                                  int8_t* value_cache, float* key_scales, float* value_scales,
+                                  const int32_t* slot_mapping, int32_t T, int32_t Hkv,
+                                  int32_t D, int32_t BS, int32_t NB, pa_dtype act_dtype,
+                                  void* stream) {
+  return cache_write_common(key, value, key_cache, value_cache, key_scales, value_scales,
+                            slot_mapping, T, Hkv, D, BS, NB, act_dtype, PA_I8, 1.f, 1.f,
+                            stream);
 }
 
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -164,6 +196,7 @@ namespace {
 // pa_decode and pa_decode_append share everything but the appended row.
 pa_status decode_common(void* out, const void* query, const void* new_key,
                         const void* new_value, const void* key_cache, const void* value_cache,
+                        const float* key_scales, const float* value_scales,
                         const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                         int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_t MBPS,
                         int32_t max_context_len, float softmax_scale, pa_dtype act_dtype,
@@ -174,8 +207,6 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
     return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_context_len out of range");
   if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
-  if (!cache_ok(act_dtype, cache_dtype))
-    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
   const int G = Hq / Hkv;
   if (!pa::decode_supported(D, G, fmt_of(act_dtype), fmt_of(cache_dtype)))
@@ -194,10 +225,14 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   if (B == 0) return ok();
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID, "null pointer argument");
+  if (cache_dtype == PA_I8 && (!key_scales || !value_scales))
+    return fail(PA_ERR_INVALID, "null scale pool");
   if (!aligned(out, 16) || !aligned(query, 16))
     return fail(PA_ERR_INVALID, "out/query must be 16-byte aligned");
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
     return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
+  if (!aligned(key_scales, 16) || !aligned(value_scales, 16))
+    return fail(PA_ERR_INVALID, "scale pools must be 16-byte aligned");
   if ((long long)B * Hq > 0x7fffffffLL / D) return fail(PA_ERR_UNSUPPORTED, "B*Hq*D too large");
   Plan p;
   if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, &p))
@@ -237,6 +272,8 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   }
   a.new_key = new_key;
   a.new_value = new_value;
+  a.key_scales = key_scales;
+  a.value_scales = value_scales;
   hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -254,7 +291,10 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     float k_scale, float v_scale, int32_t window,
                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache, nullptr, nullptr,
+                       block_tables,
                        context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len, softmax_scale,
                        act_dtype, cache_dtype, k_scale, v_scale, window, partition_tokens,
                        workspace, workspace_bytes, stream);
@@ -272,25 +312,44 @@ pa_status pa_decode_append(void* out, const void* query, const void* key, const 
     return fail(PA_ERR_INVALID, "null pointer argument");
   if (!aligned(key, 2) || !aligned(value, 2))
     return fail(PA_ERR_INVALID, "key/value must be 2-byte aligned");
-  return decode_common(out, query, key, value, key_cache, value_cache, block_tables,
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  return decode_common(out, query, key, value, key_cache, value_cache, nullptr, nullptr,
+                       block_tables,
                        context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len, softmax_scale,
                        act_dtype, cache_dtype, k_scale, v_scale, window, partition_tokens,
                        workspace, workspace_bytes, stream);
 }
 
-pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_lens,
-                           const void* key_cache, const void* value_cache,
-                           const int32_t* block_tables, const int32_t* context_lens,
-                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
-                           int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
-                           pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
-                           float v_scale, void* stream) {
+pa_status pa_decode_i8(void* out, const void* query, const int8_t* key_cache,
+                       const int8_t* value_cache, const float* key_scales,
+                       const float* value_scales, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                       float softmax_scale, pa_dtype act_dtype, int32_t window,
+                       int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache, key_scales,
+                       value_scales, block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS,
+                       max_context_len, softmax_scale, act_dtype, PA_I8, 1.f, 1.f, window,
+                       partition_tokens, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status prefill_common(void* out, const void* query, const int32_t* cu_q_lens,
+                         const void* key_cache, const void* value_cache,
+                         const float* key_scales, const float* value_scales,
+                         const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_t MBPS,
+                         int32_t max_chunk_len, float softmax_scale, pa_dtype act_dtype,
+                         pa_dtype cache_dtype, float k_scale, float v_scale, void* stream) {
   if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || MBPS < 1 || max_chunk_len < 0)
     return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_chunk_len out of range");
   if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
-  if (!cache_ok(act_dtype, cache_dtype))
-    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
   if (!pa::prefill_supported(D, Hq / Hkv, fmt_of(act_dtype), fmt_of(cache_dtype)))
     return fail(PA_ERR_UNSUPPORTED, "prefill supports head_dim 64/96/128 and Hq/Hkv <= 16");
@@ -301,10 +360,14 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_len
   if (B == 0 || max_chunk_len == 0) return ok();
   if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID, "null pointer argument");
+  if (cache_dtype == PA_I8 && (!key_scales || !value_scales))
+    return fail(PA_ERR_INVALID, "null scale pool");
   if (!aligned(out, 16) || !aligned(query, 16))
     return fail(PA_ERR_INVALID, "out/query must be 16-byte aligned");
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16))
     return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
+  if (!aligned(key_scales, 4) || !aligned(value_scales, 4))
+    return fail(PA_ERR_INVALID, "scale pools must be 4-byte aligned");
   // Query rows (position, head) of one sequence and the flat grid must fit in int32.
   if ((long long)max_chunk_len * Hq * B > 0x7fffff00LL)
     return fail(PA_ERR_UNSUPPORTED, "max_chunk_len * Hq * B too large");
@@ -327,9 +390,41 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_len
   a.softmax_scale = softmax_scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.key_scales = key_scales;
+  a.value_scales = value_scales;
   hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_lens,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                           int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                           pa_dtype act_dtype, pa_dtype cache_dtype, float k_scale,
+                           float v_scale, void* stream) {
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  return prefill_common(out, query, cu_q_lens, key_cache, value_cache, nullptr, nullptr,
+                        block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS, max_chunk_len,
+                        softmax_scale, act_dtype, cache_dtype, k_scale, v_scale, stream);
+}
+
+pa_status pa_prefill_chunk_i8(void* out, const void* query, const int32_t* cu_q_lens,
+                              const int8_t* key_cache, const int8_t* value_cache,
+                              const float* key_scales, const float* value_scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                              int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                              pa_dtype act_dtype, void* stream) {
+  return prefill_common(out, query, cu_q_lens, key_cache, value_cache, key_scales,
+                        value_scales, block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS,
+                        max_chunk_len, softmax_scale, act_dtype, PA_I8, 1.f, 1.f, stream);
 }
 
 }  // extern "C"

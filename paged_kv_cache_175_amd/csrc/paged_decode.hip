@@ -30,6 +30,12 @@
 //     [D][32] (dimension 16n + col, tokens 8q .. 8q + 7).  One more MFMA
 //     against an all-ones A tile accumulates the running sum l.
 //
+// INT8 cache (per-token/head codes, "libmir-metal 0.2.0,
+// src/native/trace/kv.rs", fn build): the codes widen exactly like E4M3, and
+// each lane also loads the fp32 scales of its eight keys; the K scales
+// multiply the scores, the V scales multiply P for the V MFMAs (the all-ones
+// tile takes the unscaled P, so l stays the plain sum).
+//
 // Append mode (pa_decode_append) also stores the decoded token's K/V into its
 // cache row in the same launch; the wave reading that row takes it from LDS.
 //
@@ -58,11 +64,15 @@ template <>
 struct Raw8<FMT_E4M3> {
   u32x2 w;
 };
+template <>
+struct Raw8<FMT_I8> {
+  u32x2 w;
+};
 
 template <int CF>
 __device__ __forceinline__ Raw8<CF> load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   Raw8<CF> x;
-  if constexpr (CF == FMT_E4M3) {
+  if constexpr (byte_fmt(CF)) {
     x.w = buf_load8(r, voff, soff);
   } else {
     x.w = buf_load16(r, voff, soff);
@@ -76,6 +86,8 @@ template <int CF, int AF>
 __device__ __forceinline__ typename Mfma<AF>::vec as_operand(const Raw8<CF>& r) {
   if constexpr (CF == FMT_E4M3) {
     return __builtin_bit_cast(typename Mfma<AF>::vec, e4m3x8_to_16<AF>(r.w));
+  } else if constexpr (CF == FMT_I8) {
+    return __builtin_bit_cast(typename Mfma<AF>::vec, i8x8_to_16<AF>(r.w));
   } else {
     return __builtin_bit_cast(typename Mfma<AF>::vec, r.w);
   }
@@ -95,6 +107,14 @@ struct PageRegs<D, FMT_E4M3> {
   u32x4 k[D / 32];         // [k-step]: tile 0 in words 0-1, tile 1 in words 2-3
   Raw8<FMT_E4M3> v[D / 16];
 };
+// INT8: as E4M3, plus the scales of the lane's eight keys 8q .. 8q + 7.
+template <int D>
+struct PageRegs<D, FMT_I8> {
+  u32x4 k[D / 32];
+  Raw8<FMT_I8> v[D / 16];
+  f32x4 ks[2];
+  f32x4 vs[2];
+};
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -110,10 +130,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     int Hkv, int MBPS, int window, int S, float qk_scale_log2, float v_scale,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
     const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
-    float k_enc_scale, float v_enc_scale) {
+    float k_enc_scale, float v_enc_scale, const float* __restrict__ key_scales,
+    const float* __restrict__ value_scales) {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
-  constexpr int EB = (CF == FMT_E4M3) ? 1 : 2;
+  constexpr int EB = byte_fmt(CF) ? 1 : 2;
   constexpr int KSTEPS = D / 32;
   constexpr int NT = D / 16;
   typedef typename Mfma<AF>::vec vec;
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // reads the page patches the row into its page registers, so nothing in
   // this launch depends on the store becoming visible.
   int row_new = -1, k_new = -1, w_new = -1;
-  if (new_key != nullptr) {
+  if (CF != FMT_I8 && new_key != nullptr) {
     const int ctx = context_lens[b];
     const int r_new = window > 0 ? (ctx - 1) % window : ctx - 1;
     const int pg_new = r_new / kPage;
@@ -178,7 +199,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       for (int d = threadIdx.x; d < D; d += 64 * W) {
         const uint16_t kx = new_key[src + d];
         const uint16_t vx = new_value[src + d];
-        if constexpr (CF == FMT_E4M3) {
+        if constexpr (byte_fmt(CF)) {
           const uint32_t kq = e4m3_encode(lo16_to_f32<AF>(kx), k_enc_scale);
           const uint32_t vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
           key_cache[page + k_page_off(row_new, d)] = static_cast<uint8_t>(kq);
@@ -238,7 +259,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       const size_t base = ((size_t)phys * Hkv + g) * page_elems * EB;
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, PAGE_BYTES);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(value_cache + base, PAGE_BYTES);
-      if constexpr (CF == FMT_E4M3) {
+      if constexpr (CF == FMT_I8) {
+        // fp32 scales of keys 8 q4 .. 8 q4 + 7 of this (block, head) page.
+        const size_t srow = ((size_t)phys * Hkv + g) * kPage;
+        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(key_scales + srow, kPage * 4);
+        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(value_scales + srow, kPage * 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          Pg.ks[h] = __builtin_bit_cast(f32x4, buf_load16(ksr, 32 * q4 + 16 * h, 0));
+          Pg.vs[h] = __builtin_bit_cast(f32x4, buf_load16(vsr, 32 * q4 + 16 * h, 0));
+        }
+      }
+      if constexpr (byte_fmt(CF)) {
 #pragma unroll
         for (int j = 0; j < KSTEPS; ++j) Pg.k[j] = buf_load16(kr, k_lane, j * K_J);
       } else {
@@ -253,7 +285,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     // K operand of key tile kt, k-step j.
     auto k_operand = [&](const PageRegs<D, CF>& Pg, int kt, int j) -> vec {
-      if constexpr (CF == FMT_E4M3) {
+      if constexpr (byte_fmt(CF)) {
         Raw8<CF> r;
         r.w = kt == 0 ? u32x2{Pg.k[j][0], Pg.k[j][1]} : u32x2{Pg.k[j][2], Pg.k[j][3]};
         return as_operand<CF, AF>(r);
@@ -266,7 +298,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // consecutive cache elements.  Register arrays are only ever indexed by
     // constants (a runtime index would move them to scratch memory).
     auto set_elem = [&](auto& raw, int e, uint32_t x) {
-      constexpr int EPW = (CF == FMT_E4M3) ? 4 : 2;   // elements per word
+      constexpr int EPW = byte_fmt(CF) ? 4 : 2;   // elements per word
       constexpr int BITS = 32 / EPW;
       constexpr uint32_t EMASK = (1u << BITS) - 1u;
       const int sh = BITS * (e % EPW);
@@ -289,7 +321,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
           for (int j = 0; j < KSTEPS; ++j) {
             const u32x4 nk = *reinterpret_cast<const u32x4*>(&newk_lds[8 * (q4 + 4 * j)]);
-            if constexpr (CF == FMT_E4M3) {
+            if constexpr (byte_fmt(CF)) {
               // The codes were staged one per 16-bit slot: pack eight into
               // two words.
               u32x2 c;
@@ -326,6 +358,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
           if (base + 8 * q4 + e >= L) {
 #pragma unroll
             for (int n = 0; n < NT; ++n) set_elem(Pg.v[n].w, e, 0u);
+            if constexpr (CF == FMT_I8) Pg.vs[e >> 2][e & 3] = 0.f;  // stale scale
           }
         }
       }
@@ -340,6 +373,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) st[kt] *= qk_scale_log2;
+      if constexpr (CF == FMT_I8) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st[kt][r] *= Pg.ks[r >> 1][2 * (r & 1) + kt];
+      }
       if (partial) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -366,12 +405,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) pv[2 * r + kt] = fast_exp2(st[kt][r] - m_run);
-      const vec pb = __builtin_convertvector(pv, vec);
-
-      // O^T += V^T P^T, and l += 1^T P^T.
+      // l += 1^T P^T.
+      const vec pb_l = __builtin_convertvector(pv, vec);
+      o_acc[NT] = Mfma<AF>::mma(ones, pb_l, o_acc[NT]);
+      // O^T += V^T P^T; with INT8 each key's V scale goes into its P.
+      vec pb = pb_l;
+      if constexpr (CF == FMT_I8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] *= Pg.vs[e >> 2][e & 3];
+        pb = __builtin_convertvector(pv, vec);
+      }
 #pragma unroll
       for (int n = 0; n < NT; ++n) o_acc[n] = Mfma<AF>::mma(as_operand<CF, AF>(Pg.v[n]), pb, o_acc[n]);
-      o_acc[NT] = Mfma<AF>::mma(ones, pb, o_acc[NT]);
     };
 
     // Two register buffers: page k is computed while page k + 1 loads.  The
@@ -507,14 +552,14 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
                        (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
                        a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o,
                        (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
-                       a.v_scale);
+                       a.v_scale, a.key_scales, a.value_scales);
   } else if (a.W == 4) {
     hipLaunchKernelGGL((decode_split<D, G, CF, AF, 4>), grid, dim3(256), 0, stream,
                        (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
                        (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
                        a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o,
                        (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
-                       a.v_scale);
+                       a.v_scale, a.key_scales, a.value_scales);
   } else {
     return hipErrorInvalidValue;
   }
@@ -531,9 +576,11 @@ hipError_t launch_fmt(const DecodeArgs& a, hipStream_t s) {
   if (a.act == FMT_BF16) {
     if (a.cache == FMT_BF16) return launch_typed<D, G, FMT_BF16, FMT_BF16>(a, s);
     if (a.cache == FMT_E4M3) return launch_typed<D, G, FMT_E4M3, FMT_BF16>(a, s);
+    if (a.cache == FMT_I8) return launch_typed<D, G, FMT_I8, FMT_BF16>(a, s);
   } else if (a.act == FMT_F16) {
     if (a.cache == FMT_F16) return launch_typed<D, G, FMT_F16, FMT_F16>(a, s);
     if (a.cache == FMT_E4M3) return launch_typed<D, G, FMT_E4M3, FMT_F16>(a, s);
+    if (a.cache == FMT_I8) return launch_typed<D, G, FMT_I8, FMT_F16>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -556,7 +603,7 @@ bool decode_supported(int D, int G, int act, int cache) {
   if (D != 64 && D != 96 && D != 128) return false;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
   if (act != FMT_BF16 && act != FMT_F16) return false;
-  return cache == act || cache == FMT_E4M3;
+  return cache == act || cache == FMT_E4M3 || cache == FMT_I8;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -17,8 +17,12 @@
 // position its rows can see.  Pages of a 16-bit cache go from global memory
 // straight into LDS (global_load_lds_dwordx4, no registers), two pages ahead
 // of the one being computed, through three LDS buffers and one barrier a
-// page.  E4M3 pages are widened to the activation format on the way, so they
-// pass through registers, one page ahead, through two buffers.
+// page.  E4M3 and INT8 pages are widened to the activation format on the
+// way, so they pass through registers, one page ahead, through two buffers.
+// An INT8 page ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build:
+// per-token/head codes with fp32 scales) also stages its 32 K and 32 V row
+// scales; the K scales multiply the scores and the V scales the P of the V
+// MFMAs (the all-ones tile takes the unscaled P).
 //
 // Per wave and page, everything is computed transposed so that the
 // probabilities never leave registers:
@@ -121,11 +125,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t* __restrict__ cu_q_lens, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int B, int MBPS,
-    int row_tiles, float qk_scale_log2, float v_scale) {
+    int row_tiles, float qk_scale_log2, float v_scale, const float* __restrict__ key_scales,
+    const float* __restrict__ value_scales) {
   constexpr int KS = D / 32;              // k-steps of S^T (32 head dims each)
   constexpr int NT = D / 16;              // 16-dim tiles of O^T
   constexpr int PAGE = BS * D;            // elements of one K (or V) page
-  constexpr bool kDma = CF != FMT_E4M3;
+  constexpr bool kDma = !byte_fmt(CF);
+  constexpr bool kI8 = CF == FMT_I8;
   constexpr int NBUF = kDma ? 3 : 2;
   constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
   constexpr int NCH = PAGE / 8;           // 8-element chunks per page (K or V)
@@ -139,6 +145,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF][PAGE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[NBUF][PAGE];
+  __shared__ __attribute__((aligned(16))) float ks_lds[kI8 ? NBUF : 1][BS];  // INT8 row scales
+  __shared__ __attribute__((aligned(16))) float vs_lds[kI8 ? NBUF : 1][BS];
 
   // --- which (KV head, sequence, row tile) this workgroup owns -----------
   const int n_items = row_tiles * Hkv * B;
@@ -244,9 +252,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Register path (E4M3): chunk c of the K page is (d / 8, t) = (c / 32,
-  // c % 32) and chunk c of the V page is (d, t / 8) = (c / 4, c % 4).
+  // Register path (E4M3, INT8): chunk c of the K page is (d / 8, t) =
+  // (c / 32, c % 32) and chunk c of the V page is (d, t / 8) = (c / 4, c % 4).
+  // Threads 0..31 also carry the page's K row scales, 32..63 its V scales.
   u32x2 kreg[kDma ? 1 : ST], vreg[kDma ? 1 : ST];
+  float sreg = 0.f;
   auto load_regs = [&](int phys) {
     const size_t page = ((size_t)phys * blk_stride + head_off) * EB;
 #pragma unroll
@@ -257,17 +267,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         vreg[i] = *reinterpret_cast<const u32x2*>(value_cache + page + (size_t)c * 8);
       }
     }
+    if constexpr (kI8) {
+      const size_t srow = ((size_t)phys * Hkv + g) * BS;
+      if (tid < BS) sreg = key_scales[srow + tid];
+      else if (tid < 2 * BS) sreg = value_scales[srow + tid - BS];
+    }
   };
-  auto store_regs = [&](int buf) {
+  auto widen = [&](u32x2 c) -> u32x4 {
+    if constexpr (kI8) {
+      return i8x8_to_16<AF>(c);
+    } else {
+      return e4m3x8_to_16<AF>(c);
+    }
+  };
+  auto store_regs = [&](int buf, int base) {
 #pragma unroll
     for (int i = 0; i < ST; ++i) {
       const int c = tid + i * kThreads;
       if (NCH % kThreads == 0 || c < NCH) {
-        *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c >> 5, c & 31) * 8]) =
-            e4m3x8_to_16<AF>(kreg[i]);
-        *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(c >> 2, c & 3) * 8]) =
-            e4m3x8_to_16<AF>(vreg[i]);
+        *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c >> 5, c & 31) * 8]) = widen(kreg[i]);
+        *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(c >> 2, c & 3) * 8]) = widen(vreg[i]);
       }
+    }
+    if constexpr (kI8) {
+      // Stale rows past the context end get scale 0 (their scores are
+      // masked anyway; a NaN V scale would survive a zero probability).
+      const int row = tid & (BS - 1);
+      const float sv = base + row < ctx ? sreg : 0.f;
+      if (tid < BS) ks_lds[buf][row] = sv;
+      else if (tid < 2 * BS) vs_lds[buf][row] = sv;
     }
   };
 
@@ -282,7 +310,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     lds_barrier();
   } else {
     load_regs(phys_of(0));
-    store_regs(0);
+    store_regs(0, 0);
     __syncthreads();
   }
 
@@ -327,6 +355,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int t = 0; t < NQ; ++t)
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) s_acc[kt][t] *= qk_scale_log2;
+        if constexpr (kI8) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const f32x4 ks4 = *reinterpret_cast<const f32x4*>(&ks_lds[cur][8 * q4 + 4 * kt]);
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) s_acc[kt][t] *= ks4;
+          }
+        }
         if constexpr (decltype(masked)::value) {
 #pragma unroll
           for (int t = 0; t < NQ; ++t)
@@ -359,6 +395,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int r = 0; r < 4; ++r) pv[4 * kt + r] = fast_exp2(s_acc[kt][t][r] - m_run[t]);
           pb[t] = __builtin_convertvector(pv, vec);
+          if constexpr (kI8) {
+            // l from the unscaled P; the V MFMAs take P times each key's V scale.
+            o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const f32x4 vs4 = *reinterpret_cast<const f32x4*>(&vs_lds[cur][8 * q4 + 4 * kt]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) pv[4 * kt + r] *= vs4[r];
+            }
+            pb[t] = __builtin_convertvector(pv, vec);
+          }
         }
       }
 
@@ -381,8 +428,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
           for (int t = 0; t < NQ; ++t) o_acc[n][t] = Mfma<AF>::mma(va, pb[t], o_acc[n][t]);
         }
+        if constexpr (!kI8) {
 #pragma unroll
-        for (int t = 0; t < NQ; ++t) o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
+          for (int t = 0; t < NQ; ++t) o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
+        }
       }
       };
       if (base + BS - 1 > pos_lo) {
@@ -403,7 +452,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       lds_barrier();
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     } else {
-      if (p + 1 < npages) store_regs(cur ^ 1);
+      if (p + 1 < npages) store_regs(cur ^ 1, base + BS);
       __syncthreads();
       cur ^= 1;
     }
@@ -427,14 +476,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D>
+// Query tiles of 16 rows per wave: as many as fit in 256 VGPRs at two waves
+// per SIMD (INT8 keeps its row scales and a second P operand live too).
+template <int D, int CF>
 constexpr int query_tiles() {
-  return D <= 96 ? 4 : 2;
+  if (D <= 64) return 4;
+  if (D <= 96) return CF == FMT_I8 ? 3 : 4;
+  return 2;
 }
 
 template <int D, int CF, int AF>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-  constexpr int NQ = query_tiles<D>();
+  constexpr int NQ = query_tiles<D, CF>();
   constexpr int RW = 16 * NQ * kWaves;
   const int G = a.Hq / a.Hkv;
   const long long row_tiles = ((long long)a.max_chunk * G + RW - 1) / RW;
@@ -447,7 +500,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
                      dim3(kThreads), 0, s, (uint16_t*)a.out, (const uint16_t*)a.query,
                      a.cu_q_lens, (const uint8_t*)a.key_cache, (const uint8_t*)a.value_cache,
                      a.block_tables, a.context_lens, a.Hq, a.Hkv, G, a.B, a.MBPS,
-                     (int)row_tiles, qk, vs);
+                     (int)row_tiles, qk, vs, a.key_scales, a.value_scales);
   return hipGetLastError();
 }
 
@@ -456,9 +509,11 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   if (a.act == FMT_BF16) {
     if (a.cache == FMT_BF16) return launch_t<D, FMT_BF16, FMT_BF16>(a, s);
     if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_BF16>(a, s);
+    if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_BF16>(a, s);
   } else if (a.act == FMT_F16) {
     if (a.cache == FMT_F16) return launch_t<D, FMT_F16, FMT_F16>(a, s);
     if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_F16>(a, s);
+    if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_F16>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -469,7 +524,7 @@ bool prefill_supported(int D, int G, int act, int cache) {
   if (D != 64 && D != 96 && D != 128) return false;
   if (G < 1 || G > 16) return false;
   if (act != FMT_BF16 && act != FMT_F16) return false;
-  return cache == act || cache == FMT_E4M3;
+  return cache == act || cache == FMT_E4M3 || cache == FMT_I8;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {

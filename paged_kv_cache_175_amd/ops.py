@@ -7,7 +7,10 @@ current stream, nothing else.  Every op runs in the HIP kernels of
 Cache dtypes follow the page "PagedAttention in mistral.rs", section "KV
 Cache Quantization": ``"auto"`` stores the activation dtype, ``"f8e4m3"``
 stores E4M3 codes (held in ``torch.uint8`` tensors) with per-tensor fp32
-scales for K and V.
+scales for K and V.  ``"i8"`` ("libmir-metal 0.2.0, src/native/trace/kv.rs",
+fn build: packed INT8 pages with per-token/head FP32 scales) stores int8
+codes in ``torch.int8`` pools plus fp32 scale pools ``[NB, Hkv, BS]``
+(:func:`alloc_scale_pools`), passed as ``key_scales`` / ``value_scales``.
 """
 
 from __future__ import annotations
@@ -32,6 +35,8 @@ def _act_code(t: torch.Tensor) -> int:
 def _cache_code(cache: torch.Tensor, act: torch.dtype) -> int:
     if cache.dtype == torch.uint8 or cache.dtype == getattr(torch, "float8_e4m3fn", None):
         return _lib.PA_F8E4M3
+    if cache.dtype == torch.int8:
+        return _lib.PA_I8
     if cache.dtype != act:
         raise TypeError(f"cache dtype {cache.dtype} must equal the activation dtype {act} "
                         "or be uint8 (E4M3 codes)")
@@ -57,7 +62,9 @@ def _stream() -> int:
 
 
 def cache_dtype_name(cache: torch.Tensor) -> str:
-    return "f8e4m3" if cache.dtype in (torch.uint8,) else "auto"
+    if cache.dtype == torch.uint8:
+        return "f8e4m3"
+    return "i8" if cache.dtype == torch.int8 else "auto"
 
 
 def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 32):
@@ -76,8 +83,30 @@ def alloc_pools(num_blocks: int, num_kv_heads: int, head_dim: int, act_dtype: to
                 cache_dtype: str = "auto", device="cuda", block_size: int = 32):
     """Allocate (uninitialised) key and value pools up front."""
     ks, vs = pool_shapes(num_blocks, num_kv_heads, head_dim, block_size)
-    dt = torch.uint8 if cache_dtype == "f8e4m3" else act_dtype
+    dt = {"f8e4m3": torch.uint8, "i8": torch.int8}.get(cache_dtype, act_dtype)
     return (torch.empty(ks, dtype=dt, device=device), torch.empty(vs, dtype=dt, device=device))
+
+
+def alloc_scale_pools(num_blocks: int, num_kv_heads: int, device="cuda", block_size: int = 32):
+    """The fp32 per-row scale pools ``[NB, Hkv, BS]`` of an INT8 cache (K, V)."""
+    shape = (num_blocks, num_kv_heads, block_size)
+    return (torch.zeros(shape, dtype=torch.float32, device=device),
+            torch.zeros(shape, dtype=torch.float32, device=device))
+
+
+def _scales(cache_code, key_scales, value_scales, NB, Hkv, BS):
+    """Scale-pool pointers of an INT8 cache (checked), else None."""
+    if cache_code != _lib.PA_I8:
+        if key_scales is not None or value_scales is not None:
+            raise ValueError("scale pools belong to an int8 cache")
+        return None
+    if key_scales is None or value_scales is None:
+        raise ValueError("an int8 cache needs key_scales and value_scales")
+    _dev(key_scales, value_scales)
+    for t in (key_scales, value_scales):
+        if t.dtype != torch.float32 or tuple(t.shape) != (NB, Hkv, BS):
+            raise ValueError(f"scale pools must be float32 [{NB}, {Hkv}, {BS}]")
+    return key_scales.data_ptr(), value_scales.data_ptr()
 
 
 def _pool_geometry(key_cache: torch.Tensor, value_cache: torch.Tensor):
@@ -92,10 +121,14 @@ def _pool_geometry(key_cache: torch.Tensor, value_cache: torch.Tensor):
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                       value_cache: torch.Tensor, slot_mapping: torch.Tensor,
-                      k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+                      k_scale: float = 1.0, v_scale: float = 1.0,
+                      key_scales: Optional[torch.Tensor] = None,
+                      value_scales: Optional[torch.Tensor] = None) -> None:
     """Write ``key``/``value`` ``[T, Hkv, D]`` into the pools at ``slot_mapping``.
 
-    Pools as from :func:`alloc_pools`; a negative slot skips its token.
+    Pools as from :func:`alloc_pools`; a negative slot skips its token.  An
+    int8 cache also writes each row's scale into ``key_scales`` /
+    ``value_scales``.
     """
     _dev(key, value, key_cache, value_cache, slot_mapping)
     _i32(slot_mapping)
@@ -107,7 +140,13 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
         raise ValueError("shape mismatch between tokens, caches and slot_mapping")
     act = _act_code(key)
     cache = _cache_code(key_cache, key.dtype)
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
     lib = _lib.load()
+    if sc is not None:
+        _lib.check(lib.pa_reshape_and_cache_i8(
+            key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            *sc, slot_mapping.data_ptr(), T, Hkv, D, BS, NB, act, _stream()))
+        return
     _lib.check(lib.pa_reshape_and_cache(
         key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         slot_mapping.data_ptr(), T, Hkv, D, BS, NB, act, cache, float(k_scale), float(v_scale),
@@ -134,13 +173,16 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
            softmax_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
            window: int = 0, partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, new_key: Optional[torch.Tensor] = None,
-           new_value: Optional[torch.Tensor] = None) -> torch.Tensor:
+           new_value: Optional[torch.Tensor] = None,
+           key_scales: Optional[torch.Tensor] = None,
+           value_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged decode attention; returns ``out`` ``[B, Hq, D]``.
 
     ``workspace`` (uint8, >= :func:`decode_workspace_bytes`) is allocated here
     when not given.  With ``new_key`` / ``new_value`` (``[B, Hkv, D]``) the
     decoded token is first stored into its cache row in the same launch
-    (``pa_decode_append``).
+    (``pa_decode_append``; not for an int8 cache).  An int8 cache reads its
+    scale pools ``key_scales`` / ``value_scales`` (``pa_decode_i8``).
     """
     _dev(query, key_cache, value_cache, block_tables, context_lens)
     _i32(block_tables, context_lens)
@@ -162,6 +204,16 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = _lib.load()
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
+    if sc is not None:
+        if new_key is not None:
+            raise ValueError("the fused append is not available for an int8 cache")
+        _lib.check(lib.pa_decode_i8(
+            out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *sc,
+            block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+            int(max_context_len), float(softmax_scale), act, int(window),
+            int(partition_tokens), ws_ptr, ws_bytes, _stream()))
+        return out
     tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
             int(max_context_len), float(softmax_scale), act, cache, float(k_scale),
             float(v_scale), int(window), int(partition_tokens), ws_ptr, ws_bytes, _stream())
@@ -189,8 +241,12 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
                   value_cache: torch.Tensor, block_tables: torch.Tensor,
                   context_lens: torch.Tensor, max_chunk_len: int, softmax_scale: float,
                   k_scale: float = 1.0, v_scale: float = 1.0,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Causal chunked prefill over the paged cache; returns ``out`` ``[total_q, Hq, D]``."""
+                  out: Optional[torch.Tensor] = None,
+                  key_scales: Optional[torch.Tensor] = None,
+                  value_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal chunked prefill over the paged cache; returns ``out`` ``[total_q, Hq, D]``.
+
+    An int8 cache reads its scale pools (``pa_prefill_chunk_i8``)."""
     _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
     _i32(cu_q_lens, block_tables, context_lens)
     total_q, Hq, D = query.shape
@@ -207,6 +263,13 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
         out = torch.empty_like(query)
     _dev(out)
     lib = _lib.load()
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
+    if sc is not None:
+        _lib.check(lib.pa_prefill_chunk_i8(
+            out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
+            value_cache.data_ptr(), *sc, block_tables.data_ptr(), context_lens.data_ptr(), B,
+            Hq, Hkv, D, BS, MBPS, int(max_chunk_len), float(softmax_scale), act, _stream()))
+        return out
     _lib.check(lib.pa_prefill_chunk(
         out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
         value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv,
@@ -222,16 +285,24 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
 
 
 def prepare_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
-                              k_scale: float = 1.0, v_scale: float = 1.0):
+                              k_scale: float = 1.0, v_scale: float = 1.0,
+                              key_scales=None, value_scales=None):
     _dev(key, value, key_cache, value_cache, slot_mapping)
     _i32(slot_mapping)
     T, Hkv, D = key.shape
     NB, _, BS, _ = _pool_geometry(key_cache, value_cache)
     lib = _lib.load()
-    args = (key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-            slot_mapping.data_ptr(), T, Hkv, D, BS, NB, _act_code(key),
-            _cache_code(key_cache, key.dtype), float(k_scale), float(v_scale), _stream())
-    fn = lib.pa_reshape_and_cache
+    cache = _cache_code(key_cache, key.dtype)
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
+    if sc is not None:
+        args = (key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                *sc, slot_mapping.data_ptr(), T, Hkv, D, BS, NB, _act_code(key), _stream())
+        fn = lib.pa_reshape_and_cache_i8
+    else:
+        args = (key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                slot_mapping.data_ptr(), T, Hkv, D, BS, NB, _act_code(key), cache,
+                float(k_scale), float(v_scale), _stream())
+        fn = lib.pa_reshape_and_cache
 
     def call():
         _lib.check(fn(*args))
@@ -241,7 +312,8 @@ def prepare_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
 def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
                    max_context_len: int, softmax_scale: float, out, workspace=None,
                    k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
-                   partition_tokens: int = 0, new_key=None, new_value=None):
+                   partition_tokens: int = 0, new_key=None, new_value=None,
+                   key_scales=None, value_scales=None):
     _dev(query, key_cache, value_cache, block_tables, context_lens, out)
     _i32(block_tables, context_lens)
     B, Hq, D = query.shape
@@ -252,12 +324,22 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
     if ws_bytes < need:
         raise PagedKVError(_lib.PA_ERR_WORKSPACE, f"workspace needs {need} bytes")
     lib = _lib.load()
+    cache = _cache_code(key_cache, query.dtype)
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
     tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
-            int(max_context_len), float(softmax_scale), _act_code(query),
-            _cache_code(key_cache, query.dtype), float(k_scale), float(v_scale), int(window),
-            int(partition_tokens), 0 if workspace is None else workspace.data_ptr(), ws_bytes,
-            _stream())
-    if new_key is None:
+            int(max_context_len), float(softmax_scale), _act_code(query), cache,
+            float(k_scale), float(v_scale), int(window), int(partition_tokens), ws_ptr,
+            ws_bytes, _stream())
+    if sc is not None:
+        if new_key is not None:
+            raise ValueError("the fused append is not available for an int8 cache")
+        args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                *sc, block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+                int(max_context_len), float(softmax_scale), _act_code(query), int(window),
+                int(partition_tokens), ws_ptr, ws_bytes, _stream())
+        fn = lib.pa_decode_i8
+    elif new_key is None:
         args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
                 value_cache.data_ptr()) + tail
         fn = lib.pa_decode
@@ -274,7 +356,8 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
 
 def prepare_prefill_chunk(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens,
                           max_chunk_len: int, softmax_scale: float, out,
-                          k_scale: float = 1.0, v_scale: float = 1.0):
+                          k_scale: float = 1.0, v_scale: float = 1.0,
+                          key_scales=None, value_scales=None):
     _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens, out)
     _i32(cu_q_lens, block_tables, context_lens)
     total_q, Hq, D = query.shape
@@ -282,11 +365,20 @@ def prepare_prefill_chunk(query, cu_q_lens, key_cache, value_cache, block_tables
     B = context_lens.numel()
     MBPS = block_tables.shape[1]
     lib = _lib.load()
-    args = (out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
-            value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv,
-            D, BS, MBPS, int(max_chunk_len), float(softmax_scale), _act_code(query),
-            _cache_code(key_cache, query.dtype), float(k_scale), float(v_scale), _stream())
-    fn = lib.pa_prefill_chunk
+    cache = _cache_code(key_cache, query.dtype)
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
+    if sc is not None:
+        args = (out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
+                value_cache.data_ptr(), *sc, block_tables.data_ptr(), context_lens.data_ptr(),
+                B, Hq, Hkv, D, BS, MBPS, int(max_chunk_len), float(softmax_scale),
+                _act_code(query), _stream())
+        fn = lib.pa_prefill_chunk_i8
+    else:
+        args = (out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
+                value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq,
+                Hkv, D, BS, MBPS, int(max_chunk_len), float(softmax_scale), _act_code(query),
+                cache, float(k_scale), float(v_scale), _stream())
+        fn = lib.pa_prefill_chunk
 
     def call():
         _lib.check(fn(*args))

@@ -332,6 +332,12 @@ def fp8_decode(B: int = 64, ctx_range=(1024, 8192), seed: int = 2) -> DecodeWork
                            act="bf16", cache="e4m3", ctx_range=ctx_range)
 
 
+def int8_decode(B: int = 64, ctx_range=(1024, 8192), seed: int = 5) -> DecodeWorkload:
+    """The FP8 decode shape with an INT8 per-token/head cache (fp32 row scales)."""
+    return decode_workload("int8_decode", seed=seed, B=B, Hq=32, Hkv=8, D=128, act="bf16",
+                           cache="int8", ctx_range=ctx_range)
+
+
 def sliding_decode(B: int = 8, window: int = 4096, pos_range=(4096, 32768),
                    seed: int = 3) -> DecodeWorkload:
     """Rolling-buffer decode: W-row ring per sequence, 32/8 heads, head_dim 128."""

@@ -25,7 +25,7 @@ from paged_kv_cache_175_amd.workloads import DecodeWorkload, PrefillWorkload
 NAN16 = {"bf16": 0x7FC0, "f16": 0x7E00}
 NAN_E4M3 = 0x7F
 TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16}
-TOL = {"bf16": 1e-2, "f16": 1e-2, "e4m3": 2e-2}
+TOL = {"bf16": 1e-2, "f16": 1e-2, "e4m3": 2e-2, "int8": 2e-2}
 
 
 def say(msg: str) -> None:
@@ -144,7 +144,7 @@ def hip_prefill(wl: PrefillWorkload, kc, vc, device="cuda"):
 
 def pool_bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
-    if t.dtype == torch.uint8:
+    if t.dtype in (torch.uint8, torch.int8):
         return t.numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -204,6 +204,134 @@ def oracle_prefill(wl: PrefillWorkload, kc, vc):
     return o_attn.prefill_chunk(wl.query, wl.act, wl.cu_q_lens, kc, vc, wl.cache,
                                 wl.block_tables, wl.context_lens, wl.scale, wl.k_scale,
                                 wl.v_scale)
+
+
+# --------------------------------------------------------------------------- INT8 cache
+# Pools of int8 codes plus fp32 scale pools [NB+1, Hkv, BS]; the scales start
+# NaN-filled, so a stale row that reaches an output shows up as NaN.
+
+NAN_F32 = float("nan")
+
+
+def gpu_pools_i8(wl, device="cuda"):
+    kshape, vshape = ops.pool_shapes(wl.pool_blocks, wl.Hkv, wl.D, wl.BS)
+    kc = torch.full(kshape, 0x7F, dtype=torch.int8, device=device)
+    vc = torch.full(vshape, 0x7F, dtype=torch.int8, device=device)
+    shape = (wl.pool_blocks, wl.Hkv, wl.BS)
+    ks = torch.full(shape, NAN_F32, dtype=torch.float32, device=device)
+    vs = torch.full(shape, NAN_F32, dtype=torch.float32, device=device)
+    return kc, vc, ks, vs
+
+
+def _gpu_write_i8(wl, pools, k_bits, v_bits, slots, device="cuda"):
+    if len(slots) == 0:
+        return
+    kc, vc, ks, vs = pools
+    ops.reshape_and_cache(_act_tensor(k_bits, wl.act, device), _act_tensor(v_bits, wl.act, device),
+                          kc, vc, torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(device),
+                          key_scales=ks, value_scales=vs)
+
+
+def hip_decode_setup_i8(wl: DecodeWorkload, device="cuda"):
+    pools = gpu_pools_i8(wl, device)
+    ks_, vs_, sl = [], [], []
+    for b in range(wl.B):
+        n = wl.cached_k[b].shape[0]
+        if n:
+            pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+            sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+            ks_.append(wl.cached_k[b])
+            vs_.append(wl.cached_v[b])
+    if sl:
+        _gpu_write_i8(wl, pools, np.concatenate(ks_), np.concatenate(vs_), np.concatenate(sl),
+                      device)
+    new_slots = np.array([pool.slots_from_table(wl.block_tables[b], [wl.new_pos[b]], wl.BS,
+                                                wl.window)[0] for b in range(wl.B)], np.int32)
+    _gpu_write_i8(wl, pools, wl.new_k, wl.new_v, new_slots, device)
+    return pools
+
+
+def hip_decode_i8(wl: DecodeWorkload, pools, partition_tokens=0, device="cuda"):
+    kc, vc, ks, vs = pools
+    q = _act_tensor(wl.query, wl.act, device)
+    return ops.decode(q, kc, vc, torch.from_numpy(wl.block_tables).to(device),
+                      torch.from_numpy(wl.context_lens).to(device),
+                      int(wl.context_lens.max(initial=0)), wl.scale, window=wl.window,
+                      partition_tokens=partition_tokens, key_scales=ks, value_scales=vs)
+
+
+def hip_prefill_setup_i8(wl: PrefillWorkload, device="cuda"):
+    pools = gpu_pools_i8(wl, device)
+    sl = pool.slots_from_table(wl.block_tables[0], np.arange(wl.prefix_len), wl.BS)
+    _gpu_write_i8(wl, pools, wl.prefix_k, wl.prefix_v, sl, device)
+    for b in range(wl.B):
+        C = int(wl.chunk_lens[b])
+        sl = pool.slots_from_table(wl.block_tables[b], np.arange(wl.prefix_len, wl.prefix_len + C),
+                                   wl.BS)
+        _gpu_write_i8(wl, pools, wl.chunk_k[b], wl.chunk_v[b], sl, device)
+    return pools
+
+
+def hip_prefill_i8(wl: PrefillWorkload, pools, device="cuda"):
+    kc, vc, ks, vs = pools
+    q = _act_tensor(wl.query, wl.act, device)
+    return ops.prefill_chunk(q, torch.from_numpy(wl.cu_q_lens).to(device), kc, vc,
+                             torch.from_numpy(wl.block_tables).to(device),
+                             torch.from_numpy(wl.context_lens).to(device),
+                             int(wl.chunk_lens.max()), wl.scale, key_scales=ks,
+                             value_scales=vs)
+
+
+def scale_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int32).numpy()
+
+
+def oracle_pools_i8(wl):
+    kc, vc = o_cache.empty_pools(wl.pool_blocks, wl.Hkv, wl.BS, wl.D, "int8", 0x7F)
+    ks, vs = o_cache.empty_scale_pools(wl.pool_blocks, wl.Hkv, wl.BS, NAN_F32)
+    return kc, vc, ks, vs
+
+
+def oracle_decode_setup_i8(wl: DecodeWorkload, seqs=None):
+    kc, vc, ks, vs = oracle_pools_i8(wl)
+    seqs = range(wl.B) if seqs is None else seqs
+    for b in seqs:
+        n = wl.cached_k[b].shape[0]
+        slots = [o_cache.slot_of(wl.block_tables[b], _oracle_row(wl, wl.cached_pos0[b] + t), wl.BS)
+                 for t in range(n)]
+        o_cache.reshape_and_cache(wl.cached_k[b], wl.cached_v[b], kc, vc, np.array(slots, np.int64),
+                                  wl.act, "int8", ks, vs)
+    for b in seqs:
+        s = o_cache.slot_of(wl.block_tables[b], _oracle_row(wl, wl.new_pos[b]), wl.BS)
+        o_cache.reshape_and_cache(wl.new_k[b:b + 1], wl.new_v[b:b + 1], kc, vc, np.array([s]),
+                                  wl.act, "int8", ks, vs)
+    return kc, vc, ks, vs
+
+
+def oracle_decode_i8(wl: DecodeWorkload, pools, seqs=None):
+    kc, vc, ks, vs = pools
+    seqs = list(range(wl.B)) if seqs is None else list(seqs)
+    return o_attn.decode(wl.query[seqs], wl.act, kc, vc, "int8", wl.block_tables[seqs],
+                         wl.context_lens[seqs], wl.scale, ks, vs, wl.window)
+
+
+def oracle_prefill_setup_i8(wl: PrefillWorkload):
+    kc, vc, ks, vs = oracle_pools_i8(wl)
+    slots = [o_cache.slot_of(wl.block_tables[0], t, wl.BS) for t in range(wl.prefix_len)]
+    o_cache.reshape_and_cache(wl.prefix_k, wl.prefix_v, kc, vc, np.array(slots, np.int64),
+                              wl.act, "int8", ks, vs)
+    for b in range(wl.B):
+        C = int(wl.chunk_lens[b])
+        slots = [o_cache.slot_of(wl.block_tables[b], wl.prefix_len + t, wl.BS) for t in range(C)]
+        o_cache.reshape_and_cache(wl.chunk_k[b], wl.chunk_v[b], kc, vc, np.array(slots, np.int64),
+                                  wl.act, "int8", ks, vs)
+    return kc, vc, ks, vs
+
+
+def oracle_prefill_i8(wl: PrefillWorkload, pools):
+    kc, vc, ks, vs = pools
+    return o_attn.prefill_chunk(wl.query, wl.act, wl.cu_q_lens, kc, vc, "int8",
+                                wl.block_tables, wl.context_lens, wl.scale, ks, vs)
 
 
 def max_abs(a: np.ndarray, b: np.ndarray) -> float:

@@ -34,7 +34,7 @@ host_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer tests run on
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_the_abi():
