@@ -126,6 +126,28 @@ pa_status pa_reshape_and_cache_i8(const void* key, const void* value, int8_t* ke
                                   void* stream);
 
 /*
+ * pa_copy_blocks -- copy whole cache blocks, for copy-on-write of blocks
+ * shared between sequences (prefix caching: "PagedAttention in mistral.rs",
+ * prefix caching notes; "libmir-metal 0.2.0, src/native/trace/kv.rs", fn
+ * build, copy-on-write page maps).
+ *
+ * block_mapping   [N][2] int32 device pairs (src, dst): block dst receives
+ *                 block src's K pages and V pages of every KV head and, for
+ *                 PA_I8, its key/value row scales.
+ * key_scales,
+ * value_scales    the [NB][Hkv][BS] fp32 scale pools of a PA_I8 cache
+ *                 (ignored, may be NULL, otherwise).
+ * cache_dtype     the pools' element type (PA_F16, PA_BF16, PA_F8E4M3, PA_I8).
+ * Caller contract: entries lie in [0, NB); destinations are distinct and no
+ * destination is also a source in the same call (copy-on-write copies into
+ * fresh blocks).  N == 0 is a no-op; N <= 65535.
+ */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, float* key_scales,
+                         float* value_scales, const int32_t* block_mapping, int32_t N,
+                         int32_t Hkv, int32_t D, int32_t BS, int32_t NB, pa_dtype cache_dtype,
+                         void* stream);
+
+/*
  * pa_decode_workspace_bytes -- bytes of scratch pa_decode needs for this
  * shape.  Same arguments as pa_decode (partition_tokens 0 = automatic).
  * Returns 0 when the call needs no workspace, and (size_t)-1 when the

@@ -180,3 +180,27 @@ def gather_f64(key_cache, value_cache, block_table_row, length: int, fmt: str,
         kv = kv * np.float64(np.float32(k_scale))
         vv = vv * np.float64(np.float32(v_scale))
     return kv, vv
+
+
+def copy_blocks(key_cache, value_cache, block_mapping, k_scales=None, v_scales=None) -> None:
+    """Copy whole blocks (every KV head, K and V, and an int8 cache's row
+    scales) from ``src`` to ``dst`` for each pair of ``block_mapping``
+    ``[N, 2]``, in place.
+
+    This is the block copy that copy-on-write of a shared, partially filled
+    block needs (prefix caching with shared blocks: "PagedAttention in
+    mistral.rs", prefix caching notes; "libmir-metal 0.2.0,
+    src/native/trace/kv.rs", fn build, copy-on-write page maps).  Sources
+    are read before any destination is written.
+    """
+    pairs = [(int(a), int(b)) for a, b in np.asarray(block_mapping).reshape(-1, 2)]
+    src_k = {a: key_cache[a].copy() for a, _ in pairs}
+    src_v = {a: value_cache[a].copy() for a, _ in pairs}
+    src_ks = {a: k_scales[a].copy() for a, _ in pairs} if k_scales is not None else None
+    src_vs = {a: v_scales[a].copy() for a, _ in pairs} if v_scales is not None else None
+    for a, b in pairs:
+        key_cache[b] = src_k[a]
+        value_cache[b] = src_v[a]
+        if src_ks is not None:
+            k_scales[b] = src_ks[a]
+            v_scales[b] = src_vs[a]

@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libpagedkv.so")
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["reshape_and_cache.hip", "paged_decode.hip", "paged_prefill.hip", "pa_api.cpp"]
+SOURCES = ["reshape_and_cache.hip", "copy_blocks.hip", "paged_decode.hip", "paged_prefill.hip",
+           "pa_api.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -34,6 +34,8 @@ SIGNATURES = {
         _f32, _f32, _vp]),
     "pa_reshape_and_cache_i8": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,

@@ -57,7 +57,18 @@ struct PrefillArgs {
   const float* value_scales;
 };
 
+struct CopyBlocksArgs {
+  void* key_cache;
+  void* value_cache;
+  float* key_scales;     // INT8 cache only
+  float* value_scales;
+  const int32_t* block_mapping;  // [N][2] (src, dst)
+  int N, Hkv, D;
+  int cache;  // Fmt code
+};
+
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 
 bool decode_supported(int D, int G, int act, int cache);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

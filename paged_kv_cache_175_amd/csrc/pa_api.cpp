@@ -178,6 +178,35 @@ pa_status pa_reshape_and_cache_i8(const void* key, const void* value, int8_t* ke
                             stream);
 }
 
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, float* key_scales,
+                         float* value_scales, const int32_t* block_mapping, int32_t N,
+                         int32_t Hkv, int32_t D, int32_t BS, int32_t NB, pa_dtype cache_dtype,
+                         void* stream) {
+  if (N < 0) return fail(PA_ERR_INVALID, "N must be >= 0 (got %d)", N);
+  if (Hkv < 1 || D < 1 || NB < 1 || BS < 1)
+    return fail(PA_ERR_INVALID, "Hkv, D, BS and NB must be positive");
+  if (cache_dtype != PA_F16 && cache_dtype != PA_BF16 && cache_dtype != PA_F8E4M3 &&
+      cache_dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "unknown cache dtype");
+  if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
+  if (D % 8 != 0 || D > 512)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8, at most 512");
+  if (N > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+  if (N == 0) return ok();
+  if (!key_cache || !value_cache || !block_mapping)
+    return fail(PA_ERR_INVALID, "null pointer argument");
+  if (cache_dtype == PA_I8 && (!key_scales || !value_scales))
+    return fail(PA_ERR_INVALID, "null scale pool");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key_scales, 16) ||
+      !aligned(value_scales, 16))
+    return fail(PA_ERR_INVALID, "pools and scale pools must be 16-byte aligned");
+  pa::CopyBlocksArgs a{key_cache, value_cache, key_scales, value_scales, block_mapping,
+                       N, Hkv, D, fmt_of(cache_dtype)};
+  hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+  return ok();
+}
+
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t max_context_len, int32_t window,
                                  int32_t partition_tokens) {

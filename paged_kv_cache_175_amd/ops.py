@@ -153,6 +153,25 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
         _stream()))
 
 
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mapping: torch.Tensor,
+                key_scales: Optional[torch.Tensor] = None,
+                value_scales: Optional[torch.Tensor] = None) -> None:
+    """Copy whole blocks ``block_mapping`` ``[N, 2]`` (src, dst) in the pools
+    (and an int8 cache's scale pools): the copies a sequence's
+    copy-on-write queues (:meth:`pool.SequenceBlocks.take_copies`)."""
+    _dev(key_cache, value_cache, block_mapping)
+    _i32(block_mapping)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [N, 2]")
+    NB, Hkv, BS, D = _pool_geometry(key_cache, value_cache)
+    cache = _cache_code(key_cache, torch.bfloat16 if key_cache.dtype != torch.float16
+                        else torch.float16)
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS) or (0, 0)
+    _lib.check(_lib.load().pa_copy_blocks(
+        key_cache.data_ptr(), value_cache.data_ptr(), sc[0], sc[1], block_mapping.data_ptr(),
+        block_mapping.shape[0], Hkv, D, BS, NB, cache, _stream()))
+
+
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: int,
                            window: int = 0, partition_tokens: int = 0) -> int:
     n = _lib.load().pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window,

@@ -9,7 +9,17 @@ What the pages fix ("PagedAttention in mistral.rs"):
 * the pool is allocated up front, which is why an oversized budget shows up
   as an out-of-memory error;
 * an F8E4M3 cache about halves the memory of an FP16 one;
-* prefix caching reuses cached prefix KV across requests.
+* prefix caching reuses cached prefix KV across requests; the libmir-metal
+  trace page ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build) names
+  copy-on-write page maps for the shared pages.
+
+Copy-on-write (a reading: the pages name it without rules): a sequence may
+share another's blocks up to any position, a partially filled last block
+included.  A block is shared while its reference count exceeds one; the
+first sequence that writes a row into a shared block gets a fresh block
+instead, and the block's contents are copied over (the caller runs the
+queued copies, ``pa_copy_blocks``, before the writer).  The other holders
+keep the original block.
 
 "Rolling buffer cache" (llama.cpp discussion 3581, opening post): with a
 window of W tokens the cache is a ring of W rows; position i goes to row
@@ -31,7 +41,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 DEFAULT_BLOCK_SIZE = 32
-CACHE_DTYPES = ("auto", "f8e4m3")
+CACHE_DTYPES = ("auto", "f8e4m3", "i8")
 MIB = 1 << 20
 
 
@@ -66,14 +76,17 @@ class PagedKVConfig:
 
 
 def element_bytes(cache_dtype: str, act_bytes: int = 2) -> int:
-    return 1 if cache_dtype == "f8e4m3" else act_bytes
+    return 1 if cache_dtype in ("f8e4m3", "i8") else act_bytes
 
 
 def bytes_per_block(cfg: PagedKVConfig, num_kv_heads: int, head_dim: int,
                     num_layers: int = 1, act_bytes: int = 2) -> int:
-    """Device bytes of one block across all layers, K and V together."""
-    return (2 * cfg.block_size * num_kv_heads * head_dim
-            * element_bytes(cfg.cache_dtype, act_bytes) * num_layers)
+    """Device bytes of one block across all layers, K and V together (an INT8
+    cache also keeps one fp32 scale per row and head)."""
+    row = head_dim * element_bytes(cfg.cache_dtype, act_bytes)
+    if cfg.cache_dtype == "i8":
+        row += 4
+    return 2 * cfg.block_size * num_kv_heads * row * num_layers
 
 
 def num_blocks(cfg: PagedKVConfig, num_kv_heads: int, head_dim: int, num_layers: int = 1,
@@ -154,6 +167,7 @@ class SequenceBlocks:
         self.window = window
         self.blocks: List[int] = []
         self.num_tokens = 0
+        self.pending_copies: List[tuple] = []   # (src, dst) block copies to run
 
     def _row(self, pos: int) -> int:
         return pos % self.window if self.window else pos
@@ -167,28 +181,56 @@ class SequenceBlocks:
         row = self._row(pos)
         return self.blocks[row // self.bs] * self.bs + row % self.bs
 
+    def _writable(self, j: int) -> None:
+        """Copy-on-write: make logical block j private before a row of it is
+        written (queues the copy of the shared contents)."""
+        blk = self.blocks[j]
+        if self.alloc.refcount(blk) > 1:
+            fresh = self.alloc.allocate()
+            self.pending_copies.append((blk, fresh))
+            self.alloc.release(blk)
+            self.blocks[j] = fresh
+
     def append(self, n: int = 1) -> List[int]:
-        """Reserve the next ``n`` positions; returns their slots."""
+        """Reserve the next ``n`` positions; returns their slots.  Writing
+        into a shared block first gives this sequence its own copy (see
+        :meth:`take_copies`)."""
         out = []
         for _ in range(n):
             pos = self.num_tokens
-            self._ensure_row(self._row(pos))
+            row = self._row(pos)
+            self._ensure_row(row)
+            self._writable(row // self.bs)
             self.num_tokens += 1
             out.append(self.slot(pos))
         return out
 
+    def take_copies(self) -> np.ndarray:
+        """The queued (src, dst) block copies as ``[N, 2]`` int32, cleared.
+        Run them (``ops.copy_blocks``) before writing the reserved slots."""
+        out = np.array(self.pending_copies, dtype=np.int32).reshape(-1, 2)
+        self.pending_copies = []
+        return out
+
     def share_prefix(self, other: "SequenceBlocks", num_tokens: int) -> None:
         """Start this (empty) sequence with ``other``'s first ``num_tokens``
-        positions, sharing whole blocks (``num_tokens`` must be whole blocks)."""
+        positions by sharing the blocks that hold them, a partially filled
+        last block included (it is copied when either side writes to it)."""
         if self.blocks or self.num_tokens:
             raise ValueError("share_prefix needs an empty sequence")
         if self.window or other.window:
             raise ValueError("shared prefixes are for full caches")
-        if num_tokens % self.bs or num_tokens > other.num_tokens:
-            raise ValueError("prefix must be whole, resident blocks")
-        for blk in other.blocks[: num_tokens // self.bs]:
+        if num_tokens > other.num_tokens:
+            raise ValueError("prefix must be resident in the other sequence")
+        for blk in other.blocks[: -(-num_tokens // self.bs)]:
             self.blocks.append(self.alloc.share(blk))
         self.num_tokens = num_tokens
+
+    def fork(self) -> "SequenceBlocks":
+        """A new sequence sharing all of this one's positions."""
+        child = SequenceBlocks(self.alloc, self.bs, self.window)
+        child.share_prefix(self, self.num_tokens)
+        return child
 
     def context_len(self) -> int:
         return self.num_tokens
@@ -225,12 +267,15 @@ def describe(cfg: PagedKVConfig, num_layers: int, cached_tokens: int) -> Dict[st
     """Cache description in the shape of a trace record (dtype, block size,
     page key, prefix cache, counts), as the libmir-metal trace builder reports."""
     return {
-        "dtype": "f8e4m3" if cfg.cache_dtype == "f8e4m3" else "auto",
-        "quant_mode": "per-tensor fp32 scale" if cfg.cache_dtype == "f8e4m3" else "none",
+        "dtype": cfg.cache_dtype,
+        "quant_mode": {"f8e4m3": "per-tensor fp32 scale",
+                       "i8": "per-token/head fp32 scale"}.get(cfg.cache_dtype, "none"),
         "decode_attention": "paged split-context decode (HIP, gfx950)",
         "block_size": cfg.block_size,
         "physical_page_key": "layer + sequence; head-major pages"
-        + ("; rolling ring" if cfg.window else ""),
+        + ("; rolling ring" if cfg.window else "")
+        + ("; packed INT8 pages and per-token/head fp32 scales" if cfg.cache_dtype == "i8"
+           else ""),
         "paged_attention": True,
         "entry_count": num_layers,
         "cached_tokens": cached_tokens,
