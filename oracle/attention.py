@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .cache import bits_to_f64, gather_f64
+from .cache import bits_to_f64, gather_f64, get_row, pool_geometry, slot_of
 
 
 def softmax_attend(q, k, v, scale: float):
@@ -102,6 +102,54 @@ def prefill_chunk(query_bits, act_fmt: str, cu_q_lens, key_cache, value_cache,
                 g = h // group
                 out[q0 + j, h] = softmax_attend(q[q0 + j, h], k[: i + 1, g, :],
                                                 v[: i + 1, g, :], scale)
+    return out
+
+
+def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_lens,
+                         key_cache, value_cache, cache_fmt: str, block_tables, context_lens,
+                         scale: float, window: int):
+    """Chunked prefill of a sliding-window layer whose cache is a ring of
+    ``window`` rows ("Rolling buffer cache", opening post: position i lives
+    in ring row i mod W).
+
+    Reading (the pages only say the ring exists and that a token attends to
+    the last W positions): the chunk has not been written into the ring
+    yet, because its later tokens would overwrite ring rows that its earlier
+    queries still need.  Query j of sequence b sits at position
+    ``i = ctx - C + j`` and attends to positions ``max(0, i - W + 1) .. i``:
+    those before the chunk (``< ctx - C``) from the ring, the chunk's own
+    from ``key_bits`` / ``value_bits`` (``[total_q, Hkv, D]``, packed like
+    the queries).
+    """
+    q = bits_to_f64(query_bits, act_fmt)
+    kn = bits_to_f64(key_bits, act_fmt)
+    vn = bits_to_f64(value_bits, act_fmt)
+    total, Hq, D = q.shape
+    group = Hq // key_cache.shape[1]
+    bs = pool_geometry(key_cache)[2]
+    out = np.zeros((total, Hq, D), dtype=np.float64)
+    for b in range(len(cu_q_lens) - 1):
+        q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        C = q1 - q0
+        ctx = int(context_lens[b])
+        start = ctx - C                      # first position of the chunk
+        for j in range(C):
+            i = start + j
+            ks, vs = [], []
+            for pos in range(max(0, i - window + 1), i + 1):
+                if pos < start:
+                    slot = slot_of(block_tables[b], pos % window, bs)
+                    k_row, v_row = get_row(key_cache, value_cache, slot // bs, slot % bs)
+                    ks.append(bits_to_f64(k_row, cache_fmt))
+                    vs.append(bits_to_f64(v_row, cache_fmt))
+                else:
+                    ks.append(kn[q0 + pos - start])
+                    vs.append(vn[q0 + pos - start])
+            k = np.stack(ks)
+            v = np.stack(vs)
+            for h in range(Hq):
+                out[q0 + j, h] = softmax_attend(q[q0 + j, h], k[:, h // group, :],
+                                                v[:, h // group, :], scale)
     return out
 
 
