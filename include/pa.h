@@ -270,6 +270,38 @@ pa_status pa_prefill_chunk_i8(void* out, const void* query, const int32_t* cu_q_
                               int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
                               pa_dtype act_dtype, void* stream);
 
+/*
+ * pa_prefill_chunk_window -- chunked prefill of a sliding-window layer whose
+ * cache is a rolling buffer ("Rolling buffer cache", llama.cpp discussion
+ * 3581, opening post): a ring of `window` rows, position i in ring row
+ * i mod window, reached through block_tables[b][0 .. window/BS - 1].
+ *
+ * key, value      [total_q][Hkv][D] act_dtype, the chunk's own K and V,
+ *                 packed like the queries, 16-byte aligned.
+ * key_cache, value_cache  the ring pools in act_dtype (16-bit caches only).
+ * context_lens    [B] int32: positions of sequence b, chunk included.  The
+ *                 ring holds the positions before the chunk,
+ *                 max(0, ctx - C_b - window) .. ctx - C_b - 1, and not yet
+ *                 the chunk itself: write it after this call (only its last
+ *                 min(C_b, window) tokens land; earlier ones would be
+ *                 overwritten within the chunk).
+ * Query j of sequence b sits at position i = context_lens[b] - C_b + j and
+ * attends to positions max(0, i - window + 1) .. i: those before the chunk
+ * from the ring, the chunk's own from key / value.
+ * Other arguments as pa_prefill_chunk (cache dtype = act_dtype).
+ * Errors: PA_ERR_INVALID for window <= 0, not a multiple of 32, or needing
+ * more than MBPS table entries; otherwise as pa_prefill_chunk.
+ * Caller contract: C_b <= context_lens[b]; ring table entries that hold
+ * positions of that range lie in [0, NB).
+ */
+pa_status pa_prefill_chunk_window(void* out, const void* query, const void* key,
+                                  const void* value, const int32_t* cu_q_lens,
+                                  const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                                  int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                                  pa_dtype act_dtype, int32_t window, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

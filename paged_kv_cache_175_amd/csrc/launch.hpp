@@ -55,6 +55,11 @@ struct PrefillArgs {
   float softmax_scale, k_scale, v_scale;
   const float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32
   const float* value_scales;
+  // Sliding-window layer: window > 0, the cache is a ring of `window` rows
+  // and key_act / value_act [total_q][Hkv][D] hold the chunk's own K/V.
+  const void* key_act;
+  const void* value_act;
+  int window;
 };
 
 struct CopyBlocksArgs {

@@ -374,7 +374,9 @@ pa_status prefill_common(void* out, const void* query, const int32_t* cu_q_lens,
                          const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                          int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_t MBPS,
                          int32_t max_chunk_len, float softmax_scale, pa_dtype act_dtype,
-                         pa_dtype cache_dtype, float k_scale, float v_scale, void* stream) {
+                         pa_dtype cache_dtype, float k_scale, float v_scale, void* stream,
+                         const void* key_act = nullptr, const void* value_act = nullptr,
+                         int32_t window = 0) {
   if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || MBPS < 1 || max_chunk_len < 0)
     return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_chunk_len out of range");
   if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
@@ -397,6 +399,11 @@ pa_status prefill_common(void* out, const void* query, const int32_t* cu_q_lens,
     return fail(PA_ERR_INVALID, "caches must be 16-byte aligned");
   if (!aligned(key_scales, 4) || !aligned(value_scales, 4))
     return fail(PA_ERR_INVALID, "scale pools must be 4-byte aligned");
+  if (window > 0) {
+    if (!key_act || !value_act) return fail(PA_ERR_INVALID, "null chunk key/value");
+    if (!aligned(key_act, 16) || !aligned(value_act, 16))
+      return fail(PA_ERR_INVALID, "chunk key/value must be 16-byte aligned");
+  }
   // Query rows (position, head) of one sequence and the flat grid must fit in int32.
   if ((long long)max_chunk_len * Hq * B > 0x7fffff00LL)
     return fail(PA_ERR_UNSUPPORTED, "max_chunk_len * Hq * B too large");
@@ -421,6 +428,9 @@ pa_status prefill_common(void* out, const void* query, const int32_t* cu_q_lens,
   a.v_scale = v_scale;
   a.key_scales = key_scales;
   a.value_scales = value_scales;
+  a.key_act = key_act;
+  a.value_act = value_act;
+  a.window = window;
   hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
@@ -454,6 +464,24 @@ pa_status pa_prefill_chunk_i8(void* out, const void* query, const int32_t* cu_q_
   return prefill_common(out, query, cu_q_lens, key_cache, value_cache, key_scales,
                         value_scales, block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS,
                         max_chunk_len, softmax_scale, act_dtype, PA_I8, 1.f, 1.f, stream);
+}
+
+pa_status pa_prefill_chunk_window(void* out, const void* query, const void* key,
+                                  const void* value, const int32_t* cu_q_lens,
+                                  const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                                  int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
+                                  pa_dtype act_dtype, int32_t window, void* stream) {
+  if (window <= 0 || window % kBlock != 0)
+    return fail(PA_ERR_INVALID, "window must be a positive multiple of 32 (got %d)", window);
+  if (MBPS < 1 || window / kBlock > MBPS)
+    return fail(PA_ERR_INVALID, "the ring of %d rows needs %d table entries (MBPS %d)", window,
+                window / kBlock, MBPS);
+  return prefill_common(out, query, cu_q_lens, key_cache, value_cache, nullptr, nullptr,
+                        block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS, max_chunk_len,
+                        softmax_scale, act_dtype, act_dtype, 1.f, 1.f, stream, key, value,
+                        window);
 }
 
 }  // extern "C"

@@ -54,6 +54,13 @@
 // and on that page the V operand is zeroed there, so no Inf or NaN reaches
 // the accumulators through a zero probability.
 //
+// Sliding-window layers (WIN): the cache is a ring of W rows, position i in
+// row i mod W ("Rolling buffer cache", opening post), and the chunk has not
+// been written into it yet, since its later tokens would overwrite rows its
+// earlier queries still need.  Query i attends to positions i - W + 1 .. i:
+// those before the chunk come from the ring pages, the chunk's own from its
+// K/V activations, staged into the same LDS layout (16-bit caches).
+//
 // Workgroup order: workgroups are dispatched to the 8 XCDs round-robin, so
 // the flat workgroup id is remapped to give each XCD a contiguous range of
 // (KV head, sequence, row tile) items.  The workgroups that read one KV
@@ -119,18 +126,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int CF, int AF, int NQ>
+template <int D, int CF, int AF, int NQ, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const int32_t* __restrict__ cu_q_lens, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int B, int MBPS,
     int row_tiles, float qk_scale_log2, float v_scale, const float* __restrict__ key_scales,
-    const float* __restrict__ value_scales) {
+    const float* __restrict__ value_scales, const uint16_t* __restrict__ key_act,
+    const uint16_t* __restrict__ value_act, int window) {
   constexpr int KS = D / 32;              // k-steps of S^T (32 head dims each)
   constexpr int NT = D / 16;              // 16-dim tiles of O^T
   constexpr int PAGE = BS * D;            // elements of one K (or V) page
-  constexpr bool kDma = !byte_fmt(CF);
+  static_assert(!WIN || CF == AF, "the window path reads 16-bit caches");
+  constexpr bool kDma = !byte_fmt(CF) && !WIN;
   constexpr bool kI8 = CF == FMT_I8;
   constexpr int NBUF = kDma ? 3 : 2;
   constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
@@ -164,7 +173,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int ctx = context_lens[b];
   const int first_pos = ctx - C;               // absolute position of query 0
   const int last_row_wg = min(rows, x * RW + RW) - 1;
-  const int npages = (first_pos + last_row_wg / G) / BS + 1;
+  // Key pages [p_lo, p_lo + npages): from the earliest key any row of the
+  // workgroup sees (0, or the start of its earliest query's window) to its
+  // latest query.
+  const int p_lo = WIN ? max(0, first_pos + (x * RW) / G - window + 1) / BS : 0;
+  const int npages = (first_pos + last_row_wg / G) / BS + 1 - p_lo;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -201,7 +214,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x4 o_acc[NT + 1][NQ];
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
-    m_run[t] = -INFINITY;
+    // A window row can meet pages that lie wholly below its window before
+    // its first live key: a finite floor keeps exp2(s - m) at 0 there.
+    m_run[t] = WIN ? -1.0e30f : -INFINITY;
 #pragma unroll
     for (int n = 0; n <= NT; ++n) o_acc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -217,7 +232,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // --- page staging ------------------------------------------------------
   const int32_t* bt = block_tables + (size_t)b * MBPS;
-  int bt_reg = lane < npages ? bt[lane] : 0;   // physical blocks of pages 0..63
+  // Physical blocks of pages 0..63 (the window path indexes its ring itself).
+  int bt_reg = !WIN && lane < npages ? bt[lane] : 0;
   const size_t head_off = (size_t)g * PAGE;
   const size_t blk_stride = (size_t)Hkv * PAGE;
   auto phys_of = [&](int q) {
@@ -299,7 +315,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  if constexpr (kDma) {
+  // Window path: item (r, c) = row r, head-dimension chunk c of a page.  A
+  // row before the chunk comes from the ring (its ring page holds rows
+  // pos mod W; the ring has every position from max(0, start - W) on); a
+  // row of the chunk from the activations; any other row is zero (never
+  // visible to a query).
+  constexpr int NIT = (BS * (D / 8) + kThreads - 1) / kThreads;
+  u32x4 wk[WIN ? NIT : 1], wv[WIN ? NIT : 1];
+  const uint16_t* kc16 = reinterpret_cast<const uint16_t*>(key_cache);
+  const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
+  auto load_win = [&](int base) {
+    const int ring_lo = max(0, first_pos - window);
+    const int phys = base < first_pos ? bt[(base % window) / BS] : 0;
+    const size_t page = (size_t)phys * blk_stride + head_off;
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int item = tid + i * kThreads;
+      u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
+      if (item < BS * (D / 8)) {
+        const int r = item & (BS - 1);
+        const int c = item / BS;
+        const int pos = base + r;
+        if (pos >= ring_lo && pos < first_pos) {
+          kw = *reinterpret_cast<const u32x4*>(kc16 + page + (size_t)(c * BS + r) * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vw[e] = (uint32_t)vc16[page + (size_t)(8 * c + 2 * e) * BS + r] |
+                    ((uint32_t)vc16[page + (size_t)(8 * c + 2 * e + 1) * BS + r] << 16);
+        } else if (pos >= first_pos && pos < ctx) {
+          const size_t row = ((size_t)(q_begin + pos - first_pos) * Hkv + g) * D + 8 * c;
+          kw = *reinterpret_cast<const u32x4*>(key_act + row);
+          vw = *reinterpret_cast<const u32x4*>(value_act + row);
+        }
+      }
+      wk[i] = kw;
+      wv[i] = vw;
+    }
+  };
+  auto store_win = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int item = tid + i * kThreads;
+      if (item < BS * (D / 8)) {
+        const int r = item & (BS - 1);
+        const int c = item / BS;
+        *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c, r) * 8]) = wk[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * c + e;
+          v_lds[buf][v_slot(d, r >> 3) * 8 + (r & 7)] =
+              static_cast<uint16_t>(wv[i][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  };
+
+  if constexpr (WIN) {
+    load_win(p_lo * BS);
+    store_win(0);
+    __syncthreads();
+  } else if constexpr (kDma) {
     dma_page(phys_of(0), 0);
     if (npages > 1) {
       dma_page(phys_of(1), 1);
@@ -316,14 +391,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   int cur = 0;
   for (int p = 0; p < npages; ++p) {
-    const int base = p * BS;
-    if constexpr (kDma) {
+    const int base = (p_lo + p) * BS;
+    if constexpr (WIN) {
+      if (p + 1 < npages) load_win(base + BS);
+    } else if constexpr (kDma) {
       if (p + 2 < npages) dma_page(phys_of(p + 2), cur == 0 ? 2 : cur - 1);
     } else {
       if (p + 1 < npages) load_regs(phys_of(p + 1));
     }
 
-    if (wave_live && base <= pos_hi) {
+    // A wave computes a page if some key of it lies in some row's window.
+    const bool in_window = !WIN || base + BS - 1 >= pos_lo - window + 1;
+    if (wave_live && base <= pos_hi && in_window) {
       auto page = [&](auto masked) {
       const uint16_t* kb = k_lds[cur];
       const uint16_t* vb = v_lds[cur];
@@ -369,8 +448,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (base + 8 * q4 + 4 * kt + r > qpos[t]) s_acc[kt][t][r] = -INFINITY;
+              for (int r = 0; r < 4; ++r) {
+                const int kp = base + 8 * q4 + 4 * kt + r;
+                if (kp > qpos[t] || (WIN && kp <= qpos[t] - window)) s_acc[kt][t][r] = -INFINITY;
+              }
         }
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
@@ -434,7 +515,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
       };
-      if (base + BS - 1 > pos_lo) {
+      // Masked where the page reaches past the earliest query, or (window)
+      // below the window of the latest one.
+      if (base + BS - 1 > pos_lo || (WIN && base <= pos_hi - window)) {
         page(std::true_type{});
       } else {
         page(std::false_type{});
@@ -452,7 +535,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       lds_barrier();
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     } else {
-      if (p + 1 < npages) store_regs(cur ^ 1, base + BS);
+      if constexpr (WIN) {
+        if (p + 1 < npages) store_win(cur ^ 1);
+      } else {
+        if (p + 1 < npages) store_regs(cur ^ 1, base + BS);
+      }
       __syncthreads();
       cur ^= 1;
     }
@@ -477,17 +564,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Query tiles of 16 rows per wave: as many as fit in 256 VGPRs at two waves
-// per SIMD (INT8 keeps its row scales and a second P operand live too).
-template <int D, int CF>
+// per SIMD (INT8 keeps its row scales and a second P operand live too, the
+// window path its staged activation rows).
+template <int D, int CF, bool WIN>
 constexpr int query_tiles() {
   if (D <= 64) return 4;
-  if (D <= 96) return CF == FMT_I8 ? 3 : 4;
+  if (D <= 96) return CF == FMT_I8 || WIN ? 3 : 4;
   return 2;
 }
 
-template <int D, int CF, int AF>
+template <int D, int CF, int AF, bool WIN>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-  constexpr int NQ = query_tiles<D, CF>();
+  constexpr int NQ = query_tiles<D, CF, WIN>();
   constexpr int RW = 16 * NQ * kWaves;
   const int G = a.Hq / a.Hkv;
   const long long row_tiles = ((long long)a.max_chunk * G + RW - 1) / RW;
@@ -496,24 +584,30 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   if (per_xcd * kXcds > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float qk = a.softmax_scale * (CF == FMT_E4M3 ? a.k_scale : 1.f) * LOG2E_P;
   const float vs = CF == FMT_E4M3 ? a.v_scale : 1.f;
-  hipLaunchKernelGGL((prefill_kernel<D, CF, AF, NQ>), dim3((unsigned)(per_xcd * kXcds)),
+  hipLaunchKernelGGL((prefill_kernel<D, CF, AF, NQ, WIN>), dim3((unsigned)(per_xcd * kXcds)),
                      dim3(kThreads), 0, s, (uint16_t*)a.out, (const uint16_t*)a.query,
                      a.cu_q_lens, (const uint8_t*)a.key_cache, (const uint8_t*)a.value_cache,
                      a.block_tables, a.context_lens, a.Hq, a.Hkv, G, a.B, a.MBPS,
-                     (int)row_tiles, qk, vs, a.key_scales, a.value_scales);
+                     (int)row_tiles, qk, vs, a.key_scales, a.value_scales,
+                     (const uint16_t*)a.key_act, (const uint16_t*)a.value_act, a.window);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+  if (a.window > 0) {
+    if (a.act == FMT_BF16 && a.cache == FMT_BF16) return launch_t<D, FMT_BF16, FMT_BF16, true>(a, s);
+    if (a.act == FMT_F16 && a.cache == FMT_F16) return launch_t<D, FMT_F16, FMT_F16, true>(a, s);
+    return hipErrorInvalidValue;
+  }
   if (a.act == FMT_BF16) {
-    if (a.cache == FMT_BF16) return launch_t<D, FMT_BF16, FMT_BF16>(a, s);
-    if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_BF16>(a, s);
-    if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_BF16>(a, s);
+    if (a.cache == FMT_BF16) return launch_t<D, FMT_BF16, FMT_BF16, false>(a, s);
+    if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_BF16, false>(a, s);
+    if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_BF16, false>(a, s);
   } else if (a.act == FMT_F16) {
-    if (a.cache == FMT_F16) return launch_t<D, FMT_F16, FMT_F16>(a, s);
-    if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_F16>(a, s);
-    if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_F16>(a, s);
+    if (a.cache == FMT_F16) return launch_t<D, FMT_F16, FMT_F16, false>(a, s);
+    if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_F16, false>(a, s);
+    if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_F16, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

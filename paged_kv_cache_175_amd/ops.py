@@ -297,6 +297,42 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
     return out
 
 
+def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                         cu_q_lens: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, max_chunk_len: int, softmax_scale: float,
+                         window: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked prefill of a sliding-window layer over its ring
+    (``pa_prefill_chunk_window``); ``key`` / ``value`` ``[total_q, Hkv, D]``
+    are the chunk's own K/V, written into the ring only after this call."""
+    _dev(query, key, value, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
+    _i32(cu_q_lens, block_tables, context_lens)
+    total_q, Hq, D = query.shape
+    NB, Hkv, BS, Dc = _pool_geometry(key_cache, value_cache)
+    B = context_lens.numel()
+    if Dc != D:
+        raise ValueError("cache shapes do not match the query")
+    if key.shape != (total_q, Hkv, D) or value.shape != (total_q, Hkv, D):
+        raise ValueError("key / value must both be [total_q, Hkv, D]")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise TypeError("key / value must have the activation dtype")
+    if cu_q_lens.numel() != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_q_lens must be [B+1] and block_tables [B, MBPS]")
+    act = _act_code(query)
+    if _cache_code(key_cache, query.dtype) != act:
+        raise TypeError("the window path reads a cache in the activation dtype")
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    _lib.check(_lib.load().pa_prefill_chunk_window(
+        out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
+        cu_q_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS,
+        block_tables.shape[1], int(max_chunk_len), float(softmax_scale), act, int(window),
+        _stream()))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Prepared calls: all marshalling done once, so that a tight loop (or a HIP
 # graph capture) pays only the ctypes call.  The returned callables launch on

@@ -194,7 +194,10 @@ class SequenceBlocks:
     def append(self, n: int = 1) -> List[int]:
         """Reserve the next ``n`` positions; returns their slots.  Writing
         into a shared block first gives this sequence its own copy (see
-        :meth:`take_copies`)."""
+        :meth:`take_copies`).  Rolling buffer: a position that a later one
+        of the same call overwrites gets slot -1 (the writer skips it), so
+        no two tokens of one write share a ring row."""
+        end = self.num_tokens + n
         out = []
         for _ in range(n):
             pos = self.num_tokens
@@ -202,7 +205,8 @@ class SequenceBlocks:
             self._ensure_row(row)
             self._writable(row // self.bs)
             self.num_tokens += 1
-            out.append(self.slot(pos))
+            lands = not self.window or pos >= end - self.window
+            out.append(self.slot(pos) if lands else -1)
         return out
 
     def take_copies(self) -> np.ndarray:

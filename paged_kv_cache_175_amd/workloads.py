@@ -310,6 +310,103 @@ def prefill_workload(name: str, seed: int, B: int, Hq: int, Hkv: int, D: int,
         chunk_v=cv, k_scale=k_scale, v_scale=v_scale, meta={"seed": seed})
 
 
+@dataclass
+class WindowPrefillWorkload:
+    """Chunked prefill of a sliding-window layer whose cache is a ring.
+
+    Sequence b has ``hist_lens[b]`` positions before its chunk; the ring
+    (``window / BS`` blocks, table row b) holds the last ``min(hist, W)`` of
+    them, positions ``hist_pos0[b]`` .. ``hist_lens[b] - 1`` with K/V
+    ``hist_k[b]`` / ``hist_v[b]``.  The chunk's K/V ``chunk_k`` /
+    ``chunk_v`` ``[total_q, Hkv, D]`` are packed like the queries.
+    """
+
+    name: str
+    act: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    BS: int
+    window: int
+    num_blocks: int
+    scale: float
+    hist_lens: np.ndarray      # int32 [B]
+    hist_pos0: np.ndarray      # int32 [B] first position still in the ring
+    chunk_lens: np.ndarray     # int32 [B]
+    cu_q_lens: np.ndarray      # int32 [B+1]
+    context_lens: np.ndarray   # int32 [B] = hist + chunk
+    block_tables: np.ndarray   # int32 [B, window / BS]
+    query: np.ndarray          # uint16 [total_q, Hq, D]
+    chunk_k: np.ndarray        # uint16 [total_q, Hkv, D]
+    chunk_v: np.ndarray
+    hist_k: list               # B x uint16 [hist - hist_pos0, Hkv, D]
+    hist_v: list
+    cache: str = ""
+    meta: dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        self.cache = self.cache or self.act
+
+    @property
+    def pool_blocks(self) -> int:
+        return self.num_blocks
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q_lens[-1])
+
+    def flops(self) -> int:
+        """4*D per (query, visible key) pair per head; query i sees min(i+1, W) keys."""
+        n = 0
+        for b in range(self.B):
+            h, C = int(self.hist_lens[b]), int(self.chunk_lens[b])
+            i = np.arange(h, h + C, dtype=np.int64)
+            n += int(np.minimum(i + 1, self.window).sum())
+        return 4 * self.D * self.Hq * n
+
+
+def window_prefill_workload(name: str, seed: int, B: int, Hq: int, Hkv: int, D: int,
+                            act: str, window: int, hist, chunk,
+                            BS: int = BLOCK_SIZE) -> WindowPrefillWorkload:
+    """Build a sliding-window chunked-prefill workload.
+
+    ``hist`` / ``chunk``: one length for every sequence, a list of B
+    lengths, or a (lo, hi) range to draw from (a tuple).  The B rings take
+    distinct blocks of one shuffled pool.
+    """
+    if window <= 0 or window % BS:
+        raise ValueError("window must be a positive multiple of the block size")
+    rng = np.random.default_rng(seed)
+
+    def lengths(spec):
+        if isinstance(spec, tuple):
+            return rng.integers(spec[0], spec[1] + 1, size=B).astype(np.int64)
+        if np.isscalar(spec):
+            return np.full(B, int(spec), dtype=np.int64)
+        return np.asarray(spec, dtype=np.int64)
+
+    H = lengths(hist)
+    C = lengths(chunk)
+    nblk = window // BS
+    nb = B * nblk
+    bt = rng.permutation(nb).astype(np.int32).reshape(B, nblk)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(C)
+    pos0 = np.maximum(H - window, 0)
+    q = _normal_bits(rng, (int(cu[-1]), Hq, D), act)
+    ck = _normal_bits(rng, (int(cu[-1]), Hkv, D), act)
+    cv = _normal_bits(rng, (int(cu[-1]), Hkv, D), act)
+    hk = [_normal_bits(rng, (int(h - p), Hkv, D), act) for h, p in zip(H, pos0)]
+    hv = [_normal_bits(rng, (int(h - p), Hkv, D), act) for h, p in zip(H, pos0)]
+    return WindowPrefillWorkload(
+        name=name, act=act, B=B, Hq=Hq, Hkv=Hkv, D=D, BS=BS, window=window, num_blocks=nb,
+        scale=float(1.0 / np.sqrt(D)), hist_lens=H.astype(np.int32),
+        hist_pos0=pos0.astype(np.int32), chunk_lens=C.astype(np.int32), cu_q_lens=cu,
+        context_lens=(H + C).astype(np.int32), block_tables=bt, query=q, chunk_k=ck,
+        chunk_v=cv, hist_k=hk, hist_v=hv, meta={"seed": seed})
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.
 

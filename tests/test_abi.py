@@ -166,3 +166,27 @@ def test_prefill_rejects(args, status):
     assert lib.pa_prefill_chunk(a["out"], a["q"], a["cu"], a["kc"], a["vc"], a["bt"], a["cl"],
                                 a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["MBPS"], a["maxc"],
                                 a["scale"], a["act"], a["cache"], 1.0, 1.0, None) == status
+
+
+@needs_lib
+@host_only
+@pytest.mark.parametrize("args,status", [
+    (dict(window=0), _lib.PA_ERR_INVALID),
+    (dict(window=48), _lib.PA_ERR_INVALID),               # not a multiple of 32
+    (dict(window=160), _lib.PA_ERR_INVALID),              # ring needs 5 entries, MBPS 4
+    (dict(key=0), _lib.PA_ERR_INVALID),
+    (dict(value=FAKE + 8), _lib.PA_ERR_INVALID),          # misaligned
+    (dict(act=_lib.PA_F8E4M3), _lib.PA_ERR_UNSUPPORTED),
+    (dict(D=80), _lib.PA_ERR_UNSUPPORTED),
+    (dict(maxc=0, cu=0), _lib.PA_OK),
+])
+def test_prefill_window_rejects(args, status):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, cu=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE,
+             B=2, Hq=4, Hkv=2, D=128, BS=32, MBPS=4, maxc=10, scale=0.1, act=_lib.PA_BF16,
+             window=128)
+    a.update(args)
+    lib = _lib.load()
+    assert lib.pa_prefill_chunk_window(a["out"], a["q"], a["key"], a["value"], a["cu"], a["kc"],
+                                       a["vc"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"],
+                                       a["D"], a["BS"], a["MBPS"], a["maxc"], a["scale"],
+                                       a["act"], a["window"], None) == status
