@@ -39,6 +39,12 @@
  *    (so the key pool is [NB][Hkv][D/8][BS][8] and the value pool
  *    [NB][Hkv][D][BS]).  Both layouts make the attention kernels' matrix-core
  *    operands single 16-byte loads.  Activations are row-major.
+ *  - Identity map ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build:
+ *    identity block maps are served as one contiguous K/V view).  Every
+ *    attention entry point accepts block_tables == NULL: logical block j of
+ *    sequence b is then physical block b*MBPS + j (the pool is a dense
+ *    [B][MBPS] cache, NB >= B*MBPS by caller contract), and no table is
+ *    read.  B*MBPS must fit in int32, else PA_ERR_INVALID.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
  *    stream).  The library never synchronises.
  *  - Errors are returned as pa_status; nothing is thrown and nothing aborts.
@@ -163,7 +169,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * out             [B][Hq][D] act_dtype, written.
  * query           [B][Hq][D] act_dtype.
  * block_tables    [B][MBPS] int32: logical block j of sequence b lives in
- *                 physical block block_tables[b*MBPS + j].
+ *                 physical block block_tables[b*MBPS + j]; NULL for the
+ *                 identity map (b*MBPS + j).
  * context_lens    [B] int32: tokens of sequence b, the decoded token included
  *                 (write it with pa_reshape_and_cache first).
  * window == 0     full cache: rows 0..L-1 with L = context_lens[b].

@@ -252,8 +252,10 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   if (partition_tokens < 0 || partition_tokens % BS != 0)
     return fail(PA_ERR_INVALID, "partition_tokens must be a non-negative multiple of block_size");
   if (B == 0) return ok();
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+  if (!out || !query || !key_cache || !value_cache || !context_lens)
     return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!block_tables && (long long)B * MBPS > 0x7fffffffLL)
+    return fail(PA_ERR_INVALID, "identity map: B * MBPS must fit in int32");
   if (cache_dtype == PA_I8 && (!key_scales || !value_scales))
     return fail(PA_ERR_INVALID, "null scale pool");
   if (!aligned(out, 16) || !aligned(query, 16))
@@ -389,8 +391,10 @@ pa_status prefill_common(void* out, const void* query, const int32_t* cu_q_lens,
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
     return fail(PA_ERR_INVALID, "E4M3 scales must be finite and > 0");
   if (B == 0 || max_chunk_len == 0) return ok();
-  if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !block_tables || !context_lens)
+  if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !context_lens)
     return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!block_tables && (long long)B * MBPS > 0x7fffffffLL)
+    return fail(PA_ERR_INVALID, "identity map: B * MBPS must fit in int32");
   if (cache_dtype == PA_I8 && (!key_scales || !value_scales))
     return fail(PA_ERR_INVALID, "null scale pool");
   if (!aligned(out, 16) || !aligned(query, 16))

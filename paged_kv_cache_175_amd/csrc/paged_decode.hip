@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       row_new = r_new - pg_new * kPage;
       w_new = (pg_new - pa) % W;
       k_new = (pg_new - pa) / W;
-      const int phys = block_tables[(size_t)b * MBPS + pg_new];
+      const int phys = block_tables ? block_tables[(size_t)b * MBPS + pg_new] : b * MBPS + pg_new;
       const size_t page = ((size_t)phys * Hkv + g) * (size_t)kPage * D;
       const size_t src = ((size_t)b * Hkv + g) * D;
       for (int d = threadIdx.x; d < D; d += 64 * W) {
@@ -239,10 +239,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const vec ones = __builtin_convertvector(f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, vec);
 
     const size_t page_elems = (size_t)kPage * D;
-    const int32_t* bt = block_tables + (size_t)b * MBPS;
     // Physical blocks of this wave's pages, lane k holding its k-th page, so
-    // the page loop never waits on a block-table load.
-    const int bt_lane = bt[pa + wave + W * (lane < npg ? lane : 0)];
+    // the page loop never waits on a block-table load.  Without a table the
+    // map is the identity (block b * MBPS + j) and nothing is loaded.
+    const int lpg = pa + wave + W * (lane < npg ? lane : 0);
+    const int bt_lane = block_tables ? block_tables[(size_t)b * MBPS + lpg] : b * MBPS + lpg;
 
     // Per-lane byte offsets inside a page (loop invariant).  K operand of
     // k-step j, key tile kt: chunk (q4 + 4j), key 2 col + kt; V operand of

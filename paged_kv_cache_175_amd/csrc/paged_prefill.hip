@@ -231,12 +231,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int v_off = v_slot(col, q4) * 8;       // + 16 * 4 * 8 * n (the swizzle ignores d / 16)
 
   // --- page staging ------------------------------------------------------
+  // Without a table the map is the identity: logical block j of sequence b
+  // is physical block b * MBPS + j.
+  const bool ident = block_tables == nullptr;
   const int32_t* bt = block_tables + (size_t)b * MBPS;
   // Physical blocks of pages 0..63 (the window path indexes its ring itself).
-  int bt_reg = !WIN && lane < npages ? bt[lane] : 0;
+  int bt_reg = !WIN && !ident && lane < npages ? bt[lane] : 0;
   const size_t head_off = (size_t)g * PAGE;
   const size_t blk_stride = (size_t)Hkv * PAGE;
   auto phys_of = [&](int q) {
+    if (ident) return b * MBPS + q;
     if ((q & 63) == 0 && q > 0) bt_reg = q + lane < npages ? bt[q + lane] : 0;
     return __builtin_amdgcn_readlane(bt_reg, q & 63);
   };
@@ -326,7 +330,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
   auto load_win = [&](int base) {
     const int ring_lo = max(0, first_pos - window);
-    const int phys = base < first_pos ? bt[(base % window) / BS] : 0;
+    const int ring_blk = (base % window) / BS;
+    const int phys = base >= first_pos ? 0 : ident ? b * MBPS + ring_blk : bt[ring_blk];
     const size_t page = (size_t)phys * blk_stride + head_off;
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {

@@ -61,6 +61,30 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+class IdentityMap:
+    """Stands in for ``block_tables`` when every sequence's blocks are the
+    identity map: logical block j of sequence b is physical block
+    ``b * max_blocks_per_seq + j`` (a dense ``[B][MBPS]`` pool).  The
+    kernels then read no table (the C ABI's NULL ``block_tables``)."""
+
+    def __init__(self, max_blocks_per_seq: int):
+        if max_blocks_per_seq < 1:
+            raise ValueError("max_blocks_per_seq must be positive")
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+
+
+def _table(block_tables, B: int):
+    """(device pointer or 0, MBPS) of a ``[B, MBPS]`` int32 table or an
+    :class:`IdentityMap`."""
+    if isinstance(block_tables, IdentityMap):
+        return 0, block_tables.max_blocks_per_seq
+    _dev(block_tables)
+    _i32(block_tables)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, MBPS]")
+    return block_tables.data_ptr(), block_tables.shape[1]
+
+
 def cache_dtype_name(cache: torch.Tensor) -> str:
     if cache.dtype == torch.uint8:
         return "f8e4m3"
@@ -203,15 +227,15 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     (``pa_decode_append``; not for an int8 cache).  An int8 cache reads its
     scale pools ``key_scales`` / ``value_scales`` (``pa_decode_i8``).
     """
-    _dev(query, key_cache, value_cache, block_tables, context_lens)
-    _i32(block_tables, context_lens)
+    _dev(query, key_cache, value_cache, context_lens)
+    _i32(context_lens)
     B, Hq, D = query.shape
     NB, Hkv, BS, Dc = _pool_geometry(key_cache, value_cache)
     if Dc != D:
         raise ValueError("cache shapes do not match the query")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables must be [B, MBPS] and context_lens [B]")
-    MBPS = block_tables.shape[1]
+    if context_lens.numel() != B:
+        raise ValueError("context_lens must be [B]")
+    bt_ptr, MBPS = _table(block_tables, B)
     act = _act_code(query)
     cache = _cache_code(key_cache, query.dtype)
     if out is None:
@@ -229,11 +253,11 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
             raise ValueError("the fused append is not available for an int8 cache")
         _lib.check(lib.pa_decode_i8(
             out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *sc,
-            block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+            bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
             int(max_context_len), float(softmax_scale), act, int(window),
             int(partition_tokens), ws_ptr, ws_bytes, _stream()))
         return out
-    tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+    tail = (bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
             int(max_context_len), float(softmax_scale), act, cache, float(k_scale),
             float(v_scale), int(window), int(partition_tokens), ws_ptr, ws_bytes, _stream())
     if new_key is None:
@@ -266,16 +290,16 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
     """Causal chunked prefill over the paged cache; returns ``out`` ``[total_q, Hq, D]``.
 
     An int8 cache reads its scale pools (``pa_prefill_chunk_i8``)."""
-    _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
-    _i32(cu_q_lens, block_tables, context_lens)
+    _dev(query, cu_q_lens, key_cache, value_cache, context_lens)
+    _i32(cu_q_lens, context_lens)
     total_q, Hq, D = query.shape
     NB, Hkv, BS, Dc = _pool_geometry(key_cache, value_cache)
     B = context_lens.numel()
     if Dc != D:
         raise ValueError("cache shapes do not match the query")
-    if cu_q_lens.numel() != B + 1 or block_tables.shape[0] != B:
-        raise ValueError("cu_q_lens must be [B+1] and block_tables [B, MBPS]")
-    MBPS = block_tables.shape[1]
+    if cu_q_lens.numel() != B + 1:
+        raise ValueError("cu_q_lens must be [B+1]")
+    bt_ptr, MBPS = _table(block_tables, B)
     act = _act_code(query)
     cache = _cache_code(key_cache, query.dtype)
     if out is None:
@@ -286,12 +310,12 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
     if sc is not None:
         _lib.check(lib.pa_prefill_chunk_i8(
             out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
-            value_cache.data_ptr(), *sc, block_tables.data_ptr(), context_lens.data_ptr(), B,
+            value_cache.data_ptr(), *sc, bt_ptr, context_lens.data_ptr(), B,
             Hq, Hkv, D, BS, MBPS, int(max_chunk_len), float(softmax_scale), act, _stream()))
         return out
     _lib.check(lib.pa_prefill_chunk(
         out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
-        value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv,
+        value_cache.data_ptr(), bt_ptr, context_lens.data_ptr(), B, Hq, Hkv,
         D, BS, MBPS, int(max_chunk_len), float(softmax_scale), act, cache, float(k_scale),
         float(v_scale), _stream()))
     return out
@@ -305,8 +329,8 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     """Chunked prefill of a sliding-window layer over its ring
     (``pa_prefill_chunk_window``); ``key`` / ``value`` ``[total_q, Hkv, D]``
     are the chunk's own K/V, written into the ring only after this call."""
-    _dev(query, key, value, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
-    _i32(cu_q_lens, block_tables, context_lens)
+    _dev(query, key, value, cu_q_lens, key_cache, value_cache, context_lens)
+    _i32(cu_q_lens, context_lens)
     total_q, Hq, D = query.shape
     NB, Hkv, BS, Dc = _pool_geometry(key_cache, value_cache)
     B = context_lens.numel()
@@ -316,8 +340,9 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
         raise ValueError("key / value must both be [total_q, Hkv, D]")
     if key.dtype != query.dtype or value.dtype != query.dtype:
         raise TypeError("key / value must have the activation dtype")
-    if cu_q_lens.numel() != B + 1 or block_tables.shape[0] != B:
-        raise ValueError("cu_q_lens must be [B+1] and block_tables [B, MBPS]")
+    if cu_q_lens.numel() != B + 1:
+        raise ValueError("cu_q_lens must be [B+1]")
+    bt_ptr, MBPS = _table(block_tables, B)
     act = _act_code(query)
     if _cache_code(key_cache, query.dtype) != act:
         raise TypeError("the window path reads a cache in the activation dtype")
@@ -327,8 +352,8 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     _lib.check(_lib.load().pa_prefill_chunk_window(
         out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
         cu_q_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS,
-        block_tables.shape[1], int(max_chunk_len), float(softmax_scale), act, int(window),
+        bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS,
+        MBPS, int(max_chunk_len), float(softmax_scale), act, int(window),
         _stream()))
     return out
 
@@ -369,11 +394,11 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
                    k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
                    partition_tokens: int = 0, new_key=None, new_value=None,
                    key_scales=None, value_scales=None):
-    _dev(query, key_cache, value_cache, block_tables, context_lens, out)
-    _i32(block_tables, context_lens)
+    _dev(query, key_cache, value_cache, context_lens, out)
+    _i32(context_lens)
     B, Hq, D = query.shape
     NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
-    MBPS = block_tables.shape[1]
+    bt_ptr, MBPS = _table(block_tables, B)
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if ws_bytes < need:
@@ -382,7 +407,7 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
     cache = _cache_code(key_cache, query.dtype)
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
     sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
-    tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+    tail = (bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
             int(max_context_len), float(softmax_scale), _act_code(query), cache,
             float(k_scale), float(v_scale), int(window), int(partition_tokens), ws_ptr,
             ws_bytes, _stream())
@@ -390,7 +415,7 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
         if new_key is not None:
             raise ValueError("the fused append is not available for an int8 cache")
         args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-                *sc, block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+                *sc, bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
                 int(max_context_len), float(softmax_scale), _act_code(query), int(window),
                 int(partition_tokens), ws_ptr, ws_bytes, _stream())
         fn = lib.pa_decode_i8
@@ -413,24 +438,24 @@ def prepare_prefill_chunk(query, cu_q_lens, key_cache, value_cache, block_tables
                           max_chunk_len: int, softmax_scale: float, out,
                           k_scale: float = 1.0, v_scale: float = 1.0,
                           key_scales=None, value_scales=None):
-    _dev(query, cu_q_lens, key_cache, value_cache, block_tables, context_lens, out)
-    _i32(cu_q_lens, block_tables, context_lens)
+    _dev(query, cu_q_lens, key_cache, value_cache, context_lens, out)
+    _i32(cu_q_lens, context_lens)
     total_q, Hq, D = query.shape
     NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
     B = context_lens.numel()
-    MBPS = block_tables.shape[1]
+    bt_ptr, MBPS = _table(block_tables, B)
     lib = _lib.load()
     cache = _cache_code(key_cache, query.dtype)
     sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
     if sc is not None:
         args = (out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
-                value_cache.data_ptr(), *sc, block_tables.data_ptr(), context_lens.data_ptr(),
+                value_cache.data_ptr(), *sc, bt_ptr, context_lens.data_ptr(),
                 B, Hq, Hkv, D, BS, MBPS, int(max_chunk_len), float(softmax_scale),
                 _act_code(query), _stream())
         fn = lib.pa_prefill_chunk_i8
     else:
         args = (out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), key_cache.data_ptr(),
-                value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq,
+                value_cache.data_ptr(), bt_ptr, context_lens.data_ptr(), B, Hq,
                 Hkv, D, BS, MBPS, int(max_chunk_len), float(softmax_scale), _act_code(query),
                 cache, float(k_scale), float(v_scale), _stream())
         fn = lib.pa_prefill_chunk

@@ -258,6 +258,30 @@ def block_table_array(seqs: Sequence[SequenceBlocks], max_blocks: Optional[int] 
     return bt
 
 
+def identity_table(B: int, max_blocks: int) -> np.ndarray:
+    """Block tables of a dense pool: sequence b owns physical blocks
+    ``b * max_blocks .. (b + 1) * max_blocks - 1`` in order.  The attention
+    entry points take such a map without a table (``ops.IdentityMap``)."""
+    return (np.arange(B, dtype=np.int64)[:, None] * max_blocks
+            + np.arange(max_blocks, dtype=np.int64)[None, :]).astype(np.int32)
+
+
+def is_identity(block_tables: np.ndarray, context_lens: Optional[np.ndarray] = None,
+                block_size: int = DEFAULT_BLOCK_SIZE) -> bool:
+    """True when every table entry the kernels read is the identity map:
+    the first ``ceil(context_lens[b] / block_size)`` entries of row b (all of
+    them without ``context_lens``) equal ``b * MBPS + j``."""
+    bt = np.asarray(block_tables)
+    ident = identity_table(bt.shape[0], bt.shape[1])
+    if context_lens is None:
+        return bool(np.array_equal(bt, ident))
+    for b, L in enumerate(np.asarray(context_lens)):
+        n = min(-(-int(L) // block_size), bt.shape[1])
+        if not np.array_equal(bt[b, :n], ident[b, :n]):
+            return False
+    return True
+
+
 def slots_from_table(block_table_row: np.ndarray, positions: np.ndarray, block_size: int,
                      window: int = 0) -> np.ndarray:
     """Vectorised slot mapping of absolute positions through one table row."""

@@ -343,6 +343,8 @@ class WindowPrefillWorkload:
     hist_k: list               # B x uint16 [hist - hist_pos0, Hkv, D]
     hist_v: list
     cache: str = ""
+    k_scale: float = 1.0       # 16-bit ring: no quantisation scales
+    v_scale: float = 1.0
     meta: dict = field(default_factory=dict)
 
     def __post_init__(self):
