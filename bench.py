@@ -41,7 +41,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mistral_decode",
                     choices=["mistral_decode", "fp8_decode", "int8_decode", "sliding_decode",
-                             "tiny_decode", "prefix_prefill"])
+                             "tiny_decode", "prefix_prefill", "sliding_prefill"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for 2 GB)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--separate-write", action="store_true",
@@ -50,6 +50,9 @@ def _args():
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
                     help="instead: time a plain device copy of this many GiB (counter scaling)")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="instead: time decode split plans and the identity map over a grid "
+                         "of batch sizes and context lengths (one JSON line per point)")
     return ap.parse_args()
 
 
@@ -101,7 +104,7 @@ def _workload(name):
     return {"mistral_decode": W.mistral_decode, "fp8_decode": W.fp8_decode,
             "int8_decode": W.int8_decode,
             "sliding_decode": W.sliding_decode, "tiny_decode": W.tiny_decode,
-            "prefix_prefill": W.prefix_prefill}[name]()
+            "prefix_prefill": W.prefix_prefill, "sliding_prefill": W.sliding_prefill}[name]()
 
 
 def _act_tensor(bits, act, torch):
@@ -422,6 +425,146 @@ def bench_prefill(wl, a, torch):
     }
 
 
+def bench_window_prefill(wl, a, torch):
+    """One step = window prefill attention of every chunk over its ring, then
+    the ring write of the chunk's landing tokens."""
+    import numpy as np
+    from paged_kv_cache_175_amd import ops, pool
+
+    dev = torch.device("cuda", 0)
+    kshape, vshape = ops.pool_shapes(wl.pool_blocks, wl.Hkv, wl.D, wl.BS)
+    kc = torch.zeros(kshape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros(vshape, dtype=torch.bfloat16, device=dev)
+    hk, hv, hs, cs = [], [], [], []
+    for b in range(wl.B):
+        pos = np.arange(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
+        hs.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+        hk.append(wl.hist_k[b])
+        hv.append(wl.hist_v[b])
+        C, ctx = int(wl.chunk_lens[b]), int(wl.context_lens[b])
+        sl = pool.slots_from_table(wl.block_tables[b], np.arange(ctx - C, ctx), wl.BS,
+                                   wl.window)
+        sl[: max(0, C - wl.window)] = -1       # overwritten within the chunk
+        cs.append(sl)
+    ops.reshape_and_cache(_act_tensor(np.concatenate(hk), wl.act, torch),
+                          _act_tensor(np.concatenate(hv), wl.act, torch), kc, vc,
+                          torch.from_numpy(np.concatenate(hs)).to(dev))
+    q = _act_tensor(wl.query, wl.act, torch)
+    k = _act_tensor(wl.chunk_k, wl.act, torch)
+    v = _act_tensor(wl.chunk_v, wl.act, torch)
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(wl.cu_q_lens).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    slots = torch.from_numpy(np.concatenate(cs)).to(dev)
+    # The step reads the pre-chunk ring; writing the chunk each step would
+    # change what the next step reads, so the write goes to a second copy.
+    kc2, vc2 = kc.clone(), vc.clone()
+    write = ops.prepare_reshape_and_cache(k, v, kc2, vc2, slots)
+
+    def run():
+        ops.prefill_chunk_window(q, k, v, cu, kc, vc, bt, cl, int(wl.chunk_lens.max()),
+                                 wl.scale, wl.window, out=out)
+
+    for _ in range(a.warmup):
+        run()
+        write()
+    torch.cuda.synchronize()
+    K = a.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for _ in range(K):
+        run()
+        write()
+    ev[1].record()
+    torch.cuda.synchronize()
+    step_s = ev[0].elapsed_time(ev[1]) / K * 1e-3
+    ev[2].record()
+    for _ in range(K):
+        run()
+    ev[3].record()
+    torch.cuda.synchronize()
+    pre_s = ev[2].elapsed_time(ev[3]) / K * 1e-3
+    flops = wl.flops()
+    tf = flops / pre_s / 1e12
+    return {
+        "metric": "sliding-window chunked prefill into a ring: attention TFLOP/s, 1 MI355X",
+        "value": round(flops / step_s / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": a.warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "window": wl.window, "history": int(wl.hist_lens[0]),
+                   "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS},
+        "prefill_us": round(pre_s * 1e6, 3), "step_us": round(step_s * 1e6, 3),
+        "tokens_per_s": round(wl.total_q / step_s, 1),
+        "roofline": {"kernel": "pa_prefill_chunk_window", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(wl.name, "prefill_"),
+                     "algorithmic_flops_per_launch": flops},
+    }
+
+
+def dispatch_sweep(a, torch):
+    """Decode launch time of the library's automatic split plan, of one pass
+    without splits, of forced partitions, and of the identity map, over a
+    grid of batch sizes and uniform context lengths (Mistral decode shape,
+    bf16).  Pools are replicated so that each launch reads cold HBM."""
+    import numpy as np
+    from paged_kv_cache_175_amd import ops
+
+    Hq, Hkv, D, BS = 32, 8, 128, 32
+    dev = torch.device("cuda", 0)
+    rows = []
+    for B in (1, 8, 32, 128):
+        for L in (256, 512, 1024, 2048, 4096, 8192, 16384):
+            M = -(-L // BS)
+            NB = B * M
+            per = NB * Hkv * BS * D * 2 * 2
+            R = max(1, min(48, (2 << 30) // per))
+            kshape, vshape = ops.pool_shapes(NB, Hkv, D, BS)
+            pools = [(torch.randn(kshape, device=dev).to(torch.bfloat16),
+                      torch.randn(vshape, device=dev).to(torch.bfloat16)) for _ in range(R)]
+            rng = np.random.default_rng(B * 100000 + L)
+            perm = torch.from_numpy(rng.permutation(NB).astype(np.int32).reshape(B, M)).to(dev)
+            q = torch.randn(B, Hq, D, device=dev).to(torch.bfloat16)
+            cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+            out = torch.empty_like(q)
+            variants = {"auto": (perm, 0), "identity": (ops.IdentityMap(M), 0),
+                        "one_pass": (perm, M * BS)}
+            for p in (256, 512, 1024, 2048):
+                if p < L:
+                    variants[f"part{p}"] = (perm, p)
+            row = {"B": B, "L": L, "replicas": R}
+            for name, (bt, part) in variants.items():
+                ws = ops.alloc_workspace(ops.decode_workspace_bytes(B, Hq, Hkv, D, L, 0, part),
+                                         dev)
+                calls = [ops.prepare_decode(q, kc, vc, bt, cl, L, 1.0 / math.sqrt(D), out, ws,
+                                            partition_tokens=part) for kc, vc in pools]
+                for _ in range(2):
+                    for c in calls:
+                        c()
+                times = []
+                for _ in range(5):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for c in calls:
+                        c()
+                    e1.record()
+                    e1.synchronize()
+                    times.append(e0.elapsed_time(e1) * 1e3 / len(calls))
+                row[name + "_us"] = round(sorted(times)[2], 2)
+            row["auto_GBps"] = round(B * L * Hkv * D * 4 / row["auto_us"] / 1e3, 1)
+            best = min((v, k) for k, v in row.items() if k.endswith("_us"))
+            row["best"] = best[1][:-3]
+            print(json.dumps(row), flush=True)
+            rows.append(row)
+            del pools
+            torch.cuda.empty_cache()
+    return {"dispatch_sweep": "decode split plans and identity map", "points": len(rows)}
+
+
 def calibrate_copy(gib, a, torch):
     n = int(gib * (1 << 30))
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -456,9 +599,14 @@ def main():
     if a.calibrate_copy > 0:
         print(json.dumps(calibrate_copy(a.calibrate_copy, a, torch)))
         return
+    if a.dispatch_sweep:
+        print(json.dumps(dispatch_sweep(a, torch)))
+        return
     wl = _workload(a.config)
     if a.config == "prefix_prefill":
         res = bench_prefill(wl, a, torch)
+    elif a.config == "sliding_prefill":
+        res = bench_window_prefill(wl, a, torch)
     else:
         res, (wl, kv_bytes) = bench_decode(wl, a, torch)
         if a.cpu_seconds > 0:

@@ -183,8 +183,11 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * partition_tokens split size hint, a multiple of BS: > 0 splits every
  *                 sequence into ceil(max_len / partition_tokens) parts whose
  *                 partial results are merged (max_len = max_context_len,
- *                 capped at window); 0 lets the library choose.  Results do
- *                 not depend on it beyond rounding.
+ *                 capped at window); 0 lets the library choose: one pass
+ *                 without workspace below 1024 tokens (max_len), from 1024
+ *                 on enough splits for ~2048 resident waves, at most one
+ *                 split per page of each of the workgroup's waves.  Results
+ *                 do not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0).
  * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV

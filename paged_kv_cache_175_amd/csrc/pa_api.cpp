@@ -55,17 +55,22 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split-context plan.  A workgroup of W waves handles one split of the pages
-// of one (sequence, KV head).  The automatic choice aims at ~2048 resident
-// waves (8 per CU on the 256 CUs of an MI355X): W = 8 while B * Hkv <= 256,
-// else W = 4; S splits per sequence so that B * Hkv * S * W ~ 2048, but with
-// at least two pages per wave on the longest sequence.  A wave holds the
-// block-table entries of its pages in one register, so a split spans at most
-// 64 * W pages.  partition_tokens > 0 forces S = ceil(len / partition_tokens).
+// Split-context plan, a dispatch by context length.  A workgroup of W waves
+// handles one split of the pages of one (sequence, KV head).  Below
+// kMinSplitContext tokens every sequence is one split: one launch, no
+// workspace (a split's merge launch costs more than it saves there).  From
+// kMinSplitContext on, the automatic choice aims at ~2048 resident waves
+// (8 per CU on the 256 CUs of an MI355X): W = 8 while B * Hkv <= 256, else
+// W = 4; S splits per sequence so that B * Hkv * S * W ~ 2048, with at least
+// one page per wave on the longest sequence.  A wave holds the block-table
+// entries of its pages in one register, so a split spans at most 64 * W
+// pages.  partition_tokens > 0 forces S = ceil(len / partition_tokens).
 struct Plan {
   int S;
   int W;
 };
+
+constexpr long long kMinSplitContext = 1024;
 
 bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, Plan* p) {
   long long L = max_len;
@@ -78,9 +83,11 @@ bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, Pl
   long long S;
   if (partition_tokens > 0) {
     S = (L + partition_tokens - 1) / partition_tokens;
+  } else if (L < kMinSplitContext) {
+    S = 1;
   } else {
     S = pairs > 0 ? kTargetWaves / (pairs * W) : 1;
-    S = std::min(S, pages / (2 * W));
+    S = std::min(S, pages / W);
     S = std::max(S, 1LL);
   }
   S = std::max(S, (pages + 64LL * W - 1) / (64LL * W));

@@ -328,16 +328,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   u32x4 wk[WIN ? NIT : 1], wv[WIN ? NIT : 1];
   const uint16_t* kc16 = reinterpret_cast<const uint16_t*>(key_cache);
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
+  // A page wholly before the chunk is all ring rows, every one written
+  // (the ring holds max(0, start - W) .. start - 1, all W rows once
+  // start >= W): it is staged as native page chunks, V included, with no
+  // per-row choice.  Other pages go row by row.
+  bool win_native = false;
   auto load_win = [&](int base) {
     const int ring_lo = max(0, first_pos - window);
     const int ring_blk = (base % window) / BS;
     const int phys = base >= first_pos ? 0 : ident ? b * MBPS + ring_blk : bt[ring_blk];
     const size_t page = (size_t)phys * blk_stride + head_off;
+    win_native = base + BS <= first_pos;
+    if (win_native) {
+#pragma unroll
+      for (int i = 0; i < NIT; ++i) {
+        const int item = tid + i * kThreads;
+        if (item < NCH) {
+          wk[i] = *reinterpret_cast<const u32x4*>(kc16 + page + (size_t)item * 8);
+          wv[i] = *reinterpret_cast<const u32x4*>(vc16 + page + (size_t)item * 8);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {
       const int item = tid + i * kThreads;
       u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
-      if (item < BS * (D / 8)) {
+      if (item < NCH) {
         const int r = item & (BS - 1);
         const int c = item / BS;
         const int pos = base + r;
@@ -357,19 +374,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       wv[i] = vw;
     }
   };
+  // Native: chunk `item` of the K page is (d / 8, t) = (item / 32, item % 32)
+  // and of the V page (d, t / 8) = (item / 4, item % 4).  Row by row: item
+  // (t, d / 8) = (item % 32, item / 32) for both, V transposed here.
   auto store_win = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {
       const int item = tid + i * kThreads;
-      if (item < BS * (D / 8)) {
+      if (item < NCH) {
         const int r = item & (BS - 1);
         const int c = item / BS;
         *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c, r) * 8]) = wk[i];
+        if (win_native) {
+          *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(item >> 2, item & 3) * 8]) = wv[i];
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * c + e;
-          v_lds[buf][v_slot(d, r >> 3) * 8 + (r & 7)] =
-              static_cast<uint16_t>(wv[i][e >> 1] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e) {
+            const int d = 8 * c + e;
+            v_lds[buf][v_slot(d, r >> 3) * 8 + (r & 7)] =
+                static_cast<uint16_t>(wv[i][e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
     }

@@ -444,6 +444,15 @@ def sliding_decode(B: int = 8, window: int = 4096, pos_range=(4096, 32768),
                            act="bf16", window=window, pos_range=pos_range)
 
 
+def sliding_prefill(B: int = 4, window: int = 4096, hist: int = 8192, chunk: int = 2048,
+                    seed: int = 6) -> WindowPrefillWorkload:
+    """Mistral-7B-shaped sliding-window layer (32/8 heads, head_dim 128, bf16,
+    4096-token window): chunks of 2048 tokens after 8192 positions, so the
+    ring is full and every query sees 4096 keys."""
+    return window_prefill_workload("sliding_prefill", seed, B=B, Hq=32, Hkv=8, D=128,
+                                   act="bf16", window=window, hist=hist, chunk=chunk)
+
+
 def prefix_prefill(B: int = 16, prefix_len: int = 2048, chunk: int = 512,
                    seed: int = 4) -> PrefillWorkload:
     """Phi-3-mini-shaped chunked prefill over a shared prefix: 32/32 heads, D=96."""
