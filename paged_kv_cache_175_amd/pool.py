@@ -1,5 +1,6 @@
 """Host-side block manager: pool sizing, block allocation, block tables and
-slot mappings (full cache and rolling buffer), shared prefix blocks.
+slot mappings (full cache and rolling buffer), shared prefix blocks, models
+mixing full and sliding-window layers.
 
 What the pages fix ("PagedAttention in mistral.rs"):
 
@@ -244,6 +245,61 @@ class SequenceBlocks:
             self.alloc.release(blk)
         self.blocks = []
         self.num_tokens = 0
+
+
+class MixedLayerKV:
+    """Block bookkeeping of a model whose layers are full-attention or
+    sliding-window ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build:
+    full-attention layers keep paged K/V, sliding layers a bounded ring, the
+    pages keyed by layer and session).
+
+    ``layer_windows[l]`` is 0 for a full layer, else its window W (a multiple
+    of the block size).  Layers with the same window advance together, so
+    they share one allocator, one table and one slot mapping per sequence
+    (a group); each layer keeps its own K/V pools of its group's block
+    count.  ``blocks`` maps a window to the pool size of its group.
+    """
+
+    def __init__(self, layer_windows: Sequence[int], block_size: int,
+                 blocks: Dict[int, int]):
+        self.layer_windows = [int(w) for w in layer_windows]
+        self.bs = block_size
+        self.windows = sorted(set(self.layer_windows))
+        for w in self.windows:
+            if w < 0 or (w and w % block_size):
+                raise ValueError("windows must be 0 or positive multiples of block_size")
+            if w not in blocks:
+                raise ValueError(f"no pool size for window {w}")
+        self.alloc = {w: BlockAllocator(int(blocks[w])) for w in self.windows}
+        self.seqs: Dict[object, Dict[int, SequenceBlocks]] = {}
+
+    def add(self, seq_id) -> None:
+        if seq_id in self.seqs:
+            raise ValueError(f"sequence {seq_id!r} exists")
+        self.seqs[seq_id] = {w: SequenceBlocks(self.alloc[w], self.bs, w) for w in self.windows}
+
+    def release(self, seq_id) -> None:
+        for s in self.seqs.pop(seq_id).values():
+            s.release()
+
+    def append(self, seq_id, n: int) -> Dict[int, List[int]]:
+        """Reserve the next ``n`` positions in every group; slots per window
+        (a ring's overwritten-within-the-call positions get -1)."""
+        return {w: s.append(n) for w, s in self.seqs[seq_id].items()}
+
+    def num_tokens(self, seq_id) -> int:
+        return self.seqs[seq_id][self.windows[0]].num_tokens
+
+    def max_blocks(self, window: int, max_context: int) -> int:
+        """Table width of a group: the ring's W / BS, or enough for max_context."""
+        return window // self.bs if window else -(-max_context // self.bs)
+
+    def tables(self, seq_ids: Sequence, window: int, max_blocks: int) -> np.ndarray:
+        """``[B, max_blocks]`` int32 tables of one group."""
+        return block_table_array([self.seqs[i][window] for i in seq_ids], max_blocks)
+
+    def context_lens(self, seq_ids: Sequence) -> np.ndarray:
+        return np.array([self.num_tokens(i) for i in seq_ids], dtype=np.int32)
 
 
 def block_table_array(seqs: Sequence[SequenceBlocks], max_blocks: Optional[int] = None,

@@ -79,3 +79,26 @@ def test_full_cache_append_never_skips():
     s = pool.SequenceBlocks(pool.BlockAllocator(8), 4)
     slots = s.append(20)
     assert len(set(slots)) == 20 and min(slots) >= 0
+
+
+def test_mixed_layers_group_slots_by_window():
+    """One group per window: full layers get growing tables, sliding layers
+    rings; layers with the same window share the group."""
+    m = pool.MixedLayerKV([0, 64, 0, 64, 128], 32, {0: 8, 64: 4, 128: 8})
+    m.add("a")
+    m.add("b")
+    s = m.append("a", 100)
+    assert sorted(s) == [0, 64, 128]
+    assert len([x for x in s[0] if x >= 0]) == 100
+    assert [x for x in s[64] if x >= 0] and s[64][:36] == [-1] * 36
+    assert min(s[128]) >= 0                                   # 100 < 128: all land
+    m.append("b", 5)
+    assert m.context_lens(["a", "b"]).tolist() == [100, 5]
+    assert m.tables(["a", "b"], 64, m.max_blocks(64, 0)).shape == (2, 2)
+    assert m.tables(["a", "b"], 0, m.max_blocks(0, 300)).shape == (2, 10)
+    # Ring groups hold exactly W / BS blocks per sequence, at most.
+    assert len(m.seqs["a"][64].blocks) == 2 and len(m.seqs["b"][64].blocks) == 1
+    m.release("a")
+    assert m.alloc[64].num_free == 3 and m.alloc[0].num_free == 7
+    with pytest.raises(ValueError):
+        pool.MixedLayerKV([0, 48], 32, {0: 4, 48: 4})
