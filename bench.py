@@ -286,7 +286,7 @@ def bench_decode(wl, a, torch):
         "other_bytes_per_step": write_bytes + qo_bytes,
         "roofline": {
             "kernel": ("pa_decode" if separate else "pa_decode_append")
-                      + " (decode_split, plus decode_merge when a sequence is split)",
+                      + " (decode_split; split sequences merge inside the launch)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(wl.name, "decode_"),

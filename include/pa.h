@@ -189,7 +189,14 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *                 split per page of each of the workgroup's waves.  Results
  *                 do not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
- *                 (may be NULL when that is 0).
+ *                 (may be NULL when that is 0), kept by the caller across
+ *                 calls: besides the split partials it holds one arrival
+ *                 counter per (sequence, KV head), which must be zero
+ *                 before the workspace is first used (zero-fill it once
+ *                 after allocating it); every call leaves them zero.  Calls
+ *                 that share a workspace must not overlap in time.  The
+ *                 last split of each (sequence, KV head) to finish merges
+ *                 the partials inside the same launch.
  * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV
  * head h / (Hq/Hkv); an empty context gives zeros.  Caller contract: table
  * entries read (logical blocks < ceil(L/BS)) lie in [0, NB);

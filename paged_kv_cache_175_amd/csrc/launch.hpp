@@ -36,6 +36,7 @@ struct DecodeArgs {
   float* ws_m;  // [B*Hq*S]
   float* ws_l;  // [B*Hq*S]
   float* ws_o;  // [B*Hq*S*D]
+  int* ws_count;  // [B*Hkv] split arrival counters, zero between launches
   const void* new_key;    // append mode: [B][Hkv][D] act, or null
   const void* new_value;
   const float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32

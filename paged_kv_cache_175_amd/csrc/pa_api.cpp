@@ -97,10 +97,13 @@ bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, Pl
   return true;
 }
 
-size_t workspace_for(int B, int Hq, int D, const Plan& p) {
+// Workspace of a split plan: m and l [B*Hq*S], o [B*Hq*S*D] fp32, then the
+// split arrival counters [B*Hkv] int32, each region 256-byte aligned.
+size_t workspace_for(int B, int Hq, int Hkv, int D, const Plan& p) {
   if (p.S <= 1) return 0;
   const size_t rows = (size_t)B * Hq * p.S;
-  return 2 * round_up(rows * sizeof(float), kAlign) + round_up(rows * D * sizeof(float), kAlign);
+  return 2 * round_up(rows * sizeof(float), kAlign) + round_up(rows * D * sizeof(float), kAlign) +
+         round_up((size_t)B * Hkv * sizeof(int), kAlign);
 }
 
 }  // namespace
@@ -222,7 +225,7 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
     return (size_t)-1;
   Plan p;
   if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, &p)) return (size_t)-1;
-  return workspace_for(B, Hq, D, p);
+  return workspace_for(B, Hq, Hkv, D, p);
 }
 
 }  // extern "C"
@@ -275,7 +278,7 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   Plan p;
   if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, &p))
     return fail(PA_ERR_INVALID, "bad partition size");
-  const size_t need = workspace_for(B, Hq, D, p);
+  const size_t need = workspace_for(B, Hq, Hkv, D, p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if (need > 0 && !aligned(workspace, kAlign))
@@ -307,6 +310,8 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
     a.ws_m = reinterpret_cast<float*>(w);
     a.ws_l = reinterpret_cast<float*>(w + round_up(rows * sizeof(float), kAlign));
     a.ws_o = reinterpret_cast<float*>(w + 2 * round_up(rows * sizeof(float), kAlign));
+    a.ws_count = reinterpret_cast<int*>(w + 2 * round_up(rows * sizeof(float), kAlign) +
+                                        round_up(rows * D * sizeof(float), kAlign));
   }
   a.new_key = new_key;
   a.new_value = new_value;

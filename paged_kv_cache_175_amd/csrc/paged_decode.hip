@@ -42,7 +42,8 @@
 // The W partial results of a workgroup are combined through LDS.  When a
 // sequence is one split (S == 1, the usual case once B * Hkv workgroups fill
 // the GPU) that is the output; otherwise each split writes (m, l, o) to the
-// workspace and a merge kernel combines the S splits: M = max m_s,
+// workspace and counts itself in, and the last split of the (sequence, KV
+// head) to arrive combines the S partials in the same launch: M = max m_s,
 // w_s = 2^(m_s - M), out = sum w_s o_s / sum w_s l_s.
 
 #include "common.hpp"
@@ -122,6 +123,79 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), mask, 64));
 }
 
+// Split partials cross workgroups, and the workgroups of one (sequence, KV
+// head) may run on different XCDs, whose L2 caches are not coherent with
+// each other.  So the partials are stored and loaded with agent-scope
+// atomics (relaxed): on gfx950 these are stores written through to, and
+// loads served from, the device's point of coherence, with no L2 write-back
+// or invalidate (a release / acquire fence would write back or drop the
+// whole L2).  A workgroup's stores are complete (s_waitcnt vmcnt(0)) before
+// it counts itself in; the last of the S to arrive merges.
+__device__ __forceinline__ void ws_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ws_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the S split partials of one (sequence, query head) with one wave,
+// lanes over the head dimension.  Partials are taken 16 at a time with
+// every load of a group issued before any use, so a group costs one memory
+// round trip; the running max is rescaled between groups.  Empty splits
+// carry m = -inf and weigh nothing.
+constexpr int kMergeGroup = 16;
+
+template <int D, int AF>
+__device__ __forceinline__ void merge_head(uint16_t* __restrict__ dst, int S, float v_scale,
+                                           const float* __restrict__ ws_m,
+                                           const float* __restrict__ ws_l,
+                                           const float* __restrict__ ws_o, size_t row,
+                                           int lane) {
+  constexpr int DPT = (D + 63) / 64;  // dims per lane
+  int dk[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) dk[k] = min(lane + 64 * k, D - 1);
+
+  float M = -INFINITY, den = 0.f, num[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) num[k] = 0.f;
+  for (int p0 = 0; p0 < S; p0 += kMergeGroup) {
+    const int n = min(kMergeGroup, S - p0);
+    float mp[kMergeGroup], lp[kMergeGroup], op[kMergeGroup][DPT];
+#pragma unroll
+    for (int i = 0; i < kMergeGroup; ++i) {
+      const size_t r = row + p0 + min(i, n - 1);
+      mp[i] = ws_load(ws_m + r);
+      lp[i] = ws_load(ws_l + r);
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) op[i][k] = ws_load(ws_o + r * D + dk[k]);
+    }
+    float Mg = M;
+#pragma unroll
+    for (int i = 0; i < kMergeGroup; ++i)
+      if (i < n) Mg = fmaxf(Mg, mp[i]);
+    if (Mg == -INFINITY) continue;  // nothing but empty splits so far
+    const float f = M == -INFINITY ? 0.f : fast_exp2(M - Mg);
+    den *= f;
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) num[k] *= f;
+#pragma unroll
+    for (int i = 0; i < kMergeGroup; ++i) {
+      const float w = (i < n && mp[i] != -INFINITY) ? fast_exp2(mp[i] - Mg) : 0.f;
+      den = fmaf(w, lp[i], den);
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) num[k] = fmaf(w, op[i][k], num[k]);
+    }
+    M = Mg;
+  }
+  const float inv = v_scale / den;
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) dst[d] = static_cast<uint16_t>(f32_to_16<AF>(num[k] * inv));
+  }
+}
+
 template <int D, int G, int CF, int AF, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_split(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
@@ -129,7 +203,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int Hkv, int MBPS, int window, int S, float qk_scale_log2, float v_scale,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-    const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
+    int* __restrict__ ws_count, const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
     float k_enc_scale, float v_enc_scale, const float* __restrict__ key_scales,
     const float* __restrict__ value_scales) {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
@@ -469,77 +543,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       out[((size_t)b * Hq + g * G + h) * D + d] = static_cast<uint16_t>(f32_to_16<AF>(num * (v_scale / den)));
     } else {
       const size_t row = ((size_t)b * Hq + g * G + h) * S + s;
-      ws_o[row * D + d] = num;
+      ws_store(ws_o + row * D + d, num);
       if (d == 0) {
-        ws_m[row] = M;
-        ws_l[row] = den;
+        ws_store(ws_m + row, M);
+        ws_store(ws_l + row, den);
       }
     }
   }
-}
+  if (S == 1) return;
 
-// Merge the S split partials of one (sequence, query head): one wave.
-// Partials are taken 16 at a time with every load of a group issued before
-// any use, so a group costs one memory round trip; the running max is
-// rescaled between groups.  Empty splits carry m = -inf and weigh nothing.
-constexpr int kMergeGroup = 16;
-
-template <int D, int AF>
-__global__ __launch_bounds__(64) void decode_merge(
-    uint16_t* __restrict__ out, const int32_t* __restrict__ context_lens, int Hq, int window,
-    int S, float v_scale, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
-    const float* __restrict__ ws_o) {
-  constexpr int DPT = (D + 63) / 64;  // dims per lane
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  int L = context_lens[b];
-  if (window > 0) L = min(L, window);
-  if (L <= 0) return;  // zeros written by the split kernel
-  const size_t row = ((size_t)b * Hq + h) * S;
-  int dk[DPT];
-#pragma unroll
-  for (int k = 0; k < DPT; ++k) dk[k] = min(lane + 64 * k, D - 1);
-
-  float M = -INFINITY, den = 0.f, num[DPT];
-#pragma unroll
-  for (int k = 0; k < DPT; ++k) num[k] = 0.f;
-  for (int p0 = 0; p0 < S; p0 += kMergeGroup) {
-    const int n = min(kMergeGroup, S - p0);
-    float mp[kMergeGroup], lp[kMergeGroup], op[kMergeGroup][DPT];
-#pragma unroll
-    for (int i = 0; i < kMergeGroup; ++i) {
-      const size_t r = row + p0 + min(i, n - 1);
-      mp[i] = ws_m[r];
-      lp[i] = ws_l[r];
-#pragma unroll
-      for (int k = 0; k < DPT; ++k) op[i][k] = ws_o[r * D + dk[k]];
-    }
-    float Mg = M;
-#pragma unroll
-    for (int i = 0; i < kMergeGroup; ++i)
-      if (i < n) Mg = fmaxf(Mg, mp[i]);
-    if (Mg == -INFINITY) continue;  // nothing but empty splits so far
-    const float f = M == -INFINITY ? 0.f : fast_exp2(M - Mg);
-    den *= f;
-#pragma unroll
-    for (int k = 0; k < DPT; ++k) num[k] *= f;
-#pragma unroll
-    for (int i = 0; i < kMergeGroup; ++i) {
-      const float w = (i < n && mp[i] != -INFINITY) ? fast_exp2(mp[i] - Mg) : 0.f;
-      den = fmaf(w, lp[i], den);
-#pragma unroll
-      for (int k = 0; k < DPT; ++k) num[k] = fmaf(w, op[i][k], num[k]);
-    }
-    M = Mg;
+  // Count this split in; the last of the S merges them.  The counter is
+  // back at zero when the launch ends.
+  __shared__ int last_split;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* cnt = ws_count + (size_t)b * Hkv + g;
+    const int arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_split = arrived == S - 1;
+    if (arrived == S - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const float inv = v_scale / den;
-  uint16_t* dst = out + ((size_t)b * Hq + h) * D;
-#pragma unroll
-  for (int k = 0; k < DPT; ++k) {
-    const int d = lane + 64 * k;
-    if (d < D) dst[d] = static_cast<uint16_t>(f32_to_16<AF>(num[k] * inv));
-  }
+  __syncthreads();
+  if (!last_split) return;
+  for (int h = wave; h < G; h += W)
+    merge_head<D, AF>(out + ((size_t)b * Hq + g * G + h) * D, S, v_scale, ws_m, ws_l, ws_o,
+                      ((size_t)b * Hq + g * G + h) * S, lane);
 }
 
 template <int D, int G, int CF, int AF>
@@ -551,24 +579,19 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_split<D, G, CF, AF, 8>), grid, dim3(512), 0, stream,
                        (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
                        (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
-                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
                        (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
                        a.v_scale, a.key_scales, a.value_scales);
   } else if (a.W == 4) {
     hipLaunchKernelGGL((decode_split<D, G, CF, AF, 4>), grid, dim3(256), 0, stream,
                        (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
                        (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
-                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
                        (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
                        a.v_scale, a.key_scales, a.value_scales);
   } else {
     return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.S <= 1) return e;
-  dim3 grid2(a.Hkv * G, a.B);
-  hipLaunchKernelGGL((decode_merge<D, AF>), grid2, dim3(64), 0, stream, (uint16_t*)a.out,
-                     a.context_lens, a.Hkv * G, a.window, a.S, vs, a.ws_m, a.ws_l, a.ws_o);
   return hipGetLastError();
 }
 

@@ -206,9 +206,11 @@ def decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: i
 
 
 def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """Decode workspace, zero-filled (its split counters must start at zero;
+    every decode leaves them at zero, so it can be reused as it is)."""
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,

@@ -116,14 +116,15 @@ def test_workspace_query():
     lib = _lib.load()
     # Single partition: nothing needed.
     assert lib.pa_decode_workspace_bytes(2, 4, 4, 64, 64, 0, 0) == 0
-    # Forced 32-token partitions over 100 tokens: 4 partitions.
+    # Forced 32-token partitions over 100 tokens: 4 partitions; then one
+    # split counter per (sequence, KV head).
     n = lib.pa_decode_workspace_bytes(2, 8, 2, 128, 100, 0, 32)
     rows = 2 * 8 * 4
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == 2 * rnd(rows * 4) + rnd(rows * 128 * 4)
+    assert n == 2 * rnd(rows * 4) + rnd(rows * 128 * 4) + rnd(2 * 2 * 4)
     # Window caps the length.
     assert lib.pa_decode_workspace_bytes(2, 8, 2, 128, 10000, 64, 32) == \
-        2 * rnd(2 * 8 * 2 * 4) + rnd(2 * 8 * 2 * 128 * 4)
+        2 * rnd(2 * 8 * 2 * 4) + rnd(2 * 8 * 2 * 128 * 4) + rnd(2 * 2 * 4)
     assert lib.pa_decode_workspace_bytes(2, 8, 2, 128, 100, 0, 33) == (1 << 64) - 1
     assert lib.pa_decode_workspace_bytes(-1, 8, 2, 128, 100, 0, 0) == (1 << 64) - 1
 
