@@ -109,13 +109,6 @@ struct Vec4<FMT_F16> {
 __device__ __forceinline__ int k_slot(int dc, int t) { return dc * BS + (t ^ (((t >> 3) & 1) << 2)); }
 __device__ __forceinline__ int v_slot(int d, int tq) { return d * 4 + (tq ^ ((d >> 1) & 3)); }
 
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Workgroup barrier that does not wait for outstanding global loads (a
 // __syncthreads would drain the LDS-direct loads still in flight for later
 // pages).  The empty asm statements keep the compiler from moving memory
