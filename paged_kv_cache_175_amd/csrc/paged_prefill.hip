@@ -444,18 +444,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
 
-      // Scores in log2 units, the causal mask, and P.  Lane element
-      // (kt, r) is key base + 8 * q4 + 4 * kt + r.  The mask is needed only
-      // where the page reaches past the earliest query of the wave; the two
-      // cases are separate instantiations so that the common, unmasked one
-      // sees only products (canonical floats) and its maxima need no NaN
-      // quieting.
+      // The causal mask and P.  Lane element (kt, r) is key
+      // base + 8 * q4 + 4 * kt + r.  The scores stay unscaled: the maxima
+      // are scaled once per lane and the softmax scale (in log2 units) goes
+      // into the exponent's FMA, which saves a multiply per score.  The mask
+      // is needed only where the page reaches past the earliest query of the
+      // wave; the two cases are separate instantiations so that the common,
+      // unmasked one sees only products (canonical floats) and its maxima
+      // need no NaN quieting.
       vec pb[NQ];
       {
-#pragma unroll
-        for (int t = 0; t < NQ; ++t)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) s_acc[kt][t] *= qk_scale_log2;
         if constexpr (kI8) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
@@ -477,7 +475,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
-          const float lmax = fmaxf(fmaxf(fmaxf(s_acc[0][t][0], s_acc[0][t][1]),
+          const float lmax = qk_scale_log2 *
+                             fmaxf(fmaxf(fmaxf(s_acc[0][t][0], s_acc[0][t][1]),
                                          fmaxf(s_acc[0][t][2], s_acc[0][t][3])),
                                    fmaxf(fmaxf(s_acc[1][t][0], s_acc[1][t][1]),
                                          fmaxf(s_acc[1][t][2], s_acc[1][t][3])));
@@ -496,7 +495,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pv[4 * kt + r] = fast_exp2(s_acc[kt][t][r] - m_run[t]);
+            for (int r = 0; r < 4; ++r)
+              pv[4 * kt + r] = fast_exp2(fmaf(s_acc[kt][t][r], qk_scale_log2, -m_run[t]));
           pb[t] = __builtin_convertvector(pv, vec);
           if constexpr (kI8) {
             // l from the unscaled P; the V MFMAs take P times each key's V scale.
@@ -586,13 +586,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Query tiles of 16 rows per wave: as many as fit in 256 VGPRs at two waves
-// per SIMD (INT8 keeps its row scales and a second P operand live too, the
-// window path its staged activation rows).
+// per SIMD (the byte formats keep their widening temporaries live too, INT8
+// its row scales and a second P operand, the window path its staged
+// activation rows).
 template <int D, int CF, bool WIN>
 constexpr int query_tiles() {
   if (D <= 64) return 4;
-  if (D <= 96) return CF == FMT_I8 || WIN ? 3 : 4;
-  return 2;
+  if (D <= 96) return byte_fmt(CF) || WIN ? 3 : 4;
+  return byte_fmt(CF) || WIN ? 2 : 3;
 }
 
 template <int D, int CF, int AF, bool WIN>
