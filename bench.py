@@ -41,7 +41,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mistral_decode",
                     choices=["mistral_decode", "fp8_decode", "int8_decode", "sliding_decode",
-                             "tiny_decode", "prefix_prefill", "sliding_prefill"])
+                             "tiny_decode", "prefix_prefill", "sliding_prefill", "cow_copy"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for 2 GB)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--separate-write", action="store_true",
@@ -61,6 +61,7 @@ def _args():
 _KERNEL_SOURCES = {
     "decode_": ("paged_decode.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
     "prefill_": ("paged_prefill.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
+    "copy_": ("copy_blocks.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
 }
 
 
@@ -104,7 +105,8 @@ def _workload(name):
     return {"mistral_decode": W.mistral_decode, "fp8_decode": W.fp8_decode,
             "int8_decode": W.int8_decode,
             "sliding_decode": W.sliding_decode, "tiny_decode": W.tiny_decode,
-            "prefix_prefill": W.prefix_prefill, "sliding_prefill": W.sliding_prefill}[name]()
+            "prefix_prefill": W.prefix_prefill, "sliding_prefill": W.sliding_prefill,
+            "cow_copy": W.cow_copy}[name]()
 
 
 def _act_tensor(bits, act, torch):
@@ -565,6 +567,70 @@ def dispatch_sweep(a, torch):
     return {"dispatch_sweep": "decode split plans and identity map", "points": len(rows)}
 
 
+def bench_copy_blocks(wl, a, torch):
+    """Copy-on-write block copies (``pa_copy_blocks``): one step = the whole
+    burst of ``N`` copies; HBM-bound, read + write bytes against 8 TB/s."""
+    from paged_kv_cache_175_amd import ops
+
+    dev = torch.device("cuda", 0)
+    kshape, vshape = ops.pool_shapes(wl.num_blocks, wl.Hkv, wl.D, wl.BS)
+    kc = torch.randn(kshape, device=dev).to(torch.bfloat16)
+    vc = torch.randn(vshape, device=dev).to(torch.bfloat16)
+    mapping = torch.from_numpy(wl.mapping).to(dev)
+    for _ in range(a.warmup):
+        ops.copy_blocks(kc, vc, mapping)
+    torch.cuda.synchronize()
+    K = a.steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        ops.copy_blocks(kc, vc, mapping)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / K * 1e-3
+    N = wl.mapping.shape[0]
+    moved = 2 * N * wl.block_bytes()       # every block read once and written once
+    gbs = moved / s / 1e9
+    res = {
+        "metric": "copy-on-write block copies: HBM GB/s (read + write), 1 MI355X",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": a.warmup,
+        "ms_per_step": round(s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "copies": N, "kv_heads": wl.Hkv, "head_dim": wl.D,
+                   "block_size": wl.BS, "block_bytes": wl.block_bytes(),
+                   "pool_blocks": wl.num_blocks},
+        "copy_us": round(s * 1e6, 3),
+        "roofline": {"kernel": "pa_copy_blocks (copy_blocks_kernel)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(wl.name, "copy_"),
+                     "algorithmic_bytes_per_launch": moved},
+    }
+    if a.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_copy(wl, moved, a.cpu_seconds)
+    return res
+
+
+def cpu_baseline_copy(wl, moved, seconds):
+    """The oracle's block copy on a pool of the same geometry, single thread."""
+    import numpy as np
+    from oracle import cache as o_cache
+
+    kc, vc = o_cache.empty_pools(wl.num_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, 0)
+    reps, t = 0, 0.0
+    while reps == 0 or t < seconds:
+        t0 = time.perf_counter()
+        o_cache.copy_blocks(kc, vc, wl.mapping)
+        t += time.perf_counter() - t0
+        reps += 1
+    per = t / reps
+    return {"value": round(moved / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full burst ({wl.mapping.shape[0]} block copies), {reps} repetitions "
+                      f"in {t:.1f} s, single thread",
+            "cpu_model": _cpu_info(), "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def calibrate_copy(gib, a, torch):
     n = int(gib * (1 << 30))
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -607,6 +673,8 @@ def main():
         res = bench_prefill(wl, a, torch)
     elif a.config == "sliding_prefill":
         res = bench_window_prefill(wl, a, torch)
+    elif a.config == "cow_copy":
+        res = bench_copy_blocks(wl, a, torch)
     else:
         res, (wl, kv_bytes) = bench_decode(wl, a, torch)
         if a.cpu_seconds > 0:

@@ -453,6 +453,39 @@ def sliding_prefill(B: int = 4, window: int = 4096, hist: int = 8192, chunk: int
                                    act="bf16", window=window, hist=hist, chunk=chunk)
 
 
+@dataclass
+class CopyWorkload:
+    """A burst of copy-on-write block copies: ``mapping`` ``[N, 2]`` (src,
+    dst) over a pool of ``num_blocks`` blocks, distinct blocks throughout."""
+
+    name: str
+    cache: str
+    Hkv: int
+    D: int
+    BS: int
+    num_blocks: int
+    mapping: np.ndarray        # int32 [N, 2]
+    meta: dict = field(default_factory=dict)
+
+    def block_bytes(self) -> int:
+        elem = {"e4m3": 1, "int8": 1}.get(self.cache, 2)
+        row = self.D * elem + (4 if self.cache == "int8" else 0)
+        return 2 * self.Hkv * self.BS * row
+
+
+def cow_copy(N: int = 2048, seed: int = 7) -> CopyWorkload:
+    """Copy-on-write after forks, Mistral-7B layer shape (8 KV heads,
+    head_dim 128, bf16 cache, 128 KiB per block): 2048 copies, e.g. 64
+    forked sequences each copying the shared partial last block of 32
+    layers, from and to random distinct blocks of a 4096-block pool."""
+    rng = np.random.default_rng(seed)
+    nb = 2 * N
+    perm = rng.permutation(nb).astype(np.int32)
+    return CopyWorkload(name="cow_copy", cache="bf16", Hkv=8, D=128, BS=BLOCK_SIZE,
+                        num_blocks=nb, mapping=np.stack([perm[:N], perm[N:]], axis=1),
+                        meta={"seed": seed})
+
+
 def prefix_prefill(B: int = 16, prefix_len: int = 2048, chunk: int = 512,
                    seed: int = 4) -> PrefillWorkload:
     """Phi-3-mini-shaped chunked prefill over a shared prefix: 32/32 heads, D=96."""
