@@ -107,7 +107,7 @@ def prefill_chunk(query_bits, act_fmt: str, cu_q_lens, key_cache, value_cache,
 
 def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_lens,
                          key_cache, value_cache, cache_fmt: str, block_tables, context_lens,
-                         scale: float, window: int):
+                         scale: float, window: int, rows=None):
     """Chunked prefill of a sliding-window layer whose cache is a ring of
     ``window`` rows ("Rolling buffer cache", opening post: position i lives
     in ring row i mod W).
@@ -120,6 +120,9 @@ def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_le
     those before the chunk (``< ctx - C``) from the ring, the chunk's own
     from ``key_bits`` / ``value_bits`` (``[total_q, Hkv, D]``, packed like
     the queries).
+
+    ``rows``: optionally, the (b, j) pairs to compute (the others stay 0),
+    for spot checks of workloads too large to compute whole.
     """
     q = bits_to_f64(query_bits, act_fmt)
     kn = bits_to_f64(key_bits, act_fmt)
@@ -134,6 +137,8 @@ def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_le
         ctx = int(context_lens[b])
         start = ctx - C                      # first position of the chunk
         for j in range(C):
+            if rows is not None and (b, j) not in rows:
+                continue
             i = start + j
             ks, vs = [], []
             for pos in range(max(0, i - window + 1), i + 1):

@@ -111,3 +111,77 @@ def test_full_size_prefill_sampled():
                 err = max(err, float(np.abs(got - ref).max()))
     P.say(f"    max-abs error {err:.3e} over {len(seqs)} sequences")
     assert err <= P.TOL[wl.cache]
+
+
+def test_full_size_int8_decode_sampled():
+    """The INT8 decode workload at full size (B=64, contexts 1024..8192), in
+    the launch configuration bench.py times: the writer, then pa_decode_i8
+    with the automatic split."""
+    wl = W.int8_decode()
+    seqs = _sample_seqs(wl)
+    P.say(f"[full int8 decode] B={wl.B} sampled seqs={seqs} "
+          f"lens={[int(wl.context_lens[b]) for b in seqs]}")
+    pools = P.hip_decode_setup_i8(wl)
+    out = P.hip_decode_i8(wl, pools)
+    torch.cuda.synchronize()
+    opools = P.oracle_decode_setup_i8(wl, seqs)
+    blocks = _blocks_of(wl, seqs)
+    for got, ref, what in zip(pools, opools, ("key codes", "value codes", "key scales",
+                                              "value scales")):
+        g = P.scale_bits(got) if got.dtype == torch.float32 else P.pool_bits(got)
+        r = ref.view(np.int32) if ref.dtype == np.float32 else ref
+        assert np.array_equal(g[blocks], r[blocks]), f"{what} differ"
+    ref = P.oracle_decode_i8(wl, opools, seqs)
+    err = P.max_abs(P.out_f64(out)[seqs], ref)
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL["int8"]
+
+
+def test_full_size_sliding_prefill_sampled():
+    """The sliding-window prefill workload at full size (B=4, W=4096, 8192
+    positions in the ring, chunks of 2048), as bench.py times it; query rows
+    at tile and page boundaries and at the window's edge, three heads."""
+    wl = W.sliding_prefill()
+    P.say(f"[full sliding prefill] B={wl.B} W={wl.window} hist={int(wl.hist_lens[0])} "
+          f"chunk={int(wl.chunk_lens[0])}")
+    kc, vc = P.gpu_pools(wl)
+    from paged_kv_cache_175_amd import ops, pool
+    hk, hv, hs = [], [], []
+    for b in range(wl.B):
+        pos = np.arange(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
+        hs.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+        hk.append(wl.hist_k[b])
+        hv.append(wl.hist_v[b])
+    P._gpu_write(wl, kc, vc, np.concatenate(hk), np.concatenate(hv), np.concatenate(hs))
+    q, k, v = (P._act_tensor(x, wl.act) for x in (wl.query, wl.chunk_k, wl.chunk_v))
+    out = P.out_f64(ops.prefill_chunk_window(
+        q, k, v, torch.from_numpy(wl.cu_q_lens).cuda(), kc, vc,
+        torch.from_numpy(wl.block_tables).cuda(), torch.from_numpy(wl.context_lens).cuda(),
+        int(wl.chunk_lens.max()), wl.scale, wl.window))
+    torch.cuda.synchronize()
+    seqs = [0, wl.B - 1]
+    okc, ovc = o_cache.empty_pools(wl.num_blocks, wl.Hkv, wl.BS, wl.D, wl.act,
+                                   P.NAN16[wl.act])
+    from oracle import pool as o_pool
+    for b in seqs:
+        pos = range(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
+        slots = [o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
+                 for p in pos]
+        o_cache.reshape_and_cache(wl.hist_k[b], wl.hist_v[b], okc, ovc,
+                                  np.array(slots, np.int64), wl.act, wl.act)
+        blocks = [int(x) for x in wl.block_tables[b]]
+        assert np.array_equal(P.pool_bits(kc)[blocks], okc[blocks]), f"ring K of {b} differs"
+        assert np.array_equal(P.pool_bits(vc)[blocks], ovc[blocks]), f"ring V of {b} differs"
+    C = int(wl.chunk_lens[0])
+    js = sorted({0, 31, 32, 191, 192, 1024, C - 2, C - 1})
+    rows = {(b, j) for b in seqs for j in js}
+    ref = o_attn.prefill_chunk_window(wl.query, wl.act, wl.chunk_k, wl.chunk_v, wl.cu_q_lens,
+                                      okc, ovc, wl.act, wl.block_tables, wl.context_lens,
+                                      wl.scale, wl.window, rows=rows)
+    heads = [0, wl.Hq // 2 + 1, wl.Hq - 1]
+    err = 0.0
+    for b, j in rows:
+        r = int(wl.cu_q_lens[b]) + j
+        err = max(err, float(np.abs(out[r, heads] - ref[r, heads]).max()))
+    P.say(f"    max-abs error {err:.3e} over {len(rows)} rows")
+    assert err <= P.TOL[wl.act]
