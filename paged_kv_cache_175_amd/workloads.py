@@ -258,18 +258,23 @@ class PrefillWorkload:
 def prefill_workload(name: str, seed: int, B: int, Hq: int, Hkv: int, D: int,
                      act: str, prefix_len: int, chunk: Optional[int] = None,
                      chunk_range: Optional[tuple] = None, cache: Optional[str] = None,
-                     BS: int = BLOCK_SIZE) -> PrefillWorkload:
+                     BS: int = BLOCK_SIZE, chunks: Optional[list] = None) -> PrefillWorkload:
     """Build a chunked-prefill workload over a shared prefix.
 
     ``prefix_len`` must be a multiple of BS (whole shared blocks).  Chunk
-    lengths are ``chunk`` for every sequence, or drawn from ``chunk_range``.
+    lengths are ``chunk`` for every sequence, the list ``chunks``, or drawn
+    from ``chunk_range``.
     """
     if prefix_len % BS:
         raise ValueError("prefix must be whole blocks")
     cache = cache or act
     rng = np.random.default_rng(seed)
     # 1. lengths
-    if chunk is not None:
+    if chunks is not None:
+        C = np.asarray(chunks, dtype=np.int64)
+        if C.shape != (B,):
+            raise ValueError("chunks must list B lengths")
+    elif chunk is not None:
         C = np.full(B, chunk, dtype=np.int64)
     else:
         lo, hi = chunk_range
