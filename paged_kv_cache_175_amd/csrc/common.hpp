@@ -122,11 +122,18 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// Cache policy of a buffer load: kCacheNT marks a non-temporal (streaming)
+// access, for data that no other instruction of the launch reads again.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheNT = 2;
+
+template <int POLICY = kCacheDefault>
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY);
 }
+template <int POLICY = kCacheDefault>
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POLICY);
 }
 
 // ---------------------------------------------------------------------------
