@@ -16,7 +16,10 @@
 // the probabilities never leave registers:
 //
 //   * S^T = K Q^T (v_mfma_f32_16x16x32): the page's 32 keys are two 16-row
-//     A tiles, tile kt row x being key 2x + kt; the G query heads of the
+//     A tiles; 16-bit caches: tile kt row x is key 16 kt + x, so each K
+//     load instruction reads whole 128-byte lines; E4M3 and INT8: tile kt
+//     row x is key 2x + kt (one 16-byte load per lane holds both tiles'
+//     8-byte chunks, whole lines again).  The G query heads of the
 //     group are the B columns (columns G..15 are zero); D/32 k-steps.  The K
 //     page layout [D/8][32][8] makes each A operand one 16-byte load (one
 //     16-byte load holds both tiles' chunks for E4M3).  Lane (q, col) then
@@ -95,7 +98,7 @@ __device__ __forceinline__ typename Mfma<AF>::vec as_operand(const Raw8<CF>& r) 
 }
 
 // Registers of one page.  16-bit caches: K operand of key tile kt and k-step
-// j is one 16-byte load (key 2 col + kt).  E4M3: one 16-byte load per k-step
+// j is one 16-byte load (key 16 kt + col).  E4M3: one 16-byte load per k-step
 // holds the 8-byte chunks of keys 2 col and 2 col + 1, which are row col of
 // key tiles 0 and 1.
 template <int D, int CF>
@@ -339,22 +342,27 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int bt_lane = block_tables ? block_tables[(size_t)b * MBPS + lpg] : b * MBPS + lpg;
 
     // Per-lane byte offsets inside a page (loop invariant).  K operand of
-    // k-step j, key tile kt: chunk (q4 + 4j), key 2 col + kt; V operand of
-    // output tile n: dim 16n + col, tokens 8 q4 .. 8 q4 + 7.
-    const int k_lane = ((q4 * kPage + 2 * col) * 8) * EB;
+    // k-step j, key tile kt: chunk (q4 + 4j), key 16 kt + col (16-bit) or
+    // keys 2 col and 2 col + 1 (bytes); V operand of output tile n: dim
+    // 16n + col, tokens 8 q4 .. 8 q4 + 7.
+    constexpr bool kContig = !byte_fmt(CF);
+    const int k_lane = ((q4 * kPage + (kContig ? col : 2 * col)) * 8) * EB;
     const int v_lane = (col * kPage + 8 * q4) * EB;
     constexpr int K_J = 4 * kPage * 8 * EB;    // byte step between k-steps
-    constexpr int K_KT = 8 * EB;               // byte step between key tiles (16-bit)
+    constexpr int K_KT = 16 * 8 * EB;          // byte step between key tiles (16-bit)
     constexpr int V_N = 16 * kPage * EB;       // byte step between output tiles
     constexpr uint32_t PAGE_BYTES = (uint32_t)kPage * D * EB;
 
-    // Cache policy: every V load and every byte-format K load reads whole
-    // 128-byte lines that nothing else in the launch reads again, so they
-    // stream (non-temporal).  A 16-bit K load reads half of each line it
-    // touches and the other key tile's load the other half; those keep the
-    // default policy so that the second read hits in L2 (streaming them
-    // measured 7% slower; streaming the rest took the FP8 decode from 125
-    // to 114 us).
+    // Cache policy: every page load reads whole 128-byte lines that nothing
+    // else in the launch reads again, so V pages and byte-format K pages
+    // stream (non-temporal; this took the FP8 decode from 125 to 114 us).
+    // 16-bit K tiles take contiguous keys so that their loads read whole
+    // lines too (interleaved tiles, key 2x + kt, shared every line between
+    // the two tiles' loads); they stream when a workgroup reads a whole
+    // sequence (S == 1: 63.2 -> 61.2 us on the Mistral batch) and keep the
+    // default policy when sequences are split (streaming was 3% slower on
+    // the 4-split sliding-window batch).
+    const bool stream_k = S == 1;
     auto load_page = [&](int k, PageRegs<D, CF>& Pg) {
       const int phys = __builtin_amdgcn_readlane(bt_lane, k);
       const size_t base = ((size_t)phys * Hkv + g) * page_elems * EB;
@@ -378,7 +386,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) Pg.k[kt][j] = load8<CF>(kr, k_lane, j * K_J + kt * K_KT);
+          for (int j = 0; j < KSTEPS; ++j)
+            Pg.k[kt][j] = stream_k ? load8<CF, kCacheNT>(kr, k_lane, j * K_J + kt * K_KT)
+                                   : load8<CF>(kr, k_lane, j * K_J + kt * K_KT);
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) Pg.v[n] = load8<CF, kCacheNT>(vr, v_lane, n * V_N);
@@ -413,12 +423,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     auto compute_page = [&](PageRegs<D, CF>& Pg, int k) {
       const int base = (pa + wave + W * k) * kPage;
       // The page holding the appended row (a wave-uniform test): put the row
-      // into the page registers.  Key row_new is row row_new / 2 of key tile
-      // row_new % 2; in V it is element row_new % 8 of lane group
-      // row_new / 8.
+      // into the page registers.  Key row_new is row row_new % 16 of key
+      // tile row_new / 16 (16-bit) or row row_new / 2 of tile row_new % 2
+      // (bytes); in V it is element row_new % 8 of lane group row_new / 8.
       if (wave == w_new && k == k_new) {
-        const int kt_new = row_new & 1;
-        if (col == (row_new >> 1)) {
+        const int kt_new = kContig ? row_new >> 4 : row_new & 1;
+        if (col == (kContig ? row_new & 15 : row_new >> 1)) {
 #pragma unroll
           for (int j = 0; j < KSTEPS; ++j) {
             const u32x4 nk = *reinterpret_cast<const u32x4*>(&newk_lds[8 * (q4 + 4 * j)]);
@@ -480,12 +490,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
           for (int r = 0; r < 4; ++r) st[kt][r] *= Pg.ks[r >> 1][2 * (r & 1) + kt];
       }
+      // Element (kt, r) of a lane is key 16 kt + 4 q4 + r (16-bit) or
+      // 8 q4 + 2 r + kt (bytes).
+      auto key_of = [&](int kt, int r) {
+        return kContig ? 16 * kt + 4 * q4 + r : 8 * q4 + 2 * r + kt;
+      };
       if (partial) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (base + 8 * q4 + 2 * r + kt >= L) st[kt][r] = -INFINITY;
+            if (base + key_of(kt, r) >= L) st[kt][r] = -INFINITY;
       }
       const float lmax = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
                                fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
@@ -501,13 +516,37 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int n = 0; n <= NT; ++n) o_acc[n] *= alpha;
         m_run = m_new;
       }
+      // P as the B operand of O^T = V^T P^T: lane (q4, col) must hold the
+      // probabilities of keys 8 q4 .. 8 q4 + 7, the tokens of its V operand.
       f32x8 pv;
+      vec pb_l;
+      if constexpr (kContig) {
+        // The lane holds keys 4 q4 + r (words x0, x1) and 16 + 4 q4 + r (y0,
+        // y1).  With X_g / Y_g the words of lane group q4 = g, the target
+        // groups hold (X0 X1), (X2 X3), (Y0 Y1), (Y2 Y3): a swap of the two
+        // lane halves between X and Y, then of odd and even lane groups.
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) pv[2 * r + kt] = fast_exp2(st[kt][r] - m_run);
+          for (int r = 0; r < 4; ++r) pv[4 * kt + r] = fast_exp2(st[kt][r] - m_run);
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_convertvector(pv, vec));
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const auto h = __builtin_amdgcn_permlane32_swap(w[i], w[2 + i], false, false);
+          const auto q = __builtin_amdgcn_permlane16_swap(h[0], h[1], false, false);
+          o[i] = q[0];       // keys 8 q4 + 2i, + 1
+          o[2 + i] = q[1];   // keys 8 q4 + 4 + 2i, + 1
+        }
+        pb_l = __builtin_bit_cast(vec, o);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) pv[2 * r + kt] = fast_exp2(st[kt][r] - m_run);
+        pb_l = __builtin_convertvector(pv, vec);
+      }
       // l += 1^T P^T.
-      const vec pb_l = __builtin_convertvector(pv, vec);
       o_acc[NT] = Mfma<AF>::mma(ones, pb_l, o_acc[NT]);
       // O^T += V^T P^T; with INT8 each key's V scale goes into its P.
       vec pb = pb_l;
