@@ -363,16 +363,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // default policy when sequences are split (streaming was 3% slower on
     // the 4-split sliding-window batch).
     const bool stream_k = S == 1;
+    // Page k of this wave; a prefetch past the last page (k >= npg) gets
+    // empty buffer ranges, so its loads return zeros without touching
+    // memory and no load sits behind a branch.
     auto load_page = [&](int k, PageRegs<D, CF>& Pg) {
-      const int phys = __builtin_amdgcn_readlane(bt_lane, k);
+      const bool live = k < npg;
+      const int phys = __builtin_amdgcn_readlane(bt_lane, live ? k : 0);
       const size_t base = ((size_t)phys * Hkv + g) * page_elems * EB;
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, PAGE_BYTES);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(value_cache + base, PAGE_BYTES);
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, live ? PAGE_BYTES : 0u);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(value_cache + base, live ? PAGE_BYTES : 0u);
       if constexpr (CF == FMT_I8) {
         // fp32 scales of keys 8 q4 .. 8 q4 + 7 of this (block, head) page.
         const size_t srow = ((size_t)phys * Hkv + g) * kPage;
-        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(key_scales + srow, kPage * 4);
-        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(value_scales + srow, kPage * 4);
+        const uint32_t sbytes = live ? kPage * 4 : 0u;
+        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(key_scales + srow, sbytes);
+        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(value_scales + srow, sbytes);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           Pg.ks[h] = __builtin_bit_cast(f32x4, buf_load16(ksr, 32 * q4 + 16 * h, 0));
@@ -559,17 +564,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       for (int n = 0; n < NT; ++n) o_acc[n] = Mfma<AF>::mma(as_operand<CF, AF>(Pg.v[n]), pb, o_acc[n]);
     };
 
-    // Two register buffers: page k is computed while page k + 1 loads.  The
-    // prefetch past the last page re-reads the last page (an L2 hit) so that
-    // no load sits behind a branch.
+    // Two register buffers: page k is computed while page k + 1 loads.
     PageRegs<D, CF> A, Bf;
     load_page(0, A);
     stage_new_row();
     for (int k = 0;;) {
-      load_page(min(k + 1, npg - 1), Bf);
+      load_page(k + 1, Bf);
       compute_page(A, k);
       if (++k >= npg) break;
-      load_page(min(k + 1, npg - 1), A);
+      load_page(k + 1, A);
       compute_page(Bf, k);
       if (++k >= npg) break;
     }
