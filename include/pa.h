@@ -186,7 +186,9 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *                 capped at window); 0 lets the library choose: one pass
  *                 without workspace below 1024 tokens (max_len), from 1024
  *                 on enough splits for ~2048 resident waves, at most one
- *                 split per page of each of the workgroup's waves.  Results
+ *                 split per page of each of the workgroup's waves and at
+ *                 most 16 splits (more if a split would exceed 64 pages
+ *                 per wave).  Results
  *                 do not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0), kept by the caller across
