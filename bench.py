@@ -182,9 +182,9 @@ def bench_decode(wl, a, torch):
     out = torch.empty_like(q0)
 
     # One step: store the new tokens and attend.  Default: the fused
-    # pa_decode_append (one launch); --separate-write (and an INT8 cache, which
-    # has no fused entry): pa_reshape_and_cache then pa_decode.
-    separate = a.separate_write or i8
+    # pa_decode_append (pa_decode_append_i8 for an INT8 cache; one launch);
+    # --separate-write: pa_reshape_and_cache then pa_decode.
+    separate = a.separate_write
     writes, decodes = [], []
     for r in range(R):
         kc, vc, ksc, vsc = pools[r]
@@ -201,7 +201,8 @@ def bench_decode(wl, a, torch):
             decodes.append(ops.prepare_decode(qs[r], kc, vc, bt, cl, max_len, wl.scale, out, ws,
                                               wl.k_scale, wl.v_scale, wl.window,
                                               a.partition_tokens, new_key=new_k,
-                                              new_value=new_v))
+                                              new_value=new_v, key_scales=ksc,
+                                              value_scales=vsc))
 
     kv_tokens = wl.kv_read_tokens()
     kv_bytes = kv_tokens * wl.Hkv * (wl.D * elem + row_extra) * 2

@@ -255,6 +255,24 @@ pa_status pa_decode_i8(void* out, const void* query, const int8_t* key_cache,
                        void* stream);
 
 /*
+ * pa_decode_append_i8 -- pa_decode_append over an INT8 cache: the decoded
+ * token's row is quantised as pa_reshape_and_cache_i8 quantises it (codes
+ * plus one fp32 scale per row for K and for V, written to key_scales /
+ * value_scales) and is part of the attention of this call.
+ * key, value      [B][Hkv][D] act_dtype, 2-byte aligned.
+ * Other arguments, outputs and errors as pa_decode_i8; caller contract as
+ * pa_decode_append.
+ */
+pa_status pa_decode_append_i8(void* out, const void* query, const void* key, const void* value,
+                              int8_t* key_cache, int8_t* value_cache, float* key_scales,
+                              float* value_scales, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                              float softmax_scale, pa_dtype act_dtype, int32_t window,
+                              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * pa_prefill_chunk -- causal attention of a chunk of new tokens per sequence
  * over everything cached for it (shared prefix blocks included).
  *

@@ -46,6 +46,9 @@ SIGNATURES = {
     "pa_decode_i8": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_append_i8": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+        _i32, _f32, ctypes.c_int, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill_chunk_i8": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
         _f32, ctypes.c_int, _vp]),

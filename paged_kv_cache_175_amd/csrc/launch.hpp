@@ -39,8 +39,8 @@ struct DecodeArgs {
   int* ws_count;  // [B*Hkv] split arrival counters, zero between launches
   const void* new_key;    // append mode: [B][Hkv][D] act, or null
   const void* new_value;
-  const float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32
-  const float* value_scales;
+  float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32 (written by an append)
+  float* value_scales;
 };
 
 struct PrefillArgs {

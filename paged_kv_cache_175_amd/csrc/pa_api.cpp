@@ -240,7 +240,7 @@ namespace {
 // pa_decode and pa_decode_append share everything but the appended row.
 pa_status decode_common(void* out, const void* query, const void* new_key,
                         const void* new_value, const void* key_cache, const void* value_cache,
-                        const float* key_scales, const float* value_scales,
+                        float* key_scales, float* value_scales,
                         const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                         int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_t MBPS,
                         int32_t max_context_len, float softmax_scale, pa_dtype act_dtype,
@@ -377,10 +377,30 @@ pa_status pa_decode_i8(void* out, const void* query, const int8_t* key_cache,
                        float softmax_scale, pa_dtype act_dtype, int32_t window,
                        int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache, key_scales,
-                       value_scales, block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS,
-                       max_context_len, softmax_scale, act_dtype, PA_I8, 1.f, 1.f, window,
-                       partition_tokens, workspace, workspace_bytes, stream);
+  // Read only: the kernel writes the scale pools only when appending.
+  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache,
+                       const_cast<float*>(key_scales), const_cast<float*>(value_scales),
+                       block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len,
+                       softmax_scale, act_dtype, PA_I8, 1.f, 1.f, window, partition_tokens,
+                       workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append_i8(void* out, const void* query, const void* key, const void* value,
+                              int8_t* key_cache, int8_t* value_cache, float* key_scales,
+                              float* value_scales, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                              float softmax_scale, pa_dtype act_dtype, int32_t window,
+                              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (B > 0 && (key == nullptr || value == nullptr))
+    return fail(PA_ERR_INVALID, "null pointer argument");
+  if (!aligned(key, 2) || !aligned(value, 2))
+    return fail(PA_ERR_INVALID, "key/value must be 2-byte aligned");
+  return decode_common(out, query, key, value, key_cache, value_cache, key_scales, value_scales,
+                       block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len,
+                       softmax_scale, act_dtype, PA_I8, 1.f, 1.f, window, partition_tokens,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -207,8 +207,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     int Hkv, int MBPS, int window, int S, float qk_scale_log2, float v_scale,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
     int* __restrict__ ws_count, const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
-    float k_enc_scale, float v_enc_scale, const float* __restrict__ key_scales,
-    const float* __restrict__ value_scales) {
+    float k_enc_scale, float v_enc_scale, float* __restrict__ key_scales,
+    float* __restrict__ value_scales) {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
   constexpr int EB = byte_fmt(CF) ? 1 : 2;
@@ -258,7 +258,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // Append mode: the decoded token's K/V (new_key / new_value [B][Hkv][D])
   // belong in cache row r_new (the last position, or its ring row).  The
   // split that owns that row's page stores it (E4M3-encoded when the cache
-  // is FP8) and stages the stored cache elements in LDS; the one wave that
+  // is FP8; INT8 codes and the row's two scales when it is INT8) and stages
+  // the stored cache elements in LDS; the one wave that
   // reads the page patches the row into its page registers, so nothing in
   // this launch depends on the store becoming visible.  The row's loads
   // are issued here, its stores only after the first page's loads, so the
@@ -266,10 +267,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   static_assert(D <= 64 * W, "one head-dimension element per thread");
   int row_new = -1, k_new = -1, w_new = -1;
   bool append = false;
-  size_t new_page = 0;
+  size_t new_page = 0, new_srow = 0;
   uint16_t kx = 0, vx = 0;
+  float new_ks = 0.f, new_vs = 0.f;       // INT8: the new row's scales
   const int d_new = threadIdx.x;
-  if (CF != FMT_I8 && new_key != nullptr) {
+  if (new_key != nullptr) {
     const int ctx = context_lens[b];
     const int r_new = window > 0 ? (ctx - 1) % window : ctx - 1;
     const int pg_new = r_new / kPage;
@@ -280,10 +282,27 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       k_new = (pg_new - pa) / W;
       const int phys = block_tables ? block_tables[(size_t)b * MBPS + pg_new] : b * MBPS + pg_new;
       new_page = ((size_t)phys * Hkv + g) * (size_t)kPage * D;
+      new_srow = ((size_t)phys * Hkv + g) * kPage + row_new;
+      const size_t src = ((size_t)b * Hkv + g) * D;
       if (d_new < D) {
-        const size_t src = ((size_t)b * Hkv + g) * D;
         kx = new_key[src + d_new];
         vx = new_value[src + d_new];
+      }
+      if constexpr (CF == FMT_I8) {
+        // Row scales (amax / 127, as the writer computes them): every wave
+        // reduces the whole row itself, so no wave waits for another.
+        float ka = 0.f, va = 0.f;
+        for (int d = lane; d < D; d += 64) {
+          ka = fmaxf(ka, fabsf(lo16_to_f32<AF>(new_key[src + d])));
+          va = fmaxf(va, fabsf(lo16_to_f32<AF>(new_value[src + d])));
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          ka = fmaxf(ka, shfl_xor_f(ka, m));
+          va = fmaxf(va, shfl_xor_f(va, m));
+        }
+        new_ks = __fdiv_rn(ka, 127.f);
+        new_vs = __fdiv_rn(va, 127.f);
       }
     }
   }
@@ -295,8 +314,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   auto stage_new_row = [&]() {
     if (append && d_new < D) {
       if constexpr (byte_fmt(CF)) {
-        const uint32_t kq = e4m3_encode(lo16_to_f32<AF>(kx), k_enc_scale);
-        const uint32_t vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
+        uint32_t kq, vq;
+        if constexpr (CF == FMT_I8) {
+          kq = i8_encode(lo16_to_f32<AF>(kx), new_ks);
+          vq = i8_encode(lo16_to_f32<AF>(vx), new_vs);
+          if (d_new == 0) {
+            key_scales[new_srow] = new_ks;
+            value_scales[new_srow] = new_vs;
+          }
+        } else {
+          kq = e4m3_encode(lo16_to_f32<AF>(kx), k_enc_scale);
+          vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
+        }
         __builtin_nontemporal_store(static_cast<uint8_t>(kq),
                                     key_cache + new_page + k_page_off(row_new, d_new));
         __builtin_nontemporal_store(static_cast<uint8_t>(vq),
@@ -467,6 +496,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (q4 == (row_new >> 3)) {
 #pragma unroll
           for (int n = 0; n < NT; ++n) set_elem(Pg.v[n].w, row_new & 7, newv_lds[16 * n + col]);
+          if constexpr (CF == FMT_I8) {
+            // The row's scales, as the patched codes were encoded with.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if (e == (row_new & 7)) {
+                Pg.ks[e >> 2][e & 3] = new_ks;
+                Pg.vs[e >> 2][e & 3] = new_vs;
+              }
+            }
+          }
         }
       }
       // Rows past the context end may hold anything (NaN included): their

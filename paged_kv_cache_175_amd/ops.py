@@ -226,8 +226,9 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     ``workspace`` (uint8, >= :func:`decode_workspace_bytes`) is allocated here
     when not given.  With ``new_key`` / ``new_value`` (``[B, Hkv, D]``) the
     decoded token is first stored into its cache row in the same launch
-    (``pa_decode_append``; not for an int8 cache).  An int8 cache reads its
-    scale pools ``key_scales`` / ``value_scales`` (``pa_decode_i8``).
+    (``pa_decode_append``).  An int8 cache reads its scale pools
+    ``key_scales`` / ``value_scales`` (``pa_decode_i8``; with the new token,
+    ``pa_decode_append_i8`` writes its codes and row scales).
     """
     _dev(query, key_cache, value_cache, context_lens)
     _i32(context_lens)
@@ -251,13 +252,17 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     lib = _lib.load()
     sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
     if sc is not None:
-        if new_key is not None:
-            raise ValueError("the fused append is not available for an int8 cache")
-        _lib.check(lib.pa_decode_i8(
-            out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *sc,
-            bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
-            int(max_context_len), float(softmax_scale), act, int(window),
-            int(partition_tokens), ws_ptr, ws_bytes, _stream()))
+        tail_i8 = (bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+                   int(max_context_len), float(softmax_scale), act, int(window),
+                   int(partition_tokens), ws_ptr, ws_bytes, _stream())
+        if new_key is None:
+            _lib.check(lib.pa_decode_i8(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                                        value_cache.data_ptr(), *sc, *tail_i8))
+        else:
+            _check_new_token(new_key, new_value, query, Hkv, D)
+            _lib.check(lib.pa_decode_append_i8(
+                out.data_ptr(), query.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
+                key_cache.data_ptr(), value_cache.data_ptr(), *sc, *tail_i8))
         return out
     tail = (bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
             int(max_context_len), float(softmax_scale), act, cache, float(k_scale),
@@ -414,13 +419,18 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
             float(k_scale), float(v_scale), int(window), int(partition_tokens), ws_ptr,
             ws_bytes, _stream())
     if sc is not None:
-        if new_key is not None:
-            raise ValueError("the fused append is not available for an int8 cache")
-        args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-                *sc, bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
-                int(max_context_len), float(softmax_scale), _act_code(query), int(window),
-                int(partition_tokens), ws_ptr, ws_bytes, _stream())
-        fn = lib.pa_decode_i8
+        tail_i8 = (bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS,
+                   int(max_context_len), float(softmax_scale), _act_code(query), int(window),
+                   int(partition_tokens), ws_ptr, ws_bytes, _stream())
+        if new_key is None:
+            args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                    value_cache.data_ptr(), *sc) + tail_i8
+            fn = lib.pa_decode_i8
+        else:
+            _check_new_token(new_key, new_value, query, Hkv, D)
+            args = (out.data_ptr(), query.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
+                    key_cache.data_ptr(), value_cache.data_ptr(), *sc) + tail_i8
+            fn = lib.pa_decode_append_i8
     elif new_key is None:
         args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
                 value_cache.data_ptr()) + tail

@@ -103,3 +103,50 @@ def test_i8_writer_zero_and_extreme_rows():
     ck[5, 1, 7] = 0x4700                         # bf16 32768 in one element
     wl.cached_k[0] = ck
     _decode_case(wl)
+
+
+def _append_case(wl, part=0):
+    """pa_decode_append_i8: the decoded token's codes and row scales are
+    written in the decode launch and take part in its attention."""
+    from paged_kv_cache_175_amd import ops, pool
+    P.say(f"[int8 decode append] {wl.name} B={wl.B} D={wl.D} window={wl.window} part={part} "
+          f"lens={list(wl.context_lens)}")
+    pools = P.gpu_pools_i8(wl)
+    ks_, vs_, sl = [], [], []
+    for b in range(wl.B):
+        n = wl.cached_k[b].shape[0]
+        if n:
+            pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+            sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+            ks_.append(wl.cached_k[b])
+            vs_.append(wl.cached_v[b])
+    if sl:
+        P._gpu_write_i8(wl, pools, np.concatenate(ks_), np.concatenate(vs_), np.concatenate(sl))
+    kc, vc, ks, vs = pools
+    out = ops.decode(P._act_tensor(wl.query, wl.act), kc, vc,
+                     torch.from_numpy(wl.block_tables).cuda(),
+                     torch.from_numpy(wl.context_lens).cuda(), int(wl.context_lens.max()),
+                     wl.scale, window=wl.window, partition_tokens=part,
+                     new_key=P._act_tensor(wl.new_k, wl.act),
+                     new_value=P._act_tensor(wl.new_v, wl.act), key_scales=ks, value_scales=vs)
+    torch.cuda.synchronize()
+    opools = P.oracle_decode_setup_i8(wl)
+    okc, ovc, oks, ovs = opools
+    assert np.array_equal(P.pool_bits(kc), okc), "key codes differ"
+    assert np.array_equal(P.pool_bits(vc), ovc), "value codes differ"
+    assert np.array_equal(P.scale_bits(ks), oks.view(np.int32)), "key scales differ"
+    assert np.array_equal(P.scale_bits(vs), ovs.view(np.int32)), "value scales differ"
+    err = P.max_abs(P.out_f64(out), P.oracle_decode_i8(wl, opools))
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL["int8"]
+
+
+@pytest.mark.parametrize("name", ["i8_mistral_small", "i8_f16_gqa2_d64", "i8_mha_d96",
+                                  "i8_sliding"])
+def test_i8_decode_append_parity(name):
+    _append_case(DECODE_CASES[name]())
+
+
+@pytest.mark.parametrize("part", [32, 128])
+def test_i8_decode_append_forced_splits(part):
+    _append_case(DECODE_CASES["i8_mistral_small"](), part)
