@@ -270,6 +270,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   size_t new_page = 0, new_srow = 0;
   uint16_t kx = 0, vx = 0;
   float new_ks = 0.f, new_vs = 0.f;       // INT8: the new row's scales
+  constexpr int DPL = CF == FMT_I8 ? (D + 63) / 64 : 1;
+  uint16_t krow[DPL], vrow[DPL];          // INT8: this lane's share of the row
   const int d_new = threadIdx.x;
   if (new_key != nullptr) {
     const int ctx = context_lens[b];
@@ -289,12 +291,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         vx = new_value[src + d_new];
       }
       if constexpr (CF == FMT_I8) {
-        // Row scales (amax / 127, as the writer computes them): every wave
-        // reduces the whole row itself, so no wave waits for another.
+        // Every wave reduces the whole row for its scales itself (below),
+        // so no wave waits for another; the loads go out now.
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          const int d = lane + 64 * i;
+          krow[i] = d < D ? new_key[src + d] : 0;
+          vrow[i] = d < D ? new_value[src + d] : 0;
+        }
+      }
+    }
+  }
+  // Store the row (non-temporal: nothing in this launch reads it back from
+  // memory; measured 1.3 us faster on the Mistral batch) and stage it in
+  // LDS, then make the LDS copy visible to every wave; the global stores
+  // need not have completed (__syncthreads would wait for them).  Every
+  // wave runs this exactly once.
+  auto stage_new_row = [&]() {
+    if constexpr (CF == FMT_I8) {
+      if (append) {
+        // Row scales, amax / 127 as the writer computes them.
         float ka = 0.f, va = 0.f;
-        for (int d = lane; d < D; d += 64) {
-          ka = fmaxf(ka, fabsf(lo16_to_f32<AF>(new_key[src + d])));
-          va = fmaxf(va, fabsf(lo16_to_f32<AF>(new_value[src + d])));
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          ka = fmaxf(ka, fabsf(lo16_to_f32<AF>(krow[i])));
+          va = fmaxf(va, fabsf(lo16_to_f32<AF>(vrow[i])));
         }
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) {
@@ -305,13 +326,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         new_vs = __fdiv_rn(va, 127.f);
       }
     }
-  }
-  // Store the row (non-temporal: nothing in this launch reads it back from
-  // memory; measured 1.3 us faster on the Mistral batch) and stage it in
-  // LDS, then make the LDS copy visible to every wave; the global stores
-  // need not have completed (__syncthreads would wait for them).  Every
-  // wave runs this exactly once.
-  auto stage_new_row = [&]() {
     if (append && d_new < D) {
       if constexpr (byte_fmt(CF)) {
         uint32_t kq, vq;
