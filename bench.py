@@ -654,7 +654,7 @@ def calibrate_copy(gib, a, torch):
 def main():
     a = _args()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                                    "(the path shards by sequence or KV head, but no "
                                    "multi-GPU code is built)"}))
         sys.exit(2)

@@ -2,7 +2,7 @@
 
 This module only draws random inputs and lays them out; it holds none of the
 method's arithmetic (no slot arithmetic, no encoding, no attention).  Both the
-HIP path and the CPU checker consume what it returns, each with its own code.
+HIP path and the CPU oracle consume what it returns, each with its own code.
 
 Values are fp32 standard normals rounded (RNE, by torch's cast) to the
 activation dtype.  The workloads are shaped like the chat runs the pages
