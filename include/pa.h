@@ -49,6 +49,9 @@
  *    stream).  The library never synchronises.
  *  - Errors are returned as pa_status; nothing is thrown and nothing aborts.
  *    Arguments the host can see are checked before anything is launched.
+ *    Sizes that would exceed a launch grid dimension (B or Hkv above 65535
+ *    for decode, Hkv above 65535 for the writer and the block copy) give
+ *    PA_ERR_UNSUPPORTED.
  *    Device data (table entries, lengths, slots) is NOT checked: the caller
  *    contracts below must hold, or the kernels read or write out of bounds.
  *  - Supported now: block_size 32; head_dim 64, 96 or 128; act dtype PA_F16

@@ -50,6 +50,7 @@ bool cache_ok(pa_dtype act, pa_dtype cache) { return cache == act || cache == PA
 size_t elem_bytes(pa_dtype d) { return d == PA_F8E4M3 ? 1 : 2; }
 
 constexpr int kBlock = 32;
+constexpr int kMaxGridDim = 65535;  // decode grid (splits, Hkv, B); writer and copy grids
 constexpr long long kTargetWaves = 2048;
 constexpr size_t kAlign = 256;
 
@@ -144,6 +145,7 @@ pa_status cache_write_common(const void* key, const void* value, void* key_cache
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
   if (D % 8 != 0 || D > 512)
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8, at most 512");
+  if (Hkv > kMaxGridDim) return fail(PA_ERR_UNSUPPORTED, "Hkv must be <= %d", kMaxGridDim);
   if ((long long)NB * BS >= (1LL << 31)) return fail(PA_ERR_INVALID, "NB*BS must be < 2^31");
   if (cache_dtype == PA_F8E4M3 &&
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
@@ -206,6 +208,7 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, float* key_scales,
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);
   if (D % 8 != 0 || D > 512)
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8, at most 512");
+  if (Hkv > kMaxGridDim) return fail(PA_ERR_UNSUPPORTED, "Hkv must be <= %d", kMaxGridDim);
   if (N > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 pairs per call");
   if (N == 0) return ok();
   if (!key_cache || !value_cache || !block_mapping)
@@ -249,6 +252,8 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
                         void* stream) {
   if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || MBPS < 1 || max_context_len < 0)
     return fail(PA_ERR_INVALID, "B, Hq, Hkv, D, MBPS, max_context_len out of range");
+  if (B > kMaxGridDim || Hkv > kMaxGridDim)
+    return fail(PA_ERR_UNSUPPORTED, "B and Hkv must be <= %d (grid dimensions)", kMaxGridDim);
   if (Hq % Hkv != 0) return fail(PA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (!act_ok(act_dtype)) return fail(PA_ERR_UNSUPPORTED, "act dtype must be PA_F16 or PA_BF16");
   if (BS != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 32 (got %d)", BS);

@@ -98,7 +98,8 @@ def _decode(**kw):
     (dict(part=32, ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),  # not 256-aligned
     (dict(scale=float("inf")), _lib.PA_ERR_INVALID),
     (dict(B=-1), _lib.PA_ERR_INVALID),
-    (dict(bt=0, B=1 << 16, MBPS=1 << 16), _lib.PA_ERR_INVALID),  # identity map overflows int32
+    (dict(bt=0, B=1 << 15, MBPS=1 << 16), _lib.PA_ERR_INVALID),  # identity map overflows int32
+    (dict(B=70000), _lib.PA_ERR_UNSUPPORTED),            # grid dimension limit
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
