@@ -15,7 +15,8 @@
  *    slot before attention runs; pa_reshape_and_cache() is that writer.
  *  - "Rolling buffer cache" (llama.cpp discussion 3581), opening post: with a
  *    sliding window of W tokens the cache is a ring of W rows and position i
- *    lives in row i mod W; pa_decode() with window > 0 reads such a ring.
+ *    lives in row i mod W; pa_decode() with window > 0 reads such a ring,
+ *    and pa_prefill_chunk_window() attends a prompt chunk over it.
  *  - same page, the prefix-caching note and section "FlashAttention V2/V3 +
  *    PagedAttention": prompt (prefill) tokens attend causally over cached
  *    blocks that may be shared between sequences; pa_prefill_chunk() is that
