@@ -1,0 +1,90 @@
+"""The hot path under HIP graph capture.
+
+The library allocates nothing and launches plain kernels (the split merge
+resets its own counters inside the launch, no memset), so a decode step and
+a prefill chunk can be captured once and replayed.  Each replay, with eager
+work in between, must reproduce the eager result bit for bit: the fused
+append rewrites the same row with the same bytes, and the split counters
+must be back at zero after every replay.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paritylib as P
+from paged_kv_cache_175_amd import ops
+from paged_kv_cache_175_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_decode_append_graph_replays(part):
+    wl = W.decode_workload("graph_decode", 91, B=6, Hq=32, Hkv=8, D=128, act="bf16",
+                           ctx_range=(1, 900))
+    P.say(f"[graph] decode append part={part} lens={list(wl.context_lens)}")
+    kc, vc = P.hip_decode_append_setup(wl)
+    q = P._act_tensor(wl.query, wl.act)
+    nk, nv = P._act_tensor(wl.new_k, wl.act), P._act_tensor(wl.new_v, wl.act)
+    bt = torch.from_numpy(wl.block_tables).cuda()
+    cl = torch.from_numpy(wl.context_lens).cuda()
+    L = int(wl.context_lens.max())
+    ws = ops.alloc_workspace(ops.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, L, 0, part),
+                             q.device)
+    eager = torch.empty_like(q)
+    ops.prepare_decode(q, kc, vc, bt, cl, L, wl.scale, eager, ws, partition_tokens=part,
+                       new_key=nk, new_value=nv)()
+    torch.cuda.synchronize()
+    ref_pools = (P.pool_bits(kc).copy(), P.pool_bits(vc).copy())
+
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ops.prepare_decode(q, kc, vc, bt, cl, L, wl.scale, out, ws, partition_tokens=part,
+                               new_key=nk, new_value=nv)()
+    torch.cuda.current_stream().wait_stream(side)
+    junk = torch.zeros(1 << 20, device="cuda")
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        junk.add_(1.0)                       # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        assert np.array_equal(P.pool_bits(kc), ref_pools[0])
+        assert np.array_equal(P.pool_bits(vc), ref_pools[1])
+    okc, ovc = P.oracle_decode_setup(wl)
+    assert P.max_abs(P.out_f64(out), P.oracle_decode(wl, okc, ovc)) <= P.TOL["bf16"]
+
+
+def test_prefill_graph_replays():
+    wl = W.prefill_workload("graph_prefill", 92, B=3, Hq=8, Hkv=2, D=128, act="bf16",
+                            prefix_len=64, chunk_range=(1, 200))
+    P.say(f"[graph] prefill chunks={list(wl.chunk_lens)}")
+    kc, vc = P.hip_prefill_setup(wl)
+    q = P._act_tensor(wl.query, wl.act)
+    cu = torch.from_numpy(wl.cu_q_lens).cuda()
+    bt = torch.from_numpy(wl.block_tables).cuda()
+    cl = torch.from_numpy(wl.context_lens).cuda()
+    C = int(wl.chunk_lens.max())
+    eager = torch.empty_like(q)
+    ops.prepare_prefill_chunk(q, cu, kc, vc, bt, cl, C, wl.scale, eager)()
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ops.prepare_prefill_chunk(q, cu, kc, vc, bt, cl, C, wl.scale, out)()
+    torch.cuda.current_stream().wait_stream(side)
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
