@@ -289,7 +289,10 @@ def bench_decode(wl, a, torch):
         "other_bytes_per_step": write_bytes + qo_bytes,
         "roofline": {
             "kernel": ("pa_decode" if separate else "pa_decode_append")
-                      + " (decode_split; split sequences merge inside the launch)",
+                      + (" (decode_balanced: equal page ranges of the batch"
+                         if wl.cache in ("e4m3", "int8") and max_len >= 1024 and wl.B <= 1024
+                         and a.partition_tokens == 0 else " (decode_split")
+                      + "; split sequences merge inside the launch)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(wl.name, "decode_"),

@@ -160,8 +160,10 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, float* key_scales,
 /*
  * pa_decode_workspace_bytes -- bytes of scratch pa_decode needs for this
  * shape.  Same arguments as pa_decode (partition_tokens 0 = automatic).
- * Returns 0 when the call needs no workspace, and (size_t)-1 when the
- * arguments are invalid.
+ * The automatic plan also depends on the cache format, which this query
+ * does not take: it returns the larger of the workspaces the plans for
+ * 16-bit and byte-format caches need.  Returns 0 when the call needs no
+ * workspace, and (size_t)-1 when the arguments are invalid.
  */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t max_context_len, int32_t window,
@@ -188,12 +190,15 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *                 sequence into ceil(max_len / partition_tokens) parts whose
  *                 partial results are merged (max_len = max_context_len,
  *                 capped at window); 0 lets the library choose: one pass
- *                 without workspace below 1024 tokens (max_len), from 1024
- *                 on enough splits for ~2048 resident waves, at most one
- *                 split per page of each of the workgroup's waves and at
- *                 most 16 splits (more if a split would exceed 64 pages
- *                 per wave).  Results
- *                 do not depend on it beyond rounding.
+ *                 without workspace below 1024 tokens (max_len); from 1024
+ *                 on, for 16-bit caches enough splits for ~2048 resident
+ *                 waves, at most one split per page of each of the
+ *                 workgroup's waves and at most 16 splits (more if a split
+ *                 would exceed 64 pages per wave), and for E4M3 and INT8
+ *                 caches (B <= 1024) equal ranges of the whole batch's
+ *                 pages, one per workgroup, whatever the mix of context
+ *                 lengths (a sequence cut between ranges is merged like the
+ *                 splits).  Results do not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0), kept by the caller across
  *                 calls: besides the split partials it holds one arrival
@@ -201,8 +206,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *                 before the workspace is first used (zero-fill it once
  *                 after allocating it); every call leaves them zero.  Calls
  *                 that share a workspace must not overlap in time.  The
- *                 last split of each (sequence, KV head) to finish merges
- *                 the partials inside the same launch.
+ *                 last split (or range) of each (sequence, KV head) to
+ *                 finish merges the partials inside the same launch.
  * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV
  * head h / (Hq/Hkv); an empty context gives zeros.  Caller contract: table
  * entries read (logical blocks < ceil(L/BS)) lie in [0, NB);

@@ -29,8 +29,10 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int B, Hkv, G, D, MBPS, window;
-  int S;  // splits per (sequence, KV head)
+  int S;  // grid mode: splits per (sequence, KV head); balanced: partials per item
   int W;  // waves per workgroup (4 or 8)
+  int N;  // balanced mode: workgroups (0 = grid mode)
+  int stream_k;  // balanced mode: 16-bit K pages non-temporal
   int act, cache;  // Fmt codes
   float softmax_scale, k_scale, v_scale;
   float* ws_m;  // [B*Hq*S]

@@ -8,12 +8,16 @@
 // addresses a W-row ring ("Rolling buffer cache", llama.cpp discussion 3581,
 // opening post) and min(L, W) rows are read.
 //
-// Work split.  A workgroup of W waves (W = 4 or 8) owns one split of the
-// pages of (sequence b, KV head g); its waves take the split's pages
-// round-robin, so they stream neighbouring pages side by side, and each wave
-// prefetches its next page into a second register buffer while it computes
-// the current one.  Per wave and page everything is computed transposed, so
-// the probabilities never leave registers:
+// Work split, two modes chosen by the host plan.  Grid mode (decode_split):
+// a workgroup of W waves (W = 4 or 8) owns one split of the pages of
+// (sequence b, KV head g); its waves take the split's pages round-robin, so
+// they stream neighbouring pages side by side.  Balanced mode
+// (decode_balanced, E4M3 and INT8 caches): the pages of the whole batch are
+// cut into equal ranges, one per workgroup, whatever the mix of context
+// lengths, and the waves claim a range's pages one at a time.  Either way
+// each wave prefetches its next page into a second register buffer while it
+// computes the current one.  Per wave and page everything is computed
+// transposed, so the probabilities never leave registers:
 //
 //   * S^T = K Q^T (v_mfma_f32_16x16x32): the page's 32 keys are two 16-row
 //     A tiles; 16-bit caches: tile kt row x is key 16 kt + x, so each K
@@ -44,10 +48,11 @@
 //
 // The W partial results of a workgroup are combined through LDS.  When a
 // sequence is one split (S == 1, the usual case once B * Hkv workgroups fill
-// the GPU) that is the output; otherwise each split writes (m, l, o) to the
-// workspace and counts itself in, and the last split of the (sequence, KV
-// head) to arrive combines the S partials in the same launch: M = max m_s,
-// w_s = 2^(m_s - M), out = sum w_s o_s / sum w_s l_s.
+// the GPU), or lies wholly in one balanced range, that is the output;
+// otherwise each split (range) writes (m, l, o) to the workspace and counts
+// itself in, and the last of the (sequence, KV head) to arrive combines the
+// S partials in the same launch: M = max m_s, w_s = 2^(m_s - M),
+// out = sum w_s o_s / sum w_s l_s.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -199,6 +204,362 @@ __device__ __forceinline__ void merge_head(uint16_t* __restrict__ dst, int S, fl
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-page work shared by both kernels.
+
+// K operand of key tile kt, k-step j.
+template <int D, int CF, int AF>
+__device__ __forceinline__ typename Mfma<AF>::vec k_operand(const PageRegs<D, CF>& Pg, int kt, int j) {
+  if constexpr (byte_fmt(CF)) {
+    Raw8<CF> r;
+    r.w = kt == 0 ? u32x2{Pg.k[j][0], Pg.k[j][1]} : u32x2{Pg.k[j][2], Pg.k[j][3]};
+    return as_operand<CF, AF>(r);
+  } else {
+    return as_operand<CF, AF>(Pg.k[kt][j]);
+  }
+}
+
+// Set element e (0..7, any lane-varying value) of a lane's eight consecutive
+// cache elements.  Register arrays are only ever indexed by constants (a
+// runtime index would move them to scratch memory).
+template <int CF, typename V>
+__device__ __forceinline__ void set_elem(V& raw, int e, uint32_t x) {
+  constexpr int EPW = byte_fmt(CF) ? 4 : 2;   // elements per word
+  constexpr int BITS = 32 / EPW;
+  constexpr uint32_t EMASK = (1u << BITS) - 1u;
+  const int sh = BITS * (e % EPW);
+  const uint32_t keep = ~(EMASK << sh);
+  const uint32_t put = (x & EMASK) << sh;
+#pragma unroll
+  for (int w = 0; w < 8 / EPW; ++w)
+    if (w == e / EPW) raw[w] = (raw[w] & keep) | put;
+}
+
+// Load one (block, KV head) page, page_id = block * Hkv + head, into
+// registers.  Cache policy: every page load reads whole 128-byte lines that
+// nothing else in the launch reads again, so V pages and byte-format K pages
+// stream (non-temporal; this took the FP8 decode from 125 to 114 us).  16-bit
+// K tiles take contiguous keys so that their loads read whole lines too
+// (interleaved tiles, key 2x + kt, shared every line between the two tiles'
+// loads); they stream when the caller says so (stream_k), which pays where
+// a workgroup reads whole sequences (63.2 -> 61.2 us on the Mistral batch)
+// and not on short splits (3% slower on the 4-split sliding-window batch).
+// A page that is not live (a prefetch past a wave's last page) gets empty
+// buffer ranges, so its loads return zeros without touching memory and no
+// load sits behind a branch.
+template <int D, int CF>
+__device__ __forceinline__ void load_page(PageRegs<D, CF>& Pg, const uint8_t* key_cache,
+                                          const uint8_t* value_cache, const float* key_scales,
+                                          const float* value_scales, uint32_t page_id, bool live,
+                                          int lane, bool stream_k) {
+  constexpr int EB = byte_fmt(CF) ? 1 : 2;
+  constexpr int KSTEPS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr bool kContig = !byte_fmt(CF);
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  // Per-lane byte offsets inside a page.  K operand of k-step j, key tile
+  // kt: chunk (q4 + 4j), key 16 kt + col (16-bit) or keys 2 col and
+  // 2 col + 1 (bytes); V operand of output tile n: dim 16n + col, tokens
+  // 8 q4 .. 8 q4 + 7.
+  const int k_lane = ((q4 * kPage + (kContig ? col : 2 * col)) * 8) * EB;
+  const int v_lane = (col * kPage + 8 * q4) * EB;
+  constexpr int K_J = 4 * kPage * 8 * EB;    // byte step between k-steps
+  constexpr int K_KT = 16 * 8 * EB;          // byte step between key tiles (16-bit)
+  constexpr int V_N = 16 * kPage * EB;       // byte step between output tiles
+  constexpr uint32_t PAGE_BYTES = (uint32_t)kPage * D * EB;
+  const size_t base = (size_t)page_id * PAGE_BYTES;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, live ? PAGE_BYTES : 0u);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(value_cache + base, live ? PAGE_BYTES : 0u);
+  if constexpr (CF == FMT_I8) {
+    // fp32 scales of keys 8 q4 .. 8 q4 + 7 of this (block, head) page.
+    const size_t srow = (size_t)page_id * kPage;
+    const uint32_t sbytes = live ? kPage * 4 : 0u;
+    const __amdgpu_buffer_rsrc_t ksr = make_rsrc(key_scales + srow, sbytes);
+    const __amdgpu_buffer_rsrc_t vsr = make_rsrc(value_scales + srow, sbytes);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      Pg.ks[h] = __builtin_bit_cast(f32x4, buf_load16(ksr, 32 * q4 + 16 * h, 0));
+      Pg.vs[h] = __builtin_bit_cast(f32x4, buf_load16(vsr, 32 * q4 + 16 * h, 0));
+    }
+  }
+  if constexpr (byte_fmt(CF)) {
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) Pg.k[j] = buf_load16<kCacheNT>(kr, k_lane, j * K_J);
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        Pg.k[kt][j] = stream_k ? load8<CF, kCacheNT>(kr, k_lane, j * K_J + kt * K_KT)
+                               : load8<CF>(kr, k_lane, j * K_J + kt * K_KT);
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) Pg.v[n] = load8<CF, kCacheNT>(vr, v_lane, n * V_N);
+}
+
+// Attend one page: positions base .. base + 31 of a sequence with L cached
+// tokens.  With `patch` (a wave-uniform flag) the page holds the appended
+// row row_new, whose stored cache elements newk / newv (and, INT8, scales
+// new_ks / new_vs) replace what the loads returned.
+template <int D, int G, int CF, int AF>
+__device__ __forceinline__ void compute_page(PageRegs<D, CF>& Pg, float& m_run,
+                                             f32x4 (&o_acc)[D / 16 + 1],
+                                             const typename Mfma<AF>::vec (&qb)[D / 32],
+                                             typename Mfma<AF>::vec ones, int base, int L,
+                                             bool patch, int row_new, const uint16_t* newk,
+                                             const uint16_t* newv, float new_ks, float new_vs,
+                                             float qk_scale_log2, int lane) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr bool kContig = !byte_fmt(CF);
+  typedef typename Mfma<AF>::vec vec;
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  // Key row_new is row row_new % 16 of key tile row_new / 16 (16-bit) or
+  // row row_new / 2 of tile row_new % 2 (bytes); in V it is element
+  // row_new % 8 of lane group row_new / 8.
+  if (patch) {
+    const int kt_new = kContig ? row_new >> 4 : row_new & 1;
+    if (col == (kContig ? row_new & 15 : row_new >> 1)) {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        const u32x4 nk = *reinterpret_cast<const u32x4*>(&newk[8 * (q4 + 4 * j)]);
+        if constexpr (byte_fmt(CF)) {
+          // The codes were staged one per 16-bit slot: pack eight into two
+          // words.
+          u32x2 c;
+#pragma unroll
+          for (int w = 0; w < 2; ++w)
+            c[w] = (nk[2 * w] & 0xffu) | ((nk[2 * w] >> 8) & 0xff00u) |
+                   ((nk[2 * w + 1] & 0xffu) << 16) | ((nk[2 * w + 1] << 8) & 0xff000000u);
+          if (kt_new == 0) {
+            Pg.k[j][0] = c[0];
+            Pg.k[j][1] = c[1];
+          } else {
+            Pg.k[j][2] = c[0];
+            Pg.k[j][3] = c[1];
+          }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            if (kt == kt_new) Pg.k[kt][j].w = nk;
+        }
+      }
+    }
+    if (q4 == (row_new >> 3)) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) set_elem<CF>(Pg.v[n].w, row_new & 7, newv[16 * n + col]);
+      if constexpr (CF == FMT_I8) {
+        // The row's scales, as the patched codes were encoded with.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e == (row_new & 7)) {
+            Pg.ks[e >> 2][e & 3] = new_ks;
+            Pg.vs[e >> 2][e & 3] = new_vs;
+          }
+        }
+      }
+    }
+  }
+  // Rows past the context end may hold anything (NaN included): their
+  // scores are masked below, and their V elements are zeroed here, since a
+  // zero probability times NaN is still NaN.  (A wave-uniform test.)
+  const bool partial = base + kPage > L;
+  if (partial) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (base + 8 * q4 + e >= L) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) set_elem<CF>(Pg.v[n].w, e, 0u);
+        if constexpr (CF == FMT_I8) Pg.vs[e >> 2][e & 3] = 0.f;  // stale scale
+      }
+    }
+  }
+
+  // S^T = K Q^T; element (kt, r) of lane (q4, col) is key 8 q4 + 2r + kt.
+  f32x4 st[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j)
+      st[kt] = Mfma<AF>::mma(k_operand<D, CF, AF>(Pg, kt, j), qb[j], st[kt]);
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) st[kt] *= qk_scale_log2;
+  if constexpr (CF == FMT_I8) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[kt][r] *= Pg.ks[r >> 1][2 * (r & 1) + kt];
+  }
+  // Element (kt, r) of a lane is key 16 kt + 4 q4 + r (16-bit) or
+  // 8 q4 + 2 r + kt (bytes).
+  auto key_of = [&](int kt, int r) { return kContig ? 16 * kt + 4 * q4 + r : 8 * q4 + 2 * r + kt; };
+  if (partial) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (base + key_of(kt, r) >= L) st[kt][r] = -INFINITY;
+  }
+  const float lmax = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                           fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
+  // The reference max only moves when some score exceeds it by more than
+  // kRescaleSlack (log2 units); it is then raised to the max over the four
+  // lanes that hold each head, so all of a head's lanes agree.
+  if (__builtin_amdgcn_ballot_w64(lmax > m_run + kRescaleSlack) != 0) {
+    float cm = fmaxf(lmax, shfl_xor_f(lmax, 16));
+    cm = fmaxf(cm, shfl_xor_f(cm, 32));
+    const float m_new = fmaxf(m_run, cm);
+    const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+    for (int n = 0; n <= NT; ++n) o_acc[n] *= alpha;
+    m_run = m_new;
+  }
+  // P as the B operand of O^T = V^T P^T: lane (q4, col) must hold the
+  // probabilities of keys 8 q4 .. 8 q4 + 7, the tokens of its V operand.
+  f32x8 pv;
+  vec pb_l;
+  if constexpr (kContig) {
+    // The lane holds keys 4 q4 + r (words x0, x1) and 16 + 4 q4 + r (y0,
+    // y1).  With X_g / Y_g the words of lane group q4 = g, the target groups
+    // hold (X0 X1), (X2 X3), (Y0 Y1), (Y2 Y3): a swap of the two lane halves
+    // between X and Y, then of odd and even lane groups.
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[4 * kt + r] = fast_exp2(st[kt][r] - m_run);
+    const u32x4 w = __builtin_bit_cast(u32x4, __builtin_convertvector(pv, vec));
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const auto h = __builtin_amdgcn_permlane32_swap(w[i], w[2 + i], false, false);
+      const auto q = __builtin_amdgcn_permlane16_swap(h[0], h[1], false, false);
+      o[i] = q[0];       // keys 8 q4 + 2i, + 1
+      o[2 + i] = q[1];   // keys 8 q4 + 4 + 2i, + 1
+    }
+    pb_l = __builtin_bit_cast(vec, o);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) pv[2 * r + kt] = fast_exp2(st[kt][r] - m_run);
+    pb_l = __builtin_convertvector(pv, vec);
+  }
+  // l += 1^T P^T.
+  o_acc[NT] = Mfma<AF>::mma(ones, pb_l, o_acc[NT]);
+  // O^T += V^T P^T; with INT8 each key's V scale goes into its P.
+  vec pb = pb_l;
+  if constexpr (CF == FMT_I8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] *= Pg.vs[e >> 2][e & 3];
+    pb = __builtin_convertvector(pv, vec);
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o_acc[n] = Mfma<AF>::mma(as_operand<CF, AF>(Pg.v[n]), pb, o_acc[n]);
+}
+
+// Q^T of the G heads of one KV head as the B operand: column = head `col`
+// (zero when col >= G), k-group q4 of k-step j = head-dimension chunk
+// (q4 + 4j).  q points at the group's first head ([G][D], contiguous; global
+// memory or LDS).
+template <int D, int G, int AF>
+__device__ __forceinline__ void q_operand(typename Mfma<AF>::vec (&qb)[D / 32], const uint16_t* q,
+                                          int lane) {
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  const uint16_t* qrow = q + (col < G ? col : 0) * D;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * (q4 + 4 * j));
+    if (col >= G) w = u32x4{0u, 0u, 0u, 0u};
+    qb[j] = __builtin_bit_cast(typename Mfma<AF>::vec, w);
+  }
+}
+
+template <int AF>
+__device__ __forceinline__ typename Mfma<AF>::vec ones_operand() {
+  return __builtin_convertvector(f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f},
+                                 typename Mfma<AF>::vec);
+}
+
+// A wave's partial result for its G heads into LDS: lane (q4, col) holds
+// O[head col][dim 16n + 4 q4 + r], and l in every row of the ones tile.
+template <int D, int G>
+__device__ __forceinline__ void put_wave_partial(float (*o)[D], float* m, float* l,
+                                                 const f32x4 (&o_acc)[D / 16 + 1], float m_run,
+                                                 int lane) {
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  if (col < G) {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[col][16 * n + 4 * q4 + r] = o_acc[n][r];
+    if (q4 == 0) {
+      m[col] = m_run;
+      l[col] = o_acc[D / 16][0];
+    }
+  }
+}
+
+// Combine the W wave partials of one (head, dim): m[w * ms], l[w * ms],
+// o[w * os].  A wave without pages there left m = -inf, and its o and l are
+// not read.
+template <int W>
+__device__ __forceinline__ void combine_waves(const float* m, const float* l, const float* o,
+                                              int ms, int os, float& M, float& num, float& den) {
+  M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < W; ++w) M = fmaxf(M, m[w * ms]);
+  num = 0.f;
+  den = 0.f;
+  if (M == -INFINITY) return;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const float mw = m[w * ms];
+    if (mw != -INFINITY) {
+      const float f = fast_exp2(mw - M);
+      num = fmaf(f, o[w * os], num);
+      den = fmaf(f, l[w * ms], den);
+    }
+  }
+}
+
+// One element of the appended row in the cache format: the 16-bit value
+// itself, its E4M3 code (scale = the tensor's scale) or its INT8 code
+// (scale = the row's amax / 127).
+template <int CF, int AF>
+__device__ __forceinline__ uint32_t encode_elem(uint16_t x, float scale) {
+  if constexpr (CF == FMT_I8) return i8_encode(lo16_to_f32<AF>(x), scale);
+  else if constexpr (CF == FMT_E4M3) return e4m3_encode(lo16_to_f32<AF>(x), scale);
+  else return x;
+}
+
+// Store element d of cache row `row` of the page at element offset `page`
+// (non-temporal: nothing in the launch reads it back from memory; measured
+// 1.3 us faster on the Mistral batch).
+template <int CF>
+__device__ __forceinline__ void store_row_elem(uint8_t* key_cache, uint8_t* value_cache,
+                                               size_t page, int row, int d, uint32_t kq,
+                                               uint32_t vq) {
+  if constexpr (byte_fmt(CF)) {
+    __builtin_nontemporal_store(static_cast<uint8_t>(kq), key_cache + page + k_page_off(row, d));
+    __builtin_nontemporal_store(static_cast<uint8_t>(vq), value_cache + page + v_page_off(row, d));
+  } else {
+    __builtin_nontemporal_store(static_cast<uint16_t>(kq),
+                                reinterpret_cast<uint16_t*>(key_cache) + page + k_page_off(row, d));
+    __builtin_nontemporal_store(static_cast<uint16_t>(vq),
+                                reinterpret_cast<uint16_t*>(value_cache) + page + v_page_off(row, d));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grid mode: workgroup (s, g, b) owns split s of the pages of (sequence b,
+// KV head g).
+
 template <int D, int G, int CF, int AF, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_split(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
@@ -211,7 +572,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     float* __restrict__ value_scales) {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
-  constexpr int EB = byte_fmt(CF) ? 1 : 2;
   constexpr int KSTEPS = D / 32;
   constexpr int NT = D / 16;
   typedef typename Mfma<AF>::vec vec;
@@ -302,11 +662,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
   }
-  // Store the row (non-temporal: nothing in this launch reads it back from
-  // memory; measured 1.3 us faster on the Mistral batch) and stage it in
-  // LDS, then make the LDS copy visible to every wave; the global stores
-  // need not have completed (__syncthreads would wait for them).  Every
-  // wave runs this exactly once.
+  // Store the row and stage it in LDS, then make the LDS copy visible to
+  // every wave; the global stores need not have completed (__syncthreads
+  // would wait for them).  Every wave runs this exactly once.
   auto stage_new_row = [&]() {
     if constexpr (CF == FMT_I8) {
       if (append) {
@@ -327,33 +685,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
     if (append && d_new < D) {
-      if constexpr (byte_fmt(CF)) {
-        uint32_t kq, vq;
-        if constexpr (CF == FMT_I8) {
-          kq = i8_encode(lo16_to_f32<AF>(kx), new_ks);
-          vq = i8_encode(lo16_to_f32<AF>(vx), new_vs);
-          if (d_new == 0) {
-            key_scales[new_srow] = new_ks;
-            value_scales[new_srow] = new_vs;
-          }
-        } else {
-          kq = e4m3_encode(lo16_to_f32<AF>(kx), k_enc_scale);
-          vq = e4m3_encode(lo16_to_f32<AF>(vx), v_enc_scale);
+      const float kes = CF == FMT_I8 ? new_ks : k_enc_scale;
+      const float ves = CF == FMT_I8 ? new_vs : v_enc_scale;
+      const uint32_t kq = encode_elem<CF, AF>(kx, kes);
+      const uint32_t vq = encode_elem<CF, AF>(vx, ves);
+      if constexpr (CF == FMT_I8) {
+        if (d_new == 0) {
+          key_scales[new_srow] = new_ks;
+          value_scales[new_srow] = new_vs;
         }
-        __builtin_nontemporal_store(static_cast<uint8_t>(kq),
-                                    key_cache + new_page + k_page_off(row_new, d_new));
-        __builtin_nontemporal_store(static_cast<uint8_t>(vq),
-                                    value_cache + new_page + v_page_off(row_new, d_new));
-        newk_lds[d_new] = static_cast<uint16_t>(kq);
-        newv_lds[d_new] = static_cast<uint16_t>(vq);
-      } else {
-        __builtin_nontemporal_store(
-            kx, reinterpret_cast<uint16_t*>(key_cache) + new_page + k_page_off(row_new, d_new));
-        __builtin_nontemporal_store(
-            vx, reinterpret_cast<uint16_t*>(value_cache) + new_page + v_page_off(row_new, d_new));
-        newk_lds[d_new] = kx;
-        newv_lds[d_new] = vx;
       }
+      store_row_elem<CF>(key_cache, value_cache, new_page, row_new, d_new, kq, vq);
+      newk_lds[d_new] = static_cast<uint16_t>(kq);
+      newv_lds[d_new] = static_cast<uint16_t>(vq);
     }
     asm volatile("" ::: "memory");
     wait_lgkmcnt0();
@@ -368,306 +712,54 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int n = 0; n <= NT; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (npg > 0) {
-    // Q^T as the B operand: column = head `col` of the group (zero when
-    // col >= G), k-group q4 of k-step j = head-dimension chunk (q4 + 4j).
     vec qb[KSTEPS];
-    {
-      const uint16_t* qrow = query + ((size_t)b * Hq + g * G + (col < G ? col : 0)) * D;
-#pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * (q4 + 4 * j));
-        if (col >= G) w = u32x4{0u, 0u, 0u, 0u};
-        qb[j] = __builtin_bit_cast(vec, w);
-      }
-    }
-    const vec ones = __builtin_convertvector(f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, vec);
+    q_operand<D, G, AF>(qb, query + ((size_t)b * Hq + g * G) * D, lane);
+    const vec ones = ones_operand<AF>();
 
-    const size_t page_elems = (size_t)kPage * D;
-    // Physical blocks of this wave's pages, lane k holding its k-th page, so
-    // the page loop never waits on a block-table load.  Without a table the
-    // map is the identity (block b * MBPS + j) and nothing is loaded.
+    // Page ids (block * Hkv + g) of this wave's pages, lane k holding its
+    // k-th page, so the page loop never waits on a block-table load.
+    // Without a table the map is the identity (block b * MBPS + j) and
+    // nothing is loaded.
     const int lpg = pa + wave + W * (lane < npg ? lane : 0);
     const int bt_lane = block_tables ? block_tables[(size_t)b * MBPS + lpg] : b * MBPS + lpg;
-
-    // Per-lane byte offsets inside a page (loop invariant).  K operand of
-    // k-step j, key tile kt: chunk (q4 + 4j), key 16 kt + col (16-bit) or
-    // keys 2 col and 2 col + 1 (bytes); V operand of output tile n: dim
-    // 16n + col, tokens 8 q4 .. 8 q4 + 7.
-    constexpr bool kContig = !byte_fmt(CF);
-    const int k_lane = ((q4 * kPage + (kContig ? col : 2 * col)) * 8) * EB;
-    const int v_lane = (col * kPage + 8 * q4) * EB;
-    constexpr int K_J = 4 * kPage * 8 * EB;    // byte step between k-steps
-    constexpr int K_KT = 16 * 8 * EB;          // byte step between key tiles (16-bit)
-    constexpr int V_N = 16 * kPage * EB;       // byte step between output tiles
-    constexpr uint32_t PAGE_BYTES = (uint32_t)kPage * D * EB;
-
-    // Cache policy: every page load reads whole 128-byte lines that nothing
-    // else in the launch reads again, so V pages and byte-format K pages
-    // stream (non-temporal; this took the FP8 decode from 125 to 114 us).
-    // 16-bit K tiles take contiguous keys so that their loads read whole
-    // lines too (interleaved tiles, key 2x + kt, shared every line between
-    // the two tiles' loads); they stream when a workgroup reads a whole
-    // sequence (S == 1: 63.2 -> 61.2 us on the Mistral batch) and keep the
-    // default policy when sequences are split (streaming was 3% slower on
-    // the 4-split sliding-window batch).
+    const uint32_t pid_lane = (uint32_t)bt_lane * Hkv + g;
     const bool stream_k = S == 1;
-    // Page k of this wave; a prefetch past the last page (k >= npg) gets
-    // empty buffer ranges, so its loads return zeros without touching
-    // memory and no load sits behind a branch.
-    auto load_page = [&](int k, PageRegs<D, CF>& Pg) {
+    auto fetch = [&](int k, PageRegs<D, CF>& Pg) {
       const bool live = k < npg;
-      const int phys = __builtin_amdgcn_readlane(bt_lane, live ? k : 0);
-      const size_t base = ((size_t)phys * Hkv + g) * page_elems * EB;
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, live ? PAGE_BYTES : 0u);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(value_cache + base, live ? PAGE_BYTES : 0u);
-      if constexpr (CF == FMT_I8) {
-        // fp32 scales of keys 8 q4 .. 8 q4 + 7 of this (block, head) page.
-        const size_t srow = ((size_t)phys * Hkv + g) * kPage;
-        const uint32_t sbytes = live ? kPage * 4 : 0u;
-        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(key_scales + srow, sbytes);
-        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(value_scales + srow, sbytes);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          Pg.ks[h] = __builtin_bit_cast(f32x4, buf_load16(ksr, 32 * q4 + 16 * h, 0));
-          Pg.vs[h] = __builtin_bit_cast(f32x4, buf_load16(vsr, 32 * q4 + 16 * h, 0));
-        }
-      }
-      if constexpr (byte_fmt(CF)) {
-#pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) Pg.k[j] = buf_load16<kCacheNT>(kr, k_lane, j * K_J);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int j = 0; j < KSTEPS; ++j)
-            Pg.k[kt][j] = stream_k ? load8<CF, kCacheNT>(kr, k_lane, j * K_J + kt * K_KT)
-                                   : load8<CF>(kr, k_lane, j * K_J + kt * K_KT);
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) Pg.v[n] = load8<CF, kCacheNT>(vr, v_lane, n * V_N);
+      load_page<D, CF>(Pg, key_cache, value_cache, key_scales, value_scales,
+                       __builtin_amdgcn_readlane(pid_lane, live ? k & 63 : 0), live, lane, stream_k);
     };
-
-    // K operand of key tile kt, k-step j.
-    auto k_operand = [&](const PageRegs<D, CF>& Pg, int kt, int j) -> vec {
-      if constexpr (byte_fmt(CF)) {
-        Raw8<CF> r;
-        r.w = kt == 0 ? u32x2{Pg.k[j][0], Pg.k[j][1]} : u32x2{Pg.k[j][2], Pg.k[j][3]};
-        return as_operand<CF, AF>(r);
-      } else {
-        return as_operand<CF, AF>(Pg.k[kt][j]);
-      }
-    };
-
-    // Set element e (0..7, any lane-varying value) of a lane's eight
-    // consecutive cache elements.  Register arrays are only ever indexed by
-    // constants (a runtime index would move them to scratch memory).
-    auto set_elem = [&](auto& raw, int e, uint32_t x) {
-      constexpr int EPW = byte_fmt(CF) ? 4 : 2;   // elements per word
-      constexpr int BITS = 32 / EPW;
-      constexpr uint32_t EMASK = (1u << BITS) - 1u;
-      const int sh = BITS * (e % EPW);
-      const uint32_t keep = ~(EMASK << sh);
-      const uint32_t put = (x & EMASK) << sh;
-#pragma unroll
-      for (int w = 0; w < 8 / EPW; ++w)
-        if (w == e / EPW) raw[w] = (raw[w] & keep) | put;
-    };
-
-    auto compute_page = [&](PageRegs<D, CF>& Pg, int k) {
-      const int base = (pa + wave + W * k) * kPage;
-      // The page holding the appended row (a wave-uniform test): put the row
-      // into the page registers.  Key row_new is row row_new % 16 of key
-      // tile row_new / 16 (16-bit) or row row_new / 2 of tile row_new % 2
-      // (bytes); in V it is element row_new % 8 of lane group row_new / 8.
-      if (wave == w_new && k == k_new) {
-        const int kt_new = kContig ? row_new >> 4 : row_new & 1;
-        if (col == (kContig ? row_new & 15 : row_new >> 1)) {
-#pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) {
-            const u32x4 nk = *reinterpret_cast<const u32x4*>(&newk_lds[8 * (q4 + 4 * j)]);
-            if constexpr (byte_fmt(CF)) {
-              // The codes were staged one per 16-bit slot: pack eight into
-              // two words.
-              u32x2 c;
-#pragma unroll
-              for (int w = 0; w < 2; ++w)
-                c[w] = (nk[2 * w] & 0xffu) | ((nk[2 * w] >> 8) & 0xff00u) |
-                       ((nk[2 * w + 1] & 0xffu) << 16) | ((nk[2 * w + 1] << 8) & 0xff000000u);
-              if (kt_new == 0) {
-                Pg.k[j][0] = c[0];
-                Pg.k[j][1] = c[1];
-              } else {
-                Pg.k[j][2] = c[0];
-                Pg.k[j][3] = c[1];
-              }
-            } else {
-#pragma unroll
-              for (int kt = 0; kt < 2; ++kt)
-                if (kt == kt_new) Pg.k[kt][j].w = nk;
-            }
-          }
-        }
-        if (q4 == (row_new >> 3)) {
-#pragma unroll
-          for (int n = 0; n < NT; ++n) set_elem(Pg.v[n].w, row_new & 7, newv_lds[16 * n + col]);
-          if constexpr (CF == FMT_I8) {
-            // The row's scales, as the patched codes were encoded with.
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (e == (row_new & 7)) {
-                Pg.ks[e >> 2][e & 3] = new_ks;
-                Pg.vs[e >> 2][e & 3] = new_vs;
-              }
-            }
-          }
-        }
-      }
-      // Rows past the context end may hold anything (NaN included): their
-      // scores are masked below, and their V elements are zeroed here, since
-      // a zero probability times NaN is still NaN.  (A wave-uniform test.)
-      const bool partial = base + kPage > L;
-      if (partial) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (base + 8 * q4 + e >= L) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) set_elem(Pg.v[n].w, e, 0u);
-            if constexpr (CF == FMT_I8) Pg.vs[e >> 2][e & 3] = 0.f;  // stale scale
-          }
-        }
-      }
-
-      // S^T = K Q^T; element (kt, r) of lane (q4, col) is key 8 q4 + 2r + kt.
-      f32x4 st[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) st[kt] = Mfma<AF>::mma(k_operand(Pg, kt, j), qb[j], st[kt]);
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) st[kt] *= qk_scale_log2;
-      if constexpr (CF == FMT_I8) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) st[kt][r] *= Pg.ks[r >> 1][2 * (r & 1) + kt];
-      }
-      // Element (kt, r) of a lane is key 16 kt + 4 q4 + r (16-bit) or
-      // 8 q4 + 2 r + kt (bytes).
-      auto key_of = [&](int kt, int r) {
-        return kContig ? 16 * kt + 4 * q4 + r : 8 * q4 + 2 * r + kt;
-      };
-      if (partial) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (base + key_of(kt, r) >= L) st[kt][r] = -INFINITY;
-      }
-      const float lmax = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
-                               fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
-      // The reference max only moves when some score exceeds it by more than
-      // kRescaleSlack (log2 units); it is then raised to the max over the
-      // four lanes that hold each head, so all of a head's lanes agree.
-      if (__builtin_amdgcn_ballot_w64(lmax > m_run + kRescaleSlack) != 0) {
-        float cm = fmaxf(lmax, shfl_xor_f(lmax, 16));
-        cm = fmaxf(cm, shfl_xor_f(cm, 32));
-        const float m_new = fmaxf(m_run, cm);
-        const float alpha = fast_exp2(m_run - m_new);
-#pragma unroll
-        for (int n = 0; n <= NT; ++n) o_acc[n] *= alpha;
-        m_run = m_new;
-      }
-      // P as the B operand of O^T = V^T P^T: lane (q4, col) must hold the
-      // probabilities of keys 8 q4 .. 8 q4 + 7, the tokens of its V operand.
-      f32x8 pv;
-      vec pb_l;
-      if constexpr (kContig) {
-        // The lane holds keys 4 q4 + r (words x0, x1) and 16 + 4 q4 + r (y0,
-        // y1).  With X_g / Y_g the words of lane group q4 = g, the target
-        // groups hold (X0 X1), (X2 X3), (Y0 Y1), (Y2 Y3): a swap of the two
-        // lane halves between X and Y, then of odd and even lane groups.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pv[4 * kt + r] = fast_exp2(st[kt][r] - m_run);
-        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_convertvector(pv, vec));
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const auto h = __builtin_amdgcn_permlane32_swap(w[i], w[2 + i], false, false);
-          const auto q = __builtin_amdgcn_permlane16_swap(h[0], h[1], false, false);
-          o[i] = q[0];       // keys 8 q4 + 2i, + 1
-          o[2 + i] = q[1];   // keys 8 q4 + 4 + 2i, + 1
-        }
-        pb_l = __builtin_bit_cast(vec, o);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) pv[2 * r + kt] = fast_exp2(st[kt][r] - m_run);
-        pb_l = __builtin_convertvector(pv, vec);
-      }
-      // l += 1^T P^T.
-      o_acc[NT] = Mfma<AF>::mma(ones, pb_l, o_acc[NT]);
-      // O^T += V^T P^T; with INT8 each key's V scale goes into its P.
-      vec pb = pb_l;
-      if constexpr (CF == FMT_I8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] *= Pg.vs[e >> 2][e & 3];
-        pb = __builtin_convertvector(pv, vec);
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) o_acc[n] = Mfma<AF>::mma(as_operand<CF, AF>(Pg.v[n]), pb, o_acc[n]);
+    auto step = [&](PageRegs<D, CF>& Pg, int k) {
+      compute_page<D, G, CF, AF>(Pg, m_run, o_acc, qb, ones, (pa + wave + W * k) * kPage, L,
+                                 wave == w_new && k == k_new, row_new, newk_lds, newv_lds, new_ks,
+                                 new_vs, qk_scale_log2, lane);
     };
 
     // Two register buffers: page k is computed while page k + 1 loads.
     PageRegs<D, CF> A, Bf;
-    load_page(0, A);
+    fetch(0, A);
     stage_new_row();
     for (int k = 0;;) {
-      load_page(k + 1, Bf);
-      compute_page(A, k);
+      fetch(k + 1, Bf);
+      step(A, k);
       if (++k >= npg) break;
-      load_page(k + 1, A);
-      compute_page(Bf, k);
+      fetch(k + 1, A);
+      step(Bf, k);
       if (++k >= npg) break;
     }
   } else {
     stage_new_row();
   }
 
-  // Combine the W waves through LDS.  Lane (q4, col) holds O[head col]
-  // [dim 16n + 4 q4 + r] and l in every row of the ones tile; waves without
-  // pages contribute (-inf, 0, 0).
-  if (col < G) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o_lds[wave][col][16 * n + 4 * q4 + r] = o_acc[n][r];
-    if (q4 == 0) {
-      m_lds[wave][col] = m_run;
-      l_lds[wave][col] = o_acc[NT][0];
-    }
-  }
+  // Combine the W waves through LDS; waves without pages contribute
+  // (-inf, 0, 0).
+  put_wave_partial<D, G>(o_lds[wave], m_lds[wave], l_lds[wave], o_acc, m_run, lane);
   __syncthreads();
   for (int i = threadIdx.x; i < G * D; i += 64 * W) {
     const int h = i / D;
     const int d = i - h * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, m_lds[w][h]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float mw = m_lds[w][h];
-        const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-        num = fmaf(f, o_lds[w][h][d], num);
-        den = fmaf(f, l_lds[w][h], den);
-      }
-    }
+    float M, num, den;
+    combine_waves<W>(&m_lds[0][h], &l_lds[0][h], &o_lds[0][h][d], G, G * D, M, num, den);
     if (S == 1) {
       out[((size_t)b * Hq + g * G + h) * D + d] = static_cast<uint16_t>(f32_to_16<AF>(num * (v_scale / den)));
     } else {
@@ -699,29 +791,478 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                       ((size_t)b * Hq + g * G + h) * S, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Balanced mode: the pages of the whole batch, item (b, g) = b * Hkv + g
+// after item b * Hkv + g - 1, are cut into equal ranges of c pages, one per
+// workgroup, so that every CU reads the same number of bytes whatever the
+// mix of context lengths.  A range covers the tail of one item, whole items
+// and the head of another; its waves take the range's pages round-robin
+// (switching query and softmax state where an item ends) and their partials
+// are combined per item through LDS.  An item wholly inside a range is
+// written straight to the output; an item cut by range boundaries is
+// combined across its workgroups through the workspace (as the splits of
+// grid mode).  Items are handled in rounds of at most SEGS items (the LDS
+// holds one partial per wave and item of a round).
+
+constexpr int kMaxBalancedB = 1024;
+
+template <int D, int G, int W>
+constexpr int balanced_segs() {
+  constexpr int s = 98304 / (W * G * D * 4);
+  return s < 1 ? 1 : (s > W ? W : s);
+}
+
+template <int D, int G, int CF, int AF, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_balanced(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
+    uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int B,
+    int Hkv, int MBPS, int window, int Smax, int stream_k, float qk_scale_log2, float v_scale,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+    int* __restrict__ ws_count, const uint16_t* __restrict__ new_key,
+    const uint16_t* __restrict__ new_value, float k_enc_scale, float v_enc_scale,
+    float* __restrict__ key_scales, float* __restrict__ value_scales) {
+  static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
+  static_assert(G >= 1 && G <= 16, "group");
+  constexpr int SEGS = balanced_segs<D, G, W>();
+  constexpr int KSTEPS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int DPL = (D + 63) / 64;       // row elements per lane
+  constexpr int QCH = G * D / 8;           // 16-byte chunks of one item's queries
+  constexpr int QPT = (SEGS * QCH + 64 * W - 1) / (64 * W);
+  typedef typename Mfma<AF>::vec vec;
+
+  __shared__ int pref[kMaxBalancedB + 1];  // pages of sequences 0 .. b-1 (per KV head)
+  __shared__ int ctx_lds[kMaxBalancedB];
+  __shared__ int wsum[W];
+  __shared__ int pmax_lds;
+  __shared__ float m_lds[SEGS][W][G];
+  __shared__ float l_lds[SEGS][W][G];
+  __shared__ __attribute__((aligned(16))) float o_lds[SEGS][W][G][D];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[SEGS][G * D];
+  __shared__ __attribute__((aligned(16))) uint16_t newk_lds[SEGS][D];
+  __shared__ __attribute__((aligned(16))) uint16_t newv_lds[SEGS][D];
+  __shared__ float nks_lds[SEGS];
+  __shared__ float nvs_lds[SEGS];
+  __shared__ int seg_off[SEGS];    // first flat page of the item
+  __shared__ int seg_len[SEGS];    // tokens the item attends to
+  __shared__ int seg_new[SEGS];    // its appended row, when this range stores it, else -1
+  __shared__ int seg_n[SEGS];      // workgroups sharing the item (0: no pages here)
+  __shared__ int seg_slot[SEGS];   // this workgroup's partial among them
+  __shared__ int seg_last[SEGS];
+  __shared__ uint32_t pid_tab[64 * W];   // page ids of the round's pages
+  __shared__ int seg_tab[64 * W];        // and their segments
+  __shared__ int next_page;              // next unclaimed page of the round
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int Hq = Hkv * G;
+  const int N = gridDim.x;
+  const int wg = blockIdx.x;
+
+  // Pages per sequence (min(len, window) tokens) and their prefix sums.
+  if (threadIdx.x == 0) {
+    pref[0] = 0;
+    pmax_lds = 0;
+  }
+  __syncthreads();
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 64 * W) {
+    const int bi = b0 + (int)threadIdx.x;
+    int P = 0;
+    if (bi < B) {
+      const int ctx = context_lens[bi];
+      ctx_lds[bi] = ctx;
+      const int L = window > 0 ? min(ctx, window) : ctx;
+      P = L > 0 ? (L + kPage - 1) / kPage : 0;
+    }
+    int x = P, mx = P;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+      mx = max(mx, __shfl_xor(mx, o, 64));
+    }
+    if (lane == 63) wsum[wave] = x;
+    if (lane == 0) atomicMax(&pmax_lds, mx);
+    __syncthreads();
+    int before = carry, tot = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const int v = wsum[w];
+      if (w < wave) before += v;
+      tot += v;
+    }
+    if (bi < B) pref[bi + 1] = before + x;
+    carry += tot;
+    __syncthreads();
+  }
+  const int T = Hkv * pref[B];           // pages of the batch (host: < 2^31)
+  // Range size: equal shares of N, at least one page per wave, few enough
+  // workgroups per item for the workspace (Smax partials), and a multiple of
+  // W.
+  int c = (T + N - 1) / N;
+  c = max(c, (pmax_lds + Smax - 2) / (Smax - 1));
+  c = max(c, W);
+  c = (c + W - 1) / W * W;  // every wave of a one-round range gets c / W pages
+
+  // Sequences with no context get zeros (their items hold no pages).
+  for (int b = wg; b < B; b += N) {
+    if (ctx_lds[b] <= 0)
+      for (int i = threadIdx.x; i < Hq * D; i += 64 * W) out[(size_t)b * Hq * D + i] = 0;
+  }
+  if ((long long)wg * c >= T) return;
+  const int x0 = wg * c;
+  const int x1 = min(x0 + c, T);
+
+  // The items holding flat pages x0 and x1 - 1: in the last sequence whose
+  // pages start at or before the page (the prefix sums do not decrease, so
+  // the sequences that start at or before it are a prefix, counted with
+  // ballots), then the head within it.
+  int n0 = 0, n1 = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int v = b < B ? Hkv * pref[b] : T;
+    n0 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v <= x0));
+    n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v <= x1 - 1));
+  }
+  auto item_at = [&](int b, int x) {
+    return b * Hkv + (x - Hkv * pref[b]) / (pref[b + 1] - pref[b]);
+  };
+  const int i_first = item_at(n0 - 1, x0);
+  const int i_end = item_at(n1 - 1, x1 - 1) + 1;
+  const vec ones = ones_operand<AF>();
+
+  for (int i0 = i_first; i0 < i_end; i0 += SEGS) {
+    const int nseg = min(SEGS, i_end - i0);
+    // Opaque copies of the thread index and of the divisors: what the
+    // round's set-up derives from them is recomputed each round, not held in
+    // registers across the page loop.
+    int tid = threadIdx.x, hkv = Hkv, cr = c, win = window;
+    asm volatile("" : "+v"(tid), "+s"(hkv), "+s"(cr), "+s"(win));
+    const int ln = tid & 63;
+    // Lane s < nseg describes segment s, item i0 + s: its first flat page
+    // soff, its length sL (tokens to attend), the flat pages [slo, shi) of
+    // it in this range, and the cache row of the appended token when this
+    // workgroup holds that row's page (snew, else -1).
+    int soff = 0, sL = 0, slo = 0, shi = 0, snew = -1;
+    if (ln < nseg) {
+      const int i = i0 + ln;
+      const int sb = i / hkv;
+      const int sg = i - sb * hkv;
+      const int P = pref[sb + 1] - pref[sb];
+      const int ctx = ctx_lds[sb];
+      soff = hkv * pref[sb] + sg * P;
+      sL = win > 0 ? min(ctx, win) : ctx;
+      slo = max(x0, soff);
+      shi = min(x1, soff + P);
+      if (new_key != nullptr && shi > slo) {
+        const int r = win > 0 ? (ctx - 1) % win : ctx - 1;
+        if (soff + r / kPage >= slo && soff + r / kPage < shi) snew = r;
+      }
+      if (wave == 0) {
+        seg_off[ln] = soff;
+        seg_len[ln] = sL;
+        seg_new[ln] = snew;
+        seg_n[ln] = shi > slo ? (soff + P - 1) / cr - soff / cr + 1 : 0;
+        seg_slot[ln] = wg - soff / cr;
+      }
+    }
+    const int rs = __builtin_amdgcn_readlane(slo, 0);
+    const int re = __builtin_amdgcn_readlane(shi, nseg - 1);
+
+    // Pages of the round, rs + k for k < span.  Wave w starts on page w;
+    // from then on each wave claims the next unclaimed page (an LDS
+    // counter), so waves that are served faster take more pages and all
+    // finish close together.  Thread k tabulates page k's segment and page id
+    // (block * Hkv + head) for the claims; a wave's first page is looked up
+    // by the wave itself.
+    const int span = re - rs;  // <= 64 * W (host plan)
+    auto page_info = [&](int k, int& seg) -> uint32_t {
+      const int p = rs + k;
+      int s = 0, po = __builtin_amdgcn_readlane(soff, 0);
+#pragma unroll
+      for (int t = 1; t < SEGS; ++t) {
+        const int so = __builtin_amdgcn_readlane(soff, t);
+        if (t < nseg && p >= so) {
+          s = t;
+          po = so;
+        }
+      }
+      const int i = i0 + s;
+      const int b = i / hkv;
+      const int j = p - po;
+      const int phys = block_tables ? block_tables[(size_t)b * MBPS + j] : b * MBPS + j;
+      seg = s;
+      return (uint32_t)phys * hkv + (i - b * hkv);
+    };
+    int tab_seg = 0;
+    uint32_t tab_pid = 0;
+    if (tid < span) tab_pid = page_info(tid, tab_seg);
+    int first_seg = 0;
+    uint32_t first_pid = 0;
+    if (wave < span) first_pid = __builtin_amdgcn_readfirstlane(page_info(wave, first_seg));
+
+    // Queries of the round's items, bound for LDS.
+    u32x4 qv[QPT];
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int t = tid + 64 * W * u;
+      qv[u] = u32x4{0u, 0u, 0u, 0u};
+      if (t < nseg * QCH) {
+        const int s = t / QCH;
+        const int i = i0 + s;
+        const int b = i / hkv;
+        qv[u] = *reinterpret_cast<const u32x4*>(
+            query + ((size_t)b * Hq + (i - b * hkv) * G) * D + 8 * (t - s * QCH));
+      }
+    }
+    // Append: wave s stores segment s's new row if this range holds its
+    // page.  Its loads go out now, its stores after the first page's loads.
+    const int my_new = wave < nseg ? __builtin_amdgcn_readlane(snew, wave) : -1;
+    uint16_t krow[DPL], vrow[DPL];
+    int new_phys = 0;
+    if (my_new >= 0) {
+      const int i = i0 + wave;
+      const int b = i / hkv;
+      const size_t src = (size_t)i * D;  // new_key [B][Hkv][D]
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) {
+        const int d = ln + 64 * u;
+        krow[u] = d < D ? new_key[src + d] : 0;
+        vrow[u] = d < D ? new_value[src + d] : 0;
+      }
+      new_phys = block_tables ? block_tables[(size_t)b * MBPS + my_new / kPage]
+                              : b * MBPS + my_new / kPage;
+    }
+
+    auto fetch = [&](uint32_t pid, bool live, PageRegs<D, CF>& Pg) {
+      load_page<D, CF>(Pg, key_cache, value_cache, key_scales, value_scales, pid, live, lane,
+                       stream_k != 0);
+    };
+    PageRegs<D, CF> A, Bf;
+    if (wave < span) fetch(first_pid, true, A);
+
+    // Queries to LDS, empty partial slots, the appended rows; then one
+    // barrier (LDS only: the global stores need not have completed).
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int t = tid + 64 * W * u;
+      if (t < nseg * QCH) *reinterpret_cast<u32x4*>(&q_lds[0][0] + 8 * t) = qv[u];
+    }
+    for (int t = tid; t < SEGS * W * G; t += 64 * W) (&m_lds[0][0][0])[t] = -INFINITY;
+    if (tid < span) {
+      pid_tab[tid] = tab_pid;
+      seg_tab[tid] = tab_seg;
+    }
+    if (tid == 0) next_page = W;
+    if (my_new >= 0) {
+      const int i = i0 + wave;
+      const int row = my_new % kPage;
+      const uint32_t pid = (uint32_t)new_phys * hkv + (i - (i / hkv) * hkv);
+      const size_t page = (size_t)pid * kPage * D;
+      float kes = k_enc_scale, ves = v_enc_scale;
+      if constexpr (CF == FMT_I8) {
+        // Row scales, amax / 127 as the writer computes them.
+        float ka = 0.f, va = 0.f;
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) {
+          ka = fmaxf(ka, fabsf(lo16_to_f32<AF>(krow[u])));
+          va = fmaxf(va, fabsf(lo16_to_f32<AF>(vrow[u])));
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          ka = fmaxf(ka, shfl_xor_f(ka, m));
+          va = fmaxf(va, shfl_xor_f(va, m));
+        }
+        kes = __fdiv_rn(ka, 127.f);
+        ves = __fdiv_rn(va, 127.f);
+        if (ln == 0) {
+          key_scales[(size_t)pid * kPage + row] = kes;
+          value_scales[(size_t)pid * kPage + row] = ves;
+          nks_lds[wave] = kes;
+          nvs_lds[wave] = ves;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) {
+        const int d = ln + 64 * u;
+        if (d < D) {
+          const uint32_t kq = encode_elem<CF, AF>(krow[u], kes);
+          const uint32_t vq = encode_elem<CF, AF>(vrow[u], ves);
+          store_row_elem<CF>(key_cache, value_cache, page, row, d, kq, vq);
+          newk_lds[wave][d] = static_cast<uint16_t>(kq);
+          newv_lds[wave][d] = static_cast<uint16_t>(vq);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    if (wave < span) {
+      float m_run = -INFINITY;
+      f32x4 o_acc[NT + 1];
+      vec qb[KSTEPS];
+      int cur = -1, cur_off = 0, cur_L = 0, cur_new = -1;
+      float cur_ks = 0.f, cur_vs = 0.f;
+      auto flush = [&]() {
+        put_wave_partial<D, G>(o_lds[cur][wave], m_lds[cur][wave], l_lds[cur][wave], o_acc,
+                               m_run, lane);
+      };
+      // Claim the next page: its round index (>= span: none left).
+      auto claim = [&]() {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&next_page, 1);
+        return __builtin_amdgcn_readfirstlane(k);
+      };
+      auto step = [&](PageRegs<D, CF>& Pg, int k, int s) {
+        if (s != cur) {
+          // A new item: keep the last one's partial, take this one's query.
+          if (cur >= 0) flush();
+          cur = s;
+          m_run = -INFINITY;
+#pragma unroll
+          for (int n = 0; n <= NT; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+          q_operand<D, G, AF>(qb, q_lds[s], lane);
+          cur_off = __builtin_amdgcn_readfirstlane(seg_off[s]);
+          cur_L = __builtin_amdgcn_readfirstlane(seg_len[s]);
+          cur_new = __builtin_amdgcn_readfirstlane(seg_new[s]);
+          if constexpr (CF == FMT_I8) {
+            if (cur_new >= 0) {
+              cur_ks = nks_lds[s];
+              cur_vs = nvs_lds[s];
+            }
+          }
+        }
+        const int j = rs + k - cur_off;
+        compute_page<D, G, CF, AF>(Pg, m_run, o_acc, qb, ones, j * kPage, cur_L,
+                                   cur_new >= 0 && j == cur_new / kPage, cur_new % kPage,
+                                   newk_lds[cur], newv_lds[cur], cur_ks, cur_vs, qk_scale_log2,
+                                   lane);
+      };
+      // Two register buffers: the current page is computed while the next
+      // claimed one loads.
+      int k = wave, s = __builtin_amdgcn_readfirstlane(first_seg);
+      for (;;) {
+        const int kn = claim();
+        const bool more = kn < span;
+        const int sn = more ? __builtin_amdgcn_readfirstlane(seg_tab[kn]) : 0;
+        fetch(more ? __builtin_amdgcn_readfirstlane(pid_tab[kn]) : 0u, more, Bf);
+        step(A, k, s);
+        if (!more) break;
+        k = kn;
+        s = sn;
+        const int km = claim();
+        const bool more2 = km < span;
+        const int sm = more2 ? __builtin_amdgcn_readfirstlane(seg_tab[km]) : 0;
+        fetch(more2 ? __builtin_amdgcn_readfirstlane(pid_tab[km]) : 0u, more2, A);
+        step(Bf, k, s);
+        if (!more2) break;
+        k = km;
+        s = sm;
+      }
+      flush();
+    }
+    __syncthreads();
+
+    // Combine each item's wave partials: the output when the item is
+    // wholly in this range, else this workgroup's partial in the workspace.
+    bool shared = false;
+    tid = threadIdx.x;
+    hkv = Hkv;
+    asm volatile("" : "+v"(tid), "+s"(hkv));
+    for (int t = tid; t < nseg * G * D; t += 64 * W) {
+      const int s = t / (G * D);
+      const int h = (t / D) % G;
+      const int d = t % D;
+      const int n = seg_n[s];
+      if (n == 0) continue;
+      const int i = i0 + s;
+      const int b = i / hkv;
+      const size_t head = (size_t)b * Hq + (i - b * hkv) * G + h;
+      float M, num, den;
+      combine_waves<W>(&m_lds[s][0][h], &l_lds[s][0][h], &o_lds[s][0][h][d], G, G * D, M, num,
+                       den);
+      if (n == 1) {
+        out[head * D + d] = static_cast<uint16_t>(f32_to_16<AF>(num * (v_scale / den)));
+      } else {
+        const size_t row = head * Smax + seg_slot[s];
+        ws_store(ws_o + row * D + d, num);
+        if (d == 0) {
+          ws_store(ws_m + row, M);
+          ws_store(ws_l + row, den);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SEGS; ++s) shared |= s < nseg && seg_n[s] > 1;
+    if (shared) {
+      // Count this workgroup in on every cut item; the last of an item's
+      // workgroups to arrive merges its partials.  Counters are back at
+      // zero when the launch ends.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid < nseg) {
+        const int s = tid;
+        const int n = seg_n[s];
+        int last = 0;
+        if (n > 1) {
+          int* cnt = ws_count + i0 + s;
+          const int arrived =
+              __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last = arrived == n - 1;
+          if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        seg_last[s] = last;
+      }
+      __syncthreads();
+      for (int t = wave; t < nseg * G; t += W) {
+        const int s = t / G;
+        if (!seg_last[s]) continue;
+        const int i = i0 + s;
+        const int b = i / hkv;
+        const size_t head = (size_t)b * Hq + (i - b * hkv) * G + (t - s * G);
+        merge_head<D, AF>(out + head * D, seg_n[s], v_scale, ws_m, ws_l, ws_o, head * Smax, lane);
+      }
+    }
+    __syncthreads();  // the LDS is reused by the next round
+  }
+}
+
+template <int D, int G, int CF, int AF, int W>
+hipError_t launch_mode(const DecodeArgs& a, float qk, float vs, hipStream_t stream) {
+  if (a.N > 0) {
+    // Balanced mode is planned for byte-format caches only.
+    if constexpr (byte_fmt(CF)) {
+      hipLaunchKernelGGL((decode_balanced<D, G, CF, AF, W>), dim3(a.N), dim3(64 * W), 0, stream,
+                         (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
+                         (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.B, a.Hkv,
+                         a.MBPS, a.window, a.S, a.stream_k, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                         a.ws_count, (const uint16_t*)a.new_key, (const uint16_t*)a.new_value,
+                         a.k_scale, a.v_scale, a.key_scales, a.value_scales);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    hipLaunchKernelGGL((decode_split<D, G, CF, AF, W>), dim3(a.S, a.Hkv, a.B), dim3(64 * W), 0,
+                       stream, (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
+                       (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv, a.MBPS,
+                       a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
+                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
+                       a.v_scale, a.key_scales, a.value_scales);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int G, int CF, int AF>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const float qk = a.softmax_scale * (CF == FMT_E4M3 ? a.k_scale : 1.f) * LOG2E;
   const float vs = CF == FMT_E4M3 ? a.v_scale : 1.f;
-  dim3 grid(a.S, a.Hkv, a.B);
-  if (a.W == 8) {
-    hipLaunchKernelGGL((decode_split<D, G, CF, AF, 8>), grid, dim3(512), 0, stream,
-                       (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
-                       (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
-                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
-                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
-                       a.v_scale, a.key_scales, a.value_scales);
-  } else if (a.W == 4) {
-    hipLaunchKernelGGL((decode_split<D, G, CF, AF, 4>), grid, dim3(256), 0, stream,
-                       (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
-                       (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv,
-                       a.MBPS, a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
-                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
-                       a.v_scale, a.key_scales, a.value_scales);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.W == 8) return launch_mode<D, G, CF, AF, 8>(a, qk, vs, stream);
+  if (a.W == 4) return launch_mode<D, G, CF, AF, 4>(a, qk, vs, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int D, int G>

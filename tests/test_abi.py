@@ -128,6 +128,21 @@ def test_workspace_query():
         2 * rnd(2 * 8 * 2 * 4) + rnd(2 * 8 * 2 * 128 * 4) + rnd(2 * 2 * 4)
     assert lib.pa_decode_workspace_bytes(2, 8, 2, 128, 100, 0, 33) == (1 << 64) - 1
     assert lib.pa_decode_workspace_bytes(-1, 8, 2, 128, 100, 0, 0) == (1 << 64) - 1
+    # From 1024 tokens the byte-format plan (equal page ranges over the batch)
+    # keeps 16 partial slots per (sequence, query head); the 16-bit plan for
+    # 32 x 8 KV heads is one pass, so the query returns the former.
+    rows = 32 * 32 * 16
+    assert lib.pa_decode_workspace_bytes(32, 32, 8, 128, 4096, 0, 0) == \
+        2 * rnd(rows * 4) + rnd(rows * 128 * 4) + rnd(32 * 8 * 4)
+    # Longer contexts: more slots, so that no range exceeds 64 pages per wave
+    # (65536 tokens = 2048 pages: ceil(2048 / 512) + 1 = 5 < 16, still 16;
+    # 2^20 tokens = 32768 pages: 64 + 1 = 65 slots).
+    rows = 1 * 8 * 65
+    assert lib.pa_decode_workspace_bytes(1, 8, 8, 64, 1 << 20, 0, 0) >= \
+        2 * rnd(rows * 4) + rnd(rows * 64 * 4) + rnd(8 * 4)
+    # Above 1024 sequences only the grid plan applies.
+    n16 = lib.pa_decode_workspace_bytes(2048, 8, 8, 64, 4096, 0, 0)
+    assert n16 == 0
 
 
 @needs_lib

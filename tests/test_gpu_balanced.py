@@ -1,0 +1,186 @@
+"""GPU parity of the length-balanced decode: the automatic plan for E4M3
+and INT8 caches once the longest context reaches 1024 tokens and B <= 1024.
+
+Balanced mode cuts the batch's pages into equal ranges, one per workgroup,
+so a range may hold the tail of one (sequence, KV head), whole ones and the
+head of another; cut items are merged across workgroups in the launch.
+The cases aim at every path of that scheme:
+
+* mixed lengths (items cut by range boundaries, merged through the
+  workspace);
+* many short sequences around one long one, with group sizes whose LDS
+  holds few items per round (G = 8 and 16 at D = 128), so that ranges take
+  several rounds;
+* sequences with no context inside the batch (zeros, no pages);
+* one long sequence (every item cut into many ranges);
+* rolling-buffer rings, both byte formats, every group size, fp16 and bf16
+  activations;
+* the fused append (the new row's page may sit in any range).
+
+Each output is compared with the oracle (fp64 attention over the same
+cache contents) within the cache format's tolerance, and the pools after an
+append bit for bit with the oracle's writer.  Repeated launches on one
+workspace must give bitwise equal outputs (the arrival counters return to
+zero).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paritylib as P
+from paged_kv_cache_175_amd import ops, pool
+from paged_kv_cache_175_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _short_around_long(name, seed, n_short, long_len, Hq, Hkv, D, act="bf16", cache=None,
+                       zeros=0):
+    """n_short contexts of 1..64 tokens and one of long_len, shuffled; then
+    `zeros` of the short ones get no context at all (context_lens 0)."""
+    rng = np.random.default_rng(seed)
+    ctx = [int(x) for x in rng.permutation(list(rng.integers(1, 65, size=n_short)) + [long_len])]
+    wl = W.decode_workload(name, seed, B=len(ctx), Hq=Hq, Hkv=Hkv, D=D, act=act, cache=cache,
+                           ctx=ctx)
+    short = [b for b in range(wl.B) if ctx[b] != long_len]
+    wl.context_lens[rng.choice(short, size=zeros, replace=False)] = 0
+    return wl
+
+
+CASES = {
+    "mix_g4_d128": lambda: W.decode_workload("bal_mix", 101, B=12, Hq=32, Hkv=8, D=128,
+                                             act="bf16", cache="e4m3", ctx_range=(1, 2200)),
+    "short_around_long_g4_d64": lambda: _short_around_long("bal_short_g4", 102, 150, 1100,
+                                                           Hq=8, Hkv=2, D=64, cache="e4m3",
+                                                           zeros=3),
+    "short_around_long_g8_d128": lambda: _short_around_long("bal_short_g8", 103, 60, 1500,
+                                                            Hq=16, Hkv=2, D=128, cache="e4m3"),
+    "short_around_long_g16_f16": lambda: _short_around_long("bal_short_g16", 104, 40, 1300,
+                                                            Hq=16, Hkv=1, D=128, act="f16",
+                                                            cache="e4m3", zeros=2),
+    "one_long_g2_d96": lambda: W.decode_workload("bal_one_long", 105, B=1, Hq=8, Hkv=4, D=96,
+                                                 act="bf16", cache="e4m3", ctx=[2000]),
+    "mha_d64_f16": lambda: W.decode_workload("bal_mha", 106, B=7, Hq=4, Hkv=4, D=64, act="f16",
+                                             cache="e4m3", ctx_range=(1, 1400)),
+    "ring_g4_d128": lambda: W.decode_workload("bal_e4m3_ring", 107, B=6, Hq=32, Hkv=8, D=128,
+                                              act="bf16", cache="e4m3", window=1024,
+                                              pos_range=(0, 5000)),
+}
+
+
+def _check_decode(wl):
+    """Output against the oracle; sequences with no context must read zeros."""
+    kc, vc = P.hip_decode_setup(wl)
+    out = P.hip_decode(wl, kc, vc)
+    torch.cuda.synchronize()
+    got = P.out_f64(out)
+    seqs = [b for b in range(wl.B) if wl.context_lens[b] > 0]
+    assert np.all(got[[b for b in range(wl.B) if wl.context_lens[b] <= 0]] == 0)
+    okc, ovc = P.oracle_decode_setup(wl, seqs)
+    err = P.max_abs(got[seqs], P.oracle_decode(wl, okc, ovc, seqs))
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL[wl.cache]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_balanced_decode(name):
+    wl = CASES[name]()
+    P.say(f"[balanced decode] {name} B={wl.B} G={wl.Hq // wl.Hkv} D={wl.D} cache={wl.cache} "
+          f"window={wl.window} max={int(wl.context_lens.max())}")
+    _check_decode(wl)
+
+
+@pytest.mark.parametrize("name", ["mix_g4_d128", "short_around_long_g8_d128",
+                                  "one_long_g2_d96", "ring_g4_d128"])
+def test_balanced_decode_append(name):
+    wl = CASES[name]()
+    P.say(f"[balanced decode append] {name} B={wl.B} cache={wl.cache} window={wl.window}")
+    kc, vc = P.hip_decode_append_setup(wl)
+    out = P.hip_decode_append(wl, kc, vc)
+    torch.cuda.synchronize()
+    okc, ovc = P.oracle_decode_setup(wl)
+    assert np.array_equal(P.pool_bits(kc), okc), "key pool differs"
+    assert np.array_equal(P.pool_bits(vc), ovc), "value pool differs"
+    err = P.max_abs(P.out_f64(out), P.oracle_decode(wl, okc, ovc))
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL[wl.cache]
+
+
+I8_CASES = {
+    "i8_mix_g4_d128": lambda: W.decode_workload("bal_i8_mix", 111, B=9, Hq=32, Hkv=8, D=128,
+                                                act="bf16", cache="int8", ctx_range=(1, 1800)),
+    "i8_short_g8": lambda: _short_around_long("bal_i8_short", 112, 40, 1100, Hq=16, Hkv=2,
+                                              D=128, cache="int8"),
+    "i8_short_g16_d64": lambda: _short_around_long("bal_i8_short16", 114, 70, 1200, Hq=16,
+                                                   Hkv=1, D=64, cache="int8"),
+    "i8_ring_f16_d64": lambda: W.decode_workload("bal_i8_ring", 113, B=5, Hq=8, Hkv=4, D=64,
+                                                 act="f16", cache="int8", window=1024,
+                                                 pos_range=(500, 3000)),
+}
+
+
+@pytest.mark.parametrize("append", [False, True])
+@pytest.mark.parametrize("name", list(I8_CASES))
+def test_balanced_decode_int8(name, append):
+    wl = I8_CASES[name]()
+    P.say(f"[balanced decode int8] {name} append={append} B={wl.B} window={wl.window}")
+    if not append:
+        pools = P.hip_decode_setup_i8(wl)
+        out = P.hip_decode_i8(wl, pools)
+    else:
+        pools = P.gpu_pools_i8(wl)
+        ks_, vs_, sl = [], [], []
+        for b in range(wl.B):
+            n = wl.cached_k[b].shape[0]
+            if n:
+                pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+                sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+                ks_.append(wl.cached_k[b])
+                vs_.append(wl.cached_v[b])
+        P._gpu_write_i8(wl, pools, np.concatenate(ks_), np.concatenate(vs_), np.concatenate(sl))
+        kc, vc, ks, vs = pools
+        out = ops.decode(P._act_tensor(wl.query, wl.act), kc, vc,
+                         torch.from_numpy(wl.block_tables).cuda(),
+                         torch.from_numpy(wl.context_lens).cuda(), int(wl.context_lens.max()),
+                         wl.scale, window=wl.window, new_key=P._act_tensor(wl.new_k, wl.act),
+                         new_value=P._act_tensor(wl.new_v, wl.act), key_scales=ks,
+                         value_scales=vs)
+    torch.cuda.synchronize()
+    opools = P.oracle_decode_setup_i8(wl)
+    kc, vc, ks, vs = pools
+    okc, ovc, oks, ovs = opools
+    assert np.array_equal(P.pool_bits(kc), okc), "key codes differ"
+    assert np.array_equal(P.pool_bits(vc), ovc), "value codes differ"
+    assert np.array_equal(P.scale_bits(ks), oks.view(np.int32)), "key scales differ"
+    assert np.array_equal(P.scale_bits(vs), ovs.view(np.int32)), "value scales differ"
+    err = P.max_abs(P.out_f64(out), P.oracle_decode_i8(wl, opools))
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL["int8"]
+
+
+def test_balanced_repeat_same_workspace():
+    """Three launches on one workspace: bitwise equal outputs, so every cut
+    item's arrival counter was back at zero after each launch."""
+    wl = CASES["short_around_long_g8_d128"]()
+    P.say(f"[balanced repeat] B={wl.B}")
+    kc, vc = P.hip_decode_setup(wl)
+    q = P._act_tensor(wl.query, wl.act)
+    bt = torch.from_numpy(wl.block_tables).cuda()
+    cl = torch.from_numpy(wl.context_lens).cuda()
+    L = int(wl.context_lens.max())
+    ws = ops.alloc_workspace(ops.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, L), "cuda")
+    assert ws is not None
+    outs = [ops.decode(q, kc, vc, bt, cl, L, wl.scale, wl.k_scale, wl.v_scale, workspace=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    # The counters [B * Hkv] int32 open the workspace's last 256-byte aligned
+    # region; the rest of that region is padding that stays zero.
+    tail = -(-(4 * wl.B * wl.Hkv) // 256) * 256
+    assert int(ws[-tail:].count_nonzero()) == 0
+    okc, ovc = P.oracle_decode_setup(wl)
+    assert P.max_abs(P.out_f64(outs[0]), P.oracle_decode(wl, okc, ovc)) <= P.TOL[wl.cache]
