@@ -597,6 +597,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int b = blockIdx.z;
   const int Hq = Hkv * G;
 
+  // With one split per sequence a wave's pages are wave + W k whatever the
+  // context length, so its table entries are loaded alongside the length
+  // rather than after it (lane k: entry wave + W k, clamped to the row;
+  // entries past the sequence's pages are never used).
+  int bt_pre = 0;
+  if (S == 1 && block_tables != nullptr)
+    bt_pre = block_tables[(size_t)b * MBPS + min(wave + W * lane, MBPS - 1)];
   int L = context_lens[b];
   if (window > 0) L = min(L, window);
   if (L <= 0) {
@@ -721,7 +728,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // Without a table the map is the identity (block b * MBPS + j) and
     // nothing is loaded.
     const int lpg = pa + wave + W * (lane < npg ? lane : 0);
-    const int bt_lane = block_tables ? block_tables[(size_t)b * MBPS + lpg] : b * MBPS + lpg;
+    const int bt_lane = block_tables == nullptr ? b * MBPS + lpg
+                        : S == 1                ? bt_pre
+                                                : block_tables[(size_t)b * MBPS + lpg];
     const uint32_t pid_lane = (uint32_t)bt_lane * Hkv + g;
     const bool stream_k = S == 1;
     auto fetch = [&](int k, PageRegs<D, CF>& Pg) {
