@@ -107,7 +107,7 @@ def prefill_chunk(query_bits, act_fmt: str, cu_q_lens, key_cache, value_cache,
 
 def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_lens,
                          key_cache, value_cache, cache_fmt: str, block_tables, context_lens,
-                         scale: float, window: int, rows=None):
+                         scale: float, window: int, rows=None, k_scale=1.0, v_scale=1.0):
     """Chunked prefill of a sliding-window layer whose cache is a ring of
     ``window`` rows ("Rolling buffer cache", opening post: position i lives
     in ring row i mod W).
@@ -120,6 +120,14 @@ def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_le
     those before the chunk (``< ctx - C``) from the ring, the chunk's own
     from ``key_bits`` / ``value_bits`` (``[total_q, Hkv, D]``, packed like
     the queries).
+
+    A quantised ring is read as the cache stores it: E4M3 codes times the
+    per-tensor scales (``k_scale``, ``v_scale``; "PagedAttention in
+    mistral.rs", section "KV Cache Quantization"), INT8 codes times their
+    row's own scale (``k_scale`` / ``v_scale`` are then the scale pools;
+    "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build).  The chunk's own
+    K/V are the activations as given, not yet quantised (the same reading as
+    above: they are not in the cache yet).
 
     ``rows``: optionally, the (b, j) pairs to compute (the others stay 0),
     for spot checks of workloads too large to compute whole.
@@ -145,8 +153,17 @@ def prefill_chunk_window(query_bits, act_fmt: str, key_bits, value_bits, cu_q_le
                 if pos < start:
                     slot = slot_of(block_tables[b], pos % window, bs)
                     k_row, v_row = get_row(key_cache, value_cache, slot // bs, slot % bs)
-                    ks.append(bits_to_f64(k_row, cache_fmt))
-                    vs.append(bits_to_f64(v_row, cache_fmt))
+                    k_row, v_row = bits_to_f64(k_row, cache_fmt), bits_to_f64(v_row, cache_fmt)
+                    if cache_fmt == "e4m3":
+                        k_row = k_row * np.float64(np.float32(k_scale))
+                        v_row = v_row * np.float64(np.float32(v_scale))
+                    elif cache_fmt == "int8":
+                        k_row = k_row * np.asarray(k_scale[slot // bs, :, slot % bs],
+                                                   np.float64)[:, None]
+                        v_row = v_row * np.asarray(v_scale[slot // bs, :, slot % bs],
+                                                   np.float64)[:, None]
+                    ks.append(k_row)
+                    vs.append(v_row)
                 else:
                     ks.append(kn[q0 + pos - start])
                     vs.append(vn[q0 + pos - start])
