@@ -41,7 +41,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mistral_decode",
                     choices=["mistral_decode", "fp8_decode", "int8_decode", "sliding_decode",
-                             "tiny_decode", "prefix_prefill", "sliding_prefill", "cow_copy"])
+                             "tiny_decode", "prefix_prefill", "sliding_prefill",
+                             "sliding_prefill_fp8", "sliding_prefill_int8", "cow_copy"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for 2 GB)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--separate-write", action="store_true",
@@ -106,6 +107,8 @@ def _workload(name):
             "int8_decode": W.int8_decode,
             "sliding_decode": W.sliding_decode, "tiny_decode": W.tiny_decode,
             "prefix_prefill": W.prefix_prefill, "sliding_prefill": W.sliding_prefill,
+            "sliding_prefill_fp8": lambda: W.sliding_prefill(cache="e4m3"),
+            "sliding_prefill_int8": lambda: W.sliding_prefill(cache="int8"),
             "cow_copy": W.cow_copy}[name]()
 
 
@@ -439,8 +442,14 @@ def bench_window_prefill(wl, a, torch):
 
     dev = torch.device("cuda", 0)
     kshape, vshape = ops.pool_shapes(wl.pool_blocks, wl.Hkv, wl.D, wl.BS)
-    kc = torch.zeros(kshape, dtype=torch.bfloat16, device=dev)
-    vc = torch.zeros(vshape, dtype=torch.bfloat16, device=dev)
+    cache_dt = {"e4m3": torch.uint8, "int8": torch.int8}.get(wl.cache, torch.bfloat16)
+    kc = torch.zeros(kshape, dtype=cache_dt, device=dev)
+    vc = torch.zeros(vshape, dtype=cache_dt, device=dev)
+    # Quantised rings: E4M3 with the workload's tensor scales, INT8 with its
+    # row scale pools.
+    ks, vs = (ops.alloc_scale_pools(wl.pool_blocks, wl.Hkv, dev) if wl.cache == "int8"
+              else (None, None))
+    qkw = dict(k_scale=wl.k_scale, v_scale=wl.v_scale, key_scales=ks, value_scales=vs)
     hk, hv, hs, cs = [], [], [], []
     for b in range(wl.B):
         pos = np.arange(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
@@ -454,7 +463,7 @@ def bench_window_prefill(wl, a, torch):
         cs.append(sl)
     ops.reshape_and_cache(_act_tensor(np.concatenate(hk), wl.act, torch),
                           _act_tensor(np.concatenate(hv), wl.act, torch), kc, vc,
-                          torch.from_numpy(np.concatenate(hs)).to(dev))
+                          torch.from_numpy(np.concatenate(hs)).to(dev), **qkw)
     q = _act_tensor(wl.query, wl.act, torch)
     k = _act_tensor(wl.chunk_k, wl.act, torch)
     v = _act_tensor(wl.chunk_v, wl.act, torch)
@@ -466,11 +475,13 @@ def bench_window_prefill(wl, a, torch):
     # The step reads the pre-chunk ring; writing the chunk each step would
     # change what the next step reads, so the write goes to a second copy.
     kc2, vc2 = kc.clone(), vc.clone()
-    write = ops.prepare_reshape_and_cache(k, v, kc2, vc2, slots)
+    ks2, vs2 = (ks.clone(), vs.clone()) if ks is not None else (None, None)
+    write = ops.prepare_reshape_and_cache(k, v, kc2, vc2, slots, wl.k_scale, wl.v_scale,
+                                          key_scales=ks2, value_scales=vs2)
 
     def run():
         ops.prefill_chunk_window(q, k, v, cu, kc, vc, bt, cl, int(wl.chunk_lens.max()),
-                                 wl.scale, wl.window, out=out)
+                                 wl.scale, wl.window, out=out, **qkw)
 
     for _ in range(a.warmup):
         run()
@@ -500,7 +511,8 @@ def bench_window_prefill(wl, a, torch):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "window": wl.window, "history": int(wl.hist_lens[0]),
-                   "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS},
+                   "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS,
+                   "ring": wl.cache},
         "prefill_us": round(pre_s * 1e6, 3), "step_us": round(step_s * 1e6, 3),
         "tokens_per_s": round(wl.total_q / step_s, 1),
         "roofline": {"kernel": "pa_prefill_chunk_window", "bound": "mfma",
@@ -675,7 +687,7 @@ def main():
     wl = _workload(a.config)
     if a.config == "prefix_prefill":
         res = bench_prefill(wl, a, torch)
-    elif a.config == "sliding_prefill":
+    elif a.config.startswith("sliding_prefill"):
         res = bench_window_prefill(wl, a, torch)
     elif a.config == "cow_copy":
         res = bench_copy_blocks(wl, a, torch)

@@ -16,7 +16,8 @@
  *  - "Rolling buffer cache" (llama.cpp discussion 3581), opening post: with a
  *    sliding window of W tokens the cache is a ring of W rows and position i
  *    lives in row i mod W; pa_decode() with window > 0 reads such a ring,
- *    and pa_prefill_chunk_window() attends a prompt chunk over it.
+ *    and pa_prefill_chunk_window() (pa_prefill_chunk_window_quant() for E4M3
+ *    and INT8 rings) attends a prompt chunk over it.
  *  - same page, the prefix-caching note and section "FlashAttention V2/V3 +
  *    PagedAttention": prompt (prefill) tokens attend causally over cached
  *    blocks that may be shared between sequences; pa_prefill_chunk() is that
@@ -347,6 +348,37 @@ pa_status pa_prefill_chunk_window(void* out, const void* query, const void* key,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
                                   int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
                                   pa_dtype act_dtype, int32_t window, void* stream);
+
+/*
+ * pa_prefill_chunk_window_quant -- pa_prefill_chunk_window over a quantised
+ * ring ("PagedAttention in mistral.rs", section "KV Cache Quantization", for
+ * E4M3; "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build, for the
+ * per-token/head INT8 cache).
+ *
+ * cache_dtype     PA_F8E4M3: the ring holds E4M3 codes standing for
+ *                 code * k_scale (K) and code * v_scale (V); key_scales and
+ *                 value_scales are ignored (may be NULL).
+ *                 PA_I8: the ring holds INT8 codes and key_scales /
+ *                 value_scales [NB][Hkv][BS] fp32 (4-byte aligned) their
+ *                 rows' scales; k_scale and v_scale are ignored.
+ *                 act_dtype: the same as pa_prefill_chunk_window.
+ * The ring rows are read at those values; the chunk's own rows (key, value)
+ * are the activations as given (they are quantised only when written into
+ * the ring after this call).  Other arguments, outputs and errors as
+ * pa_prefill_chunk_window; PA_ERR_UNSUPPORTED for another cache_dtype;
+ * PA_ERR_INVALID for E4M3 scales that are not finite and > 0, or NULL INT8
+ * scale pools.
+ */
+pa_status pa_prefill_chunk_window_quant(void* out, const void* query, const void* key,
+                                        const void* value, const int32_t* cu_q_lens,
+                                        const void* key_cache, const void* value_cache,
+                                        const float* key_scales, const float* value_scales,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t BS, int32_t MBPS, int32_t max_chunk_len,
+                                        float softmax_scale, pa_dtype act_dtype,
+                                        pa_dtype cache_dtype, float k_scale, float v_scale,
+                                        int32_t window, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,9 @@ SIGNATURES = {
     "pa_prefill_chunk_window": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
         _f32, ctypes.c_int, _i32, _vp]),
+    "pa_prefill_chunk_window_quant": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+        _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _vp]),
 }
 
 _lock = threading.Lock()

@@ -577,15 +577,36 @@ pa_status pa_prefill_chunk_window(void* out, const void* query, const void* key,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
                                   int32_t MBPS, int32_t max_chunk_len, float softmax_scale,
                                   pa_dtype act_dtype, int32_t window, void* stream) {
+  return pa_prefill_chunk_window_quant(out, query, key, value, cu_q_lens, key_cache,
+                                       value_cache, nullptr, nullptr, block_tables, context_lens,
+                                       B, Hq, Hkv, D, BS, MBPS, max_chunk_len, softmax_scale,
+                                       act_dtype, act_dtype, 1.f, 1.f, window, stream);
+}
+
+pa_status pa_prefill_chunk_window_quant(void* out, const void* query, const void* key,
+                                        const void* value, const int32_t* cu_q_lens,
+                                        const void* key_cache, const void* value_cache,
+                                        const float* key_scales, const float* value_scales,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t BS, int32_t MBPS, int32_t max_chunk_len,
+                                        float softmax_scale, pa_dtype act_dtype,
+                                        pa_dtype cache_dtype, float k_scale, float v_scale,
+                                        int32_t window, void* stream) {
   if (window <= 0 || window % kBlock != 0)
     return fail(PA_ERR_INVALID, "window must be a positive multiple of 32 (got %d)", window);
   if (MBPS < 1 || window / kBlock > MBPS)
     return fail(PA_ERR_INVALID, "the ring of %d rows needs %d table entries (MBPS %d)", window,
                 window / kBlock, MBPS);
-  return prefill_common(out, query, cu_q_lens, key_cache, value_cache, nullptr, nullptr,
-                        block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS, max_chunk_len,
-                        softmax_scale, act_dtype, act_dtype, 1.f, 1.f, stream, key, value,
-                        window);
+  if (cache_dtype != act_dtype && cache_dtype != PA_F8E4M3 && cache_dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED,
+                "ring dtype must equal the act dtype or be PA_F8E4M3 or PA_I8");
+  if (cache_dtype != PA_F8E4M3) k_scale = v_scale = 1.f;
+  if (cache_dtype != PA_I8) key_scales = value_scales = nullptr;
+  return prefill_common(out, query, cu_q_lens, key_cache, value_cache, key_scales,
+                        value_scales, block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS,
+                        max_chunk_len, softmax_scale, act_dtype, cache_dtype, k_scale, v_scale,
+                        stream, key, value, window);
 }
 
 }  // extern "C"

@@ -127,13 +127,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int B, int MBPS,
     int row_tiles, float qk_scale_log2, float v_scale, const float* __restrict__ key_scales,
     const float* __restrict__ value_scales, const uint16_t* __restrict__ key_act,
-    const uint16_t* __restrict__ value_act, int window) {
+    const uint16_t* __restrict__ value_act, int window, float ring_k_scale,
+    float ring_v_scale) {
   constexpr int KS = D / 32;              // k-steps of S^T (32 head dims each)
   constexpr int NT = D / 16;              // 16-dim tiles of O^T
   constexpr int PAGE = BS * D;            // elements of one K (or V) page
-  static_assert(!WIN || CF == AF, "the window path reads 16-bit caches");
   constexpr bool kDma = !byte_fmt(CF) && !WIN;
   constexpr bool kI8 = CF == FMT_I8;
+  // Per-key scales staged beside each page: the INT8 row scales, and for a
+  // quantised ring in the window path the ring rows' scales (1 for the
+  // chunk's own rows, which come from the activations).
+  constexpr bool kScaled = kI8 || (WIN && byte_fmt(CF));
   constexpr int NBUF = kDma ? 3 : 2;
   constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
   constexpr int NCH = PAGE / 8;           // 8-element chunks per page (K or V)
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF][PAGE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[NBUF][PAGE];
-  __shared__ __attribute__((aligned(16))) float ks_lds[kI8 ? NBUF : 1][BS];  // INT8 row scales
-  __shared__ __attribute__((aligned(16))) float vs_lds[kI8 ? NBUF : 1][BS];
+  __shared__ __attribute__((aligned(16))) float ks_lds[kScaled ? NBUF : 1][BS];  // row scales
+  __shared__ __attribute__((aligned(16))) float vs_lds[kScaled ? NBUF : 1][BS];
 
   // --- which (KV head, sequence, row tile) this workgroup owns -----------
   const int n_items = row_tiles * Hkv * B;
@@ -316,11 +320,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // row before the chunk comes from the ring (its ring page holds rows
   // pos mod W; the ring has every position from max(0, start - W) on); a
   // row of the chunk from the activations; any other row is zero (never
-  // visible to a query).
+  // visible to a query).  A quantised ring's codes are widened exactly to
+  // the activation format, and the page's row scales are staged beside it:
+  // the ring's (E4M3: the tensor scales; INT8: each row's own), 1 for the
+  // chunk's rows, 0 for the others.
   constexpr int NIT = (BS * (D / 8) + kThreads - 1) / kThreads;
   u32x4 wk[WIN ? NIT : 1], wv[WIN ? NIT : 1];
-  const uint16_t* kc16 = reinterpret_cast<const uint16_t*>(key_cache);
+  float wsc = 0.f;  // threads 0..31: K scale of row tid; 32..63: V scale of row tid - 32
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
+  // Eight ring elements of K (or V) starting at element `off` of the cache
+  // (16-bit: one 16-byte load; bytes: one 8-byte load, widened).
+  auto ring_chunk = [&](const uint8_t* cache, size_t off) -> u32x4 {
+    if constexpr (byte_fmt(CF)) {
+      return widen(*reinterpret_cast<const u32x2*>(cache + off));
+    } else {
+      return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(cache) + off);
+    }
+  };
   // A page wholly before the chunk is all ring rows, every one written
   // (the ring holds max(0, start - W) .. start - 1, all W rows once
   // start >= W): it is staged as native page chunks, V included, with no
@@ -331,14 +347,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int ring_blk = (base % window) / BS;
     const int phys = base >= first_pos ? 0 : ident ? b * MBPS + ring_blk : bt[ring_blk];
     const size_t page = (size_t)phys * blk_stride + head_off;
+    if constexpr (kScaled) {
+      if (tid < 2 * BS) {
+        const int row = tid & (BS - 1);
+        const int pos = base + row;
+        const bool is_k = tid < BS;
+        if (pos >= ring_lo && pos < first_pos) {
+          if constexpr (kI8) {
+            wsc = (is_k ? key_scales : value_scales)[((size_t)phys * Hkv + g) * BS + row];
+          } else {
+            wsc = is_k ? ring_k_scale : ring_v_scale;
+          }
+        } else {
+          wsc = pos >= first_pos && pos < ctx ? 1.f : 0.f;
+        }
+      }
+    }
     win_native = base + BS <= first_pos;
     if (win_native) {
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         const int item = tid + i * kThreads;
         if (item < NCH) {
-          wk[i] = *reinterpret_cast<const u32x4*>(kc16 + page + (size_t)item * 8);
-          wv[i] = *reinterpret_cast<const u32x4*>(vc16 + page + (size_t)item * 8);
+          wk[i] = ring_chunk(key_cache, page + (size_t)item * 8);
+          wv[i] = ring_chunk(value_cache, page + (size_t)item * 8);
         }
       }
       return;
@@ -352,11 +384,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int c = item / BS;
         const int pos = base + r;
         if (pos >= ring_lo && pos < first_pos) {
-          kw = *reinterpret_cast<const u32x4*>(kc16 + page + (size_t)(c * BS + r) * 8);
+          kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
+          if constexpr (byte_fmt(CF)) {
+            u32x2 vq = u32x2{0u, 0u};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vw[e] = (uint32_t)vc16[page + (size_t)(8 * c + 2 * e) * BS + r] |
-                    ((uint32_t)vc16[page + (size_t)(8 * c + 2 * e + 1) * BS + r] << 16);
+            for (int e = 0; e < 8; ++e)
+              vq[e >> 2] |= (uint32_t)value_cache[page + (size_t)(8 * c + e) * BS + r]
+                            << (8 * (e & 3));
+            vw = widen(vq);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              vw[e] = (uint32_t)vc16[page + (size_t)(8 * c + 2 * e) * BS + r] |
+                      ((uint32_t)vc16[page + (size_t)(8 * c + 2 * e + 1) * BS + r] << 16);
+          }
         } else if (pos >= first_pos && pos < ctx) {
           const size_t row = ((size_t)(q_begin + pos - first_pos) * Hkv + g) * D + 8 * c;
           kw = *reinterpret_cast<const u32x4*>(key_act + row);
@@ -389,6 +430,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
         }
       }
+    }
+    if constexpr (kScaled) {
+      if (tid < BS) ks_lds[buf][tid] = wsc;
+      else if (tid < 2 * BS) vs_lds[buf][tid - BS] = wsc;
     }
   };
 
@@ -454,7 +499,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // need no NaN quieting.
       vec pb[NQ];
       {
-        if constexpr (kI8) {
+        if constexpr (kScaled) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
             const f32x4 ks4 = *reinterpret_cast<const f32x4*>(&ks_lds[cur][8 * q4 + 4 * kt]);
@@ -498,7 +543,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int r = 0; r < 4; ++r)
               pv[4 * kt + r] = fast_exp2(fmaf(s_acc[kt][t][r], qk_scale_log2, -m_run[t]));
           pb[t] = __builtin_convertvector(pv, vec);
-          if constexpr (kI8) {
+          if constexpr (kScaled) {
             // l from the unscaled P; the V MFMAs take P times each key's V scale.
             o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
 #pragma unroll
@@ -531,7 +576,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
           for (int t = 0; t < NQ; ++t) o_acc[n][t] = Mfma<AF>::mma(va, pb[t], o_acc[n][t]);
         }
-        if constexpr (!kI8) {
+        if constexpr (!kScaled) {
 #pragma unroll
           for (int t = 0; t < NQ; ++t) o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
         }
@@ -588,11 +633,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Query tiles of 16 rows per wave: as many as fit in 256 VGPRs at two waves
 // per SIMD (the byte formats keep their widening temporaries live too, INT8
 // its row scales and a second P operand, the window path its staged
-// activation rows).
+// activation rows, and over a quantised ring both).
 template <int D, int CF, bool WIN>
 constexpr int query_tiles() {
   if (D <= 64) return 4;
-  if (D <= 96) return byte_fmt(CF) || WIN ? 3 : 4;
+  if (D <= 96) return WIN && byte_fmt(CF) ? 2 : byte_fmt(CF) || WIN ? 3 : 4;
   return byte_fmt(CF) || WIN ? 2 : 3;
 }
 
@@ -605,22 +650,34 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   const long long items = row_tiles * a.Hkv * a.B;
   const long long per_xcd = (items + kXcds - 1) / kXcds;
   if (per_xcd * kXcds > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float qk = a.softmax_scale * (CF == FMT_E4M3 ? a.k_scale : 1.f) * LOG2E_P;
-  const float vs = CF == FMT_E4M3 ? a.v_scale : 1.f;
+  // An E4M3 cache's tensor scales fold into the score and output scales
+  // when every key is a cache row; in the window path the chunk's own rows
+  // are not, so there the ring rows carry them as row scales.
+  constexpr bool kFold = CF == FMT_E4M3 && !WIN;
+  const float qk = a.softmax_scale * (kFold ? a.k_scale : 1.f) * LOG2E_P;
+  const float vs = kFold ? a.v_scale : 1.f;
   hipLaunchKernelGGL((prefill_kernel<D, CF, AF, NQ, WIN>), dim3((unsigned)(per_xcd * kXcds)),
                      dim3(kThreads), 0, s, (uint16_t*)a.out, (const uint16_t*)a.query,
                      a.cu_q_lens, (const uint8_t*)a.key_cache, (const uint8_t*)a.value_cache,
                      a.block_tables, a.context_lens, a.Hq, a.Hkv, G, a.B, a.MBPS,
                      (int)row_tiles, qk, vs, a.key_scales, a.value_scales,
-                     (const uint16_t*)a.key_act, (const uint16_t*)a.value_act, a.window);
+                     (const uint16_t*)a.key_act, (const uint16_t*)a.value_act, a.window,
+                     a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   if (a.window > 0) {
-    if (a.act == FMT_BF16 && a.cache == FMT_BF16) return launch_t<D, FMT_BF16, FMT_BF16, true>(a, s);
-    if (a.act == FMT_F16 && a.cache == FMT_F16) return launch_t<D, FMT_F16, FMT_F16, true>(a, s);
+    if (a.act == FMT_BF16) {
+      if (a.cache == FMT_BF16) return launch_t<D, FMT_BF16, FMT_BF16, true>(a, s);
+      if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_BF16, true>(a, s);
+      if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_BF16, true>(a, s);
+    } else if (a.act == FMT_F16) {
+      if (a.cache == FMT_F16) return launch_t<D, FMT_F16, FMT_F16, true>(a, s);
+      if (a.cache == FMT_E4M3) return launch_t<D, FMT_E4M3, FMT_F16, true>(a, s);
+      if (a.cache == FMT_I8) return launch_t<D, FMT_I8, FMT_F16, true>(a, s);
+    }
     return hipErrorInvalidValue;
   }
   if (a.act == FMT_BF16) {

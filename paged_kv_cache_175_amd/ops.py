@@ -332,10 +332,15 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
                          cu_q_lens: torch.Tensor, key_cache: torch.Tensor,
                          value_cache: torch.Tensor, block_tables: torch.Tensor,
                          context_lens: torch.Tensor, max_chunk_len: int, softmax_scale: float,
-                         window: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         window: int, out: Optional[torch.Tensor] = None,
+                         k_scale: float = 1.0, v_scale: float = 1.0,
+                         key_scales: Optional[torch.Tensor] = None,
+                         value_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Chunked prefill of a sliding-window layer over its ring
     (``pa_prefill_chunk_window``); ``key`` / ``value`` ``[total_q, Hkv, D]``
-    are the chunk's own K/V, written into the ring only after this call."""
+    are the chunk's own K/V, written into the ring only after this call.  An
+    E4M3 ring (uint8) reads with ``k_scale`` / ``v_scale``, an INT8 ring
+    with its scale pools (``pa_prefill_chunk_window_quant``)."""
     _dev(query, key, value, cu_q_lens, key_cache, value_cache, context_lens)
     _i32(cu_q_lens, context_lens)
     total_q, Hq, D = query.shape
@@ -351,16 +356,24 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
         raise ValueError("cu_q_lens must be [B+1]")
     bt_ptr, MBPS = _table(block_tables, B)
     act = _act_code(query)
-    if _cache_code(key_cache, query.dtype) != act:
-        raise TypeError("the window path reads a cache in the activation dtype")
+    cache = _cache_code(key_cache, query.dtype)
     if out is None:
         out = torch.empty_like(query)
     _dev(out)
-    _lib.check(_lib.load().pa_prefill_chunk_window(
+    if cache == act:
+        _lib.check(_lib.load().pa_prefill_chunk_window(
+            out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
+            cu_q_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS,
+            MBPS, int(max_chunk_len), float(softmax_scale), act, int(window),
+            _stream()))
+        return out
+    sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS) or (0, 0)
+    _lib.check(_lib.load().pa_prefill_chunk_window_quant(
         out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
-        cu_q_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS,
-        MBPS, int(max_chunk_len), float(softmax_scale), act, int(window),
+        cu_q_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), sc[0], sc[1],
+        bt_ptr, context_lens.data_ptr(), B, Hq, Hkv, D, BS, MBPS, int(max_chunk_len),
+        float(softmax_scale), act, cache, float(k_scale), float(v_scale), int(window),
         _stream()))
     return out
 

@@ -374,13 +374,15 @@ class WindowPrefillWorkload:
 
 
 def window_prefill_workload(name: str, seed: int, B: int, Hq: int, Hkv: int, D: int,
-                            act: str, window: int, hist, chunk,
-                            BS: int = BLOCK_SIZE) -> WindowPrefillWorkload:
+                            act: str, window: int, hist, chunk, BS: int = BLOCK_SIZE,
+                            cache: Optional[str] = None) -> WindowPrefillWorkload:
     """Build a sliding-window chunked-prefill workload.
 
     ``hist`` / ``chunk``: one length for every sequence, a list of B
     lengths, or a (lo, hi) range to draw from (a tuple).  The B rings take
-    distinct blocks of one shuffled pool.
+    distinct blocks of one shuffled pool.  ``cache``: the ring's format (the
+    activation format by default; "e4m3" gets per-tensor scales amax / 448
+    over the history and the chunk, "int8" quantises per row when written).
     """
     if window <= 0 or window % BS:
         raise ValueError("window must be a positive multiple of the block size")
@@ -406,12 +408,17 @@ def window_prefill_workload(name: str, seed: int, B: int, Hq: int, Hkv: int, D: 
     cv = _normal_bits(rng, (int(cu[-1]), Hkv, D), act)
     hk = [_normal_bits(rng, (int(h - p), Hkv, D), act) for h, p in zip(H, pos0)]
     hv = [_normal_bits(rng, (int(h - p), Hkv, D), act) for h, p in zip(H, pos0)]
+    k_scale = v_scale = 1.0
+    if cache == "e4m3":
+        k_scale = _amax_scale(hk + [ck], act)
+        v_scale = _amax_scale(hv + [cv], act)
     return WindowPrefillWorkload(
         name=name, act=act, B=B, Hq=Hq, Hkv=Hkv, D=D, BS=BS, window=window, num_blocks=nb,
         scale=float(1.0 / np.sqrt(D)), hist_lens=H.astype(np.int32),
         hist_pos0=pos0.astype(np.int32), chunk_lens=C.astype(np.int32), cu_q_lens=cu,
         context_lens=(H + C).astype(np.int32), block_tables=bt, query=q, chunk_k=ck,
-        chunk_v=cv, hist_k=hk, hist_v=hv, meta={"seed": seed})
+        chunk_v=cv, hist_k=hk, hist_v=hv, cache=cache or act, k_scale=k_scale,
+        v_scale=v_scale, meta={"seed": seed})
 
 
 # ---------------------------------------------------------------------------
@@ -450,12 +457,15 @@ def sliding_decode(B: int = 8, window: int = 4096, pos_range=(4096, 32768),
 
 
 def sliding_prefill(B: int = 4, window: int = 4096, hist: int = 8192, chunk: int = 2048,
-                    seed: int = 6) -> WindowPrefillWorkload:
+                    seed: int = 6, cache: Optional[str] = None) -> WindowPrefillWorkload:
     """Mistral-7B-shaped sliding-window layer (32/8 heads, head_dim 128, bf16,
     4096-token window): chunks of 2048 tokens after 8192 positions, so the
-    ring is full and every query sees 4096 keys."""
-    return window_prefill_workload("sliding_prefill", seed, B=B, Hq=32, Hkv=8, D=128,
-                                   act="bf16", window=window, hist=hist, chunk=chunk)
+    ring is full and every query sees 4096 keys.  ``cache``: "e4m3" or
+    "int8" for a quantised ring (named sliding_prefill_fp8 / _int8)."""
+    name = {None: "sliding_prefill", "e4m3": "sliding_prefill_fp8",
+            "int8": "sliding_prefill_int8"}[cache]
+    return window_prefill_workload(name, seed, B=B, Hq=32, Hkv=8, D=128, act="bf16",
+                                   window=window, hist=hist, chunk=chunk, cache=cache)
 
 
 @dataclass

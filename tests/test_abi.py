@@ -208,3 +208,29 @@ def test_prefill_window_rejects(args, status):
                                        a["vc"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"],
                                        a["D"], a["BS"], a["MBPS"], a["maxc"], a["scale"],
                                        a["act"], a["window"], None) == status
+
+
+@needs_lib
+@host_only
+@pytest.mark.parametrize("args,status", [
+    (dict(cache=_lib.PA_F16), _lib.PA_ERR_UNSUPPORTED),            # neither act nor quantised
+    (dict(cache=_lib.PA_F8E4M3, ksc=0.0), _lib.PA_ERR_INVALID),    # E4M3 scale must be > 0
+    (dict(cache=_lib.PA_F8E4M3, vsc=float("inf")), _lib.PA_ERR_INVALID),
+    (dict(cache=_lib.PA_I8, kscales=0), _lib.PA_ERR_INVALID),       # INT8 needs its pools
+    (dict(cache=_lib.PA_I8, vscales=FAKE + 2), _lib.PA_ERR_INVALID),  # misaligned pool
+    (dict(cache=_lib.PA_F8E4M3, window=48), _lib.PA_ERR_INVALID),
+    (dict(cache=_lib.PA_I8, window=160), _lib.PA_ERR_INVALID),
+    (dict(cache=_lib.PA_F8E4M3, maxc=0, cu=0), _lib.PA_OK),
+    (dict(cache=_lib.PA_I8, maxc=0, cu=0), _lib.PA_OK),
+])
+def test_prefill_window_quant_rejects(args, status):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, cu=FAKE, kc=FAKE, vc=FAKE, kscales=FAKE,
+             vscales=FAKE, bt=FAKE, cl=FAKE, B=2, Hq=4, Hkv=2, D=128, BS=32, MBPS=4, maxc=10,
+             scale=0.1, act=_lib.PA_BF16, cache=_lib.PA_F8E4M3, ksc=0.5, vsc=0.5, window=128)
+    a.update(args)
+    lib = _lib.load()
+    assert lib.pa_prefill_chunk_window_quant(
+        a["out"], a["q"], a["key"], a["value"], a["cu"], a["kc"], a["vc"], a["kscales"],
+        a["vscales"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["MBPS"],
+        a["maxc"], a["scale"], a["act"], a["cache"], a["ksc"], a["vsc"], a["window"],
+        None) == status

@@ -137,14 +137,18 @@ def test_full_size_int8_decode_sampled():
     assert err <= P.TOL["int8"]
 
 
-def test_full_size_sliding_prefill_sampled():
-    """The sliding-window prefill workload at full size (B=4, W=4096, 8192
-    positions in the ring, chunks of 2048), as bench.py times it; query rows
-    at tile and page boundaries and at the window's edge, three heads."""
-    wl = W.sliding_prefill()
-    P.say(f"[full sliding prefill] B={wl.B} W={wl.window} hist={int(wl.hist_lens[0])} "
-          f"chunk={int(wl.chunk_lens[0])}")
-    kc, vc = P.gpu_pools(wl)
+@pytest.mark.parametrize("cache", [None, "e4m3", "int8"])
+def test_full_size_sliding_prefill_sampled(cache):
+    """The sliding-window prefill workloads at full size (B=4, W=4096, 8192
+    positions in the ring, chunks of 2048), as bench.py times them, over a
+    bf16, E4M3 or INT8 ring; query rows at tile and page boundaries and at
+    the window's edge, three heads."""
+    wl = W.sliding_prefill(cache=cache)
+    P.say(f"[full sliding prefill] ring={wl.cache} B={wl.B} W={wl.window} "
+          f"hist={int(wl.hist_lens[0])} chunk={int(wl.chunk_lens[0])}")
+    i8 = wl.cache == "int8"
+    pools = P.gpu_pools_i8(wl) if i8 else (*P.gpu_pools(wl), None, None)
+    kc, vc, ks, vs = pools
     from paged_kv_cache_175_amd import ops, pool
     hk, hv, hs = [], [], []
     for b in range(wl.B):
@@ -152,36 +156,47 @@ def test_full_size_sliding_prefill_sampled():
         hs.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
         hk.append(wl.hist_k[b])
         hv.append(wl.hist_v[b])
-    P._gpu_write(wl, kc, vc, np.concatenate(hk), np.concatenate(hv), np.concatenate(hs))
+    if i8:
+        P._gpu_write_i8(wl, pools, np.concatenate(hk), np.concatenate(hv), np.concatenate(hs))
+    else:
+        P._gpu_write(wl, kc, vc, np.concatenate(hk), np.concatenate(hv), np.concatenate(hs))
     q, k, v = (P._act_tensor(x, wl.act) for x in (wl.query, wl.chunk_k, wl.chunk_v))
     out = P.out_f64(ops.prefill_chunk_window(
         q, k, v, torch.from_numpy(wl.cu_q_lens).cuda(), kc, vc,
         torch.from_numpy(wl.block_tables).cuda(), torch.from_numpy(wl.context_lens).cuda(),
-        int(wl.chunk_lens.max()), wl.scale, wl.window))
+        int(wl.chunk_lens.max()), wl.scale, wl.window, k_scale=wl.k_scale, v_scale=wl.v_scale,
+        key_scales=ks, value_scales=vs))
     torch.cuda.synchronize()
     seqs = [0, wl.B - 1]
-    okc, ovc = o_cache.empty_pools(wl.num_blocks, wl.Hkv, wl.BS, wl.D, wl.act,
-                                   P.NAN16[wl.act])
+    if i8:
+        okc, ovc, oks, ovs = P.oracle_pools_i8(wl)
+    else:
+        fill = P.NAN_E4M3 if wl.cache == "e4m3" else P.NAN16[wl.act]
+        okc, ovc = o_cache.empty_pools(wl.num_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, fill)
+        oks, ovs = wl.k_scale, wl.v_scale
     from oracle import pool as o_pool
     for b in seqs:
         pos = range(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
         slots = [o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
                  for p in pos]
         o_cache.reshape_and_cache(wl.hist_k[b], wl.hist_v[b], okc, ovc,
-                                  np.array(slots, np.int64), wl.act, wl.act)
+                                  np.array(slots, np.int64), wl.act, wl.cache, oks, ovs)
         blocks = [int(x) for x in wl.block_tables[b]]
         assert np.array_equal(P.pool_bits(kc)[blocks], okc[blocks]), f"ring K of {b} differs"
         assert np.array_equal(P.pool_bits(vc)[blocks], ovc[blocks]), f"ring V of {b} differs"
+        if i8:
+            assert np.array_equal(P.scale_bits(ks)[blocks], oks.view(np.int32)[blocks])
+            assert np.array_equal(P.scale_bits(vs)[blocks], ovs.view(np.int32)[blocks])
     C = int(wl.chunk_lens[0])
     js = sorted({0, 31, 32, 191, 192, 1024, C - 2, C - 1})
     rows = {(b, j) for b in seqs for j in js}
     ref = o_attn.prefill_chunk_window(wl.query, wl.act, wl.chunk_k, wl.chunk_v, wl.cu_q_lens,
-                                      okc, ovc, wl.act, wl.block_tables, wl.context_lens,
-                                      wl.scale, wl.window, rows=rows)
+                                      okc, ovc, wl.cache, wl.block_tables, wl.context_lens,
+                                      wl.scale, wl.window, rows=rows, k_scale=oks, v_scale=ovs)
     heads = [0, wl.Hq // 2 + 1, wl.Hq - 1]
     err = 0.0
     for b, j in rows:
         r = int(wl.cu_q_lens[b]) + j
         err = max(err, float(np.abs(out[r, heads] - ref[r, heads]).max()))
     P.say(f"    max-abs error {err:.3e} over {len(rows)} rows")
-    assert err <= P.TOL[wl.act]
+    assert err <= P.TOL[wl.cache]
