@@ -138,6 +138,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // quantised ring in the window path the ring rows' scales (1 for the
   // chunk's own rows, which come from the activations).
   constexpr bool kScaled = kI8 || (WIN && byte_fmt(CF));
+  // Order of the P and V MFMA work of a page: tile-major where its V
+  // operands fit in registers beside everything else (measured: sliding
+  // prefill, D = 128, 2 tiles, 744 -> 779 TFLOP/s), else P first (D >= 96
+  // with 3 or more tiles of a 16-bit or INT8 cache spilled tile-major).
+  constexpr bool kTileMajor = D <= 64 || NQ <= 2 || CF == FMT_E4M3;
   constexpr int NBUF = kDma ? 3 : 2;
   constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
   constexpr int NCH = PAGE / 8;           // 8-element chunks per page (K or V)
@@ -497,7 +502,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // wave; the two cases are separate instantiations so that the common,
       // unmasked one sees only products (canonical floats) and its maxima
       // need no NaN quieting.
-      vec pb[NQ];
       {
         if constexpr (kScaled) {
 #pragma unroll
@@ -518,67 +522,104 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if (kp > qpos[t] || (WIN && kp <= qpos[t] - window)) s_acc[kt][t][r] = -INFINITY;
               }
         }
+        // The running maxima.  Raising one is rare (a ballot finds a score
+        // more than kSlack above it); it is then raised to the maximum over
+        // the four lanes that hold the query (never lowered), and unchanged
+        // maxima keep their accumulators as they are.
+        float lmax[NQ];
 #pragma unroll
-        for (int t = 0; t < NQ; ++t) {
-          const float lmax = qk_scale_log2 *
-                             fmaxf(fmaxf(fmaxf(s_acc[0][t][0], s_acc[0][t][1]),
-                                         fmaxf(s_acc[0][t][2], s_acc[0][t][3])),
-                                   fmaxf(fmaxf(s_acc[1][t][0], s_acc[1][t][1]),
-                                         fmaxf(s_acc[1][t][2], s_acc[1][t][3])));
-          if (__builtin_amdgcn_ballot_w64(lmax > m_run[t] + kSlack) != 0) {
-            // Raise the maximum of every query of this tile to its maximum
-            // over the four lanes that hold it (and never lower it).
-            float cm = fmaxf(lmax, shfl_xor_f(lmax, 16));
-            cm = fmaxf(cm, shfl_xor_f(cm, 32));
-            const float m_new = fmaxf(m_run[t], cm);
-            const float alpha = fast_exp2(m_run[t] - m_new);
+        for (int t = 0; t < NQ; ++t)
+          lmax[t] = qk_scale_log2 * fmaxf(fmaxf(fmaxf(s_acc[0][t][0], s_acc[0][t][1]),
+                                                fmaxf(s_acc[0][t][2], s_acc[0][t][3])),
+                                          fmaxf(fmaxf(s_acc[1][t][0], s_acc[1][t][1]),
+                                                fmaxf(s_acc[1][t][2], s_acc[1][t][3])));
+        auto raise_max = [&](int t) {
+          float cm = fmaxf(lmax[t], shfl_xor_f(lmax[t], 16));
+          cm = fmaxf(cm, shfl_xor_f(cm, 32));
+          const float m_new = fmaxf(m_run[t], cm);
+          const float alpha = m_new == m_run[t] ? 1.f : fast_exp2(m_run[t] - m_new);
 #pragma unroll
-            for (int n = 0; n <= NT; ++n) o_acc[n][t] *= alpha;
-            m_run[t] = m_new;
+          for (int n = 0; n <= NT; ++n) o_acc[n][t] *= alpha;
+          m_run[t] = m_new;
+        };
+        if constexpr (kTileMajor) {
+          // One test for all tiles, so that the block after it holds every
+          // tile's exponentials and V MFMAs.
+          bool raise = false;
+#pragma unroll
+          for (int t = 0; t < NQ; ++t) raise |= lmax[t] > m_run[t] + kSlack;
+          if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) raise_max(t);
           }
-          f32x8 pv;
+        } else {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              pv[4 * kt + r] = fast_exp2(fmaf(s_acc[kt][t][r], qk_scale_log2, -m_run[t]));
-          pb[t] = __builtin_convertvector(pv, vec);
-          if constexpr (kScaled) {
-            // l from the unscaled P; the V MFMAs take P times each key's V scale.
-            o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-              const f32x4 vs4 = *reinterpret_cast<const f32x4*>(&vs_lds[cur][8 * q4 + 4 * kt]);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) pv[4 * kt + r] *= vs4[r];
-            }
-            pb[t] = __builtin_convertvector(pv, vec);
-          }
+          for (int t = 0; t < NQ; ++t)
+            if (__builtin_amdgcn_ballot_w64(lmax[t] > m_run[t] + kSlack) != 0) raise_max(t);
         }
       }
 
-      // O^T += V^T P^T; on the sequence's last page, tokens at or past the
-      // context end are zeroed in the V operand.
-      {
-        u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
-        if constexpr (decltype(masked)::value) {
+      // P and O^T += V^T P^T.  On the sequence's last page, tokens at or past
+      // the context end are zeroed in the V operand.
+      u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
+      if constexpr (decltype(masked)::value) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tok = base + 8 * q4 + 2 * e;
-            keep[e] = (tok < ctx ? 0xffffu : 0u) | (tok + 1 < ctx ? 0xffff0000u : 0u);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int tok = base + 8 * q4 + 2 * e;
+          keep[e] = (tok < ctx ? 0xffffu : 0u) | (tok + 1 < ctx ? 0xffff0000u : 0u);
         }
+      }
+      auto v_operand = [&](int n) {
+        u32x4 vw = *reinterpret_cast<const u32x4*>(&vb[v_off + n * 16 * 4 * 8]);
+        if constexpr (decltype(masked)::value) vw &= keep;
+        return __builtin_bit_cast(vec, vw);
+      };
+      // P of tile t (and, beside the unscaled P, the P that weights V when
+      // the keys carry V scales); l += 1^T P^T from the unscaled P.
+      auto p_operand = [&](int t) -> vec {
+        f32x8 pv;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            pv[4 * kt + r] = fast_exp2(fmaf(s_acc[kt][t][r], qk_scale_log2, -m_run[t]));
+        vec pb = __builtin_convertvector(pv, vec);
+        o_acc[NT][t] = Mfma<AF>::mma(ones, pb, o_acc[NT][t]);
+        if constexpr (kScaled) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const f32x4 vs4 = *reinterpret_cast<const f32x4*>(&vs_lds[cur][8 * q4 + 4 * kt]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[4 * kt + r] *= vs4[r];
+          }
+          pb = __builtin_convertvector(pv, vec);
+        }
+        return pb;
+      };
+      if constexpr (kTileMajor) {
+        // One query tile at a time: a tile's V MFMAs are issued between the
+        // next tile's exponentials, so the wave keeps the matrix core and
+        // the VALU busy together (all V operands stay in registers).
+        vec va[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) va[n] = v_operand(n);
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+          const vec pb = p_operand(t);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) o_acc[n][t] = Mfma<AF>::mma(va[n], pb, o_acc[n][t]);
+        }
+      } else {
+        // Every tile's P first, then the V MFMAs one V operand at a time:
+        // fewer registers, for the shapes where the tile-major order spills.
+        vec pb[NQ];
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) pb[t] = p_operand(t);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          u32x4 vw = *reinterpret_cast<const u32x4*>(&vb[v_off + n * 16 * 4 * 8]);
-          if constexpr (decltype(masked)::value) vw &= keep;
-          const vec va = __builtin_bit_cast(vec, vw);
+          const vec va = v_operand(n);
 #pragma unroll
           for (int t = 0; t < NQ; ++t) o_acc[n][t] = Mfma<AF>::mma(va, pb[t], o_acc[n][t]);
-        }
-        if constexpr (!kScaled) {
-#pragma unroll
-          for (int t = 0; t < NQ; ++t) o_acc[NT][t] = Mfma<AF>::mma(ones, pb[t], o_acc[NT][t]);
         }
       }
       };
