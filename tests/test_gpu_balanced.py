@@ -184,3 +184,37 @@ def test_balanced_repeat_same_workspace():
     assert int(ws[-tail:].count_nonzero()) == 0
     okc, ovc = P.oracle_decode_setup(wl)
     assert P.max_abs(P.out_f64(outs[0]), P.oracle_decode(wl, okc, ovc)) <= P.TOL[wl.cache]
+
+
+@pytest.mark.parametrize("cache", ["e4m3", "int8"])
+def test_balanced_identity_map(cache):
+    """A dense pool behind a NULL table (the identity map, block b * MBPS + j)
+    through the balanced plan: bitwise equal to the same pool behind the
+    explicit identity table, and within tolerance of the oracle."""
+    import dataclasses
+    wl = W.decode_workload("bal_ident", 121, B=5, Hq=16, Hkv=4, D=128, act="bf16", cache=cache,
+                           ctx_range=(1, 2600))
+    B, M = wl.block_tables.shape
+    wl = dataclasses.replace(wl, block_tables=pool.identity_table(B, M), num_blocks=B * M)
+    P.say(f"[balanced identity map] cache={cache} lens={list(wl.context_lens)}")
+    L = int(wl.context_lens.max())
+    cl = torch.from_numpy(wl.context_lens).cuda()
+    q = P._act_tensor(wl.query, wl.act)
+    if cache == "int8":
+        kc, vc, ks, vs = P.hip_decode_setup_i8(wl)
+        kw = dict(key_scales=ks, value_scales=vs)
+    else:
+        kc, vc = P.hip_decode_setup(wl)
+        kw = dict(k_scale=wl.k_scale, v_scale=wl.v_scale)
+    outs = [ops.decode(q, kc, vc, table, cl, L, wl.scale, **kw)
+            for table in (ops.IdentityMap(M), torch.from_numpy(wl.block_tables).cuda())]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    if cache == "int8":
+        ref = P.oracle_decode_i8(wl, P.oracle_decode_setup_i8(wl))
+    else:
+        okc, ovc = P.oracle_decode_setup(wl)
+        ref = P.oracle_decode(wl, okc, ovc)
+    err = P.max_abs(P.out_f64(outs[0]), ref)
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL[cache]

@@ -21,11 +21,14 @@ from paged_kv_cache_175_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("part", [0, 64])
-def test_decode_append_graph_replays(part):
+@pytest.mark.parametrize("cache,part", [("bf16", 0), ("bf16", 64), ("e4m3", 0)])
+def test_decode_append_graph_replays(cache, part):
+    """bf16 one pass and forced splits; E4M3 over 1024+ tokens takes the
+    balanced plan (equal page ranges, cut sequences merged in the launch)."""
     wl = W.decode_workload("graph_decode", 91, B=6, Hq=32, Hkv=8, D=128, act="bf16",
-                           ctx_range=(1, 900))
-    P.say(f"[graph] decode append part={part} lens={list(wl.context_lens)}")
+                           cache=cache, ctx_range=(1, 900) if cache == "bf16" else (1, 2500))
+    sc = dict(k_scale=wl.k_scale, v_scale=wl.v_scale)
+    P.say(f"[graph] decode append cache={cache} part={part} lens={list(wl.context_lens)}")
     kc, vc = P.hip_decode_append_setup(wl)
     q = P._act_tensor(wl.query, wl.act)
     nk, nv = P._act_tensor(wl.new_k, wl.act), P._act_tensor(wl.new_v, wl.act)
@@ -36,7 +39,7 @@ def test_decode_append_graph_replays(part):
                              q.device)
     eager = torch.empty_like(q)
     ops.prepare_decode(q, kc, vc, bt, cl, L, wl.scale, eager, ws, partition_tokens=part,
-                       new_key=nk, new_value=nv)()
+                       new_key=nk, new_value=nv, **sc)()
     torch.cuda.synchronize()
     ref_pools = (P.pool_bits(kc).copy(), P.pool_bits(vc).copy())
 
@@ -47,7 +50,7 @@ def test_decode_append_graph_replays(part):
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
             ops.prepare_decode(q, kc, vc, bt, cl, L, wl.scale, out, ws, partition_tokens=part,
-                               new_key=nk, new_value=nv)()
+                               new_key=nk, new_value=nv, **sc)()
     torch.cuda.current_stream().wait_stream(side)
     junk = torch.zeros(1 << 20, device="cuda")
     for i in range(3):
