@@ -1241,27 +1241,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 template <int D, int G, int CF, int AF, int W>
-hipError_t launch_mode(const DecodeArgs& a, float qk, float vs, hipStream_t stream) {
-  if (a.N > 0) {
-    // Balanced mode is planned for byte-format caches only.
-    if constexpr (byte_fmt(CF)) {
-      hipLaunchKernelGGL((decode_balanced<D, G, CF, AF, W>), dim3(a.N), dim3(64 * W), 0, stream,
-                         (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
-                         (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.B, a.Hkv,
-                         a.MBPS, a.window, a.S, a.stream_k, qk, vs, a.ws_m, a.ws_l, a.ws_o,
-                         a.ws_count, (const uint16_t*)a.new_key, (const uint16_t*)a.new_value,
-                         a.k_scale, a.v_scale, a.key_scales, a.value_scales);
-    } else {
-      return hipErrorInvalidValue;
-    }
-  } else {
-    hipLaunchKernelGGL((decode_split<D, G, CF, AF, W>), dim3(a.S, a.Hkv, a.B), dim3(64 * W), 0,
-                       stream, (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
-                       (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv, a.MBPS,
-                       a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
-                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
-                       a.v_scale, a.key_scales, a.value_scales);
-  }
+hipError_t launch_grid(const DecodeArgs& a, float qk, float vs, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split<D, G, CF, AF, W>), dim3(a.S, a.Hkv, a.B), dim3(64 * W), 0,
+                     stream, (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
+                     (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv, a.MBPS,
+                     a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
+                     (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
+                     a.v_scale, a.key_scales, a.value_scales);
   return hipGetLastError();
 }
 
@@ -1269,8 +1255,23 @@ template <int D, int G, int CF, int AF>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const float qk = a.softmax_scale * (CF == FMT_E4M3 ? a.k_scale : 1.f) * LOG2E;
   const float vs = CF == FMT_E4M3 ? a.v_scale : 1.f;
-  if (a.W == 8) return launch_mode<D, G, CF, AF, 8>(a, qk, vs, stream);
-  if (a.W == 4) return launch_mode<D, G, CF, AF, 4>(a, qk, vs, stream);
+  if (a.N > 0) {
+    // Balanced mode is planned for byte-format caches only, with W = 8.
+    if constexpr (byte_fmt(CF)) {
+      if (a.W != 8) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((decode_balanced<D, G, CF, AF, 8>), dim3(a.N), dim3(512), 0, stream,
+                         (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
+                         (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.B, a.Hkv,
+                         a.MBPS, a.window, a.S, a.stream_k, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                         a.ws_count, (const uint16_t*)a.new_key, (const uint16_t*)a.new_value,
+                         a.k_scale, a.v_scale, a.key_scales, a.value_scales);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  if (a.W == 8) return launch_grid<D, G, CF, AF, 8>(a, qk, vs, stream);
+  if (a.W == 4) return launch_grid<D, G, CF, AF, 4>(a, qk, vs, stream);
   return hipErrorInvalidValue;
 }
 
