@@ -171,6 +171,14 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t partition_tokens);
 
 /*
+ * pa_decode_workspace_bytes_for -- the same for one cache format: exactly
+ * what pa_decode (and its _append / _i8 forms) needs with that cache_dtype.
+ */
+size_t pa_decode_workspace_bytes_for(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int32_t max_context_len, int32_t window,
+                                     int32_t partition_tokens, pa_dtype cache_dtype);
+
+/*
  * pa_decode -- one query token per sequence attends over its cached tokens.
  *
  * out             [B][Hq][D] act_dtype, written.

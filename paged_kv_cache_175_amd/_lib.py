@@ -37,6 +37,8 @@ SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes_for": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            ctypes.c_int]),
     "pa_decode": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp, _sz, _vp]),

@@ -283,6 +283,19 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   return std::max(workspace_for(B, Hq, Hkv, D, p16), workspace_for(B, Hq, Hkv, D, p8));
 }
 
+size_t pa_decode_workspace_bytes_for(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int32_t max_context_len, int32_t window,
+                                     int32_t partition_tokens, pa_dtype cache_dtype) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || max_context_len < 0 || window < 0 ||
+      partition_tokens < 0)
+    return (size_t)-1;
+  Plan p;
+  if (!make_plan(B, Hkv, max_context_len, window, partition_tokens,
+                 cache_dtype == PA_F8E4M3 || cache_dtype == PA_I8, &p))
+    return (size_t)-1;
+  return workspace_for(B, Hq, Hkv, D, p);
+}
+
 }  // extern "C"
 
 namespace {

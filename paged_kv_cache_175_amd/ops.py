@@ -197,9 +197,17 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mappin
 
 
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: int,
-                           window: int = 0, partition_tokens: int = 0) -> int:
-    n = _lib.load().pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window,
-                                              partition_tokens)
+                           window: int = 0, partition_tokens: int = 0,
+                           cache_dtype: Optional[int] = None) -> int:
+    """Workspace bytes of a decode call; with ``cache_dtype`` (a PA_* code)
+    exactly that format's need, else the largest over the formats."""
+    lib = _lib.load()
+    if cache_dtype is None:
+        n = lib.pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window,
+                                          partition_tokens)
+    else:
+        n = lib.pa_decode_workspace_bytes_for(B, Hq, Hkv, D, max_context_len, window,
+                                              partition_tokens, int(cache_dtype))
     if n == (1 << 64) - 1:
         raise PagedKVError(_lib.PA_ERR_INVALID, "invalid workspace query")
     return int(n)
@@ -244,7 +252,8 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     if out is None:
         out = torch.empty_like(query)
     _dev(out)
-    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens,
+                                  cache)
     if workspace is None:
         workspace = alloc_workspace(need, query.device)
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
@@ -419,7 +428,8 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
     B, Hq, D = query.shape
     NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
     bt_ptr, MBPS = _table(block_tables, B)
-    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens,
+                                  _cache_code(key_cache, query.dtype))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if ws_bytes < need:
         raise PagedKVError(_lib.PA_ERR_WORKSPACE, f"workspace needs {need} bytes")

@@ -140,6 +140,15 @@ def test_workspace_query():
     rows = 1 * 8 * 65
     assert lib.pa_decode_workspace_bytes(1, 8, 8, 64, 1 << 20, 0, 0) >= \
         2 * rnd(rows * 4) + rnd(rows * 64 * 4) + rnd(8 * 4)
+    # The per-format query: a 16-bit cache needs none here, a byte cache the
+    # balanced plan's slots.
+    rows = 32 * 32 * 16
+    assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == 0
+    for fmt in (_lib.PA_F8E4M3, _lib.PA_I8):
+        assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, fmt) == \
+            2 * rnd(rows * 4) + rnd(rows * 128 * 4) + rnd(32 * 8 * 4)
+    assert lib.pa_decode_workspace_bytes_for(-1, 8, 2, 128, 100, 0, 0, _lib.PA_BF16) == \
+        (1 << 64) - 1
     # Above 1024 sequences only the grid plan applies.
     n16 = lib.pa_decode_workspace_bytes(2048, 8, 8, 64, 4096, 0, 0)
     assert n16 == 0
