@@ -52,6 +52,14 @@ CASES = {
     "i8_aligned_d96": lambda: W.window_prefill_workload(
         "wq_i8_aligned", 166, B=2, Hq=6, Hkv=2, D=96, act="bf16", window=256,
         hist=[256, 512], chunk=[256, 64], cache="int8"),
+    # Empty chunks inside the batch, an empty history, a history of exactly
+    # the window.
+    "e4m3_empty_chunks_f16_d64": lambda: W.window_prefill_workload(
+        "wq_e4m3_empty", 167, B=4, Hq=8, Hkv=2, D=64, act="f16", window=64,
+        hist=[10, 100, 0, 64], chunk=[0, 30, 5, 0], cache="e4m3"),
+    "i8_empty_chunks_d64": lambda: W.window_prefill_workload(
+        "wq_i8_empty", 168, B=4, Hq=8, Hkv=2, D=64, act="bf16", window=64,
+        hist=[10, 100, 0, 64], chunk=[0, 30, 5, 0], cache="int8"),
 }
 
 
@@ -156,3 +164,40 @@ def test_window_prefill_quantised_ring_parity(name):
                 ob, orow = s_o // wl.BS, s_o % wl.BS
                 assert np.array_equal(gks[hb, :, hr], oks[ob, :, orow]), (b, p)
                 assert np.array_equal(gvs[hb, :, hr], ovs[ob, :, orow]), (b, p)
+
+
+@pytest.mark.parametrize("cache", ["e4m3", "int8"])
+def test_quantised_ring_identity_map(cache):
+    """Rings in a dense pool (sequence b's ring blocks b * M .. b * M + M - 1)
+    behind a NULL table: bitwise equal to the same rings behind the explicit
+    identity table, and within tolerance of the oracle."""
+    import dataclasses
+    wl = W.window_prefill_workload("wq_ident", 169, B=3, Hq=8, Hkv=2, D=128, act="bf16",
+                                   window=128, hist=[0, 70, 400], chunk=[90, 200, 31],
+                                   cache=cache)
+    M = wl.window // wl.BS
+    wl = dataclasses.replace(wl, block_tables=pool.identity_table(wl.B, M))
+    P.say(f"[window prefill, {cache} ring, identity map] hist={list(wl.hist_lens)} "
+          f"chunks={list(wl.chunk_lens)}")
+    pools = P.gpu_pools_i8(wl) if cache == "int8" else (*P.gpu_pools(wl), None, None)
+    sl, hk, hv = [], [], []
+    for b in range(wl.B):
+        pos = np.arange(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
+        sl.extend(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+        hk.append(wl.hist_k[b])
+        hv.append(wl.hist_v[b])
+    _write(wl, pools, _act(np.concatenate(hk), wl.act), _act(np.concatenate(hv), wl.act), sl)
+    kc, vc, ks, vs = pools
+    q, k, v = (_act(x, wl.act) for x in (wl.query, wl.chunk_k, wl.chunk_v))
+    outs = [ops.prefill_chunk_window(q, k, v, torch.from_numpy(wl.cu_q_lens).cuda(), kc, vc,
+                                     table, torch.from_numpy(wl.context_lens).cuda(),
+                                     int(wl.chunk_lens.max()), wl.scale, wl.window,
+                                     k_scale=wl.k_scale, v_scale=wl.v_scale, key_scales=ks,
+                                     value_scales=vs)
+            for table in (ops.IdentityMap(M), torch.from_numpy(wl.block_tables).cuda())]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref, _ = oracle_run(wl)
+    err = P.max_abs(P.out_f64(outs[0]), ref)
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL[cache]
