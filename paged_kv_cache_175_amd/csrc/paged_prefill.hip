@@ -526,13 +526,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // more than kSlack above it); it is then raised to the maximum over
         // the four lanes that hold the query (never lowered), and unchanged
         // maxima keep their accumulators as they are.
+        // The lane's maxima use the NaN-propagating maximum (gfx950's
+        // three-input v_maximum3_f32): fmaxf must quiet signalling NaNs in
+        // IEEE mode, which costs a canonicalising max per MFMA result.
+        // Scores here are finite or -inf, so both give the same value.
         float lmax[NQ];
 #pragma unroll
-        for (int t = 0; t < NQ; ++t)
-          lmax[t] = qk_scale_log2 * fmaxf(fmaxf(fmaxf(s_acc[0][t][0], s_acc[0][t][1]),
-                                                fmaxf(s_acc[0][t][2], s_acc[0][t][3])),
-                                          fmaxf(fmaxf(s_acc[1][t][0], s_acc[1][t][1]),
-                                                fmaxf(s_acc[1][t][2], s_acc[1][t][3])));
+        for (int t = 0; t < NQ; ++t) {
+          const f32x4 a = s_acc[0][t], c = s_acc[1][t];
+          const float m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), a[2]);
+          const float m2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], c[0]), c[1]);
+          const float m3 = __builtin_elementwise_maximum(c[2], c[3]);
+          lmax[t] = qk_scale_log2 *
+                    __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, m2), m3);
+        }
         auto raise_max = [&](int t) {
           float cm = fmaxf(lmax[t], shfl_xor_f(lmax[t], 16));
           cm = fmaxf(cm, shfl_xor_f(cm, 32));
