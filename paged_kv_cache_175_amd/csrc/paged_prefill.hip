@@ -500,8 +500,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // into the exponent's FMA, which saves a multiply per score.  The mask
       // is needed only where the page reaches past the earliest query of the
       // wave; the two cases are separate instantiations so that the common,
-      // unmasked one sees only products (canonical floats) and its maxima
-      // need no NaN quieting.
+      // unmasked one carries no per-score compares and selects.
       {
         if constexpr (kScaled) {
 #pragma unroll
