@@ -213,12 +213,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // o_acc[NT] is the all-ones tile: every row holds the running sum l.
   float m_run[NQ];
+  // Tile-major shapes (which have the registers for it) test raw maxima
+  // against a raw threshold: a raw score above m_thr is more than kSlack
+  // above m_run once scaled (m_thr = (m_run + kSlack) / scale; the scale is
+  // >= 0, checked by the host), which saves a multiply and an add per tile
+  // and page.  The others scale the maxima and test them against m_run.
+  float m_thr[NQ];
   f32x4 o_acc[NT + 1][NQ];
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
     // A window row can meet pages that lie wholly below its window before
     // its first live key: a finite floor keeps exp2(s - m) at 0 there.
     m_run[t] = WIN ? -1.0e30f : -INFINITY;
+    m_thr[t] = -INFINITY;
 #pragma unroll
     for (int n = 0; n <= NT; ++n) o_acc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -528,7 +535,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // The lane's maxima use the NaN-propagating maximum (gfx950's
         // three-input v_maximum3_f32): fmaxf must quiet signalling NaNs in
         // IEEE mode, which costs a canonicalising max per MFMA result.
-        // Scores here are finite or -inf, so both give the same value.
+        // Scores here are finite or -inf, so both give the same value.  The
+        // maxima stay raw until a raise; the test compares them with m_thr.
         float lmax[NQ];
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
@@ -536,24 +544,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const float m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), a[2]);
           const float m2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], c[0]), c[1]);
           const float m3 = __builtin_elementwise_maximum(c[2], c[3]);
-          lmax[t] = qk_scale_log2 *
-                    __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, m2), m3);
+          lmax[t] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, m2), m3);
+          if constexpr (!kTileMajor) lmax[t] *= qk_scale_log2;
         }
         auto raise_max = [&](int t) {
-          float cm = fmaxf(lmax[t], shfl_xor_f(lmax[t], 16));
+          const float lm = kTileMajor ? qk_scale_log2 * lmax[t] : lmax[t];
+          float cm = fmaxf(lm, shfl_xor_f(lm, 16));
           cm = fmaxf(cm, shfl_xor_f(cm, 32));
           const float m_new = fmaxf(m_run[t], cm);
           const float alpha = m_new == m_run[t] ? 1.f : fast_exp2(m_run[t] - m_new);
 #pragma unroll
           for (int n = 0; n <= NT; ++n) o_acc[n][t] *= alpha;
           m_run[t] = m_new;
+          if constexpr (kTileMajor) m_thr[t] = (m_new + kSlack) / qk_scale_log2;
         };
         if constexpr (kTileMajor) {
           // One test for all tiles, so that the block after it holds every
           // tile's exponentials and V MFMAs.
           bool raise = false;
 #pragma unroll
-          for (int t = 0; t < NQ; ++t) raise |= lmax[t] > m_run[t] + kSlack;
+          for (int t = 0; t < NQ; ++t) raise |= lmax[t] > m_thr[t];
           if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
             for (int t = 0; t < NQ; ++t) raise_max(t);
