@@ -301,8 +301,9 @@ pa_status pa_decode_append_i8(void* out, const void* query, const void* key, con
  * Query j of sequence b sits at absolute position context_lens[b] - C_b + j
  * and attends to positions 0 .. that position.
  * max_chunk_len   host-side upper bound of C_b (sizes the grid).
- * softmax_scale   finite and >= 0 (each lane's running maximum is taken
- *                 over raw scores and then scaled); else PA_ERR_INVALID.
+ * softmax_scale   finite and > 0 (each lane's running maximum is taken
+ *                 over raw scores and then scaled, and masked raw scores
+ *                 are -inf before scaling); else PA_ERR_INVALID.
  *                 The same holds for every prefill entry point below.
  * Caller contract: C_b <= context_lens[b]; table entries for logical blocks
  * < ceil(context_lens[b]/BS) lie in [0, NB).

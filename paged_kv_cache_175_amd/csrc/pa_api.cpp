@@ -500,9 +500,10 @@ pa_status prefill_common(void* out, const void* query, const int32_t* cu_q_lens,
   if (!pa::prefill_supported(D, Hq / Hkv, fmt_of(act_dtype), fmt_of(cache_dtype)))
     return fail(PA_ERR_UNSUPPORTED, "prefill supports head_dim 64/96/128 and Hq/Hkv <= 16");
   // The prefill kernel scales each lane's maximum raw score, which is the
-  // maximum scaled score only for a scale >= 0.
-  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
-    return fail(PA_ERR_INVALID, "prefill softmax_scale must be finite and >= 0");
+  // maximum scaled score only for a positive scale, and masks raw scores
+  // with -inf before scaling them (-inf * 0 would be NaN).
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+    return fail(PA_ERR_INVALID, "prefill softmax_scale must be finite and > 0");
   if (cache_dtype == PA_F8E4M3 &&
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
     return fail(PA_ERR_INVALID, "E4M3 scales must be finite and > 0");

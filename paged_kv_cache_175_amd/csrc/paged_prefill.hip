@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Tile-major shapes (which have the registers for it) test raw maxima
   // against a raw threshold: a raw score above m_thr is more than kSlack
   // above m_run once scaled (m_thr = (m_run + kSlack) / scale; the scale is
-  // >= 0, checked by the host), which saves a multiply and an add per tile
+  // > 0, checked by the host), which saves a multiply and an add per tile
   // and page.  The others scale the maxima and test them against m_run.
   float m_thr[NQ];
   f32x4 o_acc[NT + 1][NQ];

@@ -28,6 +28,26 @@ TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16}
 TOL = {"bf16": 1e-2, "f16": 1e-2, "e4m3": 2e-2, "int8": 2e-2}
 
 
+def sharp_tol(wl, v_parts) -> float:
+    """Output tolerance for a softmax whose weights sit on a few keys (a
+    softmax scale far above 1/sqrt(D)).  Each weight P_j is rounded to the
+    activation format before the V product (relative error <= u: 2^-9 for
+    bf16, 2^-12 for f16) and the row sum is taken from the same rounded
+    weights, so the output moves by at most u * max_j |V_j - out| / (1 - u)
+    <= 2u * max|V| (approximately).  When many keys share the weight the
+    errors average out and TOL holds; here they need not.  `v_parts`: the
+    V rows as activation bits (uint16 arrays)."""
+    bits = np.concatenate([np.asarray(x, dtype=np.uint16).reshape(-1) for x in v_parts])
+    if wl.act == "bf16":
+        v = (bits.astype(np.uint32) << 16).view(np.float32)
+        u = 2.0 ** -9
+    else:
+        v = bits.view(np.float16).astype(np.float32)
+        u = 2.0 ** -12
+    vmax = float(np.abs(v).max(initial=0.0))
+    return max(TOL[wl.cache], 2 * u * vmax / (1 - u))
+
+
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

@@ -184,6 +184,7 @@ def test_cache_write_rejects(args, status):
     (dict(Hq=6, Hkv=4), _lib.PA_ERR_INVALID),
     (dict(cu=0), _lib.PA_ERR_INVALID),
     (dict(scale=-0.1), _lib.PA_ERR_INVALID),       # maxima are scaled after the max
+    (dict(scale=0.0), _lib.PA_ERR_INVALID),        # masked -inf scores times 0
     (dict(scale=float("nan")), _lib.PA_ERR_INVALID),
     (dict(maxc=0, cu=0), _lib.PA_OK),
 ])
@@ -208,6 +209,7 @@ def test_prefill_rejects(args, status):
     (dict(act=_lib.PA_F8E4M3), _lib.PA_ERR_UNSUPPORTED),
     (dict(D=80), _lib.PA_ERR_UNSUPPORTED),
     (dict(scale=-1.0), _lib.PA_ERR_INVALID),
+    (dict(scale=0.0), _lib.PA_ERR_INVALID),
     (dict(maxc=0, cu=0), _lib.PA_OK),
 ])
 def test_prefill_window_rejects(args, status):

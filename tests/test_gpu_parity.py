@@ -211,6 +211,28 @@ PREFILL_CASES = {
 }
 
 
+@pytest.mark.parametrize("name,scale", [("prefix_small_d96", 1e-6), ("prefix_f16_d64", 1e-6),
+                                        ("gqa16_f16_fp8_d128", 1e-6), ("long_chunk_d96", 1.0),
+                                        ("gqa8_d64", 1.0), ("no_prefix", 1.0)])
+def test_prefill_softmax_scale_edges(name, scale):
+    """softmax_scale 1e-6 (nearly uniform weights: each output row is close
+    to the mean of its visible V rows; masked keys must still weigh
+    nothing) and 1.0 (raw scores of about +-sqrt(D) spread far beyond the
+    running maximum's slack, so the maxima are raised again and again),
+    against the oracle."""
+    import dataclasses
+    wl = dataclasses.replace(PREFILL_CASES[name](), scale=scale)
+    P.say(f"[prefill scale {scale}] {wl.name} D={wl.D} act={wl.act} cache={wl.cache}")
+    kc, vc = P.hip_prefill_setup(wl)
+    out = P.hip_prefill(wl, kc, vc)
+    torch.cuda.synchronize()
+    okc, ovc = P.oracle_prefill_setup(wl)
+    err = P.max_abs(P.out_f64(out), P.oracle_prefill(wl, okc, ovc))
+    tol = P.sharp_tol(wl, [wl.prefix_v, *wl.chunk_v]) if scale >= 1.0 else P.TOL[wl.cache]
+    P.say(f"    max-abs error {err:.3e} (tolerance {tol:.3e})")
+    assert err <= tol
+
+
 @pytest.mark.parametrize("name", list(PREFILL_CASES))
 def test_prefill_parity(name):
     wl = PREFILL_CASES[name]()

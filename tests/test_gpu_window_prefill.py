@@ -141,3 +141,23 @@ def test_window_prefill_parity(name):
             kh, vh = o_cache.get_row(gk, gv, s_h // wl.BS, s_h % wl.BS)
             ko, vo = o_cache.get_row(okc, ovc, s_o // wl.BS, s_o % wl.BS)
             assert np.array_equal(kh, ko) and np.array_equal(vh, vo), (b, p)
+
+
+@pytest.mark.parametrize("name,scale", [("full_ring_gqa4_d128", 1e-6),
+                                        ("chunk_over_window_f16_d64", 1e-6),
+                                        ("full_ring_gqa4_d128", 1.0),
+                                        ("gqa16_small_ring_d128", 1.0)])
+def test_window_prefill_softmax_scale_edges(name, scale):
+    """softmax_scale 1e-6 (nearly uniform weights over each query's window,
+    keys outside it still weighing nothing) and 1.0
+    (maxima raised again and again) through the window path, against the
+    oracle."""
+    import dataclasses
+    wl = dataclasses.replace(CASES[name](), scale=scale)
+    P.say(f"[window prefill scale {scale}] {wl.name} D={wl.D} act={wl.act} W={wl.window}")
+    out, _, _, _ = hip_run(wl)
+    ref, _, _ = oracle_run(wl)
+    err = P.max_abs(P.out_f64(out), ref)
+    tol = P.sharp_tol(wl, [*wl.hist_v, wl.chunk_v]) if scale >= 1.0 else P.TOL[wl.act]
+    P.say(f"    max-abs error {err:.3e} (tolerance {tol:.3e})")
+    assert err <= tol
