@@ -161,6 +161,27 @@ def test_balanced_decode_int8(name, append):
     assert err <= P.TOL["int8"]
 
 
+@pytest.mark.parametrize("name,scale", [("mix_g4_d128", 0.0), ("ring_g4_d128", 1e-6),
+                                        ("short_around_long_g8_d128", 1.0),
+                                        ("mha_d64_f16", 1.0)])
+def test_balanced_softmax_scale_edges(name, scale):
+    """Scales 0, 1e-6 and 1.0 through the balanced plan (cut items merged
+    through the workspace), against the oracle."""
+    import dataclasses
+    wl = dataclasses.replace(CASES[name](), scale=scale)
+    P.say(f"[balanced decode scale {scale}] {name} B={wl.B} cache={wl.cache}")
+    kc, vc = P.hip_decode_setup(wl)
+    out = P.hip_decode(wl, kc, vc)
+    torch.cuda.synchronize()
+    got = P.out_f64(out)
+    seqs = [b for b in range(wl.B) if wl.context_lens[b] > 0]
+    okc, ovc = P.oracle_decode_setup(wl, seqs)
+    err = P.max_abs(got[seqs], P.oracle_decode(wl, okc, ovc, seqs))
+    tol = P.sharp_tol(wl, [*wl.cached_v, wl.new_v]) if scale >= 1.0 else P.TOL[wl.cache]
+    P.say(f"    max-abs error {err:.3e} (tolerance {tol:.3e})")
+    assert err <= tol
+
+
 def test_balanced_repeat_same_workspace():
     """Three launches on one workspace: bitwise equal outputs, so every cut
     item's arrival counter was back at zero after each launch."""

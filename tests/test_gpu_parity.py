@@ -85,6 +85,29 @@ def test_decode_append_parity(name):
     _check_decode_append(DECODE_CASES[name]())
 
 
+@pytest.mark.parametrize("name,scale,part", [
+    ("mistral_small", 0.0, 0), ("mistral_small", 1e-6, 96), ("sliding_fp8", 0.0, 0),
+    ("sliding_small", 1e-6, 0), ("mistral_small", 1.0, 32), ("fp8_f16_mha_d64", 1.0, 0),
+    ("gqa2_bf16_d64", 1.0, 0), ("sliding_small", 1.0, 0)])
+def test_decode_softmax_scale_edges(name, scale, part):
+    """Decode scales every score before its maximum and mask, so it takes
+    any finite scale: 0 (uniform weights over the context), 1e-6, and 1.0
+    (weights on a few keys, maxima raised again and again), one pass and
+    split, against the oracle."""
+    import dataclasses
+    wl = dataclasses.replace(DECODE_CASES[name](), scale=scale)
+    P.say(f"[decode scale {scale}] {wl.name} D={wl.D} act={wl.act} cache={wl.cache} "
+          f"W={wl.window} part={part}")
+    kc, vc = P.hip_decode_setup(wl)
+    out = P.hip_decode(wl, kc, vc, part)
+    torch.cuda.synchronize()
+    okc, ovc = P.oracle_decode_setup(wl)
+    err = P.max_abs(P.out_f64(out), P.oracle_decode(wl, okc, ovc))
+    tol = P.sharp_tol(wl, [*wl.cached_v, wl.new_v]) if scale >= 1.0 else P.TOL[wl.cache]
+    P.say(f"    max-abs error {err:.3e} (tolerance {tol:.3e})")
+    assert err <= tol
+
+
 @pytest.mark.parametrize("part", [32, 96, 512])
 def test_decode_append_forced_splits(part):
     _check_decode_append(DECODE_CASES["mistral_small"](), partition_tokens=part)
