@@ -305,6 +305,7 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
                   value_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal chunked prefill over the paged cache; returns ``out`` ``[total_q, Hq, D]``.
 
+    ``softmax_scale`` must be finite and > 0 (the library rejects others).
     An int8 cache reads its scale pools (``pa_prefill_chunk_i8``)."""
     _dev(query, cu_q_lens, key_cache, value_cache, context_lens)
     _i32(cu_q_lens, context_lens)
@@ -349,7 +350,8 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     (``pa_prefill_chunk_window``); ``key`` / ``value`` ``[total_q, Hkv, D]``
     are the chunk's own K/V, written into the ring only after this call.  An
     E4M3 ring (uint8) reads with ``k_scale`` / ``v_scale``, an INT8 ring
-    with its scale pools (``pa_prefill_chunk_window_quant``)."""
+    with its scale pools (``pa_prefill_chunk_window_quant``).
+    ``softmax_scale`` must be finite and > 0."""
     _dev(query, key, value, cu_q_lens, key_cache, value_cache, context_lens)
     _i32(cu_q_lens, context_lens)
     total_q, Hq, D = query.shape
