@@ -604,6 +604,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   int bt_pre = 0;
   if (S == 1 && block_tables != nullptr)
     bt_pre = block_tables[(size_t)b * MBPS + min(wave + W * lane, MBPS - 1)];
+  // The query operands, and in append mode the decoded row, depend on
+  // neither the length nor the table: their loads go out in the same first
+  // round, so the first page's loads wait for one round trip, not three.
+  vec qb[KSTEPS];
+  q_operand<D, G, AF>(qb, query + ((size_t)b * Hq + g * G) * D, lane);
+  static_assert(D <= 64 * W, "one head-dimension element per thread");
+  constexpr int DPL = CF == FMT_I8 ? (D + 63) / 64 : 1;
+  uint16_t kx = 0, vx = 0;
+  uint16_t krow[DPL], vrow[DPL];          // INT8: this lane's share of the row
+  const int d_new = threadIdx.x;
+  const size_t new_src = ((size_t)b * Hkv + g) * D;
+  if (new_key != nullptr) {
+    if (d_new < D) {
+      kx = new_key[new_src + d_new];
+      vx = new_value[new_src + d_new];
+    }
+    if constexpr (CF == FMT_I8) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const int d = lane + 64 * i;
+        krow[i] = d < D ? new_key[new_src + d] : 0;
+        vrow[i] = d < D ? new_value[new_src + d] : 0;
+      }
+    }
+  }
   int L = context_lens[b];
   if (window > 0) L = min(L, window);
   if (L <= 0) {
@@ -629,44 +654,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // the stored cache elements in LDS; the one wave that
   // reads the page patches the row into its page registers, so nothing in
   // this launch depends on the store becoming visible.  The row's loads
-  // are issued here, its stores only after the first page's loads, so the
-  // append adds no memory round trip before the page stream starts.
-  static_assert(D <= 64 * W, "one head-dimension element per thread");
+  // went out with the first round (above), its stores only after the first
+  // page's loads, so the append adds no memory round trip before the page
+  // stream starts.
   int row_new = -1, k_new = -1, w_new = -1;
   bool append = false;
-  size_t new_page = 0, new_srow = 0;
-  uint16_t kx = 0, vx = 0;
+  int pg_new = 0;                         // logical page of the new row
   float new_ks = 0.f, new_vs = 0.f;       // INT8: the new row's scales
-  constexpr int DPL = CF == FMT_I8 ? (D + 63) / 64 : 1;
-  uint16_t krow[DPL], vrow[DPL];          // INT8: this lane's share of the row
-  const int d_new = threadIdx.x;
   if (new_key != nullptr) {
     const int ctx = context_lens[b];
     const int r_new = window > 0 ? (ctx - 1) % window : ctx - 1;
-    const int pg_new = r_new / kPage;
+    pg_new = r_new / kPage;
     if (pg_new >= pa && pg_new < pb) {
       append = true;
       row_new = r_new - pg_new * kPage;
       w_new = (pg_new - pa) % W;
       k_new = (pg_new - pa) / W;
-      const int phys = block_tables ? block_tables[(size_t)b * MBPS + pg_new] : b * MBPS + pg_new;
-      new_page = ((size_t)phys * Hkv + g) * (size_t)kPage * D;
-      new_srow = ((size_t)phys * Hkv + g) * kPage + row_new;
-      const size_t src = ((size_t)b * Hkv + g) * D;
-      if (d_new < D) {
-        kx = new_key[src + d_new];
-        vx = new_value[src + d_new];
-      }
-      if constexpr (CF == FMT_I8) {
-        // Every wave reduces the whole row for its scales itself (below),
-        // so no wave waits for another; the loads go out now.
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          const int d = lane + 64 * i;
-          krow[i] = d < D ? new_key[src + d] : 0;
-          vrow[i] = d < D ? new_value[src + d] : 0;
-        }
-      }
     }
   }
   // Store the row and stage it in LDS, then make the LDS copy visible to
@@ -692,6 +695,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
     if (append && d_new < D) {
+      // The row's block is looked up only here, after the first page's
+      // loads: the stores are the only use of it.
+      const int phys = block_tables ? block_tables[(size_t)b * MBPS + pg_new] : b * MBPS + pg_new;
+      const size_t new_page = ((size_t)phys * Hkv + g) * (size_t)kPage * D;
+      const size_t new_srow = ((size_t)phys * Hkv + g) * kPage + row_new;
       const float kes = CF == FMT_I8 ? new_ks : k_enc_scale;
       const float ves = CF == FMT_I8 ? new_vs : v_enc_scale;
       const uint32_t kq = encode_elem<CF, AF>(kx, kes);
@@ -719,8 +727,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int n = 0; n <= NT; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (npg > 0) {
-    vec qb[KSTEPS];
-    q_operand<D, G, AF>(qb, query + ((size_t)b * Hq + g * G) * D, lane);
     const vec ones = ones_operand<AF>();
 
     // Page ids (block * Hkv + g) of this wave's pages, lane k holding its
