@@ -23,9 +23,12 @@
  *    blocks that may be shared between sequences; pa_prefill_chunk() is that
  *    causal attention over a block table.
  *  - "libmir-metal 0.2.0, src/native/trace/kv.rs", fn build: the pages are
- *    head-major, which fixes the layout below; a quantised cache keeps packed
- *    INT8 pages with one FP32 scale per token and head and dequantises inside
- *    paged attention for prefill and decode: the *_i8 entry points.
+ *    head-major (one page per block and KV head, the layout below keeps
+ *    that; the order of elements inside a page is this library's own
+ *    choice, made for the matrix-core operands); a quantised cache keeps
+ *    packed INT8 pages with one FP32 scale per token and head and
+ *    dequantises inside paged attention for prefill and decode: the *_i8
+ *    entry points.
  *
  * Conventions for every entry point:
  *
@@ -35,7 +38,8 @@
  *    between calls.
  *  - Cache pools are head-major: one (block, KV head) page is a contiguous
  *    run of block_size * head_dim elements, pages ordered [num_blocks]
- *    [num_kv_heads].  Inside a page (t = row 0..block_size-1, d = 0..D-1):
+ *    [num_kv_heads].  Inside a page (t = row 0..block_size-1, d = 0..D-1),
+ *    not row-major [BS][D] but tiled, as this library lays it out:
  *      key page   [D/8][block_size][8]  element (t, d) at ((d/8)*BS + t)*8 + d%8
  *      value page [D][block_size]       element (t, d) at d*BS + t
  *    (so the key pool is [NB][Hkv][D/8][BS][8] and the value pool
@@ -80,6 +84,9 @@ extern "C" {
 #endif
 
 typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F8E4M3 = 2, PA_I8 = 3 } pa_dtype;
+
+/* Counters at the start of every decode workspace, at least (see pa_decode). */
+#define PA_DECODE_MIN_COUNTERS 16384
 
 typedef enum {
   PA_OK = 0,
@@ -209,18 +216,27 @@ size_t pa_decode_workspace_bytes_for(int32_t B, int32_t Hq, int32_t Hkv, int32_t
  *                 lengths (a sequence cut between ranges is merged like the
  *                 splits).  Results do not depend on it beyond rounding.
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
- *                 (may be NULL when that is 0), kept by the caller across
- *                 calls: besides the split partials it holds one arrival
- *                 counter per (sequence, KV head), which must be zero
- *                 before the workspace is first used (zero-fill it once
- *                 after allocating it); every call leaves them zero.  Calls
- *                 that share a workspace must not overlap in time.  The
- *                 last split (or range) of each (sequence, KV head) to
- *                 finish merges the partials inside the same launch.
+ *                 (may be NULL when that is 0), 256-byte aligned, kept by
+ *                 the caller across calls.  It starts with the counter
+ *                 region: one int32 arrival counter per (sequence, KV head),
+ *                 max(B*Hkv, PA_DECODE_MIN_COUNTERS) of them, at byte 0;
+ *                 the split partials follow it.  The counter region must be
+ *                 zero when a call that needs a workspace starts; the call
+ *                 leaves it zero.  So a workspace zero-filled once stays
+ *                 valid for every call with B*Hkv <= PA_DECODE_MIN_COUNTERS,
+ *                 whatever the other arguments; a call with a larger B*Hkv
+ *                 than the last call that used the workspace needs its first
+ *                 4*B*Hkv bytes zeroed first (that earlier call's partials
+ *                 may lie there).  Calls that share a workspace must not
+ *                 overlap in time.  The last split (or range) of each
+ *                 (sequence, KV head) to finish merges the partials inside
+ *                 the same launch.
  * Output is out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t with KV
  * head h / (Hq/Hkv); an empty context gives zeros.  Caller contract: table
  * entries read (logical blocks < ceil(L/BS)) lie in [0, NB);
- * context_lens[b] <= max_context_len and (window == 0) <= MBPS*BS.
+ * context_lens[b] <= max_context_len and (window == 0) <= MBPS*BS.  A
+ * length above max_context_len is clamped to it on the device (a wrong
+ * result for that sequence, never a read past the pages the plan covers).
  */
 pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     const void* value_cache, const int32_t* block_tables,
@@ -305,8 +321,9 @@ pa_status pa_decode_append_i8(void* out, const void* query, const void* key, con
  *                 over raw scores and then scaled, and masked raw scores
  *                 are -inf before scaling); else PA_ERR_INVALID.
  *                 The same holds for every prefill entry point below.
- * Caller contract: C_b <= context_lens[b]; table entries for logical blocks
- * < ceil(context_lens[b]/BS) lie in [0, NB).
+ * Caller contract: C_b <= context_lens[b] <= MBPS*BS; table entries for
+ * logical blocks < ceil(context_lens[b]/BS) lie in [0, NB).  A length above
+ * MBPS*BS is clamped to it on the device.
  */
 pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* cu_q_lens,
                            const void* key_cache, const void* value_cache,

@@ -29,6 +29,10 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int B, Hkv, G, D, MBPS, window;
+  // Tokens a sequence may attend to at most: max_context_len, capped at the
+  // window.  The kernels clamp each length to it, so a length above the
+  // host's bound cannot take a wave past the pages the plan sized it for.
+  int len_cap;
   int S;  // grid mode: splits per (sequence, KV head); balanced: partials per item
   int W;  // waves per workgroup (4 or 8)
   int N;  // balanced mode: workgroups (0 = grid mode)
@@ -38,7 +42,7 @@ struct DecodeArgs {
   float* ws_m;  // [B*Hq*S]
   float* ws_l;  // [B*Hq*S]
   float* ws_o;  // [B*Hq*S*D]
-  int* ws_count;  // [B*Hkv] split arrival counters, zero between launches
+  int* ws_count;  // split arrival counters (B*Hkv used), zero between launches
   const void* new_key;    // append mode: [B][Hkv][D] act, or null
   const void* new_value;
   float* key_scales;    // INT8 cache: [NB][Hkv][BS] fp32 (written by an append)

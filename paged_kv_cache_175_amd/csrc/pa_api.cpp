@@ -17,6 +17,9 @@
 #include <atomic>
 
 #include "launch.hpp"
+#include "plan.hpp"
+
+namespace plan = pa::plan;
 
 namespace {
 
@@ -50,12 +53,9 @@ bool cache_ok(pa_dtype act, pa_dtype cache) { return cache == act || cache == PA
 
 size_t elem_bytes(pa_dtype d) { return d == PA_F8E4M3 ? 1 : 2; }
 
-constexpr int kBlock = 32;
+constexpr int kBlock = plan::kBlock;
 constexpr int kMaxGridDim = 65535;  // decode grid (splits, Hkv, B); writer and copy grids
-constexpr long long kTargetWaves = 2048;
-constexpr size_t kAlign = 256;
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr size_t kAlign = plan::kAlign;
 
 // Compute units of the current device, queried once per device.
 int device_cus() {
@@ -71,89 +71,13 @@ int device_cus() {
   return n;
 }
 
-// Decode plan, a dispatch by cache format and context length.
-//
-// Grid mode (decode_split): a workgroup of W waves handles one split of the
-// pages of one (sequence, KV head).  Below kMinSplitContext tokens every
-// sequence is one split: one launch, no workspace (a split's merge costs
-// more than it saves there).  From kMinSplitContext on, the automatic choice
-// aims at ~2048 resident waves (8 per CU on the 256 CUs of an MI355X):
-// W = 8 while B * Hkv <= 256, else W = 4; S splits per sequence so that
-// B * Hkv * S * W ~ 2048, with at least one page per wave on the longest
-// sequence and at most kMaxAutoSplits.  A wave holds the block-table entries
-// of its pages in one register, so a split spans at most 64 * W pages.
-// partition_tokens > 0 forces S = ceil(len / partition_tokens).
-//
-// Balanced mode (decode_balanced), for E4M3 and INT8 caches from
-// kMinSplitContext tokens on (partition_tokens == 0): the batch's pages are
-// cut into equal ranges, one per workgroup (W = 8, a multiple of the CU
-// count of workgroups), whatever the mix of context lengths; S is then the
-// number of partial slots per (sequence, KV head).  Measured on the C3 shape
-// (B = 64, 1024..8192 tokens): INT8 131 -> 118 us, E4M3 118.5 -> 117.4 us.
-// With 16-bit caches the grid plan stayed faster (Mistral batch 57.6 vs
-// 59.9 us; rolling batch 27.6 vs 29.8 us): its prefix scan and the merges of
-// the sequences cut between ranges cost more than the balance gains there.
-struct Plan {
-  int S;          // grid mode: splits per sequence; balanced: partial slots per item
-  int W;
-  bool balanced;  // one equal range of the batch's pages per workgroup
-};
-
-constexpr long long kMinSplitContext = 1024;
-// The last split to finish merges the partials 16 per memory round trip;
-// more than 16 automatic splits cost more in that merge than they gain
-// (single sequence, 8192 tokens: 16 splits 12.9 us, 32 splits 15.5 us).
-constexpr long long kMaxAutoSplits = 16;
-// Balanced mode (decode_balanced): the kernel keeps the batch's page prefix
-// sums in LDS, for at most kMaxBalancedB sequences.
-constexpr int kMaxBalancedB = 1024;
-constexpr long long kMinBalancedSlots = 16;
-
-bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens, bool byte_cache,
-               Plan* p) {
-  long long L = max_len;
-  if (window > 0 && window < L) L = window;
-  if (L < 1) L = 1;
-  if (partition_tokens < 0 || partition_tokens % kBlock != 0) return false;
-  const long long pages = (L + kBlock - 1) / kBlock;
-  const long long pairs = (long long)B * Hkv;
-  if (byte_cache && partition_tokens == 0 && L >= kMinSplitContext && B <= kMaxBalancedB &&
-      pairs * pages < (1LL << 31)) {
-    // Balanced mode: ranges of at most 64 * W pages (a wave's table
-    // register), and partial slots enough that no item spans more of them.
-    p->balanced = true;
-    p->W = 8;
-    p->S = (int)std::max(kMinBalancedSlots, (pages + 64LL * p->W - 1) / (64LL * p->W) + 1);
-    return true;
-  }
-  p->balanced = false;
-  const int W = pairs > 256 ? 4 : 8;
-  long long S;
-  if (partition_tokens > 0) {
-    S = (L + partition_tokens - 1) / partition_tokens;
-  } else if (L < kMinSplitContext) {
-    S = 1;
-  } else {
-    S = pairs > 0 ? kTargetWaves / (pairs * W) : 1;
-    S = std::min(S, pages / W);
-    S = std::min(S, kMaxAutoSplits);
-    S = std::max(S, 1LL);
-  }
-  S = std::max(S, (pages + 64LL * W - 1) / (64LL * W));
-  if (S > 65535) return false;
-  p->S = (int)S;
-  p->W = W;
-  return true;
-}
-
-// Workspace of a split plan: m and l [B*Hq*S], o [B*Hq*S*D] fp32, then the
-// split arrival counters [B*Hkv] int32, each region 256-byte aligned.
-size_t workspace_for(int B, int Hq, int Hkv, int D, const Plan& p) {
-  if (p.S <= 1) return 0;
-  const size_t rows = (size_t)B * Hq * p.S;
-  return 2 * round_up(rows * sizeof(float), kAlign) + round_up(rows * D * sizeof(float), kAlign) +
-         round_up((size_t)B * Hkv * sizeof(int), kAlign);
-}
+using plan::Plan;
+using plan::make_plan;
+using plan::workspace_for;
+using plan::ws_layout;
+using plan::WsLayout;
+using plan::counter_bytes;
+using plan::kMinCounters;
 
 }  // namespace
 
@@ -368,16 +292,13 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   a.D = D;
   a.MBPS = MBPS;
   a.window = window;
+  a.len_cap = (int)plan::len_cap(max_context_len, window);
   a.S = p.S;
   a.W = p.W;
   if (p.balanced) {
-    // One range per CU, or a multiple of the CU count so that no range
-    // exceeds 64 * W pages.
-    const long long L = window > 0 ? std::min(window, max_context_len) : max_context_len;
-    const long long tmax = (long long)B * Hkv * ((L + kBlock - 1) / kBlock);
     const long long cus = device_cus();
     if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
-    a.N = (int)(cus * std::max(1LL, (tmax + cus * 64 * p.W - 1) / (cus * 64 * p.W)));
+    a.N = (int)plan::balanced_workgroups(B, Hkv, max_context_len, window, cus, p.W);
     a.stream_k = 1;
   }
   a.act = fmt_of(act_dtype);
@@ -386,13 +307,12 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
-    const size_t rows = (size_t)B * Hq * p.S;
+    const WsLayout l = ws_layout(B, Hq, Hkv, D, p.S);
     char* w = static_cast<char*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(w);
-    a.ws_l = reinterpret_cast<float*>(w + round_up(rows * sizeof(float), kAlign));
-    a.ws_o = reinterpret_cast<float*>(w + 2 * round_up(rows * sizeof(float), kAlign));
-    a.ws_count = reinterpret_cast<int*>(w + 2 * round_up(rows * sizeof(float), kAlign) +
-                                        round_up(rows * D * sizeof(float), kAlign));
+    a.ws_count = reinterpret_cast<int*>(w);
+    a.ws_m = reinterpret_cast<float*>(w + l.m);
+    a.ws_l = reinterpret_cast<float*>(w + l.l);
+    a.ws_o = reinterpret_cast<float*>(w + l.o);
   }
   a.new_key = new_key;
   a.new_value = new_value;
@@ -480,6 +400,7 @@ pa_status pa_decode_append_i8(void* out, const void* query, const void* key, con
 }
 
 }  // extern "C"
+
 
 namespace {
 

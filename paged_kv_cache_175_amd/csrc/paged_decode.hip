@@ -56,6 +56,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "plan.hpp"
 
 namespace pa {
 
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int Hkv, int MBPS, int window, int S, float qk_scale_log2, float v_scale,
+    int Hkv, int MBPS, int window, int len_cap, int S, float qk_scale_log2, float v_scale,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
     int* __restrict__ ws_count, const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
     float k_enc_scale, float v_enc_scale, float* __restrict__ key_scales,
@@ -629,8 +630,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
   }
-  int L = context_lens[b];
-  if (window > 0) L = min(L, window);
+  // Clamped to the host's bound: the split plan sized S and W for it (at
+  // most 64 pages per wave, the lanes of its table register).
+  const int L = min(context_lens[b], len_cap);
   if (L <= 0) {
     // Empty context: zeros, written once by split 0.
     if (s == 0) {
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 // grid mode).  Items are handled in rounds of at most SEGS items (the LDS
 // holds one partial per wave and item of a round).
 
-constexpr int kMaxBalancedB = 1024;
+constexpr int kMaxBalancedB = plan::kMaxBalancedB;
 
 template <int D, int G, int W>
 constexpr int balanced_segs() {
@@ -832,7 +834,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int B,
-    int Hkv, int MBPS, int window, int Smax, int stream_k, float qk_scale_log2, float v_scale,
+    int Hkv, int MBPS, int window, int len_cap, int Smax, int stream_k, float qk_scale_log2,
+    float v_scale,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
     int* __restrict__ ws_count, const uint16_t* __restrict__ new_key,
     const uint16_t* __restrict__ new_value, float k_enc_scale, float v_enc_scale,
@@ -888,7 +891,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (bi < B) {
       const int ctx = context_lens[bi];
       ctx_lds[bi] = ctx;
-      const int L = window > 0 ? min(ctx, window) : ctx;
+      // Clamped to the host's bound, which sized the ranges (at most 64 * W
+      // pages each) and the partial slots per item.
+      const int L = min(ctx, len_cap);
       P = L > 0 ? (L + kPage - 1) / kPage : 0;
     }
     int x = P, mx = P;
@@ -915,15 +920,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int T = Hkv * pref[B];           // pages of the batch (host: < 2^31)
   // Range size: equal shares of N, at least one page per wave, few enough
   // workgroups per item for the workspace (Smax partials), and a multiple of
-  // W.
-  int c = (T + N - 1) / N;
-  c = max(c, (pmax_lds + Smax - 2) / (Smax - 1));
-  c = max(c, W);
-  c = (c + W - 1) / W * W;  // every wave of a one-round range gets c / W pages
+  // W (every wave of a one-round range gets c / W pages).
+  const int c = plan::balanced_range_pages(T, N, pmax_lds, Smax, W);
 
   // Sequences with no context get zeros (their items hold no pages).
   for (int b = wg; b < B; b += N) {
-    if (ctx_lds[b] <= 0)
+    if (min(ctx_lds[b], len_cap) <= 0)
       for (int i = threadIdx.x; i < Hq * D; i += 64 * W) out[(size_t)b * Hq * D + i] = 0;
   }
   if ((long long)wg * c >= T) return;
@@ -968,7 +970,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       const int P = pref[sb + 1] - pref[sb];
       const int ctx = ctx_lds[sb];
       soff = hkv * pref[sb] + sg * P;
-      sL = win > 0 ? min(ctx, win) : ctx;
+      sL = min(ctx, len_cap);
       slo = max(x0, soff);
       shi = min(x1, soff + P);
       if (new_key != nullptr && shi > slo) {
@@ -1251,7 +1253,7 @@ hipError_t launch_grid(const DecodeArgs& a, float qk, float vs, hipStream_t stre
   hipLaunchKernelGGL((decode_split<D, G, CF, AF, W>), dim3(a.S, a.Hkv, a.B), dim3(64 * W), 0,
                      stream, (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
                      (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv, a.MBPS,
-                     a.window, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
+                     a.window, a.len_cap, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
                      (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
                      a.v_scale, a.key_scales, a.value_scales);
   return hipGetLastError();
@@ -1268,7 +1270,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((decode_balanced<D, G, CF, AF, 8>), dim3(a.N), dim3(512), 0, stream,
                          (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
                          (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.B, a.Hkv,
-                         a.MBPS, a.window, a.S, a.stream_k, qk, vs, a.ws_m, a.ws_l, a.ws_o,
+                         a.MBPS, a.window, a.len_cap, a.S, a.stream_k, qk, vs, a.ws_m, a.ws_l, a.ws_o,
                          a.ws_count, (const uint16_t*)a.new_key, (const uint16_t*)a.new_value,
                          a.k_scale, a.v_scale, a.key_scales, a.value_scales);
       return hipGetLastError();

@@ -172,7 +172,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int C = cu_q_lens[b + 1] - q_begin;
   const int rows = C * G;
   if (x * RW >= rows) return;
-  const int ctx = context_lens[b];
+  // A full cache holds at most MBPS * BS positions (the table row); a length
+  // above that is clamped so no table read leaves the row.  The window path
+  // indexes its ring modulo the window, inside the row whatever the length.
+  const int ctx = WIN ? context_lens[b] : min(context_lens[b], MBPS * BS);
   const int first_pos = ctx - C;               // absolute position of query 0
   const int last_row_wg = min(rows, x * RW + RW) - 1;
   // Key pages [p_lo, p_lo + npages): from the earliest key any row of the

@@ -213,12 +213,56 @@ def decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: i
     return int(n)
 
 
+# The decode workspace begins with its split arrival counters: 4 bytes per
+# (sequence, KV head), at least MIN_COUNTERS of them (include/pa.h).  They
+# must be zero when a call starts; a call leaves its own counters at zero and
+# writes its partials just past its counter region.  So once zeroed, the
+# counters stay valid for every later call whose B * Hkv does not exceed that
+# of the last call that wrote partials (or MIN_COUNTERS); a larger one finds
+# partials where its counters lie and has them zeroed first.  A workspace
+# tensor records how many leading counters are known to be zero.
+MIN_COUNTERS = 16384
+_CLEAN = "_pa_clean_counters"
+
+
 def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """Decode workspace, zero-filled (its split counters must start at zero;
-    every decode leaves them at zero, so it can be reused as it is)."""
+    """Decode workspace, zero-filled: reusable across calls of any shape
+    through :func:`decode` / :func:`prepare_decode`, which zero its counters
+    again when a call has more (sequence, KV head) pairs than the workspace
+    is known to have clean."""
     if nbytes == 0:
         return None
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    setattr(ws, _CLEAN, nbytes // 4)
+    return ws
+
+
+def _check_workspace(workspace: torch.Tensor, device) -> None:
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, the query on {device}")
+
+
+def _ready_counters(workspace: Optional[torch.Tensor], need: int, pairs: int) -> None:
+    """Zero the workspace's counters for a call over ``pairs`` (sequence, KV
+    head) pairs if they may hold partials of an earlier call, then record
+    what the call leaves clean."""
+    if workspace is None or need == 0:
+        return
+    clean = getattr(workspace, _CLEAN, MIN_COUNTERS)
+    if pairs > clean:
+        workspace[:4 * pairs].zero_()
+    # The call writes partials from its counter region's end on.
+    setattr(workspace, _CLEAN, max(pairs, MIN_COUNTERS))
+
+
+def _check_out(out: torch.Tensor, like: torch.Tensor) -> None:
+    if out.shape != like.shape or out.dtype != like.dtype or out.device != like.device:
+        raise ValueError(f"out must be {tuple(like.shape)} {like.dtype} on {like.device}")
+    _dev(out)
 
 
 def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
@@ -251,13 +295,18 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     cache = _cache_code(key_cache, query.dtype)
     if out is None:
         out = torch.empty_like(query)
-    _dev(out)
+    _check_out(out, query)
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens,
                                   cache)
     if workspace is None:
         workspace = alloc_workspace(need, query.device)
+    else:
+        _check_workspace(workspace, query.device)
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    if ws_bytes < need:
+        raise PagedKVError(_lib.PA_ERR_WORKSPACE, f"workspace needs {need} bytes (got {ws_bytes})")
+    _ready_counters(workspace, need, B * Hkv)
     lib = _lib.load()
     sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
     if sc is not None:
@@ -321,7 +370,7 @@ def prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, key_cache: torch
     cache = _cache_code(key_cache, query.dtype)
     if out is None:
         out = torch.empty_like(query)
-    _dev(out)
+    _check_out(out, query)
     lib = _lib.load()
     sc = _scales(cache, key_scales, value_scales, NB, Hkv, BS)
     if sc is not None:
@@ -370,7 +419,7 @@ def prefill_chunk_window(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     cache = _cache_code(key_cache, query.dtype)
     if out is None:
         out = torch.empty_like(query)
-    _dev(out)
+    _check_out(out, query)
     if cache == act:
         _lib.check(_lib.load().pa_prefill_chunk_window(
             out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
@@ -425,16 +474,20 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
                    k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
                    partition_tokens: int = 0, new_key=None, new_value=None,
                    key_scales=None, value_scales=None):
-    _dev(query, key_cache, value_cache, context_lens, out)
+    _dev(query, key_cache, value_cache, context_lens)
     _i32(context_lens)
+    _check_out(out, query)
     B, Hq, D = query.shape
     NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
     bt_ptr, MBPS = _table(block_tables, B)
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, window, partition_tokens,
                                   _cache_code(key_cache, query.dtype))
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _check_workspace(workspace, query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     if ws_bytes < need:
         raise PagedKVError(_lib.PA_ERR_WORKSPACE, f"workspace needs {need} bytes")
+    pairs = B * Hkv
     lib = _lib.load()
     cache = _cache_code(key_cache, query.dtype)
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
@@ -466,7 +519,12 @@ def prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
                 key_cache.data_ptr(), value_cache.data_ptr()) + tail
         fn = lib.pa_decode_append
 
+    # The counter check is host-side bookkeeping: a zero fill is launched
+    # only when another call's partials may lie where this call's counters do.
+    _ready_counters(workspace, need, pairs)
+
     def call():
+        _ready_counters(workspace, need, pairs)
         _lib.check(fn(*args))
     return call
 
@@ -475,8 +533,9 @@ def prepare_prefill_chunk(query, cu_q_lens, key_cache, value_cache, block_tables
                           max_chunk_len: int, softmax_scale: float, out,
                           k_scale: float = 1.0, v_scale: float = 1.0,
                           key_scales=None, value_scales=None):
-    _dev(query, cu_q_lens, key_cache, value_cache, context_lens, out)
+    _dev(query, cu_q_lens, key_cache, value_cache, context_lens)
     _i32(cu_q_lens, context_lens)
+    _check_out(out, query)
     total_q, Hq, D = query.shape
     NB, Hkv, BS, _ = _pool_geometry(key_cache, value_cache)
     B = context_lens.numel()

@@ -1,0 +1,150 @@
+// plan_check.cpp -- host-only check of the decode plan's invariants
+// (paged_kv_cache_175_amd/csrc/plan.hpp), which the kernels rely on for
+// staying inside their buffers:
+//
+//   grid mode     every wave of every split holds at most kPagesPerWave
+//                 pages (its table register), for every length up to the
+//                 length cap; at most 65535 splits;
+//   balanced mode a range spans at most kPagesPerWave * W pages, the ranges
+//                 cover the batch, and no item meets more ranges than it has
+//                 partial slots, for random length mixes up to the cap;
+//   workspace     the counter region at offset 0 holds B*Hkv counters and
+//                 is the same region for every shape with B*Hkv <=
+//                 kMinCounters; the partial regions follow it, disjoint.
+//
+// Built with g++ and run by tests/test_plan_host.py.  Prints one line and
+// exits 0 when every case holds, 1 (naming the case) otherwise.
+
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "../paged_kv_cache_175_amd/csrc/plan.hpp"
+
+using namespace pa::plan;
+
+static long long g_cases = 0;
+
+#define CHECK(cond, ...)                                   \
+  do {                                                     \
+    if (!(cond)) {                                         \
+      std::printf("FAIL %s: ", #cond);                     \
+      std::printf(__VA_ARGS__);                            \
+      std::printf("\n");                                   \
+      std::exit(1);                                        \
+    }                                                      \
+  } while (0)
+
+static long long pages_of(long long L) { return L > 0 ? (L + kBlock - 1) / kBlock : 0; }
+
+static void check_grid(int B, int Hkv, int max_len, int window, int part, const Plan& p) {
+  const long long cap = len_cap(max_len, window);
+  CHECK(p.S >= 1 && p.S <= 65535, "S=%d", p.S);
+  CHECK(p.W == 4 || p.W == 8, "W=%d", p.W);
+  // Lengths the kernel may meet after clamping: a spread over [1, cap].
+  std::vector<long long> lens = {1, 2, 31, 32, 33, 63, 64, 65, cap, cap - 1, cap - 31, cap / 2,
+                                 cap / 3 + 7};
+  for (long long L : lens) {
+    if (L < 1 || L > cap) continue;
+    const long long P = pages_of(L);
+    for (int s = 0; s < p.S; ++s) {
+      const long long a = (long long)s * P / p.S, b = (long long)(s + 1) * P / p.S;
+      for (int w = 0; w < p.W; ++w) {
+        const long long npg = b - a > w ? (b - a - w + p.W - 1) / p.W : 0;
+        CHECK(npg <= kPagesPerWave, "B=%d Hkv=%d max_len=%d window=%d part=%d L=%lld s=%d npg=%lld",
+              B, Hkv, max_len, window, part, L, s, npg);
+      }
+    }
+    ++g_cases;
+  }
+}
+
+static void check_balanced(std::mt19937_64& rng, int B, int Hkv, int max_len, int window,
+                           const Plan& p) {
+  const long long cap = len_cap(max_len, window);
+  CHECK(p.W == 8 && p.S >= 2, "W=%d S=%d", p.W, p.S);
+  for (long long cus : {1LL, 80LL, 256LL, 304LL}) {
+    const long long N = balanced_workgroups(B, Hkv, max_len, window, cus, p.W);
+    CHECK(N >= 1 && N % cus == 0 && N < (1LL << 31), "N=%lld", N);
+    for (int trial = 0; trial < 6; ++trial) {
+      // Length mixes: all at the cap, one long among short ones, uniform.
+      std::vector<long long> P(B);
+      for (int b = 0; b < B; ++b) {
+        long long L;
+        if (trial == 0) L = cap;
+        else if (trial == 1) L = b == 0 ? cap : 1;
+        else if (trial == 2) L = b == B - 1 ? cap : 0;
+        else L = std::uniform_int_distribution<long long>(0, cap)(rng);
+        P[b] = pages_of(L);
+      }
+      long long T = 0, pmax = 0;
+      for (long long x : P) {
+        T += Hkv * x;
+        pmax = x > pmax ? x : pmax;
+      }
+      CHECK(T < (1LL << 31), "T=%lld", T);
+      const long long c = balanced_range_pages((int)T, (int)N, (int)pmax, p.S, p.W);
+      CHECK(c >= p.W && c % p.W == 0, "c=%lld", c);
+      CHECK(c <= kPagesPerWave * p.W, "B=%d Hkv=%d max_len=%d window=%d cus=%lld c=%lld", B, Hkv,
+            max_len, window, cus, c);
+      CHECK(N * c >= T, "ranges do not cover the batch: N=%lld c=%lld T=%lld", N, c, T);
+      long long off = 0;
+      for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g, off += P[b]) {
+          if (P[b] == 0) continue;
+          const long long ranges = (off + P[b] - 1) / c - off / c + 1;
+          CHECK(ranges <= p.S, "item (%d,%d) of %lld pages meets %lld ranges, %d slots", b, g,
+                P[b], ranges, p.S);
+        }
+      }
+      ++g_cases;
+    }
+  }
+}
+
+static void check_workspace(int B, int Hq, int Hkv, int D, const Plan& p) {
+  const size_t need = workspace_for(B, Hq, Hkv, D, p);
+  if (p.S <= 1) {
+    CHECK(need == 0, "one split needs no workspace");
+    return;
+  }
+  const WsLayout w = ws_layout(B, Hq, Hkv, D, p.S);
+  const size_t rows = (size_t)B * Hq * p.S;
+  CHECK(w.m >= (size_t)B * Hkv * 4, "counters");
+  CHECK(w.m >= kMinCounters * 4, "counter region below its minimum");
+  if ((size_t)B * Hkv <= kMinCounters) CHECK(w.m == counter_bytes(1, 1), "counter region moved");
+  CHECK(w.l >= w.m + rows * 4 && w.o >= w.l + rows * 4 && w.total >= w.o + rows * D * 4,
+        "regions overlap");
+  CHECK(w.m % kAlign == 0 && w.l % kAlign == 0 && w.o % kAlign == 0, "alignment");
+  CHECK(need == w.total, "size");
+}
+
+int main() {
+  std::mt19937_64 rng(12345);
+  const int Bs[] = {1, 2, 3, 8, 32, 64, 129, 1024, 2048};
+  const int Hkvs[] = {1, 2, 8, 32};
+  const int lens[] = {0, 1, 31, 32, 33, 512, 1000, 1023, 1024, 1025, 2048, 4096, 8191, 8192,
+                      32768, 65536, 131072, 1 << 20};
+  const int windows[] = {0, 32, 1024, 4096, 65536};
+  const int parts[] = {0, 32, 256, 1024, 4096};
+  for (int B : Bs)
+    for (int Hkv : Hkvs)
+      for (int max_len : lens)
+        for (int window : windows)
+          for (int part : parts)
+            for (int byte_cache = 0; byte_cache < 2; ++byte_cache) {
+              Plan p{};
+              if (!make_plan(B, Hkv, max_len, window, part, byte_cache != 0, &p)) continue;
+              if (p.balanced) {
+                CHECK(byte_cache && part == 0 && B <= kMaxBalancedB, "balanced for B=%d", B);
+                if ((long long)B * Hkv * pages_of(len_cap(max_len, window)) < (1LL << 26))
+                  check_balanced(rng, B, Hkv, max_len, window, p);
+              } else {
+                check_grid(B, Hkv, max_len, window, part, p);
+              }
+              check_workspace(B, 4 * Hkv, Hkv, 128, p);
+            }
+  std::printf("ok %lld cases\n", g_cases);
+  return 0;
+}

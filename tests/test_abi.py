@@ -117,15 +117,17 @@ def test_workspace_query():
     lib = _lib.load()
     # Single partition: nothing needed.
     assert lib.pa_decode_workspace_bytes(2, 4, 4, 64, 64, 0, 0) == 0
-    # Forced 32-token partitions over 100 tokens: 4 partitions; then one
-    # split counter per (sequence, KV head).
+    # Forced 32-token partitions over 100 tokens: 4 partitions.  The split
+    # counters come first, one per (sequence, KV head) but never fewer than
+    # PA_DECODE_MIN_COUNTERS, so their region does not move with the shape.
     n = lib.pa_decode_workspace_bytes(2, 8, 2, 128, 100, 0, 32)
     rows = 2 * 8 * 4
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == 2 * rnd(rows * 4) + rnd(rows * 128 * 4) + rnd(2 * 2 * 4)
+    cnt = lambda pairs: rnd(max(pairs, 16384) * 4)
+    assert n == 2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(2 * 2)
     # Window caps the length.
     assert lib.pa_decode_workspace_bytes(2, 8, 2, 128, 10000, 64, 32) == \
-        2 * rnd(2 * 8 * 2 * 4) + rnd(2 * 8 * 2 * 128 * 4) + rnd(2 * 2 * 4)
+        2 * rnd(2 * 8 * 2 * 4) + rnd(2 * 8 * 2 * 128 * 4) + cnt(2 * 2)
     assert lib.pa_decode_workspace_bytes(2, 8, 2, 128, 100, 0, 33) == (1 << 64) - 1
     assert lib.pa_decode_workspace_bytes(-1, 8, 2, 128, 100, 0, 0) == (1 << 64) - 1
     # From 1024 tokens the byte-format plan (equal page ranges over the batch)
@@ -133,20 +135,20 @@ def test_workspace_query():
     # 32 x 8 KV heads is one pass, so the query returns the former.
     rows = 32 * 32 * 16
     assert lib.pa_decode_workspace_bytes(32, 32, 8, 128, 4096, 0, 0) == \
-        2 * rnd(rows * 4) + rnd(rows * 128 * 4) + rnd(32 * 8 * 4)
+        2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(32 * 8)
     # Longer contexts: more slots, so that no range exceeds 64 pages per wave
     # (65536 tokens = 2048 pages: ceil(2048 / 512) + 1 = 5 < 16, still 16;
     # 2^20 tokens = 32768 pages: 64 + 1 = 65 slots).
     rows = 1 * 8 * 65
     assert lib.pa_decode_workspace_bytes(1, 8, 8, 64, 1 << 20, 0, 0) >= \
-        2 * rnd(rows * 4) + rnd(rows * 64 * 4) + rnd(8 * 4)
+        2 * rnd(rows * 4) + rnd(rows * 64 * 4) + cnt(8)
     # The per-format query: a 16-bit cache needs none here, a byte cache the
     # balanced plan's slots.
     rows = 32 * 32 * 16
     assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == 0
     for fmt in (_lib.PA_F8E4M3, _lib.PA_I8):
         assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, fmt) == \
-            2 * rnd(rows * 4) + rnd(rows * 128 * 4) + rnd(32 * 8 * 4)
+            2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(32 * 8)
     assert lib.pa_decode_workspace_bytes_for(-1, 8, 2, 128, 100, 0, 0, _lib.PA_BF16) == \
         (1 << 64) - 1
     # Above 1024 sequences only the grid plan applies.

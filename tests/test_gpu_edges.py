@@ -1,5 +1,6 @@
 """GPU edge cases: empty chunks inside a prefill batch (causal and window),
-and the in-launch split merge reusing one workspace call after call.
+the in-launch split merge reusing one workspace call after call and across
+shapes, and context lengths above the host's bound.
 
 The split merge keeps one arrival counter per (sequence, KV head) in the
 workspace and leaves it at zero; a counter left behind would make the next
@@ -99,3 +100,59 @@ def test_window_prefill_batch_with_empty_chunks():
     err = P.max_abs(P.out_f64(out), ref)
     P.say(f"    max-abs error {err:.3e}")
     assert err <= P.TOL[wl.act]
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace serves calls of different shapes in a row: the split
+    counters sit at the start of the workspace whatever the shape, so the
+    partials of one call never land where a later call's counters are (16
+    splits of one sequence, then 4 splits of two, then the first again)."""
+    a = W.decode_workload("ws_shape_a", 84, B=1, Hq=32, Hkv=8, D=128, act="bf16", ctx=[4096])
+    b = W.decode_workload("ws_shape_b", 85, B=2, Hq=32, Hkv=8, D=128, act="bf16",
+                          ctx=[4000, 1500])
+    calls = ((a, 256), (b, 1024), (a, 1024), (b, 256))
+    size = max(ops.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D,
+                                          int(wl.context_lens.max()), 0, part)
+               for wl, part in calls)
+    ws = ops.alloc_workspace(size, torch.device("cuda"))
+    runs = []
+    for wl, part in calls:
+        P.say(f"[edges] {wl.name} B={wl.B} partition {part} on one shared workspace")
+        kc, vc = P.hip_decode_setup(wl)
+        q = P._act_tensor(wl.query, wl.act)
+        L = int(wl.context_lens.max())
+        out = ops.decode(q, kc, vc, torch.from_numpy(wl.block_tables).cuda(),
+                         torch.from_numpy(wl.context_lens).cuda(), L, wl.scale,
+                         partition_tokens=part, workspace=ws)
+        runs.append((wl, out))
+    torch.cuda.synchronize()
+    for wl, out in runs:
+        okc, ovc = P.oracle_decode_setup(wl)
+        err = P.max_abs(P.out_f64(out), P.oracle_decode(wl, okc, ovc))
+        P.say(f"    {wl.name}: max-abs error {err:.3e}")
+        assert err <= P.TOL["bf16"]
+
+
+@pytest.mark.parametrize("cache", ["bf16", "e4m3"])
+def test_length_above_bound_is_clamped(cache):
+    """A context length above max_context_len (a broken caller contract) is
+    clamped to the bound on the device: that sequence attends to its first
+    max_context_len tokens, the others are unaffected.  The table row and
+    the pool hold every real block, so the call stays in bounds either way."""
+    wl = W.decode_workload(f"clamp_{cache}", 86, B=4, Hq=16, Hkv=4, D=128, act="bf16",
+                           cache=cache, ctx=[3000, 1800, 2200, 1200])
+    bound = 2200
+    P.say(f"[edges] {wl.name}: context 3000 passed with max_context_len {bound}")
+    kc, vc = P.hip_decode_setup(wl)
+    q = P._act_tensor(wl.query, wl.act)
+    out = ops.decode(q, kc, vc, torch.from_numpy(wl.block_tables).cuda(),
+                     torch.from_numpy(wl.context_lens).cuda(), bound, wl.scale,
+                     wl.k_scale, wl.v_scale)
+    torch.cuda.synchronize()
+    okc, ovc = P.oracle_decode_setup(wl)
+    lens = np.minimum(wl.context_lens, bound).astype(np.int32)
+    ref = o_attn.decode(wl.query, wl.act, okc, ovc, wl.cache, wl.block_tables, lens, wl.scale,
+                        wl.k_scale, wl.v_scale)
+    err = P.max_abs(P.out_f64(out), ref)
+    P.say(f"    max-abs error {err:.3e}")
+    assert err <= P.TOL[cache]
