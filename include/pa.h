@@ -248,6 +248,34 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the split scratch is a fixed array in the library's
+ * own device memory, PA_DECODE_SCRATCH_BYTES on each GPU the library runs on
+ * (held until the process ends), instead of a caller's workspace.
+ *
+ * Arguments, outputs and errors as pa_decode, without workspace and
+ * workspace_bytes.  Allocates nothing.  The first call on a device looks up
+ * that device's array and zeroes its counter region with a small kernel on
+ * `stream`; every call leaves the counters zero.
+ * PA_ERR_WORKSPACE (nothing launched) when the call's plan needs more than
+ * PA_DECODE_SCRATCH_BYTES, or splits with B*Hkv above
+ * PA_DECODE_MIN_COUNTERS; pa_decode with a workspace serves those.
+ * Every call on one GPU shares that GPU's array and leaves its partials
+ * there: calls that overlap in time on one GPU (two streams without
+ * ordering, two host threads) race and give wrong results.
+ */
+#define PA_DECODE_SCRATCH_BYTES (64u << 20)
+
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                            float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                            float k_scale, float v_scale, int32_t window,
+                            int32_t partition_tokens, void* stream);
+
+/*
  * pa_decode_append -- pa_reshape_and_cache of the decoded token followed by
  * pa_decode, in one launch.
  *

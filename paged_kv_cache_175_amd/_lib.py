@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PA_F16, PA_BF16, PA_F8E4M3, PA_I8 = 0, 1, 2, 3
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+# Scratch of pa_decode_noalloc (PA_DECODE_SCRATCH_BYTES in include/pa.h).
+PA_DECODE_SCRATCH_BYTES = 64 << 20
 STATUS_NAMES = {
     PA_OK: "PA_OK",
     PA_ERR_INVALID: "PA_ERR_INVALID",
@@ -42,6 +44,9 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+        ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp]),
     "pa_decode_append": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         ctypes.c_int, ctypes.c_int, _f32, _f32, _i32, _i32, _vp, _sz, _vp]),

@@ -15,6 +15,7 @@
 #include <cstring>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "launch.hpp"
 #include "plan.hpp"
@@ -401,6 +402,92 @@ pa_status pa_decode_append_i8(void* out, const void* query, const void* key, con
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// The decode scratch of pa_decode_noalloc: a fixed array in device memory,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never uses its name as an address (on the host it is only a stand-in
+// for the symbol): the device address comes from hipGetSymbolAddress, once
+// per device, and only that pointer is handed to kernels.
+
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Zero n 32-bit words (the counter region) on the stream: a kernel, not a
+// memset node, so the set-up may also sit inside a captured graph.
+__global__ void zero_words(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// The current device's scratch address, set up on the first call on that
+// device: the symbol's address there, and its counter region zeroed (a
+// decode leaves its counters zero, so this is needed once).
+pa_status scratch_for_current_device(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    const int words = (int)(counter_bytes(0, 0) / sizeof(int));
+    hipLaunchKernelGGL(zero_words, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<int*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch counter zero-fill launch");
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t BS, int32_t MBPS, int32_t max_context_len,
+                            float softmax_scale, pa_dtype act_dtype, pa_dtype cache_dtype,
+                            float k_scale, float v_scale, int32_t window,
+                            int32_t partition_tokens, void* stream) {
+  if (!cache_ok(act_dtype, cache_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "cache dtype must equal the act dtype or be PA_F8E4M3");
+  // The scratch need of this call's plan; invalid arguments are reported by
+  // the checks of decode_common below.
+  const size_t need = pa_decode_workspace_bytes_for(B, Hq, Hkv, D, max_context_len, window,
+                                                    partition_tokens, cache_dtype);
+  if (need != (size_t)-1 && need > 0) {
+    if (need > (size_t)PA_DECODE_SCRATCH_BYTES)
+      return fail(PA_ERR_WORKSPACE,
+                  "this decode needs %zu bytes of scratch; the no-allocation entry point has "
+                  "%zu (use pa_decode with a workspace)",
+                  need, (size_t)PA_DECODE_SCRATCH_BYTES);
+    if ((long long)B * Hkv > (long long)kMinCounters)
+      return fail(PA_ERR_WORKSPACE,
+                  "a split decode over %lld (sequence, KV head) pairs; the no-allocation entry "
+                  "point keeps counters for %zu (use pa_decode with a workspace)",
+                  (long long)B * Hkv, kMinCounters);
+  }
+  void* ws = nullptr;
+  const pa_status st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+  if (st != PA_OK) return st;
+  return decode_common(out, query, nullptr, nullptr, key_cache, value_cache, nullptr, nullptr,
+                       block_tables, context_lens, B, Hq, Hkv, D, BS, MBPS, max_context_len,
+                       softmax_scale, act_dtype, cache_dtype, k_scale, v_scale, window,
+                       partition_tokens, ws, (size_t)PA_DECODE_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
 
 namespace {
 

@@ -250,3 +250,29 @@ def test_prefill_window_quant_rejects(args, status):
         a["vscales"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["MBPS"],
         a["maxc"], a["scale"], a["act"], a["cache"], a["ksc"], a["vsc"], a["window"],
         None) == status
+
+
+@needs_lib
+@host_only
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """pa_decode_noalloc refuses, before touching the device, a plan whose
+    scratch exceeds PA_DECODE_SCRATCH_BYTES or whose split counters exceed
+    PA_DECODE_MIN_COUNTERS (those calls belong to pa_decode with a workspace)."""
+    lib = _lib.load()
+
+    def call(B, Hkv, maxlen, cache):
+        return lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, 4 * Hkv, Hkv, 128,
+                                     32, 256, maxlen, 0.1, _lib.PA_BF16, cache, 1.0, 1.0, 0, 0,
+                                     None)
+    # A byte cache from 1024 tokens plans 16 partial slots per query head:
+    # 1024 x 32 heads x 16 x (128 + 2) x 4 bytes, well past 64 MiB.
+    need = lib.pa_decode_workspace_bytes_for(1024, 32, 8, 128, 8192, 0, 0, _lib.PA_F8E4M3)
+    assert need > _lib.PA_DECODE_SCRATCH_BYTES
+    assert call(1024, 8, 8192, _lib.PA_F8E4M3) == _lib.PA_ERR_WORKSPACE
+    assert b"scratch" in lib.pa_last_error()
+    # Split counters beyond the fixed region: 4096 x 8 pairs with forced splits.
+    r = lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 8, 8, 64, 32, 256, 2048,
+                              0.1, _lib.PA_BF16, _lib.PA_BF16, 1.0, 1.0, 0, 1024, None)
+    assert r == _lib.PA_ERR_WORKSPACE
+    # Malformed arguments are reported as by pa_decode.
+    assert call(2, 2, 100, _lib.PA_I8) == _lib.PA_ERR_UNSUPPORTED
