@@ -34,14 +34,15 @@ struct DecodeArgs {
   // host's bound cannot take a wave past the pages the plan sized it for.
   int len_cap;
   int S;  // grid mode: splits per (sequence, KV head); balanced: partials per item
+  int pair;  // grid mode, one split: short sequences help long ones
   int W;  // waves per workgroup (4 or 8)
   int N;  // balanced mode: workgroups (0 = grid mode)
   int stream_k;  // balanced mode: 16-bit K pages non-temporal
   int act, cache;  // Fmt codes
   float softmax_scale, k_scale, v_scale;
-  float* ws_m;  // [B*Hq*S]
-  float* ws_l;  // [B*Hq*S]
-  float* ws_o;  // [B*Hq*S*D]
+  float* ws_m;  // [B*Hq*slots]
+  float* ws_l;  // [B*Hq*slots]
+  float* ws_o;  // [B*Hq*slots*D]
   int* ws_count;  // split arrival counters (B*Hkv used), zero between launches
   const void* new_key;    // append mode: [B][Hkv][D] act, or null
   const void* new_value;

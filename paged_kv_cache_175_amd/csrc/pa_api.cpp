@@ -202,8 +202,9 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   // The plan depends on the cache format, which this query does not take:
   // the larger of the two workspaces.
   Plan p16, p8;
-  if (!make_plan(B, Hkv, max_context_len, window, partition_tokens, false, &p16) ||
-      !make_plan(B, Hkv, max_context_len, window, partition_tokens, true, &p8))
+  const int G = Hq % Hkv == 0 ? Hq / Hkv : 1;
+  if (!make_plan(B, Hkv, G, D, max_context_len, window, partition_tokens, false, &p16) ||
+      !make_plan(B, Hkv, G, D, max_context_len, window, partition_tokens, true, &p8))
     return (size_t)-1;
   return std::max(workspace_for(B, Hq, Hkv, D, p16), workspace_for(B, Hq, Hkv, D, p8));
 }
@@ -215,7 +216,8 @@ size_t pa_decode_workspace_bytes_for(int32_t B, int32_t Hq, int32_t Hkv, int32_t
       partition_tokens < 0)
     return (size_t)-1;
   Plan p;
-  if (!make_plan(B, Hkv, max_context_len, window, partition_tokens,
+  const int G = Hq % Hkv == 0 ? Hq / Hkv : 1;
+  if (!make_plan(B, Hkv, G, D, max_context_len, window, partition_tokens,
                  cache_dtype == PA_F8E4M3 || cache_dtype == PA_I8, &p))
     return (size_t)-1;
   return workspace_for(B, Hq, Hkv, D, p);
@@ -271,7 +273,7 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
     return fail(PA_ERR_INVALID, "scale pools must be 16-byte aligned");
   if ((long long)B * Hq > 0x7fffffffLL / D) return fail(PA_ERR_UNSUPPORTED, "B*Hq*D too large");
   Plan p;
-  if (!make_plan(B, Hkv, max_context_len, window, partition_tokens,
+  if (!make_plan(B, Hkv, G, D, max_context_len, window, partition_tokens,
                  cache_dtype == PA_F8E4M3 || cache_dtype == PA_I8, &p))
     return fail(PA_ERR_INVALID, "bad partition size");
   const size_t need = workspace_for(B, Hq, Hkv, D, p);
@@ -296,6 +298,7 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   a.len_cap = (int)plan::len_cap(max_context_len, window);
   a.S = p.S;
   a.W = p.W;
+  a.pair = p.pair ? 1 : 0;
   if (p.balanced) {
     const long long cus = device_cus();
     if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
@@ -308,7 +311,7 @@ pa_status decode_common(void* out, const void* query, const void* new_key,
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
-    const WsLayout l = ws_layout(B, Hq, Hkv, D, p.S);
+    const WsLayout l = ws_layout(B, Hq, Hkv, D, p.slots);
     char* w = static_cast<char*>(workspace);
     a.ws_count = reinterpret_cast<int*>(w);
     a.ws_m = reinterpret_cast<float*>(w + l.m);

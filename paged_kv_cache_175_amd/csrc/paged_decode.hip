@@ -321,6 +321,12 @@ __device__ __forceinline__ void compute_page(PageRegs<D, CF>& Pg, float& m_run,
   // row row_new / 2 of tile row_new % 2 (bytes); in V it is element
   // row_new % 8 of lane group row_new / 8.
   if (patch) {
+    // Lane-derived addresses are recomputed here from an opaque copy of the
+    // lane index rather than kept live across the caller's page loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int col = ln & 15;
+    const int q4 = ln >> 4;
     const int kt_new = kContig ? row_new >> 4 : row_new & 1;
     if (col == (kContig ? row_new & 15 : row_new >> 1)) {
 #pragma unroll
@@ -558,30 +564,159 @@ __device__ __forceinline__ void store_row_elem(uint8_t* key_cache, uint8_t* valu
 }
 
 // ---------------------------------------------------------------------------
-// Grid mode: workgroup (s, g, b) owns split s of the pages of (sequence b,
-// KV head g).
+// Grid mode: workgroup (s, g, b) reads split s of the pages of (sequence b,
+// KV head g).  Pair mode (one split per sequence, the plan's choice for
+// batches whose longest sequences would otherwise stream alone at the end):
+// workgroup (0, g, b) also reads the tail of the (b', g) item that the
+// batch's ranking pairs with b, when b is the shorter of the two
+// (plan::pair_split).
+//
+// An item read by several workgroups (its splits, or its owner and its
+// helper) is merged by the last of them to finish (finish_item).
+//
+// The decoded token's row (append mode) is encoded by the wave that reads
+// its page, from the activations, stored into its cache row and patched
+// into that page's registers: no workgroup barrier, and nothing in the
+// launch depends on the stores landing.
+
+// Wave partial of an empty job: the combine skips m = -inf.
+template <int G>
+__device__ __forceinline__ void put_empty_partial(float* m, int lane) {
+  if (lane < G) m[lane] = -INFINITY;
+}
+
+// The decoded token's row of (sequence, KV head) `src` (an index into
+// new_key / new_value [B][Hkv][D]), lane-major: elements d = lane + 64 i.
+template <int D>
+__device__ __forceinline__ void load_new_row(uint16_t (&kr)[(D + 63) / 64],
+                                             uint16_t (&vr)[(D + 63) / 64],
+                                             const uint16_t* new_key, const uint16_t* new_value,
+                                             size_t src, int lane) {
+#pragma unroll
+  for (int i = 0; i < (D + 63) / 64; ++i) {
+    const int d = lane + 64 * i;
+    kr[i] = d < D ? new_key[src * D + d] : 0;
+    vr[i] = d < D ? new_value[src * D + d] : 0;
+  }
+}
+
+// The row in the cache format, as the writer stores it: the 16-bit values,
+// E4M3 codes (tensor scales) or INT8 codes with the row's own scales
+// (amax / 127; a reduction over the wave, so every lane must take part).
+template <int D, int CF, int AF>
+__device__ __forceinline__ void encode_new_row(const uint16_t (&kr)[(D + 63) / 64],
+                                               const uint16_t (&vr)[(D + 63) / 64],
+                                               uint32_t (&kq)[(D + 63) / 64],
+                                               uint32_t (&vq)[(D + 63) / 64], float k_enc_scale,
+                                               float v_enc_scale, float& ks, float& vs) {
+  constexpr int DPL = (D + 63) / 64;
+  ks = k_enc_scale;
+  vs = v_enc_scale;
+  if constexpr (CF == FMT_I8) {
+    float ka = 0.f, va = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      ka = fmaxf(ka, fabsf(lo16_to_f32<AF>(kr[i])));
+      va = fmaxf(va, fabsf(lo16_to_f32<AF>(vr[i])));
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      ka = fmaxf(ka, shfl_xor_f(ka, m));
+      va = fmaxf(va, shfl_xor_f(va, m));
+    }
+    ks = __fdiv_rn(ka, 127.f);
+    vs = __fdiv_rn(va, 127.f);
+  }
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    kq[i] = encode_elem<CF, AF>(kr[i], ks);
+    vq[i] = encode_elem<CF, AF>(vr[i], vs);
+  }
+}
+
+// Finish one item (sequence bj, KV head g) of this workgroup: combine the W
+// wave partials of job j from LDS; with one part that is the output.  With
+// several, this part publishes its partial (agent-scope stores, complete
+// before it counts itself in) and the last part of the item to count in
+// merges all of them in slot order (merge_head, one wave per query head), so
+// the output is the same bits whichever part merges.
+template <int D, int G, int AF, int W, int NJ>
+__device__ __forceinline__ void finish_item(
+    int j, int bj, int g, int Hkv, int nparts, int slot, float v_scale,
+    const float (&m_lds)[NJ][W][G], const float (&l_lds)[NJ][W][G],
+    const float (&o_lds)[NJ][W][G][D], int* flag, uint16_t* __restrict__ out,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+    int* __restrict__ ws_count, int nslots) {
+  const int tid = threadIdx.x;
+  const size_t head0 = (size_t)bj * Hkv * G + (size_t)g * G;
+  for (int i = tid; i < G * D; i += 64 * W) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M, num, den;
+    combine_waves<W>(&m_lds[j][0][h], &l_lds[j][0][h], &o_lds[j][0][h][d], G, G * D, M, num, den);
+    if (nparts == 1) {
+      out[head0 * D + i] = static_cast<uint16_t>(f32_to_16<AF>(num * (v_scale / den)));
+    } else {
+      const size_t row = (head0 + h) * nslots + slot;
+      ws_store(ws_o + row * D + d, num);
+      if (d == 0) {
+        ws_store(ws_m + row, M);
+        ws_store(ws_l + row, den);
+      }
+    }
+  }
+  if (nparts == 1) return;
+  // Count this part in; the last of the item merges.  The counter is back at
+  // zero when the launch ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = ws_count + (size_t)bj * Hkv + g;
+    const int arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = arrived == nparts - 1;
+    if (arrived == nparts - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!*flag) return;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int h = wave; h < G; h += W)
+    merge_head<D, AF>(out + (head0 + h) * D, nparts, v_scale, ws_m, ws_l, ws_o,
+                      (head0 + h) * nslots, tid & 63);
+}
 
 template <int D, int G, int CF, int AF, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_split(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int Hkv, int MBPS, int window, int len_cap, int S, float qk_scale_log2, float v_scale,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-    int* __restrict__ ws_count, const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
-    float k_enc_scale, float v_enc_scale, float* __restrict__ key_scales,
-    float* __restrict__ value_scales) {
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int B,
+    int Hkv, int MBPS, int window, int len_cap, int S, int pair, float qk_scale_log2,
+    float v_scale, float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+    int* __restrict__ ws_count, const uint16_t* __restrict__ new_key,
+    const uint16_t* __restrict__ new_value, float k_enc_scale, float v_enc_scale,
+    float* __restrict__ key_scales, float* __restrict__ value_scales) {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
   constexpr int KSTEPS = D / 32;
   constexpr int NT = D / 16;
+  constexpr int DPL = (D + 63) / 64;
+  // Two jobs (own item, help) where their wave partials fit side by side.
+  constexpr int NJ = plan::pair_fits(W, G, D) ? 2 : 1;
   typedef typename Mfma<AF>::vec vec;
 
-  __shared__ float m_lds[W][G];
-  __shared__ float l_lds[W][G];
-  __shared__ __attribute__((aligned(16))) float o_lds[W][G][D];
-  __shared__ __attribute__((aligned(16))) uint16_t newk_lds[D];
-  __shared__ __attribute__((aligned(16))) uint16_t newv_lds[D];
+  constexpr int TAB = 64 * W;             // pages of one job at most (plan)
+  __shared__ float m_lds[NJ][W][G];
+  __shared__ float l_lds[NJ][W][G];
+  __shared__ __attribute__((aligned(16))) float o_lds[NJ][W][G][D];
+  // Page ids (block * Hkv + g) of the jobs' pages: the own job's first,
+  // then the help job's.
+  __shared__ uint32_t pid_tab[NJ * TAB];
+  __shared__ int next_idx;                // next unclaimed page index
+  // Per job: the appended row, in the cache format, and (INT8) its scales.
+  __shared__ __attribute__((aligned(16))) uint16_t row_lds[NJ][2][D];
+  __shared__ float row_scale[NJ][2];
+  // The help job's queries.
+  __shared__ __attribute__((aligned(16))) uint16_t qh_lds[NJ > 1 ? G * D : 8];
+  __shared__ int flag_lds[NJ];
 
   // The wave index is uniform across the wave; saying so keeps everything
   // derived from it (page counts, prefetch indices) in scalar registers.
@@ -590,222 +725,291 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // load before the next page's loads are issued.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int col = lane & 15;
-  const int q4 = lane >> 4;
-
   const int s = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int Hq = Hkv * G;
+  const bool append = new_key != nullptr;
+  const bool paired = NJ > 1 && pair != 0;
+  const int nslots = paired ? 2 : S;
 
-  // With one split per sequence a wave's pages are wave + W k whatever the
-  // context length, so its table entries are loaded alongside the length
-  // rather than after it (lane k: entry wave + W k, clamped to the row;
-  // entries past the sequence's pages are never used).
+  // --- first round: loads that need neither a length nor the plan --------
+  // With one split per sequence the own job's pages are wave + W k whatever
+  // the length, so its table entries go out with the length (lane k: entry
+  // wave + W k, clamped to the row; entries past the job are never used).
   int bt_pre = 0;
   if (S == 1 && block_tables != nullptr)
     bt_pre = block_tables[(size_t)b * MBPS + min(wave + W * lane, MBPS - 1)];
-  // The query operands, and in append mode the decoded row, depend on
-  // neither the length nor the table: their loads go out in the same first
-  // round, so the first page's loads wait for one round trip, not three.
   vec qb[KSTEPS];
   q_operand<D, G, AF>(qb, query + ((size_t)b * Hq + g * G) * D, lane);
-  static_assert(D <= 64 * W, "one head-dimension element per thread");
-  constexpr int DPL = CF == FMT_I8 ? (D + 63) / 64 : 1;
-  uint16_t kx = 0, vx = 0;
-  uint16_t krow[DPL], vrow[DPL];          // INT8: this lane's share of the row
-  const int d_new = threadIdx.x;
-  const size_t new_src = ((size_t)b * Hkv + g) * D;
-  if (new_key != nullptr) {
-    if (d_new < D) {
-      kx = new_key[new_src + d_new];
-      vx = new_value[new_src + d_new];
+  int lens_lane = 0;                      // pair mode: the batch's lengths (B <= 64)
+  if (paired && lane < B) lens_lane = context_lens[lane];
+  const int ctx = context_lens[b];
+  uint16_t krow[DPL], vrow[DPL];          // wave 0: the own item's appended row
+  if (append && wave == 0)
+    load_new_row<D>(krow, vrow, new_key, new_value, (size_t)b * Hkv + g, lane);
+
+  // --- the plan ----------------------------------------------------------
+  // Lengths are clamped to the host's bound, which the plan was sized for
+  // (at most 64 pages per wave).
+  const int L = min(ctx, len_cap);
+  const int P = L > 0 ? (L + kPage - 1) / kPage : 0;
+  int own_lo = 0, own_hi = P;             // own job: pages [own_lo, own_hi) of sequence b
+  int own_parts = 1, own_slot = 0;
+  int hb = -1, help_lo = 0, help_hi = 0, Lh = 0, ctx_h = 0;  // help job on sequence hb
+  if (paired) {
+    // Rank the sequences by pages (ties by index), longest first; rank r
+    // pairs with rank B - 1 - r.
+    const int Lx = min(lens_lane, len_cap);
+    const int Px = lane < B && Lx > 0 ? (Lx + kPage - 1) / kPage : 0;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int pj = __builtin_amdgcn_readlane(Px, j);
+      rank += (pj > Px) || (pj == Px && j < lane);
     }
-    if constexpr (CF == FMT_I8) {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const int d = lane + 64 * i;
-        krow[i] = d < D ? new_key[new_src + d] : 0;
-        vrow[i] = d < D ? new_value[new_src + d] : 0;
+    const int r = __builtin_amdgcn_readlane(rank, b);
+    const int pr = B - 1 - r;
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && rank == pr);
+    const int partner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    const int Pp = __builtin_amdgcn_readlane(Px, partner);
+    if (r < pr) {
+      own_hi = plan::pair_split(P, Pp);
+      own_parts = own_hi < P ? 2 : 1;
+    } else if (r > pr) {
+      const int a = plan::pair_split(Pp, P);
+      if (a < Pp) {
+        hb = partner;
+        help_lo = a;
+        help_hi = Pp;
+        ctx_h = __builtin_amdgcn_readlane(lens_lane, partner);
+        Lh = min(ctx_h, len_cap);
       }
     }
+  } else if (S > 1) {
+    own_lo = (int)((long long)s * P / S);
+    own_hi = (int)((long long)(s + 1) * P / S);
+    own_parts = S;
+    own_slot = s;
   }
-  // Clamped to the host's bound: the split plan sized S and W for it (at
-  // most 64 pages per wave, the lanes of its table register).
-  const int L = min(context_lens[b], len_cap);
-  if (L <= 0) {
-    // Empty context: zeros, written once by split 0.
-    if (s == 0) {
+  if (P == 0) {
+    // Empty context: zeros, written once (its splits all have no pages).
+    own_parts = 1;
+    if (s == 0)
       for (int i = threadIdx.x; i < G * D; i += 64 * W) out[((size_t)b * Hq + g * G) * D + i] = 0;
-    }
-    return;
+    if (hb < 0) return;
   }
 
-  // Pages [pa, pb) of the sequence belong to this split; wave w takes pages
-  // pa + w, pa + w + W, ... so the waves of the workgroup stream neighbouring
-  // pages side by side.
-  const int P = (L + kPage - 1) / kPage;
-  const int pa = (int)((long long)s * P / S);
-  const int pb = (int)((long long)(s + 1) * P / S);
-  const int npg = pb - pa > wave ? (pb - pa - wave + W - 1) / W : 0;  // <= 64 (host plan)
+  // The jobs' pages, as one list: index i < n0 is page own_lo + i of
+  // sequence b, index n0 + j page help_lo + j of sequence hb.  Wave w starts
+  // on index w (when the own job has that many pages); from then on each
+  // wave claims the next unclaimed index (an LDS counter), so waves the
+  // memory system serves faster take more pages and all finish close
+  // together (with a static round-robin, the waves of one workgroup
+  // finished up to ~8 us apart on the Mistral batch).
+  const int n0 = P > 0 ? own_hi - own_lo : 0;      // <= TAB (plan)
+  const int n1 = help_hi - help_lo;                // <= TAB
+  const int N = n0 + n1;
 
-  // Append mode: the decoded token's K/V (new_key / new_value [B][Hkv][D])
-  // belong in cache row r_new (the last position, or its ring row).  The
-  // split that owns that row's page stores it (E4M3-encoded when the cache
-  // is FP8; INT8 codes and the row's two scales when it is INT8) and stages
-  // the stored cache elements in LDS; the one wave that
-  // reads the page patches the row into its page registers, so nothing in
-  // this launch depends on the store becoming visible.  The row's loads
-  // went out with the first round (above), its stores only after the first
-  // page's loads, so the append adds no memory round trip before the page
-  // stream starts.
-  int row_new = -1, k_new = -1, w_new = -1;
-  bool append = false;
-  int pg_new = 0;                         // logical page of the new row
-  float new_ks = 0.f, new_vs = 0.f;       // INT8: the new row's scales
-  if (new_key != nullptr) {
-    const int ctx = context_lens[b];
-    const int r_new = window > 0 ? (ctx - 1) % window : ctx - 1;
-    pg_new = r_new / kPage;
-    if (pg_new >= pa && pg_new < pb) {
-      append = true;
-      row_new = r_new - pg_new * kPage;
-      w_new = (pg_new - pa) % W;
-      k_new = (pg_new - pa) / W;
+  // Table entries: thread (wave, lane) holds index wave + W lane of each
+  // job.  With one split per sequence the own job's came in the first round.
+  const int ti = wave + W * lane;
+  uint32_t own_pid = 0, help_pid = 0;
+  if (ti < n0) {
+    const int pg = own_lo + ti;
+    own_pid = (uint32_t)(S == 1 ? (block_tables ? bt_pre : b * MBPS + pg)
+                                : (block_tables ? block_tables[(size_t)b * MBPS + pg]
+                                                : b * MBPS + pg)) * Hkv + g;
+  }
+  if (NJ > 1 && ti < n1) {
+    const int pg = help_lo + ti;
+    help_pid = (uint32_t)(block_tables ? block_tables[(size_t)hb * MBPS + pg]
+                                       : hb * MBPS + pg) * Hkv + g;
+  }
+  // The help job's queries and appended row (second round).
+  constexpr int QCH = G * D / 8;          // 16-byte chunks of the queries
+  constexpr int QPT = (QCH + 64 * W - 1) / (64 * W);
+  u32x4 qv[QPT];
+  if (NJ > 1 && n1 > 0) {
+    const uint16_t* src = query + ((size_t)hb * Hq + g * G) * D;
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int c = threadIdx.x + 64 * W * u;
+      qv[u] = c < QCH ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // Store the row and stage it in LDS, then make the LDS copy visible to
-  // every wave; the global stores need not have completed (__syncthreads
-  // would wait for them).  Every wave runs this exactly once.
-  auto stage_new_row = [&]() {
-    if constexpr (CF == FMT_I8) {
-      if (append) {
-        // Row scales, amax / 127 as the writer computes them.
-        float ka = 0.f, va = 0.f;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          ka = fmaxf(ka, fabsf(lo16_to_f32<AF>(krow[i])));
-          va = fmaxf(va, fabsf(lo16_to_f32<AF>(vrow[i])));
-        }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-          ka = fmaxf(ka, shfl_xor_f(ka, m));
-          va = fmaxf(va, shfl_xor_f(va, m));
-        }
-        new_ks = __fdiv_rn(ka, 127.f);
-        new_vs = __fdiv_rn(va, 127.f);
-      }
-    }
-    if (append && d_new < D) {
-      // The row's block is looked up only here, after the first page's
-      // loads: the stores are the only use of it.
-      const int phys = block_tables ? block_tables[(size_t)b * MBPS + pg_new] : b * MBPS + pg_new;
-      const size_t new_page = ((size_t)phys * Hkv + g) * (size_t)kPage * D;
-      const size_t new_srow = ((size_t)phys * Hkv + g) * kPage + row_new;
-      const float kes = CF == FMT_I8 ? new_ks : k_enc_scale;
-      const float ves = CF == FMT_I8 ? new_vs : v_enc_scale;
-      const uint32_t kq = encode_elem<CF, AF>(kx, kes);
-      const uint32_t vq = encode_elem<CF, AF>(vx, ves);
-      if constexpr (CF == FMT_I8) {
-        if (d_new == 0) {
-          key_scales[new_srow] = new_ks;
-          value_scales[new_srow] = new_vs;
-        }
-      }
-      store_row_elem<CF>(key_cache, value_cache, new_page, row_new, d_new, kq, vq);
-      newk_lds[d_new] = static_cast<uint16_t>(kq);
-      newv_lds[d_new] = static_cast<uint16_t>(vq);
-    }
-    asm volatile("" ::: "memory");
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
+  // Appended rows: the own item's (cache row r0, list index i0) and the help
+  // item's (r1, i1), when they lie in this workgroup's pages.
+  int r0 = -1, r1 = -1;
+  if (append && L > 0) {
+    const int r = window > 0 ? (ctx - 1) % window : ctx - 1;
+    if (r < L) r0 = r;
+  }
+  if (append && n1 > 0) {
+    const int r = window > 0 ? (ctx_h - 1) % window : ctx_h - 1;
+    if (r < Lh) r1 = r;
+  }
+  const int i0 = r0 >= 0 && r0 / kPage - own_lo >= 0 && r0 / kPage - own_lo < n0
+                     ? r0 / kPage - own_lo : -1;
+  const int i1 = r1 >= 0 && r1 / kPage - help_lo >= 0 && r1 / kPage - help_lo < n1
+                     ? n0 + r1 / kPage - help_lo : -1;
+  uint16_t hrow_k[DPL], hrow_v[DPL];      // wave 1 (0 if W == 1): the help row
+  const int hwave = W > 1 ? 1 : 0;
+  if (NJ > 1 && i1 >= 0 && wave == hwave)
+    load_new_row<D>(hrow_k, hrow_v, new_key, new_value, (size_t)hb * Hkv + g, lane);
 
   // o_acc[NT] is the all-ones tile: every row holds the running sum l.
   float m_run = -INFINITY;
   f32x4 o_acc[NT + 1];
 #pragma unroll
   for (int n = 0; n <= NT; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const vec ones = ones_operand<AF>();
+  const bool stream_k = S == 1;
+  auto fetch = [&](uint32_t pid, bool live, PageRegs<D, CF>& Pg) {
+    load_page<D, CF>(Pg, key_cache, value_cache, key_scales, value_scales, pid, live, lane,
+                     stream_k);
+  };
 
-  if (npg > 0) {
-    const vec ones = ones_operand<AF>();
+  // The first page: index `wave`, its id in this wave's own table register.
+  const bool first_live = wave < n0;
+  PageRegs<D, CF> A, Bf;
+  fetch(first_live ? __builtin_amdgcn_readlane(own_pid, 0) : 0u, first_live, A);
+  asm volatile("" ::: "memory");
 
-    // Page ids (block * Hkv + g) of this wave's pages, lane k holding its
-    // k-th page, so the page loop never waits on a block-table load.
-    // Without a table the map is the identity (block b * MBPS + j) and
-    // nothing is loaded.
-    const int lpg = pa + wave + W * (lane < npg ? lane : 0);
-    const int bt_lane = block_tables == nullptr ? b * MBPS + lpg
-                        : S == 1                ? bt_pre
-                                                : block_tables[(size_t)b * MBPS + lpg];
-    const uint32_t pid_lane = (uint32_t)bt_lane * Hkv + g;
-    const bool stream_k = S == 1;
-    auto fetch = [&](int k, PageRegs<D, CF>& Pg) {
-      const bool live = k < npg;
-      load_page<D, CF>(Pg, key_cache, value_cache, key_scales, value_scales,
-                       __builtin_amdgcn_readlane(pid_lane, live ? k & 63 : 0), live, lane, stream_k);
-    };
-    auto step = [&](PageRegs<D, CF>& Pg, int k) {
-      compute_page<D, G, CF, AF>(Pg, m_run, o_acc, qb, ones, (pa + wave + W * k) * kPage, L,
-                                 wave == w_new && k == k_new, row_new, newk_lds, newv_lds, new_ks,
-                                 new_vs, qk_scale_log2, lane);
-    };
-
-    // Two register buffers: page k is computed while page k + 1 loads.
-    PageRegs<D, CF> A, Bf;
-    fetch(0, A);
-    stage_new_row();
-    for (int k = 0;;) {
-      fetch(k + 1, Bf);
-      step(A, k);
-      if (++k >= npg) break;
-      fetch(k + 1, A);
-      step(Bf, k);
-      if (++k >= npg) break;
+  // Tables, the help job's queries and the appended rows (encoded as the
+  // writer encodes them) to LDS; then one barrier (LDS only: the page loads
+  // in flight need not complete).
+  if (ti < n0) pid_tab[ti] = own_pid;
+  if (NJ > 1 && ti < n1) pid_tab[TAB * (NJ - 1) + ti] = help_pid;
+  if (NJ > 1 && n1 > 0) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int c = threadIdx.x + 64 * W * u;
+      if (c < QCH) *reinterpret_cast<u32x4*>(&qh_lds[8 * c]) = qv[u];
     }
-  } else {
-    stage_new_row();
   }
-
-  // Combine the W waves through LDS; waves without pages contribute
-  // (-inf, 0, 0).
-  put_wave_partial<D, G>(o_lds[wave], m_lds[wave], l_lds[wave], o_acc, m_run, lane);
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += 64 * W) {
-    const int h = i / D;
-    const int d = i - h * D;
-    float M, num, den;
-    combine_waves<W>(&m_lds[0][h], &l_lds[0][h], &o_lds[0][h][d], G, G * D, M, num, den);
-    if (S == 1) {
-      out[((size_t)b * Hq + g * G + h) * D + d] = static_cast<uint16_t>(f32_to_16<AF>(num * (v_scale / den)));
-    } else {
-      const size_t row = ((size_t)b * Hq + g * G + h) * S + s;
-      ws_store(ws_o + row * D + d, num);
-      if (d == 0) {
-        ws_store(ws_m + row, M);
-        ws_store(ws_l + row, den);
+  auto stage_row = [&](int j, const uint16_t (&kr)[DPL], const uint16_t (&vr)[DPL]) {
+    uint32_t kq[DPL], vq[DPL];
+    float ks, vs;
+    encode_new_row<D, CF, AF>(kr, vr, kq, vq, k_enc_scale, v_enc_scale, ks, vs);
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+      const int d = lane + 64 * u;
+      if (d < D) {
+        row_lds[j][0][d] = static_cast<uint16_t>(kq[u]);
+        row_lds[j][1][d] = static_cast<uint16_t>(vq[u]);
       }
     }
-  }
-  if (S == 1) return;
+    if (lane == 0) {
+      row_scale[j][0] = ks;
+      row_scale[j][1] = vs;
+    }
+  };
+  if (i0 >= 0 && wave == 0) stage_row(0, krow, vrow);
+  if (NJ > 1 && i1 >= 0 && wave == hwave) stage_row(NJ - 1, hrow_k, hrow_v);
+  if (threadIdx.x == 0) next_idx = min(n0, W);
+  asm volatile("" ::: "memory");
+  wait_lgkmcnt0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
-  // Count this split in; the last of the S merges them.  The counter is
-  // back at zero when the launch ends.
-  __shared__ int last_split;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* cnt = ws_count + (size_t)b * Hkv + g;
-    const int arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_split = arrived == S - 1;
-    if (arrived == S - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Claim the next index (>= N: none left).
+  auto claim = [&]() {
+    int k = 0;
+    if (lane == 0) k = atomicAdd(&next_idx, 1);
+    return __builtin_amdgcn_readfirstlane(k);
+  };
+  auto pid_of = [&](int i) {
+    return __builtin_amdgcn_readfirstlane(i < n0 ? pid_tab[i] : pid_tab[TAB * (NJ - 1) + i - n0]);
+  };
+  int job = 0;                            // the job of the wave's current state
+  bool had0 = false;                      // the wave attended an own-job page
+  auto step = [&](PageRegs<D, CF>& Pg, int i) {
+    const bool help = NJ > 1 && i >= n0;
+    if (help && job == 0) {
+      // First help page of this wave: keep the own job's wave partial (if
+      // it read any), take the help job's queries and a fresh state.  An
+      // opaque copy of the lane index keeps the LDS addresses from being
+      // hoisted out of the page loop.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      if (had0)
+        put_wave_partial<D, G>(o_lds[0][wave], m_lds[0][wave], l_lds[0][wave], o_acc, m_run, ln);
+      m_run = -INFINITY;
+#pragma unroll
+      for (int n = 0; n <= NT; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      q_operand<D, G, AF>(qb, qh_lds, ln);
+      job = 1;
+    }
+    had0 |= !help;
+    const int jj = help ? NJ - 1 : 0;
+    const int base = (help ? help_lo + i - n0 : own_lo + i) * kPage;
+    const bool patch = i == (help ? i1 : i0);
+    const int row = (help ? r1 : r0) % kPage;
+    if (patch) {
+      // The appended row goes into its cache row here (the values patched
+      // in below).
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const size_t pid = pid_of(i);
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) {
+        const int d = ln + 64 * u;
+        if (d < D)
+          store_row_elem<CF>(key_cache, value_cache, pid * kPage * D, row, d, row_lds[jj][0][d],
+                             row_lds[jj][1][d]);
+      }
+      if constexpr (CF == FMT_I8) {
+        if (ln == 0) {
+          key_scales[pid * kPage + row] = row_scale[jj][0];
+          value_scales[pid * kPage + row] = row_scale[jj][1];
+        }
+      }
+    }
+    compute_page<D, G, CF, AF>(Pg, m_run, o_acc, qb, ones, base, help ? Lh : L, patch, row,
+                               row_lds[jj][0], row_lds[jj][1], row_scale[jj][0],
+                               row_scale[jj][1], qk_scale_log2, lane);
+  };
+
+  // Two register buffers: the current page is computed while the next
+  // claimed one loads.
+  int cur = first_live ? wave : claim();
+  if (!first_live && cur < N) fetch(pid_of(cur), true, A);
+  if (cur < N) {
+    for (;;) {
+      const int nx = claim();
+      const bool more = nx < N;
+      fetch(more ? pid_of(nx) : 0u, more, Bf);
+      step(A, cur);
+      if (!more) break;
+      cur = nx;
+      const int ny = claim();
+      const bool more2 = ny < N;
+      fetch(more2 ? pid_of(ny) : 0u, more2, A);
+      step(Bf, cur);
+      if (!more2) break;
+      cur = ny;
+    }
   }
+
+  // Wave partials of the last job; a job this wave read no page of gets an
+  // empty partial.
+  if (job == 1)
+    put_wave_partial<D, G>(o_lds[NJ - 1][wave], m_lds[NJ - 1][wave], l_lds[NJ - 1][wave], o_acc,
+                           m_run, lane);
+  else if (had0)
+    put_wave_partial<D, G>(o_lds[0][wave], m_lds[0][wave], l_lds[0][wave], o_acc, m_run, lane);
+  if (!had0) put_empty_partial<G>(m_lds[0][wave], lane);
+  if (NJ > 1 && n1 > 0 && job == 0) put_empty_partial<G>(m_lds[NJ - 1][wave], lane);
   __syncthreads();
-  if (!last_split) return;
-  for (int h = wave; h < G; h += W)
-    merge_head<D, AF>(out + ((size_t)b * Hq + g * G + h) * D, S, v_scale, ws_m, ws_l, ws_o,
-                      ((size_t)b * Hq + g * G + h) * S, lane);
+
+  // The help job first (its owner is waiting to merge it), then the own job.
+  if (NJ > 1 && n1 > 0)
+    finish_item<D, G, AF, W, NJ>(NJ - 1, hb, g, Hkv, 2, 1, v_scale, m_lds, l_lds, o_lds,
+                                 &flag_lds[NJ - 1], out, ws_m, ws_l, ws_o, ws_count, nslots);
+  if (P > 0)
+    finish_item<D, G, AF, W, NJ>(0, b, g, Hkv, own_parts, own_slot, v_scale, m_lds,
+                                 l_lds, o_lds, &flag_lds[0], out, ws_m, ws_l, ws_o, ws_count,
+                                 nslots);
 }
 
 // ---------------------------------------------------------------------------
@@ -1250,12 +1454,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
 template <int D, int G, int CF, int AF, int W>
 hipError_t launch_grid(const DecodeArgs& a, float qk, float vs, hipStream_t stream) {
+  if (a.pair && !plan::pair_fits(W, G, D)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_split<D, G, CF, AF, W>), dim3(a.S, a.Hkv, a.B), dim3(64 * W), 0,
                      stream, (uint16_t*)a.out, (const uint16_t*)a.query, (uint8_t*)a.key_cache,
-                     (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.Hkv, a.MBPS,
-                     a.window, a.len_cap, a.S, qk, vs, a.ws_m, a.ws_l, a.ws_o, a.ws_count,
-                     (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.k_scale,
-                     a.v_scale, a.key_scales, a.value_scales);
+                     (uint8_t*)a.value_cache, a.block_tables, a.context_lens, a.B, a.Hkv,
+                     a.MBPS, a.window, a.len_cap, a.S, a.pair, qk, vs, a.ws_m, a.ws_l,
+                     a.ws_o, a.ws_count, (const uint16_t*)a.new_key,
+                     (const uint16_t*)a.new_value, a.k_scale, a.v_scale, a.key_scales,
+                     a.value_scales);
   return hipGetLastError();
 }
 

@@ -65,7 +65,32 @@ struct Plan {
   int S;          // grid mode: splits per sequence; balanced: partial slots per item
   int W;
   bool balanced;  // one equal range of the batch's pages per workgroup
+  bool pair;      // grid mode, one split: short sequences help long ones (below)
+  int slots;      // workspace partials per (sequence, query head)
 };
+
+// Pair mode: one split per (sequence, KV head) leaves the longest sequences
+// streaming alone at the end, at one CU's rate.  Every workgroup ranks the
+// sequences by pages (B <= kMaxPairB, one wave) and pairs rank r with rank
+// B - 1 - r; the workgroup of the shorter sequence of a pair also reads the
+// tail of the longer one (pair_split), for the same KV head.  Its wave
+// partials of the two jobs sit side by side in LDS, beside a copy of the
+// help job's queries per wave; pair mode is built where these take at most
+// 48 KiB (two workgroups of 4 waves still fit a CU).
+constexpr int kMaxPairB = 64;
+constexpr bool pair_fits(int W, int G, int D) {
+  return 2 * W * G * D * 4 + W * G * D * 2 <= 49152;
+}
+// A help job shorter than this is not worth its merge.
+constexpr int kMinHelpPages = 4;
+
+// The longer item of a pair (Pl >= Ps pages) keeps pages [0, a); its helper
+// reads [a, Pl), so that the two workgroups read the same number of pages.
+// No help (a = Pl) when fewer than kMinHelpPages would move.
+constexpr int pair_split(int Pl, int Ps) {
+  const int a = (Pl + Ps + 1) / 2;
+  return Pl - a >= kMinHelpPages ? a : Pl;
+}
 
 // Tokens a sequence may attend to at most (the kernels clamp each length to
 // it): max_context_len, capped at the window.
@@ -73,13 +98,14 @@ constexpr long long len_cap(long long max_len, int window) {
   return window > 0 ? min_of<long long>(window, max_len) : max_len;
 }
 
-inline bool make_plan(int B, int Hkv, int max_len, int window, int partition_tokens,
-                      bool byte_cache, Plan* p) {
+inline bool make_plan(int B, int Hkv, int G, int D, int max_len, int window,
+                      int partition_tokens, bool byte_cache, Plan* p) {
   long long L = len_cap(max_len, window);
   if (L < 1) L = 1;
   if (partition_tokens < 0 || partition_tokens % kBlock != 0) return false;
   const long long pages = (L + kBlock - 1) / kBlock;
   const long long pairs = (long long)B * Hkv;
+  p->pair = false;
   if (byte_cache && partition_tokens == 0 && L >= kMinSplitContext && B <= kMaxBalancedB &&
       pairs * pages < (1LL << 31)) {
     // Balanced mode: ranges of at most kPagesPerWave * W pages, and partial
@@ -88,6 +114,7 @@ inline bool make_plan(int B, int Hkv, int max_len, int window, int partition_tok
     p->W = 8;
     p->S = (int)max_of(kMinBalancedSlots,
                        (pages + kPagesPerWave * p->W - 1) / (kPagesPerWave * p->W) + 1);
+    p->slots = p->S;
     return true;
   }
   p->balanced = false;
@@ -103,10 +130,14 @@ inline bool make_plan(int B, int Hkv, int max_len, int window, int partition_tok
     S = min_of(S, kMaxAutoSplits);
     S = max_of(S, 1LL);
   }
+  // A wave holds at most kPagesPerWave pages.
   S = max_of(S, (pages + kPagesPerWave * W - 1) / (kPagesPerWave * W));
   if (S > 65535) return false;
   p->S = (int)S;
   p->W = W;
+  p->pair = S == 1 && partition_tokens == 0 && L >= kMinSplitContext && B <= kMaxPairB &&
+            pair_fits(W, G, D);
+  p->slots = p->pair ? 2 : p->S;
   return true;
 }
 
@@ -155,8 +186,8 @@ inline WsLayout ws_layout(int B, int Hq, int Hkv, int D, int S) {
 }
 
 inline size_t workspace_for(int B, int Hq, int Hkv, int D, const Plan& p) {
-  if (p.S <= 1) return 0;
-  return ws_layout(B, Hq, Hkv, D, p.S).total;
+  if (p.slots <= 1) return 0;
+  return ws_layout(B, Hq, Hkv, D, p.slots).total;
 }
 
 }  // namespace plan

@@ -354,6 +354,16 @@ def oracle_prefill_i8(wl: PrefillWorkload, pools):
                                 wl.block_tables, wl.context_lens, wl.scale, ks, vs)
 
 
+def same_output(a, b, tol: float, what: str = "") -> float:
+    """Two decode outputs of the same inputs agree within ``tol`` (max-abs).
+    The decode kernels' waves claim pages as they go, so the summation order
+    and the last bits may differ from one launch to the next; the cache
+    writes and the prefill outputs are bit-exact and are compared as such."""
+    d = max_abs(out_f64(a), out_f64(b))
+    assert d <= tol, f"{what}: outputs differ by {d}"
+    return d
+
+
 def max_abs(a: np.ndarray, b: np.ndarray) -> float:
     if a.size == 0:
         return 0.0

@@ -2,9 +2,11 @@
 // (paged_kv_cache_175_amd/csrc/plan.hpp), which the kernels rely on for
 // staying inside their buffers:
 //
-//   grid mode     every wave of every split holds at most kPagesPerWave
-//                 pages (its table register), for every length up to the
-//                 length cap; at most 65535 splits;
+//   grid mode     the splits cover the item; every wave of every split holds at most
+//                 kPagesPerWave pages (its table register), for every length
+//                 up to the length cap; at most 65535 splits;
+//   pair mode     every page of every item is read exactly once (by its own
+//                 workgroup or its one helper), and every job fits a wave;
 //   balanced mode a range spans at most kPagesPerWave * W pages, the ranges
 //                 cover the batch, and no item meets more ranges than it has
 //                 partial slots, for random length mixes up to the cap;
@@ -38,24 +40,78 @@ static long long g_cases = 0;
 
 static long long pages_of(long long L) { return L > 0 ? (L + kBlock - 1) / kBlock : 0; }
 
+static long long wave_pages(long long n, int w, int W) { return n > w ? (n - w + W - 1) / W : 0; }
+
 static void check_grid(int B, int Hkv, int max_len, int window, int part, const Plan& p) {
   const long long cap = len_cap(max_len, window);
   CHECK(p.S >= 1 && p.S <= 65535, "S=%d", p.S);
   CHECK(p.W == 4 || p.W == 8, "W=%d", p.W);
+  CHECK(p.slots == (p.pair ? 2 : p.S), "slots=%d", p.slots);
+  CHECK(!p.pair || (p.S == 1 && B <= kMaxPairB), "pair mode with S=%d B=%d", p.S, B);
   // Lengths the kernel may meet after clamping: a spread over [1, cap].
   std::vector<long long> lens = {1, 2, 31, 32, 33, 63, 64, 65, cap, cap - 1, cap - 31, cap / 2,
                                  cap / 3 + 7};
   for (long long L : lens) {
     if (L < 1 || L > cap) continue;
-    const long long P = pages_of(L);
+    const int P = (int)pages_of(L);
+    long long covered = 0;
     for (int s = 0; s < p.S; ++s) {
-      const long long a = (long long)s * P / p.S, b = (long long)(s + 1) * P / p.S;
+      // Split s of the kernel: pages [s P / S, (s + 1) P / S).
+      const int a = (int)((long long)s * P / p.S), b = (int)((long long)(s + 1) * P / p.S);
+      CHECK(a <= b && (s > 0 || a == 0) && (s + 1 < p.S || b == P), "split %d: [%d, %d) of %d",
+            s, a, b, P);
+      covered += b - a;
       for (int w = 0; w < p.W; ++w) {
-        const long long npg = b - a > w ? (b - a - w + p.W - 1) / p.W : 0;
+        const long long npg = wave_pages(b - a, w, p.W);
         CHECK(npg <= kPagesPerWave, "B=%d Hkv=%d max_len=%d window=%d part=%d L=%lld s=%d npg=%lld",
               B, Hkv, max_len, window, part, L, s, npg);
       }
     }
+    CHECK(covered == P, "splits cover %lld of %d pages", covered, P);
+    ++g_cases;
+  }
+}
+
+// Pair mode: rank by pages (ties by index), pair rank r with B - 1 - r, the
+// shorter item's workgroup reads [a, Pl) of the longer one (pair_split), as
+// the kernel computes it from the batch's lengths.  Every page of every item
+// is read exactly once, no workgroup helps more than one item, every job
+// fits a wave's table register, and an item is divided in two at most.
+static void check_pairs(std::mt19937_64& rng, const Plan& p, int B, long long cap) {
+  for (int trial = 0; trial < 8; ++trial) {
+    std::vector<int> P(B);
+    for (int b = 0; b < B; ++b) {
+      long long L = trial == 0 ? cap : trial == 1 ? (b % 2 ? cap : 0)
+                  : std::uniform_int_distribution<long long>(0, cap)(rng);
+      P[b] = (int)pages_of(L);
+    }
+    std::vector<int> rank(B, 0);
+    for (int i = 0; i < B; ++i)
+      for (int j = 0; j < B; ++j) rank[i] += P[j] > P[i] || (P[j] == P[i] && j < i);
+    std::vector<int> by_rank(B);
+    for (int i = 0; i < B; ++i) by_rank[rank[i]] = i;
+    std::vector<long long> read(B, 0);
+    std::vector<int> helped_by(B, -1);
+    for (int b = 0; b < B; ++b) {
+      const int r = rank[b], pr = B - 1 - r, partner = by_rank[pr];
+      int own_hi = P[b];
+      if (r < pr) own_hi = pair_split(P[b], P[partner]);
+      read[b] += own_hi;
+      for (int w = 0; w < p.W; ++w)
+        CHECK(wave_pages(own_hi, w, p.W) <= kPagesPerWave, "own job too long");
+      if (r > pr) {
+        const int a = pair_split(P[partner], P[b]);
+        if (a < P[partner]) {
+          CHECK(helped_by[partner] < 0, "item %d helped twice", partner);
+          helped_by[partner] = b;
+          read[partner] += P[partner] - a;
+          for (int w = 0; w < p.W; ++w)
+            CHECK(wave_pages(P[partner] - a, w, p.W) <= kPagesPerWave, "help job too long");
+        }
+      }
+    }
+    for (int b = 0; b < B; ++b)
+      CHECK(read[b] == P[b], "item %d: %lld of %d pages read", b, read[b], P[b]);
     ++g_cases;
   }
 }
@@ -105,12 +161,12 @@ static void check_balanced(std::mt19937_64& rng, int B, int Hkv, int max_len, in
 
 static void check_workspace(int B, int Hq, int Hkv, int D, const Plan& p) {
   const size_t need = workspace_for(B, Hq, Hkv, D, p);
-  if (p.S <= 1) {
-    CHECK(need == 0, "one split needs no workspace");
+  if (p.slots <= 1) {
+    CHECK(need == 0, "one part per item needs no workspace");
     return;
   }
-  const WsLayout w = ws_layout(B, Hq, Hkv, D, p.S);
-  const size_t rows = (size_t)B * Hq * p.S;
+  const WsLayout w = ws_layout(B, Hq, Hkv, D, p.slots);
+  const size_t rows = (size_t)B * Hq * p.slots;
   CHECK(w.m >= (size_t)B * Hkv * 4, "counters");
   CHECK(w.m >= kMinCounters * 4, "counter region below its minimum");
   if ((size_t)B * Hkv <= kMinCounters) CHECK(w.m == counter_bytes(1, 1), "counter region moved");
@@ -134,16 +190,23 @@ int main() {
         for (int window : windows)
           for (int part : parts)
             for (int byte_cache = 0; byte_cache < 2; ++byte_cache) {
+             for (int G : {1, 4, 16}) {
               Plan p{};
-              if (!make_plan(B, Hkv, max_len, window, part, byte_cache != 0, &p)) continue;
+              if (!make_plan(B, Hkv, G, 128, max_len, window, part, byte_cache != 0, &p))
+                continue;
               if (p.balanced) {
                 CHECK(byte_cache && part == 0 && B <= kMaxBalancedB, "balanced for B=%d", B);
                 if ((long long)B * Hkv * pages_of(len_cap(max_len, window)) < (1LL << 26))
                   check_balanced(rng, B, Hkv, max_len, window, p);
               } else {
                 check_grid(B, Hkv, max_len, window, part, p);
+                if (p.pair) {
+                  CHECK(pair_fits(p.W, G, 128), "pair mode without room in LDS");
+                  check_pairs(rng, p, B, len_cap(max_len, window));
+                }
               }
-              check_workspace(B, 4 * Hkv, Hkv, 128, p);
+              check_workspace(B, G * Hkv, Hkv, 128, p);
+             }
             }
   std::printf("ok %lld cases\n", g_cases);
   return 0;

@@ -142,10 +142,17 @@ def test_workspace_query():
     rows = 1 * 8 * 65
     assert lib.pa_decode_workspace_bytes(1, 8, 8, 64, 1 << 20, 0, 0) >= \
         2 * rnd(rows * 4) + rnd(rows * 64 * 4) + cnt(8)
-    # The per-format query: a 16-bit cache needs none here, a byte cache the
-    # balanced plan's slots.
+    # The per-format query: a 16-bit cache takes one split per sequence in
+    # pair mode here (two partial slots per query head: its own and its
+    # helper's), a byte cache the balanced plan's slots.
+    rows2 = 32 * 32 * 2
+    assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == \
+        2 * rnd(rows2 * 4) + rnd(rows2 * 128 * 4) + cnt(32 * 8)
+    # Above 64 sequences no pair mode: one split, no workspace.
+    assert lib.pa_decode_workspace_bytes_for(65, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == 0
+    # Below 1024 tokens one pass.
+    assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 1000, 0, 0, _lib.PA_BF16) == 0
     rows = 32 * 32 * 16
-    assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == 0
     for fmt in (_lib.PA_F8E4M3, _lib.PA_I8):
         assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, fmt) == \
             2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(32 * 8)

@@ -183,8 +183,9 @@ def test_balanced_softmax_scale_edges(name, scale):
 
 
 def test_balanced_repeat_same_workspace():
-    """Three launches on one workspace: bitwise equal outputs, so every cut
-    item's arrival counter was back at zero after each launch."""
+    """Three launches on one workspace: each output matches (a counter left
+    behind would make a merge run early or never), and the counter region
+    is all zero after them."""
     wl = CASES["short_around_long_g8_d128"]()
     P.say(f"[balanced repeat] B={wl.B}")
     kc, vc = P.hip_decode_setup(wl)
@@ -198,11 +199,11 @@ def test_balanced_repeat_same_workspace():
             for _ in range(3)]
     torch.cuda.synchronize()
     for o in outs[1:]:
-        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
-    # The counters [B * Hkv] int32 open the workspace's last 256-byte aligned
-    # region; the rest of that region is padding that stays zero.
-    tail = -(-(4 * wl.B * wl.Hkv) // 256) * 256
-    assert int(ws[-tail:].count_nonzero()) == 0
+        P.same_output(o, outs[0], P.TOL[wl.cache], "repeat on one workspace")
+    # The counter region opens the workspace: max(B * Hkv, 16384) int32,
+    # all back at zero.
+    region = 4 * max(wl.B * wl.Hkv, ops.MIN_COUNTERS)
+    assert int(ws[:region].count_nonzero()) == 0
     okc, ovc = P.oracle_decode_setup(wl)
     assert P.max_abs(P.out_f64(outs[0]), P.oracle_decode(wl, okc, ovc)) <= P.TOL[wl.cache]
 
@@ -210,8 +211,8 @@ def test_balanced_repeat_same_workspace():
 @pytest.mark.parametrize("cache", ["e4m3", "int8"])
 def test_balanced_identity_map(cache):
     """A dense pool behind a NULL table (the identity map, block b * MBPS + j)
-    through the balanced plan: bitwise equal to the same pool behind the
-    explicit identity table, and within tolerance of the oracle."""
+    through the balanced plan: within tolerance of the same pool behind the
+    explicit identity table and of the oracle."""
     import dataclasses
     wl = W.decode_workload("bal_ident", 121, B=5, Hq=16, Hkv=4, D=128, act="bf16", cache=cache,
                            ctx_range=(1, 2600))
@@ -230,7 +231,7 @@ def test_balanced_identity_map(cache):
     outs = [ops.decode(q, kc, vc, table, cl, L, wl.scale, **kw)
             for table in (ops.IdentityMap(M), torch.from_numpy(wl.block_tables).cuda())]
     torch.cuda.synchronize()
-    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    P.same_output(outs[0], outs[1], P.TOL[cache], "identity map vs table")
     if cache == "int8":
         ref = P.oracle_decode_i8(wl, P.oracle_decode_setup_i8(wl))
     else:

