@@ -19,7 +19,7 @@ from typing import Optional
 
 import torch
 
-from . import _lib
+from . import _lib, pool
 from ._lib import PagedKVError  # noqa: F401  (re-export)
 
 _ACT = {torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
@@ -103,12 +103,44 @@ def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: i
             (num_blocks, num_kv_heads, head_dim, block_size))
 
 
+def _free_bytes(device) -> Optional[int]:
+    device = torch.device(device)
+    if device.type != "cuda":
+        return None
+    return torch.cuda.mem_get_info(device)[0]
+
+
 def alloc_pools(num_blocks: int, num_kv_heads: int, head_dim: int, act_dtype: torch.dtype,
                 cache_dtype: str = "auto", device="cuda", block_size: int = 32):
-    """Allocate (uninitialised) key and value pools up front."""
+    """Allocate (uninitialised) key and value pools up front.  Raises
+    :class:`pool.PoolTooLarge` before allocating when they exceed the
+    device's free memory."""
     ks, vs = pool_shapes(num_blocks, num_kv_heads, head_dim, block_size)
     dt = {"f8e4m3": torch.uint8, "i8": torch.int8}.get(cache_dtype, act_dtype)
+    elem = torch.empty((), dtype=dt).element_size()
+    need = 2 * num_blocks * num_kv_heads * head_dim * block_size * elem
+    pool.check_pool_fits(need, _free_bytes(device))
     return (torch.empty(ks, dtype=dt, device=device), torch.empty(vs, dtype=dt, device=device))
+
+
+def alloc_model_pools(cfg: "pool.PagedKVConfig", num_kv_heads: int, head_dim: int,
+                      act_dtype: torch.dtype, num_layers: int = 1, device="cuda"):
+    """The pools of every layer of a model, sized by ``cfg`` (budget in MiB,
+    fraction of free memory, or context size) and checked as a whole against
+    the budget and the free memory before the first allocation.  Returns
+    ``(num_blocks, [(key_cache, value_cache[, key_scales, value_scales]), ...])``."""
+    act_bytes = torch.empty((), dtype=act_dtype).element_size()
+    n = pool.plan_pool(cfg, num_kv_heads, head_dim, num_layers, act_bytes,
+                       _free_bytes(device))
+    layers = []
+    for _ in range(num_layers):
+        kc, vc = alloc_pools(n, num_kv_heads, head_dim, act_dtype, cfg.cache_dtype, device,
+                             cfg.block_size)
+        if cfg.cache_dtype == "i8":
+            layers.append((kc, vc) + alloc_scale_pools(n, num_kv_heads, device, cfg.block_size))
+        else:
+            layers.append((kc, vc))
+    return n, layers
 
 
 def alloc_scale_pools(num_blocks: int, num_kv_heads: int, device="cuda", block_size: int = 32):

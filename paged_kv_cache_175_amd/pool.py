@@ -105,6 +105,49 @@ def num_blocks(cfg: PagedKVConfig, num_kv_heads: int, head_dim: int, num_layers:
     raise ValueError("no pool size configured")
 
 
+def pool_bytes(cfg: PagedKVConfig, blocks: int, num_kv_heads: int, head_dim: int,
+               num_layers: int = 1, act_bytes: int = 2) -> int:
+    """Device bytes of ``blocks`` blocks in every layer (K, V and, for an
+    INT8 cache, the row scales)."""
+    return blocks * bytes_per_block(cfg, num_kv_heads, head_dim, num_layers, act_bytes)
+
+
+class PoolTooLarge(MemoryError):
+    """The pool does not fit: raised before anything is allocated (the pages
+    allocate the pool up front, so an oversized budget is an out-of-memory
+    error at start-up; here it is this error, with the sizes)."""
+
+
+def check_pool_fits(need_bytes: int, free_bytes: Optional[int],
+                    budget_bytes: Optional[int] = None) -> None:
+    """Raise :class:`PoolTooLarge` when ``need_bytes`` exceeds the budget or
+    the device's free memory (either may be None: not checked)."""
+    if budget_bytes is not None and need_bytes > budget_bytes:
+        raise PoolTooLarge(f"the KV pool needs {need_bytes / MIB:.1f} MiB, more than its "
+                           f"budget of {budget_bytes / MIB:.1f} MiB")
+    if free_bytes is not None and need_bytes > free_bytes:
+        raise PoolTooLarge(f"the KV pool needs {need_bytes / MIB:.1f} MiB but the device has "
+                           f"{free_bytes / MIB:.1f} MiB free; lower gpu_mem_mb / gpu_mem_usage "
+                           f"or the context size")
+
+
+def plan_pool(cfg: PagedKVConfig, num_kv_heads: int, head_dim: int, num_layers: int = 1,
+              act_bytes: int = 2, free_bytes: Optional[int] = None) -> int:
+    """Blocks per layer for ``cfg``, checked against the budget and the free
+    memory before any allocation; raises :class:`PoolTooLarge`."""
+    n = num_blocks(cfg, num_kv_heads, head_dim, num_layers, act_bytes, free_bytes)
+    if n < 1:
+        raise PoolTooLarge("the budget does not hold one block of every layer")
+    budget = None
+    if cfg.gpu_mem_mb is not None:
+        budget = cfg.gpu_mem_mb * MIB
+    elif cfg.gpu_mem_usage is not None:
+        budget = int(cfg.gpu_mem_usage * free_bytes)
+    check_pool_fits(pool_bytes(cfg, n, num_kv_heads, head_dim, num_layers, act_bytes),
+                    free_bytes, budget)
+    return n
+
+
 class OutOfBlocks(RuntimeError):
     pass
 
