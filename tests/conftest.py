@@ -6,6 +6,15 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+# The oracle's process pool forks its workers from a server started now,
+# before any test initialises the GPU.
+import oracle_side  # noqa: E402
+
+oracle_side.start()
 
 
 def pytest_configure(config):

@@ -1,22 +1,25 @@
 """GPU parity at the benchmark workloads' full sizes, in the launch
 configuration bench.py times (the fused write + decode entry with the
-library's automatic split; the prefill kernel over the full shared-prefix
-batch).
+library's automatic plan; the prefill kernel over the full shared-prefix
+batch; the window prefill over full rings).
 
-The oracle cannot afford every output at these sizes, so it computes sampled
-ones: whole sequences for decode (the longest, the shortest and two drawn
-with a fixed seed), and for prefill the query rows at workgroup-tile and
-page boundaries of two sequences, for three heads.  The cache pages those
-samples read are compared byte for byte with the oracle's writer.
+Decode and the shared-prefix prefill are checked whole: every block of the
+pools byte for byte against the oracle's writer, and every output (every
+sequence and head; every query row of the prefill) against the oracle's
+attention.  The window prefill is checked on every ring byte for byte and on
+every sequence and head at the query rows around tile, page and window
+boundaries (the oracle gathers a window of 4096 ring rows per query row one
+by one, too slow for all 8192 rows).  The oracle runs over a process pool
+(``oracle_side``), its functions unchanged.
 """
 
 import numpy as np
 import pytest
 import torch
 
+import oracle_side as S
 import paritylib as P
-from oracle import attention as o_attn
-from oracle import cache as o_cache
+from paged_kv_cache_175_amd import ops, pool
 from paged_kv_cache_175_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -28,128 +31,90 @@ FULL_DECODE = {
 }
 
 
-def _sample_seqs(wl, n_random=2, seed=1234):
-    lens = wl.context_lens
-    picks = [int(np.argmax(lens)), int(np.argmin(lens))]
-    rng = np.random.default_rng(seed)
-    for b in rng.permutation(wl.B):
-        if len(picks) >= 2 + n_random:
-            break
-        if int(b) not in picks:
-            picks.append(int(b))
-    return picks
-
-
-def _blocks_of(wl, seqs):
-    blocks = set()
-    for b in seqs:
-        L = int(wl.context_lens[b])
-        if wl.window:
-            L = min(L, wl.window)
-        nblk = -(-L // wl.BS)
-        blocks.update(int(x) for x in wl.block_tables[b, :nblk])
-    return sorted(blocks)
+def _same_pool(got: torch.Tensor, ref: np.ndarray, what: str) -> None:
+    g = P.scale_bits(got) if got.dtype == torch.float32 else P.pool_bits(got)
+    r = ref.view(np.int32) if ref.dtype == np.float32 else ref
+    assert g.shape == r.shape, what
+    bad = np.flatnonzero((g != r).reshape(g.shape[0], -1).any(axis=1))
+    assert bad.size == 0, f"{what}: {bad.size} blocks differ, first {bad[:8].tolist()}"
 
 
 @pytest.mark.parametrize("name", list(FULL_DECODE))
-def test_full_size_decode_sampled(name):
+def test_full_size_decode(name):
     wl = FULL_DECODE[name]()
-    seqs = _sample_seqs(wl)
     P.say(f"[full decode] {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
-          f"cache={wl.cache} window={wl.window} sampled seqs={seqs} "
-          f"lens={[int(wl.context_lens[b]) for b in seqs]}")
+          f"cache={wl.cache} window={wl.window} lens {int(wl.context_lens.min())}.."
+          f"{int(wl.context_lens.max())}; oracle on {S.workers()} processes")
     kc, vc = P.hip_decode_append_setup(wl)
-    out = P.hip_decode_append(wl, kc, vc)          # automatic split, as timed
+    out = P.hip_decode_append(wl, kc, vc)          # automatic plan, as timed
     torch.cuda.synchronize()
-    okc, ovc = P.oracle_decode_setup(wl, seqs)
-    blocks = _blocks_of(wl, seqs)
-    assert np.array_equal(P.pool_bits(kc)[blocks], okc[blocks]), "key pages differ"
-    assert np.array_equal(P.pool_bits(vc)[blocks], ovc[blocks]), "value pages differ"
-    ref = P.oracle_decode(wl, okc, ovc, seqs)
-    err = P.max_abs(P.out_f64(out)[seqs], ref)
-    P.say(f"    max-abs error {err:.3e}")
+    (okc, ovc), ref = S.full_decode(wl)
+    _same_pool(kc, okc, "key pool")
+    _same_pool(vc, ovc, "value pool")
+    err = P.max_abs(P.out_f64(out), ref)
+    P.say(f"    max-abs error {err:.3e} over all {wl.B} sequences x {wl.Hq} heads "
+          f"(tolerance {P.TOL[wl.cache]:.0e})")
     assert err <= P.TOL[wl.cache]
 
 
-def test_full_size_prefill_sampled():
+def test_full_size_prefill():
     wl = W.prefix_prefill()
     P.say(f"[full prefill] {wl.name} B={wl.B} Hq={wl.Hq} D={wl.D} prefix={wl.prefix_len} "
-          f"chunk={int(wl.chunk_lens[0])}")
+          f"chunk={int(wl.chunk_lens[0])}; oracle on {S.workers()} processes")
     kc, vc = P.hip_prefill_setup(wl)
     out = P.out_f64(P.hip_prefill(wl, kc, vc))
     torch.cuda.synchronize()
-    kbits, vbits = P.pool_bits(kc), P.pool_bits(vc)
-
-    okc, ovc = P.oracle_pools(wl)
-    slots = [o_cache.slot_of(wl.block_tables[0], t, wl.BS) for t in range(wl.prefix_len)]
-    o_cache.reshape_and_cache(wl.prefix_k, wl.prefix_v, okc, ovc, np.array(slots, np.int64),
-                              wl.act, wl.cache, wl.k_scale, wl.v_scale)
-    seqs = [0, wl.B - 1]
-    heads = [0, wl.Hq // 2 + 1, wl.Hq - 1]
-    err = 0.0
-    for b in seqs:
-        C = int(wl.chunk_lens[b])
-        ctx = int(wl.context_lens[b])
-        slots = [o_cache.slot_of(wl.block_tables[b], wl.prefix_len + t, wl.BS)
-                 for t in range(C)]
-        o_cache.reshape_and_cache(wl.chunk_k[b], wl.chunk_v[b], okc, ovc,
-                                  np.array(slots, np.int64), wl.act, wl.cache, wl.k_scale,
-                                  wl.v_scale)
-        blocks = [int(x) for x in wl.block_tables[b, :-(-ctx // wl.BS)]]
-        assert np.array_equal(kbits[blocks], okc[blocks]), f"key pages of seq {b} differ"
-        assert np.array_equal(vbits[blocks], ovc[blocks]), f"value pages of seq {b} differ"
-        k, v = o_cache.gather_f64(okc, ovc, wl.block_tables[b], ctx, wl.cache, wl.k_scale,
-                                  wl.v_scale)
-        q = o_cache.bits_to_f64(wl.query[wl.cu_q_lens[b]:wl.cu_q_lens[b + 1]], wl.act)
-        G = wl.Hq // wl.Hkv
-        for j in sorted({0, 1, 31, 32, 63, 64, 255, 256, C - 2, C - 1}):
-            i = ctx - C + j
-            for h in heads:
-                ref = o_attn.softmax_attend(q[j, h], k[:i + 1, h // G], v[:i + 1, h // G],
-                                            wl.scale)
-                got = out[wl.cu_q_lens[b] + j, h]
-                err = max(err, float(np.abs(got - ref).max()))
-    P.say(f"    max-abs error {err:.3e} over {len(seqs)} sequences")
+    (okc, ovc), ref = S.full_prefill(wl)
+    _same_pool(kc, okc, "key pool")
+    _same_pool(vc, ovc, "value pool")
+    err = P.max_abs(out, ref)
+    P.say(f"    max-abs error {err:.3e} over all {wl.total_q} rows x {wl.Hq} heads "
+          f"(tolerance {P.TOL[wl.cache]:.0e})")
     assert err <= P.TOL[wl.cache]
 
 
-def test_full_size_int8_decode_sampled():
+def test_full_size_int8_decode():
     """The INT8 decode workload at full size (B=64, contexts 1024..8192), in
     the launch configuration bench.py times: the writer, then pa_decode_i8
-    with the automatic split."""
+    with the automatic plan."""
     wl = W.int8_decode()
-    seqs = _sample_seqs(wl)
-    P.say(f"[full int8 decode] B={wl.B} sampled seqs={seqs} "
-          f"lens={[int(wl.context_lens[b]) for b in seqs]}")
+    P.say(f"[full int8 decode] B={wl.B} lens {int(wl.context_lens.min())}.."
+          f"{int(wl.context_lens.max())}; oracle on {S.workers()} processes")
     pools = P.hip_decode_setup_i8(wl)
     out = P.hip_decode_i8(wl, pools)
     torch.cuda.synchronize()
-    opools = P.oracle_decode_setup_i8(wl, seqs)
-    blocks = _blocks_of(wl, seqs)
-    for got, ref, what in zip(pools, opools, ("key codes", "value codes", "key scales",
-                                              "value scales")):
-        g = P.scale_bits(got) if got.dtype == torch.float32 else P.pool_bits(got)
-        r = ref.view(np.int32) if ref.dtype == np.float32 else ref
-        assert np.array_equal(g[blocks], r[blocks]), f"{what} differ"
-    ref = P.oracle_decode_i8(wl, opools, seqs)
-    err = P.max_abs(P.out_f64(out)[seqs], ref)
-    P.say(f"    max-abs error {err:.3e}")
+    opools, ref = S.full_decode(wl)
+    for got, r, what in zip(pools, opools, ("key codes", "value codes", "key scales",
+                                            "value scales")):
+        _same_pool(got, r, what)
+    err = P.max_abs(P.out_f64(out), ref)
+    P.say(f"    max-abs error {err:.3e} over all {wl.B} sequences x {wl.Hq} heads "
+          f"(tolerance {P.TOL['int8']:.0e})")
     assert err <= P.TOL["int8"]
 
 
+def _window_rows(C: int, W_: int) -> list:
+    """Chunk rows at workgroup-tile (64 rows x query tiles), page and window
+    edges, and the last rows."""
+    rows = {0, 1, 31, 32, 63, 64, 127, 128, 191, 192, 255, 256, 1023, 1024, C // 2, C - 2, C - 1}
+    return sorted(r for r in rows if 0 <= r < C)
+
+
 @pytest.mark.parametrize("cache", [None, "e4m3", "int8"])
-def test_full_size_sliding_prefill_sampled(cache):
+def test_full_size_sliding_prefill(cache):
     """The sliding-window prefill workloads at full size (B=4, W=4096, 8192
     positions in the ring, chunks of 2048), as bench.py times them, over a
-    bf16, E4M3 or INT8 ring; query rows at tile and page boundaries and at
-    the window's edge, three heads."""
+    bf16, E4M3 or INT8 ring: every ring byte, and every sequence and head at
+    the boundary rows."""
     wl = W.sliding_prefill(cache=cache)
+    C = int(wl.chunk_lens[0])
+    rows = _window_rows(C, wl.window)
     P.say(f"[full sliding prefill] ring={wl.cache} B={wl.B} W={wl.window} "
-          f"hist={int(wl.hist_lens[0])} chunk={int(wl.chunk_lens[0])}")
+          f"hist={int(wl.hist_lens[0])} chunk={C} rows/seq={len(rows)}; "
+          f"oracle on {S.workers()} processes")
     i8 = wl.cache == "int8"
     pools = P.gpu_pools_i8(wl) if i8 else (*P.gpu_pools(wl), None, None)
     kc, vc, ks, vs = pools
-    from paged_kv_cache_175_amd import ops, pool
     hk, hv, hs = [], [], []
     for b in range(wl.B):
         pos = np.arange(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
@@ -167,36 +132,13 @@ def test_full_size_sliding_prefill_sampled(cache):
         int(wl.chunk_lens.max()), wl.scale, wl.window, k_scale=wl.k_scale, v_scale=wl.v_scale,
         key_scales=ks, value_scales=vs))
     torch.cuda.synchronize()
-    seqs = [0, wl.B - 1]
-    if i8:
-        okc, ovc, oks, ovs = P.oracle_pools_i8(wl)
-    else:
-        fill = P.NAN_E4M3 if wl.cache == "e4m3" else P.NAN16[wl.act]
-        okc, ovc = o_cache.empty_pools(wl.num_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, fill)
-        oks, ovs = wl.k_scale, wl.v_scale
-    from oracle import pool as o_pool
-    for b in seqs:
-        pos = range(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
-        slots = [o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
-                 for p in pos]
-        o_cache.reshape_and_cache(wl.hist_k[b], wl.hist_v[b], okc, ovc,
-                                  np.array(slots, np.int64), wl.act, wl.cache, oks, ovs)
-        blocks = [int(x) for x in wl.block_tables[b]]
-        assert np.array_equal(P.pool_bits(kc)[blocks], okc[blocks]), f"ring K of {b} differs"
-        assert np.array_equal(P.pool_bits(vc)[blocks], ovc[blocks]), f"ring V of {b} differs"
-        if i8:
-            assert np.array_equal(P.scale_bits(ks)[blocks], oks.view(np.int32)[blocks])
-            assert np.array_equal(P.scale_bits(vs)[blocks], ovs.view(np.int32)[blocks])
-    C = int(wl.chunk_lens[0])
-    js = sorted({0, 31, 32, 191, 192, 1024, C - 2, C - 1})
-    rows = {(b, j) for b in seqs for j in js}
-    ref = o_attn.prefill_chunk_window(wl.query, wl.act, wl.chunk_k, wl.chunk_v, wl.cu_q_lens,
-                                      okc, ovc, wl.cache, wl.block_tables, wl.context_lens,
-                                      wl.scale, wl.window, rows=rows, k_scale=oks, v_scale=ovs)
-    heads = [0, wl.Hq // 2 + 1, wl.Hq - 1]
+    opools, ref = S.window_prefill_rows(wl, {b: rows for b in range(wl.B)})
+    names = ("ring K", "ring V", "ring K scales", "ring V scales")
+    for got, r, what in zip((kc, vc, ks, vs), opools, names):
+        _same_pool(got, r, what)
     err = 0.0
-    for b, j in rows:
-        r = int(wl.cu_q_lens[b]) + j
-        err = max(err, float(np.abs(out[r, heads] - ref[r, heads]).max()))
-    P.say(f"    max-abs error {err:.3e} over {len(rows)} rows")
+    for (b, j), r in ref.items():
+        err = max(err, P.max_abs(out[int(wl.cu_q_lens[b]) + j], r))
+    P.say(f"    max-abs error {err:.3e} over {len(ref)} rows x {wl.Hq} heads "
+          f"(tolerance {P.TOL[wl.cache]:.0e})")
     assert err <= P.TOL[wl.cache]
