@@ -48,7 +48,10 @@ def _args():
     ap.add_argument("--separate-write", action="store_true",
                     help="time pa_reshape_and_cache + pa_decode instead of pa_decode_append")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+                    help="seconds each core repeats the oracle's step for the CPU baseline "
+                         "(0 = skip)")
+    ap.add_argument("--no-sub-results", action="store_true",
+                    help="default workload only: leave out the other workloads' lines")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
                     help="instead: time a plain device copy of this many GiB (counter scaling)")
     ap.add_argument("--dispatch-sweep", action="store_true",
@@ -146,7 +149,7 @@ def bench_decode(wl, a, torch):
     elem = 1 if wl.cache in ("e4m3", "int8") else 2
     row_extra = 4 if i8 else 0          # an INT8 row also carries its fp32 scale
     pool_bytes = 2 * (math.prod(kshape) * elem + wl.pool_blocks * wl.Hkv * wl.BS * row_extra)
-    R = a.replicas or max(1, math.ceil(2e9 / pool_bytes))
+    R = a.replicas or min(64, max(1, math.ceil(2e9 / pool_bytes)))
 
     kc0 = torch.zeros(kshape, dtype=cache_dt, device=dev)
     vc0 = torch.zeros(vshape, dtype=cache_dt, device=dev)
@@ -305,22 +308,69 @@ def bench_decode(wl, a, torch):
     return res, (wl, kv_bytes)
 
 
-def cpu_baseline_decode(wl, kv_bytes, seconds):
-    """The CPU oracle on the same inputs: untimed pool population, then timed
-    repetitions of (writer for the new tokens + decode of every sequence)."""
+# --------------------------------------------------------------------------- CPU baseline
+# The oracle (unchanged) on every core of this process's CPU share: one
+# single-threaded worker process per core (at most 16, a host's share per
+# GPU), each on its own group of sequences with its own compact pool (the
+# blocks its sequences own, renumbered).  The workers populate their pools
+# untimed, meet at a barrier, then repeat their step for the time budget; the
+# batch's step time is the slowest group's.  Workers are forked from a
+# forkserver started before this process touches the GPU.
+
+_MP = None
+
+
+def _cpu_cores() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _start_cpu_pool() -> None:
+    global _MP
+    if _MP is not None:
+        return
+    import multiprocessing as mp
+    _MP = mp.get_context("forkserver")
+    _MP.set_forkserver_preload(["numpy", "oracle.attention", "oracle.cache", "oracle.pool"])
+    from multiprocessing import forkserver
+    forkserver.ensure_running()
+
+
+def _groups(weights, n):
+    """Indices in at most n groups of about equal total weight."""
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    from oracle import attention as o_attn
+    order = np.argsort(-np.asarray(weights, dtype=np.float64), kind="stable")
+    groups, load = [[] for _ in range(n)], [0.0] * n
+    for i in order:
+        g = load.index(min(load))
+        groups[g].append(int(i))
+        load[g] += float(weights[i])
+    return [sorted(g) for g in groups if g]
+
+
+def _compact(tables, nblk):
+    """Renumber the first nblk[r] entries of each table row into 0..n-1."""
+    import numpy as np
+    used = np.unique(np.concatenate([tables[r, :nblk[r]] for r in range(len(nblk))]))
+    local = {int(x): k for k, x in enumerate(used)}
+    out = np.zeros_like(tables)
+    for r in range(len(nblk)):
+        out[r, :nblk[r]] = [local[int(x)] for x in tables[r, :nblk[r]]]
+    return out, int(used.size)
+
+
+def _cpu_pools(wl):
+    from oracle import cache as o_cache
+    kc, vc = o_cache.empty_pools(wl.pool_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, 0)
+    if wl.cache == "int8":
+        return kc, vc, *o_cache.empty_scale_pools(wl.pool_blocks, wl.Hkv, wl.BS)
+    return kc, vc, wl.k_scale, wl.v_scale
+
+
+def _cpu_setup_decode(wl):
+    import numpy as np
     from oracle import cache as o_cache
     from oracle import pool as o_pool
-
-    kc, vc = o_cache.empty_pools(wl.pool_blocks, wl.Hkv, wl.BS, wl.D, wl.cache, 0)
-    ks, vs = wl.k_scale, wl.v_scale
-    if wl.cache == "int8":
-        ks, vs = o_cache.empty_scale_pools(wl.pool_blocks, wl.Hkv, wl.BS)
+    kc, vc, ks, vs = _cpu_pools(wl)
 
     def row(pos):
         return o_pool.ring_index(int(pos), wl.window) if wl.window else int(pos)
@@ -333,32 +383,229 @@ def cpu_baseline_decode(wl, kv_bytes, seconds):
                                   wl.act, wl.cache, ks, vs)
     new_slots = np.array([o_cache.slot_of(wl.block_tables[b], row(wl.new_pos[b]), wl.BS)
                           for b in range(wl.B)])
+    return wl, (kc, vc, ks, vs), new_slots
 
-    def step():
-        o_cache.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, new_slots, wl.act, wl.cache,
-                                  ks, vs)
-        o_attn.decode(wl.query, wl.act, kc, vc, wl.cache, wl.block_tables, wl.context_lens,
-                      wl.scale, ks, vs, wl.window)
 
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+def _cpu_step_decode(state):
+    from oracle import attention as o_attn
+    from oracle import cache as o_cache
+    wl, (kc, vc, ks, vs), new_slots = state
+    o_cache.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, new_slots, wl.act, wl.cache, ks, vs)
+    o_attn.decode(wl.query, wl.act, kc, vc, wl.cache, wl.block_tables, wl.context_lens,
+                  wl.scale, ks, vs, wl.window)
+
+
+def _cpu_setup_prefill(wl):
+    import numpy as np
+    from oracle import cache as o_cache
+    kc, vc, ks, vs = _cpu_pools(wl)
+    slots = [o_cache.slot_of(wl.block_tables[0], t, wl.BS) for t in range(wl.prefix_len)]
+    o_cache.reshape_and_cache(wl.prefix_k, wl.prefix_v, kc, vc, np.array(slots), wl.act,
+                              wl.cache, ks, vs)
+    chunk_slots = [np.array([o_cache.slot_of(wl.block_tables[b], wl.prefix_len + t, wl.BS)
+                             for t in range(int(wl.chunk_lens[b]))]) for b in range(wl.B)]
+    return wl, (kc, vc, ks, vs), chunk_slots
+
+
+def _cpu_step_prefill(state):
+    from oracle import attention as o_attn
+    from oracle import cache as o_cache
+    wl, (kc, vc, ks, vs), chunk_slots = state
+    for b in range(wl.B):
+        o_cache.reshape_and_cache(wl.chunk_k[b], wl.chunk_v[b], kc, vc, chunk_slots[b], wl.act,
+                                  wl.cache, ks, vs)
+    o_attn.prefill_chunk(wl.query, wl.act, wl.cu_q_lens, kc, vc, wl.cache, wl.block_tables,
+                         wl.context_lens, wl.scale, ks, vs)
+
+
+def _cpu_setup_window(wl):
+    import numpy as np
+    from oracle import cache as o_cache
+    from oracle import pool as o_pool
+    kc, vc, ks, vs = _cpu_pools(wl)
+    for b in range(wl.B):
+        pos = range(int(wl.hist_pos0[b]), int(wl.hist_lens[b]))
+        slots = [o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
+                 for p in pos]
+        o_cache.reshape_and_cache(wl.hist_k[b], wl.hist_v[b], kc, vc, np.array(slots), wl.act,
+                                  wl.cache, ks, vs)
+    return wl, (kc, vc, ks, vs)
+
+
+def _cpu_step_window(state):
+    from oracle import attention as o_attn
+    wl, (kc, vc, ks, vs) = state
+    o_attn.prefill_chunk_window(wl.query, wl.act, wl.chunk_k, wl.chunk_v, wl.cu_q_lens, kc, vc,
+                                wl.cache, wl.block_tables, wl.context_lens, wl.scale,
+                                wl.window, rows=wl.rows, k_scale=ks, v_scale=vs)
+
+
+_CPU_KINDS = {"decode": (_cpu_setup_decode, _cpu_step_decode),
+              "prefill": (_cpu_setup_prefill, _cpu_step_prefill),
+              "window": (_cpu_setup_window, _cpu_step_window)}
+
+
+def _cpu_worker(job, barrier, results):
+    import types
+    from threadpoolctl import threadpool_limits
     try:
-        if ctx:
-            ctx.__enter__()
-        reps, t = 0, 0.0
-        while reps == 0 or t < seconds:
+        with threadpool_limits(limits=1):
+            setup, step = _CPU_KINDS[job.pop("kind")]
+            seconds = job.pop("seconds")
+            jid = job.pop("id")
+            state = setup(types.SimpleNamespace(**job))
+            barrier.wait(timeout=1800)
             t0 = time.perf_counter()
-            step()
-            t += time.perf_counter() - t0
-            reps += 1
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    per = t / reps
+            reps = 0
+            while True:
+                step(state)
+                reps += 1
+                t = time.perf_counter() - t0
+                if t >= seconds:
+                    break
+        results.put((jid, reps, t, None))
+    except Exception as e:  # pragma: no cover - reported to the parent
+        barrier.abort()
+        results.put((job.get("id", -1), 0, 0.0, repr(e)))
+
+
+def _cpu_run(jobs, seconds):
+    """Run every job in its own worker process; returns the slowest job's
+    seconds per step and the reps and seconds of each."""
+    _start_cpu_pool()
+    n = len(jobs)
+    barrier = _MP.Barrier(n)
+    results = _MP.Queue()
+    for i, j in enumerate(jobs):
+        j.update(id=i, seconds=seconds)
+    procs = [_MP.Process(target=_cpu_worker, args=(j, barrier, results)) for j in jobs]
+    for p in procs:
+        p.start()
+    got = [results.get(timeout=3600) for _ in range(n)]
+    for p in procs:
+        p.join()
+    errs = [e for (_, _, _, e) in got if e]
+    if errs:
+        raise RuntimeError(f"CPU baseline worker failed: {errs[0]}")
+    per = max(t / reps for (_, reps, t, _) in got)
+    return per, got
+
+
+def _decode_job(wl, g):
+    import numpy as np
+    L = wl.context_lens.astype(np.int64)
+    if wl.window:
+        L = np.minimum(L, wl.window)
+    nblk = [int(-(-int(L[b]) // wl.BS)) for b in g]
+    tables, nb = _compact(wl.block_tables[g], nblk)
+    return dict(kind="decode", act=wl.act, cache=wl.cache, B=len(g), Hq=wl.Hq, Hkv=wl.Hkv,
+                D=wl.D, BS=wl.BS, window=wl.window, scale=wl.scale, k_scale=wl.k_scale,
+                v_scale=wl.v_scale, pool_blocks=nb, block_tables=tables,
+                context_lens=wl.context_lens[g], query=wl.query[g],
+                cached_pos0=wl.cached_pos0[g], cached_k=[wl.cached_k[b] for b in g],
+                cached_v=[wl.cached_v[b] for b in g], new_pos=wl.new_pos[g],
+                new_k=wl.new_k[g], new_v=wl.new_v[g])
+
+
+def cpu_baseline_decode(wl, kv_bytes, seconds):
+    """The oracle on the same inputs, the batch's sequences spread over the
+    CPU's cores: per group, untimed pool population, then timed repetitions
+    of (writer for the group's new tokens + decode of its sequences)."""
+    import numpy as np
+    L = wl.context_lens.astype(np.int64)
+    if wl.window:
+        L = np.minimum(L, wl.window)
+    groups = _groups(L + 64, _cpu_cores())
+    per, got = _cpu_run([_decode_job(wl, g) for g in groups], seconds)
+    reps = min(r for (_, r, _, _) in got)
     return {
-        "value": round(kv_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "tokens_per_s": round(wl.B / per, 3), "seconds_per_step": round(per, 4),
+        "value": round(kv_bytes / per / 1e9, 4), "unit": "GB/s", "cores": len(groups),
+        "kind": "oracle", "tokens_per_s": round(wl.B / per, 3),
+        "seconds_per_step": round(per, 4),
         "sample": f"full workload ({wl.B} sequences, {wl.kv_read_tokens()} tokens per KV head): "
-                  f"writer + fp64 decode, {reps} repetitions in {t:.1f} s, single thread",
+                  f"writer + fp64 decode, sequences split by tokens over {len(groups)} "
+                  f"single-threaded processes, each repeating its step for {seconds:.0f} s "
+                  f"(at least {reps} repetitions); step time = the slowest group's",
+        "cpu_model": _cpu_info(), "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def cpu_baseline_prefill(wl, seconds):
+    """The oracle's writer + chunked prefill on the same inputs, one group of
+    sequences per core (each job writes the shared prefix into its own pool,
+    untimed, then times the chunk writes and the prefill of its sequences)."""
+    import numpy as np
+    nsh = wl.prefix_len // wl.BS
+    groups = _groups(wl.chunk_lens.astype(np.int64), _cpu_cores())
+    jobs = []
+    for g in groups:
+        nblk = [int(-(-int(wl.context_lens[b]) // wl.BS)) for b in g]
+        assert all(np.array_equal(wl.block_tables[b, :nsh], wl.block_tables[0, :nsh]) for b in g)
+        tables, nb = _compact(wl.block_tables[g], nblk)
+        rows = np.concatenate([np.arange(wl.cu_q_lens[b], wl.cu_q_lens[b + 1]) for b in g])
+        cu = np.zeros(len(g) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(wl.chunk_lens[g])
+        jobs.append(dict(kind="prefill", act=wl.act, cache=wl.cache, B=len(g), Hq=wl.Hq,
+                         Hkv=wl.Hkv, D=wl.D, BS=wl.BS, scale=wl.scale, k_scale=wl.k_scale,
+                         v_scale=wl.v_scale, pool_blocks=nb, prefix_len=wl.prefix_len,
+                         prefix_k=wl.prefix_k, prefix_v=wl.prefix_v,
+                         chunk_lens=wl.chunk_lens[g], chunk_k=[wl.chunk_k[b] for b in g],
+                         chunk_v=[wl.chunk_v[b] for b in g], cu_q_lens=cu,
+                         context_lens=wl.context_lens[g], block_tables=tables,
+                         query=wl.query[rows]))
+    per, got = _cpu_run(jobs, seconds)
+    reps = min(r for (_, r, _, _) in got)
+    flops = wl.flops()
+    return {
+        "value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": len(groups),
+        "kind": "oracle", "tokens_per_s": round(wl.total_q / per, 3),
+        "seconds_per_step": round(per, 3),
+        "sample": f"full workload ({wl.B} sequences x {int(wl.chunk_lens[0])} query rows): "
+                  f"chunk writer + fp64 causal prefill, sequences split over {len(groups)} "
+                  f"single-threaded processes, each repeating its step for {seconds:.0f} s "
+                  f"(at least {reps} repetitions); step time = the slowest group's",
+        "cpu_model": _cpu_info(), "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def cpu_baseline_window(wl, seconds, rows_per_core=16):
+    """The oracle's window prefill on a bounded sample: each core takes one
+    sequence's ring (populated untimed) and ``rows_per_core`` query rows
+    spread over the chunk, every head; the value is the sample's attention
+    FLOPs over the slowest core's time."""
+    import numpy as np
+    n = _cpu_cores()
+    C = int(wl.chunk_lens[0])
+    jobs, flops, nrows = [], 0, 0
+    for i in range(n):
+        b = i % wl.B
+        k = i // wl.B
+        per_seq = -(-n // wl.B)
+        rows = sorted({int((k + per_seq * r) * C // (per_seq * rows_per_core))
+                       for r in range(rows_per_core)})
+        tables, nb = _compact(wl.block_tables[b:b + 1], [wl.block_tables.shape[1]])
+        q0, q1 = int(wl.cu_q_lens[b]), int(wl.cu_q_lens[b + 1])
+        start = int(wl.context_lens[b]) - (q1 - q0)
+        for j in rows:
+            flops += 4 * wl.D * wl.Hq * min(start + j + 1, wl.window)
+        nrows += len(rows)
+        jobs.append(dict(kind="window", act=wl.act, cache=wl.cache, B=1, Hq=wl.Hq, Hkv=wl.Hkv,
+                         D=wl.D, BS=wl.BS, window=wl.window, scale=wl.scale,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale, pool_blocks=nb,
+                         hist_lens=wl.hist_lens[b:b + 1], hist_pos0=wl.hist_pos0[b:b + 1],
+                         chunk_lens=wl.chunk_lens[b:b + 1], cu_q_lens=np.array([0, q1 - q0]),
+                         context_lens=wl.context_lens[b:b + 1], block_tables=tables,
+                         query=wl.query[q0:q1], chunk_k=wl.chunk_k[q0:q1],
+                         chunk_v=wl.chunk_v[q0:q1], hist_k=[wl.hist_k[b]],
+                         hist_v=[wl.hist_v[b]], rows={(0, j) for j in rows}))
+    per, got = _cpu_run(jobs, seconds)
+    return {
+        "value": round(flops / per / 1e12, 9), "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+        "seconds_per_step": round(per, 3),
+        "sample": f"{nrows} query rows ({rows_per_core} per core, spread over the chunks of "
+                  f"all {wl.B} sequences), every head, over full rings of {wl.window} rows: "
+                  f"fp64 window attention ({flops:.3e} FLOP), {n} single-threaded processes; "
+                  f"time = the slowest core's; ring population untimed",
         "cpu_model": _cpu_info(), "host_cpus": len(os.sched_getaffinity(0)),
     }
 
@@ -385,23 +632,32 @@ def bench_prefill(wl, a, torch):
                               np.arange(wl.prefix_len, wl.prefix_len + int(wl.chunk_lens[b])),
                               wl.BS) for b in range(wl.B)])).to(dev)
     q = _act_tensor(wl.query, wl.act, torch)
-    out = torch.empty_like(q)
-    write = ops.prepare_reshape_and_cache(ck, cv, kc, vc, chunk_slots)
-    run = ops.prepare_prefill_chunk(q, torch.from_numpy(wl.cu_q_lens).to(dev), kc, vc,
-                                    torch.from_numpy(wl.block_tables).to(dev),
-                                    torch.from_numpy(wl.context_lens).to(dev),
-                                    int(wl.chunk_lens.max()), wl.scale, out)
-    for _ in range(a.warmup):
-        write()
-        run()
+    # Replicas of the pools, the queries and the output (and the chunk's K/V),
+    # so that consecutive steps touch different copies (>= 2 GB in all) and
+    # the 256 MB last-level cache cannot hold a step's working set.
+    rep_bytes = 2 * kc.numel() * 2 + 2 * q.numel() * 2 + 2 * ck.numel() * 2
+    R = a.replicas or max(1, math.ceil(2e9 / rep_bytes))
+    cu = torch.from_numpy(wl.cu_q_lens).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    writes, runs = [], []
+    for r in range(R):
+        kr, vr = (kc, vc) if r == 0 else (kc.clone(), vc.clone())
+        qr, ckr, cvr = (q, ck, cv) if r == 0 else (q.clone(), ck.clone(), cv.clone())
+        writes.append(ops.prepare_reshape_and_cache(ckr, cvr, kr, vr, chunk_slots))
+        runs.append(ops.prepare_prefill_chunk(qr, cu, kr, vr, bt, cl, int(wl.chunk_lens.max()),
+                                              wl.scale, torch.empty_like(q)))
+    for i in range(a.warmup):
+        writes[i % R]()
+        runs[i % R]()
     torch.cuda.synchronize()
     K = a.steps
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(K):
-        write()
-        run()
+        writes[i % R]()
+        runs[i % R]()
     t1.record()
     torch.cuda.synchronize()
     step_s = t0.elapsed_time(t1) / K * 1e-3
@@ -410,7 +666,7 @@ def bench_prefill(wl, a, torch):
     t3 = torch.cuda.Event(enable_timing=True)
     t2.record()
     for i in range(K):
-        run()
+        runs[i % R]()
     t3.record()
     torch.cuda.synchronize()
     pre_s = t2.elapsed_time(t3) / K * 1e-3
@@ -423,7 +679,8 @@ def bench_prefill(wl, a, torch):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "prefix_len": wl.prefix_len,
-                   "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS},
+                   "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS, "replicas": R,
+                   "step": "pa_reshape_and_cache (chunk) + pa_prefill_chunk"},
         "prefill_us": round(pre_s * 1e6, 3), "step_us": round(step_s * 1e6, 3),
         "tokens_per_s": round(wl.total_q / step_s, 1),
         "roofline": {"kernel": "pa_prefill_chunk", "bound": "mfma", "achieved": round(tf, 2),
@@ -474,31 +731,47 @@ def bench_window_prefill(wl, a, torch):
     slots = torch.from_numpy(np.concatenate(cs)).to(dev)
     # The step reads the pre-chunk ring; writing the chunk each step would
     # change what the next step reads, so the write goes to a second copy.
-    kc2, vc2 = kc.clone(), vc.clone()
-    ks2, vs2 = (ks.clone(), vs.clone()) if ks is not None else (None, None)
-    write = ops.prepare_reshape_and_cache(k, v, kc2, vc2, slots, wl.k_scale, wl.v_scale,
-                                          key_scales=ks2, value_scales=vs2)
+    # Replicas of everything a step touches (>= 2 GB in all) rotate so that
+    # the 256 MB last-level cache cannot hold a step's working set.
+    clone = lambda t: None if t is None else t.clone()  # noqa: E731
+    ring_bytes = 2 * kc.numel() * kc.element_size() + (2 * ks.numel() * 4 if ks is not None
+                                                       else 0)
+    rep_bytes = 2 * ring_bytes + 2 * q.numel() * 2 + 2 * k.numel() * 2
+    R = a.replicas or max(1, math.ceil(2e9 / rep_bytes))
+    runs, writes = [], []
+    for r in range(R):
+        if r == 0:
+            kr, vr, ksr, vsr, qr, kk, vv = kc, vc, ks, vs, q, k, v
+        else:
+            kr, vr, ksr, vsr = kc.clone(), vc.clone(), clone(ks), clone(vs)
+            qr, kk, vv = q.clone(), k.clone(), v.clone()
+        writes.append(ops.prepare_reshape_and_cache(kk, vv, kr.clone(), vr.clone(), slots,
+                                                    wl.k_scale, wl.v_scale,
+                                                    key_scales=clone(ksr),
+                                                    value_scales=clone(vsr)))
+        o = out if r == 0 else torch.empty_like(q)
+        kw = dict(k_scale=wl.k_scale, v_scale=wl.v_scale, key_scales=ksr, value_scales=vsr)
+        runs.append(lambda qr=qr, kk=kk, vv=vv, kr=kr, vr=vr, o=o, kw=kw:
+                    ops.prefill_chunk_window(qr, kk, vv, cu, kr, vr, bt, cl,
+                                             int(wl.chunk_lens.max()), wl.scale, wl.window,
+                                             out=o, **kw))
 
-    def run():
-        ops.prefill_chunk_window(q, k, v, cu, kc, vc, bt, cl, int(wl.chunk_lens.max()),
-                                 wl.scale, wl.window, out=out, **qkw)
-
-    for _ in range(a.warmup):
-        run()
-        write()
+    for i in range(a.warmup):
+        runs[i % R]()
+        writes[i % R]()
     torch.cuda.synchronize()
     K = a.steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     ev[0].record()
-    for _ in range(K):
-        run()
-        write()
+    for i in range(K):
+        runs[i % R]()
+        writes[i % R]()
     ev[1].record()
     torch.cuda.synchronize()
     step_s = ev[0].elapsed_time(ev[1]) / K * 1e-3
     ev[2].record()
-    for _ in range(K):
-        run()
+    for i in range(K):
+        runs[i % R]()
     ev[3].record()
     torch.cuda.synchronize()
     pre_s = ev[2].elapsed_time(ev[3]) / K * 1e-3
@@ -512,7 +785,8 @@ def bench_window_prefill(wl, a, torch):
         "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "window": wl.window, "history": int(wl.hist_lens[0]),
                    "chunk_len": int(wl.chunk_lens[0]), "block_size": wl.BS,
-                   "ring": wl.cache},
+                   "ring": wl.cache, "replicas": R,
+                   "step": "pa_prefill_chunk_window + ring write of the landing tokens"},
         "prefill_us": round(pre_s * 1e6, 3), "step_us": round(step_s * 1e6, 3),
         "tokens_per_s": round(wl.total_q / step_s, 1),
         "roofline": {"kernel": "pa_prefill_chunk_window", "bound": "mfma",
@@ -666,6 +940,21 @@ def calibrate_copy(gib, a, torch):
             "us_per_copy": round(s * 1e6, 2), "GBps_read_plus_write": round(2 * n / s / 1e9, 1)}
 
 
+SUB_RESULTS = (("C1", "tiny_decode"), ("C3", "fp8_decode"), ("C4", "sliding_decode"),
+               ("C5", "prefix_prefill"))
+
+
+def _sub_result(res):
+    """What another workload's line adds to the default one: its time, its
+    roofline (with the recorded traffic) and its own value."""
+    keep = ("value", "unit", "ms_per_step", "step_us", "decode_us", "prefill_us",
+            "decode_launch_us_p10_p50_p90", "tokens_per_s")
+    d = {"workload": res["config"]["workload"]}
+    d.update({k: res[k] for k in keep if k in res})
+    d["roofline"] = res["roofline"]
+    return d
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -673,6 +962,8 @@ def main():
                                    "(the path shards by sequence or KV head, but no "
                                    "multi-GPU code is built)"}))
         sys.exit(2)
+    if a.cpu_seconds > 0:
+        _start_cpu_pool()           # before anything touches the GPU
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -687,12 +978,27 @@ def main():
     wl = _workload(a.config)
     if a.config == "prefix_prefill":
         res = bench_prefill(wl, a, torch)
+        if a.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_prefill(wl, a.cpu_seconds)
     elif a.config.startswith("sliding_prefill"):
         res = bench_window_prefill(wl, a, torch)
+        if a.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_window(wl, a.cpu_seconds)
     elif a.config == "cow_copy":
         res = bench_copy_blocks(wl, a, torch)
     else:
         res, (wl, kv_bytes) = bench_decode(wl, a, torch)
+        if a.config == "mistral_decode" and not a.no_sub_results and not a.partition_tokens:
+            subs = {}
+            for tag, name in SUB_RESULTS:
+                torch.cuda.empty_cache()
+                w = _workload(name)
+                r = bench_prefill(w, a, torch) if name == "prefix_prefill" else \
+                    bench_decode(w, a, torch)[0]
+                subs[tag] = _sub_result(r)
+                del w, r
+            torch.cuda.empty_cache()
+            res["sub_results"] = subs
         if a.cpu_seconds > 0:
             res["cpu_baseline"] = cpu_baseline_decode(wl, kv_bytes, a.cpu_seconds)
         from paged_kv_cache_175_amd import pool
