@@ -41,10 +41,13 @@
  *    [num_kv_heads].  Inside a page (t = row 0..block_size-1, d = 0..D-1),
  *    not row-major [BS][D] but tiled, as this library lays it out:
  *      key page   [D/8][block_size][8]  element (t, d) at ((d/8)*BS + t)*8 + d%8
- *      value page [D][block_size]       element (t, d) at d*BS + t
+ *      value page [BS/8][D][8]          element (t, d) at ((t/8)*D + d)*8 + t%8
  *    (so the key pool is [NB][Hkv][D/8][BS][8] and the value pool
- *    [NB][Hkv][D][BS]).  Both layouts make the attention kernels' matrix-core
- *    operands single 16-byte loads.  Activations are row-major.
+ *    [NB][Hkv][BS/8][D][8]).  Both layouts make the attention kernels'
+ *    matrix-core operands single 16-byte loads (8 dims of one key; 8 keys
+ *    of one dim); the value page groups its keys by 8 so that one new row
+ *    lands in D 16-byte runs rather than D scattered elements.
+ *    Activations are row-major.
  *  - Identity map ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build:
  *    identity block maps are served as one contiguous K/V view).  Every
  *    attention entry point accepts block_tables == NULL: logical block j of

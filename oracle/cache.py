@@ -9,8 +9,11 @@ exactly those bytes so that writes can be compared one for one:
 
 * key pool   ``[num_blocks][num_kv_heads][head_dim/8][block_size][8]``:
   row t, dimension d of a page sits at ``((d // 8) * block_size + t) * 8 + d % 8``;
-* value pool ``[num_blocks][num_kv_heads][head_dim][block_size]``: row t,
-  dimension d sits at ``d * block_size + t`` (the page is stored transposed).
+* value pool ``[num_blocks][num_kv_heads][block_size/8][head_dim][8]``: the
+  page's rows in groups of 8; row t, dimension d sits at
+  ``((t // 8) * head_dim + d) * 8 + t % 8``.  (A block size that is not a
+  multiple of 8, which only the oracle's own small tests use, makes one
+  group of ``block_size`` rows: ``[1][head_dim][block_size]``.)
 
 The helpers :func:`put_row` / :func:`get_row` are the only places that know
 this layout; everything else works with logical rows ``[num_kv_heads, D]``.
@@ -74,9 +77,16 @@ def empty_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: i
     if head_dim % 8:
         raise ValueError("head_dim must be a multiple of 8")
     dt = storage_dtype(fmt)
+    tg = value_group(block_size)
     k = np.full((num_blocks, num_kv_heads, head_dim // 8, block_size, 8), fill, dtype=dt)
-    v = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=dt)
+    v = np.full((num_blocks, num_kv_heads, block_size // tg, head_dim, tg), fill, dtype=dt)
     return k, v
+
+
+def value_group(block_size: int) -> int:
+    """Rows per group of a value page: 8, or the whole block when the
+    block size is not a multiple of 8."""
+    return 8 if block_size % 8 == 0 else block_size
 
 
 def pool_geometry(key_cache):
@@ -88,15 +98,17 @@ def pool_geometry(key_cache):
 def put_row(key_cache, value_cache, blk: int, off: int, k_row, v_row) -> None:
     """Store one token's K and V rows ``[Hkv, D]`` at (block, row)."""
     hkv, d8 = key_cache.shape[1], key_cache.shape[2]
+    tg = value_cache.shape[4]
     key_cache[blk, :, :, off, :] = np.asarray(k_row).reshape(hkv, d8, 8)
-    value_cache[blk, :, :, off] = np.asarray(v_row)
+    value_cache[blk, :, off // tg, :, off % tg] = np.asarray(v_row)
 
 
 def get_row(key_cache, value_cache, blk: int, off: int):
     """One token's stored K and V rows ``[Hkv, D]`` at (block, row)."""
     hkv, d8 = key_cache.shape[1], key_cache.shape[2]
+    tg = value_cache.shape[4]
     k = key_cache[blk, :, :, off, :].reshape(hkv, d8 * 8)
-    v = value_cache[blk, :, :, off]
+    v = value_cache[blk, :, off // tg, :, off % tg]
     return k, v
 
 

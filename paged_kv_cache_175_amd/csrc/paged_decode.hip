@@ -33,8 +33,8 @@
 //     ballot) is the max taken across the four lanes of a head and O
 //     rescaled, so a page normally needs no cross-lane reduction at all.
 //   * O^T += V^T P^T: the eight probabilities of a lane are exactly its B
-//     operand; the A operands are single loads from the transposed V page
-//     [D][32] (dimension 16n + col, tokens 8q .. 8q + 7).  One more MFMA
+//     operand; the A operands are single loads from the V page
+//     [4][D][8] (dimension 16n + col, tokens 8q .. 8q + 7).  One more MFMA
 //     against an all-ones A tile accumulates the running sum l.
 //
 // INT8 cache (per-token/head codes, "libmir-metal 0.2.0,
@@ -264,10 +264,10 @@ __device__ __forceinline__ void load_page(PageRegs<D, CF>& Pg, const uint8_t* ke
   // 2 col + 1 (bytes); V operand of output tile n: dim 16n + col, tokens
   // 8 q4 .. 8 q4 + 7.
   const int k_lane = ((q4 * kPage + (kContig ? col : 2 * col)) * 8) * EB;
-  const int v_lane = (col * kPage + 8 * q4) * EB;
+  const int v_lane = (q4 * D + col) * 8 * EB;
   constexpr int K_J = 4 * kPage * 8 * EB;    // byte step between k-steps
   constexpr int K_KT = 16 * 8 * EB;          // byte step between key tiles (16-bit)
-  constexpr int V_N = 16 * kPage * EB;       // byte step between output tiles
+  constexpr int V_N = 16 * 8 * EB;           // byte step between output tiles
   constexpr uint32_t PAGE_BYTES = (uint32_t)kPage * D * EB;
   const size_t base = (size_t)page_id * PAGE_BYTES;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(key_cache + base, live ? PAGE_BYTES : 0u);
@@ -548,18 +548,18 @@ __device__ __forceinline__ uint32_t encode_elem(uint16_t x, float scale) {
 // Store element d of cache row `row` of the page at element offset `page`
 // (non-temporal: nothing in the launch reads it back from memory; measured
 // 1.3 us faster on the Mistral batch).
-template <int CF>
+template <int D, int CF>
 __device__ __forceinline__ void store_row_elem(uint8_t* key_cache, uint8_t* value_cache,
                                                size_t page, int row, int d, uint32_t kq,
                                                uint32_t vq) {
   if constexpr (byte_fmt(CF)) {
     __builtin_nontemporal_store(static_cast<uint8_t>(kq), key_cache + page + k_page_off(row, d));
-    __builtin_nontemporal_store(static_cast<uint8_t>(vq), value_cache + page + v_page_off(row, d));
+    __builtin_nontemporal_store(static_cast<uint8_t>(vq), value_cache + page + v_page_off(row, d, D));
   } else {
     __builtin_nontemporal_store(static_cast<uint16_t>(kq),
                                 reinterpret_cast<uint16_t*>(key_cache) + page + k_page_off(row, d));
     __builtin_nontemporal_store(static_cast<uint16_t>(vq),
-                                reinterpret_cast<uint16_t*>(value_cache) + page + v_page_off(row, d));
+                                reinterpret_cast<uint16_t*>(value_cache) + page + v_page_off(row, d, D));
   }
 }
 
@@ -955,7 +955,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       for (int u = 0; u < DPL; ++u) {
         const int d = ln + 64 * u;
         if (d < D)
-          store_row_elem<CF>(key_cache, value_cache, pid * kPage * D, row, d, row_lds[jj][0][d],
+          store_row_elem<D, CF>(key_cache, value_cache, pid * kPage * D, row, d, row_lds[jj][0][d],
                              row_lds[jj][1][d]);
       }
       if constexpr (CF == FMT_I8) {
@@ -1311,7 +1311,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (d < D) {
           const uint32_t kq = encode_elem<CF, AF>(krow[u], kes);
           const uint32_t vq = encode_elem<CF, AF>(vrow[u], ves);
-          store_row_elem<CF>(key_cache, value_cache, page, row, d, kq, vq);
+          store_row_elem<D, CF>(key_cache, value_cache, page, row, d, kq, vq);
           newk_lds[wave][d] = static_cast<uint16_t>(kq);
           newv_lds[wave][d] = static_cast<uint16_t>(vq);
         }

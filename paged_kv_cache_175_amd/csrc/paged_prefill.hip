@@ -37,9 +37,9 @@
 //                  keys in natural order;
 //   O^T += V^T P^T (A operand = V^T: eight consecutive tokens of one head
 //                  dimension, one 16-byte LDS read).
-// LDS pages keep the cache's chunk layout (K [D/8][32][8], V [D][32]) with the
-// 16-byte chunks of each row XOR-swizzled so that both operand reads are free
-// of bank conflicts.
+// LDS pages hold K as [D/8][32] chunks of 8 elements and V as [D][4] chunks
+// (dimension, 8-token group) with the 16-byte chunks of each row
+// XOR-swizzled so that both operand reads are free of bank conflicts.
 // The running sum l of each query comes out of the same MFMAs: one more
 // O^T tile whose V^T rows are all ones gives sum_k P[k][q] in every row, so
 // l is accumulated from the rounded P that also weights V, and is rescaled
@@ -267,8 +267,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int s = u * 64 + lane;             // K slot
       dma_src[i] = k_slot(s >> 5, s & 31) * 16;
     } else {
-      const int s = (u - D / 16) * 64 + lane;  // V slot
-      dma_src[i] = v_slot(s >> 2, s & 3) * 16;
+      // V slot s = (d, x) holds the chunk of token group x ^ swizzle(d),
+      // which the cache keeps at chunk (group * D + d).
+      const int s = (u - D / 16) * 64 + lane;
+      const int d = s >> 2;
+      const int tq = (s & 3) ^ ((d >> 1) & 3);
+      dma_src[i] = (tq * D + d) * 16;
     }
   }
   auto dma_page = [&](int phys, int buf) {
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   // Register path (E4M3, INT8): chunk c of the K page is (d / 8, t) =
-  // (c / 32, c % 32) and chunk c of the V page is (d, t / 8) = (c / 4, c % 4).
+  // (c / 32, c % 32) and chunk c of the V page is (d, t / 8) = (c % D, c / D).
   // Threads 0..31 also carry the page's K row scales, 32..63 its V scales.
   u32x2 kreg[kDma ? 1 : ST], vreg[kDma ? 1 : ST];
   float sreg = 0.f;
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int c = tid + i * kThreads;
       if (NCH % kThreads == 0 || c < NCH) {
         *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c >> 5, c & 31) * 8]) = widen(kreg[i]);
-        *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(c >> 2, c & 3) * 8]) = widen(vreg[i]);
+        *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(c % D, c / D) * 8]) = widen(vreg[i]);
       }
     }
     if constexpr (kI8) {
@@ -404,14 +408,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             u32x2 vq = u32x2{0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              vq[e >> 2] |= (uint32_t)value_cache[page + (size_t)(8 * c + e) * BS + r]
+              vq[e >> 2] |= (uint32_t)value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 +
+                                                  (r & 7)]
                             << (8 * (e & 3));
             vw = widen(vq);
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              vw[e] = (uint32_t)vc16[page + (size_t)(8 * c + 2 * e) * BS + r] |
-                      ((uint32_t)vc16[page + (size_t)(8 * c + 2 * e + 1) * BS + r] << 16);
+            for (int e = 0; e < 4; ++e) {
+              const size_t at = page + ((size_t)(r >> 3) * D + 8 * c + 2 * e) * 8 + (r & 7);
+              vw[e] = (uint32_t)vc16[at] | ((uint32_t)vc16[at + 8] << 16);
+            }
           }
         } else if (pos >= first_pos && pos < ctx) {
           const size_t row = ((size_t)(q_begin + pos - first_pos) * Hkv + g) * D + 8 * c;
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
   // Native: chunk `item` of the K page is (d / 8, t) = (item / 32, item % 32)
-  // and of the V page (d, t / 8) = (item / 4, item % 4).  Row by row: item
+  // and of the V page (d, t / 8) = (item % D, item / D).  Row by row: item
   // (t, d / 8) = (item % 32, item / 32) for both, V transposed here.
   auto store_win = [&](int buf) {
 #pragma unroll
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int c = item / BS;
         *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c, r) * 8]) = wk[i];
         if (win_native) {
-          *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(item >> 2, item & 3) * 8]) = wv[i];
+          *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(item % D, item / D) * 8]) = wv[i];
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {

@@ -14,8 +14,8 @@
 // their K and V rows with fully coalesced 16-byte loads into LDS, then writes
 // them out token-fastest: consecutive lanes handle consecutive tokens, so
 // when the tokens fill consecutive rows of a page (a prefill chunk) the K
-// chunks of the [D/8][32][8] page and the V elements of the transposed
-// [D][32] page leave as contiguous runs instead of scattered 2-byte stores.
+// chunks of the [D/8][32][8] page and the V elements of the [4][D][8] page
+// (8-token groups) leave as contiguous runs instead of scattered stores.
 // Decode-time writes (one token per sequence) take the same path.
 #include "common.hpp"
 #include "launch.hpp"
@@ -129,15 +129,16 @@ __global__ __launch_bounds__(kThreads) void cache_write(
       *reinterpret_cast<u32x4*>(key_cache + dst) = kw;
     }
   }
-  // V: token-fastest single elements of the transposed page.
+  // V: single elements, token-fastest within each group of 8 tokens, then
+  // dimension, then group (the page's own order).
   for (int i = tid; i < kGroup * D; i += kThreads) {
-    const int n = i % kGroup;
-    const int d = i / kGroup;
+    const int n = (i / (8 * D)) * 8 + (i & 7);
+    const int d = (i >> 3) % D;
     const int slot = slot_s[n];
     if (slot < 0) continue;
     const int blk = slot / kPage;
     const int off = slot - blk * kPage;
-    const size_t dst = ((size_t)blk * Hkv + h) * page_elems + v_page_off(off, d);
+    const size_t dst = ((size_t)blk * Hkv + h) * page_elems + v_page_off(off, d, D);
     const uint16_t x = v_s[n * ROW + d];
     if constexpr (CF == FMT_E4M3) {
       value_cache[dst] = static_cast<uint8_t>(e4m3_encode(lo16_to_f32<AF>(x), v_scale));

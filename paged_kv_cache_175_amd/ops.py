@@ -94,13 +94,13 @@ def cache_dtype_name(cache: torch.Tensor) -> str:
 def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 32):
     """Shapes of the key and value pools.
 
-    Key pages are ``[head_dim/8][block_size][8]`` and value pages are stored
-    transposed, ``[head_dim][block_size]`` (the layout of include/pa.h).
+    Key pages are ``[head_dim/8][block_size][8]`` and value pages
+    ``[block_size/8][head_dim][8]`` (the layout of include/pa.h).
     """
-    if head_dim % 8:
-        raise ValueError("head_dim must be a multiple of 8")
+    if head_dim % 8 or block_size % 8:
+        raise ValueError("head_dim and block_size must be multiples of 8")
     return ((num_blocks, num_kv_heads, head_dim // 8, block_size, 8),
-            (num_blocks, num_kv_heads, head_dim, block_size))
+            (num_blocks, num_kv_heads, block_size // 8, head_dim, 8))
 
 
 def _free_bytes(device) -> Optional[int]:
@@ -167,10 +167,12 @@ def _scales(cache_code, key_scales, value_scales, NB, Hkv, BS):
 
 def _pool_geometry(key_cache: torch.Tensor, value_cache: torch.Tensor):
     """(NB, Hkv, BS, D) of a pair of pools; raises on malformed shapes."""
-    if key_cache.dim() != 5 or key_cache.shape[4] != 8 or value_cache.dim() != 4:
-        raise ValueError("key_cache must be [NB, Hkv, D/8, BS, 8] and value_cache [NB, Hkv, D, BS]")
+    if key_cache.dim() != 5 or key_cache.shape[4] != 8 or value_cache.dim() != 5:
+        raise ValueError("key_cache must be [NB, Hkv, D/8, BS, 8] and value_cache "
+                         "[NB, Hkv, BS/8, D, 8]")
     NB, Hkv, D8, BS, _ = key_cache.shape
-    if tuple(value_cache.shape) != (NB, Hkv, D8 * 8, BS) or value_cache.dtype != key_cache.dtype:
+    if (BS % 8 or tuple(value_cache.shape) != (NB, Hkv, BS // 8, D8 * 8, 8)
+            or value_cache.dtype != key_cache.dtype):
         raise ValueError("value_cache does not match key_cache")
     return NB, Hkv, BS, D8 * 8
 

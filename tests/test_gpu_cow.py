@@ -58,8 +58,9 @@ def test_fork_append_decode_scenario():
     order = rng.permutation(NB)
     g_alloc = pool.BlockAllocator(NB, order=order)
     o_alloc = pool.BlockAllocator(NB, order=order)
-    gk = torch.full((NB, Hkv, D // 8, BS, 8), 0x7FC0, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-    gv = torch.full((NB, Hkv, D, BS), 0x7FC0, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    kshape, vshape = ops.pool_shapes(NB, Hkv, D, BS)
+    gk = torch.full(kshape, 0x7FC0, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    gv = torch.full(vshape, 0x7FC0, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     okc, ovc = o_cache.empty_pools(NB, Hkv, BS, D, act, 0x7FC0)
     gseqs, oseqs = [pool.SequenceBlocks(g_alloc, BS)], [pool.SequenceBlocks(o_alloc, BS)]
     copies_seen = 0

@@ -192,9 +192,9 @@ def test_e4m3_decode_all_codes():
     kc = torch.zeros(ks, dtype=torch.uint8, device="cuda")
     vc = torch.zeros(vs, dtype=torch.uint8, device="cuda")
     codes = np.arange(256, dtype=np.uint8).reshape(2, D)
-    # Token 0 of blocks 0 and 1 (value pages are [D][BS]).
-    vc[0, 0, :, 0] = torch.from_numpy(codes[0]).cuda()
-    vc[1, 0, :, 0] = torch.from_numpy(codes[1]).cuda()
+    # Token 0 of blocks 0 and 1 (value pages are [BS/8][D][8]).
+    vc[0, 0, 0, :, 0] = torch.from_numpy(codes[0]).cuda()
+    vc[1, 0, 0, :, 0] = torch.from_numpy(codes[1]).cuda()
     q = torch.randn(2, 1, D, device="cuda").to(torch.bfloat16)
     bt = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
     cl = torch.tensor([1, 1], dtype=torch.int32, device="cuda")

@@ -194,9 +194,10 @@ def test_p6_split_merge_equals_single_pass(cuts):
 
 
 @pytest.mark.parametrize("cache_fmt", ["bf16", "e4m3"])
-def test_p7_writer_touches_only_written_slots(cache_fmt):
+@pytest.mark.parametrize("BS", [4, 16])
+def test_p7_writer_touches_only_written_slots(cache_fmt, BS):
     rng = np.random.default_rng(7)
-    act, Hkv, D, BS, NB, T = "bf16", 3, 8, 4, 6, 9
+    act, Hkv, D, NB, T = "bf16", 3, 8, 6, 9
     kc, vc = cache.empty_pools(NB, Hkv, BS, D, cache_fmt, NAN_BITS[cache_fmt])
     slots = rng.permutation(NB * BS)[:T].astype(np.int32)
     slots[2] = -1
@@ -228,7 +229,9 @@ def test_p7_writer_touches_only_written_slots(cache_fmt):
     kr, vr = cache.get_row(kc, vc, blk, off)
     for d in range(D):
         assert flat_k[((d // 8) * BS + off) * 8 + d % 8] == kr[1, d]
-        assert flat_v[d * BS + off] == vr[1, d]
+        # Value rows in groups of 8 (one group when BS is not a multiple of 8).
+        tg = 8 if BS % 8 == 0 else BS
+        assert flat_v[((off // tg) * D + d) * tg + off % tg] == vr[1, d]
 
 
 # --- P9: brute force against scalar loops that never see a block table -----
