@@ -310,7 +310,8 @@ __device__ __forceinline__ void compute_page(PageRegs<D, CF>& Pg, float& m_run,
                                              typename Mfma<AF>::vec ones, int base, int L,
                                              bool patch, int row_new, const uint16_t* newk,
                                              const uint16_t* newv, float new_ks, float new_vs,
-                                             float qk_scale_log2, int lane) {
+                                             uint8_t* kpage, uint8_t* vpage, float qk_scale_log2,
+                                             int lane) {
   constexpr int KSTEPS = D / 32;
   constexpr int NT = D / 16;
   constexpr bool kContig = !byte_fmt(CF);
@@ -354,9 +355,49 @@ __device__ __forceinline__ void compute_page(PageRegs<D, CF>& Pg, float& m_run,
         }
       }
     }
+    if (kpage != nullptr) {
+      // With kpage / vpage the patched row also goes to the cache here, as
+      // whole 128-byte lines: the rest of each line is written back as it
+      // was loaded.  A K line is one 8-element chunk of 8 consecutive keys
+      // (16-bit) or of 16 (bytes); 16 consecutive dims of a V row group are
+      // one line of bytes, two of 16-bit elements.  Full-line writes need no
+      // read-modify-write below the cache, which the row's scattered
+      // elements did.
+      if constexpr (byte_fmt(CF)) {
+        if ((col >> 3) == (row_new >> 4)) {
+#pragma unroll
+          for (int j = 0; j < KSTEPS; ++j)
+            __builtin_nontemporal_store(
+                Pg.k[j], reinterpret_cast<u32x4*>(kpage + (size_t)(((q4 + 4 * j) * kPage + 2 * col) * 8)));
+        }
+      } else {
+        if ((col >> 3) == ((row_new & 15) >> 3)) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if (kt == kt_new) {
+#pragma unroll
+              for (int j = 0; j < KSTEPS; ++j)
+                __builtin_nontemporal_store(
+                    Pg.k[kt][j].w,
+                    reinterpret_cast<u32x4*>(
+                        kpage + (size_t)(((q4 + 4 * j) * kPage + 16 * kt + col) * 16)));
+            }
+          }
+        }
+      }
+    }
     if (q4 == (row_new >> 3)) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) set_elem<CF>(Pg.v[n].w, row_new & 7, newv[16 * n + col]);
+      if (vpage != nullptr) {
+        constexpr int EB = byte_fmt(CF) ? 1 : 2;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          auto* dst = reinterpret_cast<decltype(Pg.v[n].w)*>(
+              vpage + (size_t)((q4 * D + 16 * n + col) * 8 * EB));
+          __builtin_nontemporal_store(Pg.v[n].w, dst);
+        }
+      }
       if constexpr (CF == FMT_I8) {
         // The row's scales, as the patched codes were encoded with.
 #pragma unroll
@@ -945,29 +986,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int base = (help ? help_lo + i - n0 : own_lo + i) * kPage;
     const bool patch = i == (help ? i1 : i0);
     const int row = (help ? r1 : r0) % kPage;
-    if (patch) {
-      // The appended row goes into its cache row here (the values patched
-      // in below).
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const size_t pid = pid_of(i);
-#pragma unroll
-      for (int u = 0; u < DPL; ++u) {
-        const int d = ln + 64 * u;
-        if (d < D)
-          store_row_elem<D, CF>(key_cache, value_cache, pid * kPage * D, row, d, row_lds[jj][0][d],
-                             row_lds[jj][1][d]);
-      }
-      if constexpr (CF == FMT_I8) {
-        if (ln == 0) {
-          key_scales[pid * kPage + row] = row_scale[jj][0];
-          value_scales[pid * kPage + row] = row_scale[jj][1];
-        }
+    // The page that holds the appended row: compute_page patches the row
+    // into the loaded page and stores it to the cache (INT8: its scales
+    // here).
+    constexpr int EB = byte_fmt(CF) ? 1 : 2;
+    const size_t pid = patch ? (size_t)pid_of(i) : 0;
+    if constexpr (CF == FMT_I8) {
+      if (patch && lane == 0) {
+        key_scales[pid * kPage + row] = row_scale[jj][0];
+        value_scales[pid * kPage + row] = row_scale[jj][1];
       }
     }
+    const size_t pbytes = pid * kPage * D * EB;
     compute_page<D, G, CF, AF>(Pg, m_run, o_acc, qb, ones, base, help ? Lh : L, patch, row,
                                row_lds[jj][0], row_lds[jj][1], row_scale[jj][0],
-                               row_scale[jj][1], qk_scale_log2, lane);
+                               row_scale[jj][1], patch ? key_cache + pbytes : nullptr,
+                               patch ? value_cache + pbytes : nullptr, qk_scale_log2, lane);
   };
 
   // Two register buffers: the current page is computed while the next
@@ -1360,8 +1394,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int j = rs + k - cur_off;
         compute_page<D, G, CF, AF>(Pg, m_run, o_acc, qb, ones, j * kPage, cur_L,
                                    cur_new >= 0 && j == cur_new / kPage, cur_new % kPage,
-                                   newk_lds[cur], newv_lds[cur], cur_ks, cur_vs, qk_scale_log2,
-                                   lane);
+                                   newk_lds[cur], newv_lds[cur], cur_ks, cur_vs, nullptr,
+                                   nullptr, qk_scale_log2, lane);
       };
       // Two register buffers: the current page is computed while the next
       // claimed one loads.
