@@ -775,12 +775,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int nslots = paired ? 2 : S;
 
   // --- first round: loads that need neither a length nor the plan --------
-  // With one split per sequence the own job's pages are wave + W k whatever
-  // the length, so its table entries go out with the length (lane k: entry
-  // wave + W k, clamped to the row; entries past the job are never used).
+  // The own job's table entries go out with the length, for the split's
+  // range at the longest length the plan allows (lane k: entry lo_spec +
+  // wave + W k, clamped to the row): with one split per sequence that range
+  // starts at page 0 whatever the length; with several it is the split's
+  // range whenever the sequence is that long (a full ring, the common case
+  // of a sliding-window batch).  Otherwise the entries are loaded again
+  // after the plan; entries past the job are never used.
+  const int p_cap = (int)((len_cap + kPage - 1) / kPage);
+  const int lo_spec = S == 1 ? 0 : (int)((long long)s * p_cap / S);
   int bt_pre = 0;
-  if (S == 1 && block_tables != nullptr)
-    bt_pre = block_tables[(size_t)b * MBPS + min(wave + W * lane, MBPS - 1)];
+  if (block_tables != nullptr)
+    bt_pre = block_tables[(size_t)b * MBPS + min(lo_spec + wave + W * lane, MBPS - 1)];
   vec qb[KSTEPS];
   q_operand<D, G, AF>(qb, query + ((size_t)b * Hq + g * G) * D, lane);
   int lens_lane = 0;                      // pair mode: the batch's lengths (B <= 64)
@@ -852,14 +858,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int N = n0 + n1;
 
   // Table entries: thread (wave, lane) holds index wave + W lane of each
-  // job.  With one split per sequence the own job's came in the first round.
+  // job (the own job's from the first round when its range is the one
+  // guessed there).
   const int ti = wave + W * lane;
   uint32_t own_pid = 0, help_pid = 0;
   if (ti < n0) {
     const int pg = own_lo + ti;
-    own_pid = (uint32_t)(S == 1 ? (block_tables ? bt_pre : b * MBPS + pg)
-                                : (block_tables ? block_tables[(size_t)b * MBPS + pg]
-                                                : b * MBPS + pg)) * Hkv + g;
+    own_pid = (uint32_t)(block_tables ? (own_lo == lo_spec ? bt_pre
+                                                           : block_tables[(size_t)b * MBPS + pg])
+                                      : b * MBPS + pg) * Hkv + g;
   }
   if (NJ > 1 && ti < n1) {
     const int pg = help_lo + ti;
