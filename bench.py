@@ -63,7 +63,7 @@ def _args():
 # Sources whose change alters a kernel's memory traffic: the kernel file plus
 # the shared device helpers and the host planner that picks its grid.
 _KERNEL_SOURCES = {
-    "decode_": ("paged_decode.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
+    "decode_": ("paged_decode.hip", "common.hpp", "launch.hpp", "pa_api.cpp", "plan.hpp"),
     "prefill_": ("paged_prefill.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
     "copy_": ("copy_blocks.hip", "common.hpp", "launch.hpp", "pa_api.cpp"),
 }
@@ -137,6 +137,30 @@ def _cpu_info():
 # --------------------------------------------------------------------------- decode
 
 
+def _lib_code(name):
+    from paged_kv_cache_175_amd import _lib
+    return getattr(_lib, name)
+
+
+def _decode_plan_name(wl, max_len, partition_tokens, ws_bytes):
+    """Which decode kernel and plan the library picks (from the size of the
+    workspace it asks for)."""
+    from paged_kv_cache_175_amd import ops
+    if partition_tokens:
+        return "decode_split, forced splits"
+    if ws_bytes == 0:
+        return "decode_split, one workgroup per sequence and KV head"
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    rows = wl.B * wl.Hq * 2
+    pair = (rnd(max(wl.B * wl.Hkv, ops.MIN_COUNTERS) * 4) + 2 * rnd(rows * 4)
+            + rnd(rows * wl.D * 4))
+    if ws_bytes == pair and wl.B <= 64:
+        return "decode_split, pair mode"
+    if wl.cache in ("e4m3", "int8") and max_len >= 1024:
+        return "decode_balanced: equal page ranges of the batch"
+    return "decode_split, split sequences"
+
+
 def bench_decode(wl, a, torch):
     import numpy as np
     from paged_kv_cache_175_amd import ops, pool
@@ -186,6 +210,10 @@ def bench_decode(wl, a, torch):
                                       a.partition_tokens)
     ws = ops.alloc_workspace(need, dev)
     out = torch.empty_like(q0)
+    fmt = {"e4m3": _lib_code("PA_F8E4M3"), "int8": _lib_code("PA_I8"),
+           "f16": _lib_code("PA_F16")}.get(wl.cache, _lib_code("PA_BF16"))
+    need_fmt = ops.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, max_len, wl.window,
+                                          a.partition_tokens, fmt)
 
     # One step: store the new tokens and attend.  Default: the fused
     # pa_decode_append (pa_decode_append_i8 for an INT8 cache; one launch);
@@ -295,10 +323,8 @@ def bench_decode(wl, a, torch):
         "other_bytes_per_step": write_bytes + qo_bytes,
         "roofline": {
             "kernel": ("pa_decode" if separate else "pa_decode_append")
-                      + (" (decode_balanced: equal page ranges of the batch"
-                         if wl.cache in ("e4m3", "int8") and max_len >= 1024 and wl.B <= 1024
-                         and a.partition_tokens == 0 else " (decode_split")
-                      + "; split sequences merge inside the launch)",
+                      + f" ({_decode_plan_name(wl, max_len, a.partition_tokens, need_fmt)}; "
+                        "split sequences merge inside the launch)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(wl.name, "decode_"),

@@ -79,6 +79,8 @@ constexpr int BS = 32;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
+// Pages in flight per workgroup on the LDS-direct path (16-bit caches).
+constexpr int kLookahead = 2;
 constexpr float LOG2E_P = 1.4426950408889634f;
 // Scores (in log2 units) may exceed the running maximum by this much before
 // the maximum is raised.
@@ -108,6 +110,22 @@ struct Vec4<FMT_F16> {
 // functions map a slot back to its cache chunk.
 __device__ __forceinline__ int k_slot(int dc, int t) { return dc * BS + (t ^ (((t >> 3) & 1) << 2)); }
 __device__ __forceinline__ int v_slot(int d, int tq) { return d * 4 + (tq ^ ((d >> 1) & 3)); }
+
+// Wait until at most `later` pages' LDS-direct loads (U per page and wave)
+// are still in flight: the count must be an immediate, so the few possible
+// values are spelled out.
+template <int LA, int U>
+__device__ __forceinline__ void wait_pages(int later) {
+  if (LA > 3 && later >= 3) {
+    wait_vmcnt<3 * U>();
+  } else if (LA > 2 && later == 2) {
+    wait_vmcnt<2 * U>();
+  } else if (later == 1) {
+    wait_vmcnt<U>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 
 // Workgroup barrier that does not wait for outstanding global loads (a
 // __syncthreads would drain the LDS-direct loads still in flight for later
@@ -143,7 +161,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // prefill, D = 128, 2 tiles, 744 -> 779 TFLOP/s), else P first (D >= 96
   // with 3 or more tiles of a 16-bit or INT8 cache spilled tile-major).
   constexpr bool kTileMajor = D <= 64 || NQ <= 2 || CF == FMT_E4M3;
-  constexpr int NBUF = kDma ? 3 : 2;
+  // LDS-direct staging keeps LA pages in flight (LA + 1 buffers; the page a
+  // wave computes is the oldest).
+  constexpr int LA = kDma ? kLookahead : 1;
+  constexpr int NBUF = kDma ? LA + 1 : 2;
   constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
   constexpr int NCH = PAGE / 8;           // 8-element chunks per page (K or V)
   constexpr int RW = 16 * NQ * kWaves;    // rows per workgroup
@@ -463,13 +484,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     store_win(0);
     __syncthreads();
   } else if constexpr (kDma) {
-    dma_page(phys_of(0), 0);
-    if (npages > 1) {
-      dma_page(phys_of(1), 1);
-      wait_vmcnt<UPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      if (i < npages) dma_page(phys_of(i), i);
+    wait_pages<LA, UPW>(min(LA, npages) - 1);   // page 0 has landed
     lds_barrier();
   } else {
     load_regs(phys_of(0));
@@ -483,7 +501,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (WIN) {
       if (p + 1 < npages) load_win(base + BS);
     } else if constexpr (kDma) {
-      if (p + 2 < npages) dma_page(phys_of(p + 2), cur == 0 ? 2 : cur - 1);
+      // Into the buffer of page p - 1, which every wave has finished.
+      if (p + LA < npages) dma_page(phys_of(p + LA), cur == 0 ? NBUF - 1 : cur - 1);
     } else {
       if (p + 1 < npages) load_regs(phys_of(p + 1));
     }
@@ -657,14 +676,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if constexpr (kDma) {
-      // This wave's share of page p + 1 has landed (page p + 2 may still be
-      // in flight); the barrier publishes every wave's share and retires
-      // buffer `cur` for reuse.
-      if (p + 2 < npages) {
-        wait_vmcnt<UPW>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      // This wave's share of page p + 1 has landed (the later pages may
+      // still be in flight); the barrier publishes every wave's share and
+      // retires buffer `cur` for reuse.
+      wait_pages<LA, UPW>(max(0, min(LA - 1, npages - 2 - p)));
       lds_barrier();
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     } else {

@@ -52,15 +52,18 @@ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // partition_tokens > 0 forces S = ceil(len / partition_tokens).
 //
 // Balanced mode (decode_balanced), for E4M3 and INT8 caches from
-// kMinSplitContext tokens on (partition_tokens == 0): the batch's pages are
-// cut into equal ranges, one per workgroup (W = 8, a multiple of the CU
-// count of workgroups), whatever the mix of context lengths; S is then the
-// number of partial slots per (sequence, KV head).  Measured on the FP8
+// kMinSplitContext tokens on (partition_tokens == 0) where the grid plan is
+// not pair mode: the batch's pages are cut into equal ranges, one per
+// workgroup (W = 8, a multiple of the CU count of workgroups), whatever the
+// mix of context lengths; S is then the number of partial slots per
+// (sequence, KV head).  Against the grid plan without pairs, on the FP8
 // decode shape (B = 64, 1024..8192 tokens): INT8 131 -> 118 us, E4M3 118.5
-// -> 117.4 us.  With 16-bit caches the grid plan stayed faster (Mistral
-// batch 57.6 vs 59.9 us; rolling batch 27.6 vs 29.8 us): its prefix scan and
-// the merges of the sequences cut between ranges cost more than the balance
-// gains there.
+// -> 117.4 us; pair mode beats both there (E4M3 107.7 us, INT8 104.3 us),
+// so a byte cache takes balanced mode only where pairs do not apply (more
+// than kMaxPairB sequences, or several splits per sequence).  With 16-bit
+// caches the grid plan stayed faster (Mistral batch 57.6 vs 59.9 us;
+// rolling batch 27.6 vs 29.8 us): its prefix scan and the merges of the
+// sequences cut between ranges cost more than the balance gains there.
 struct Plan {
   int S;          // grid mode: splits per sequence; balanced: partial slots per item
   int W;
@@ -105,19 +108,7 @@ inline bool make_plan(int B, int Hkv, int G, int D, int max_len, int window,
   if (partition_tokens < 0 || partition_tokens % kBlock != 0) return false;
   const long long pages = (L + kBlock - 1) / kBlock;
   const long long pairs = (long long)B * Hkv;
-  p->pair = false;
-  if (byte_cache && partition_tokens == 0 && L >= kMinSplitContext && B <= kMaxBalancedB &&
-      pairs * pages < (1LL << 31)) {
-    // Balanced mode: ranges of at most kPagesPerWave * W pages, and partial
-    // slots enough that no item spans more of them.
-    p->balanced = true;
-    p->W = 8;
-    p->S = (int)max_of(kMinBalancedSlots,
-                       (pages + kPagesPerWave * p->W - 1) / (kPagesPerWave * p->W) + 1);
-    p->slots = p->S;
-    return true;
-  }
-  p->balanced = false;
+  // The grid plan.
   const int W = pairs > 256 ? 4 : 8;
   long long S;
   if (partition_tokens > 0) {
@@ -132,11 +123,25 @@ inline bool make_plan(int B, int Hkv, int G, int D, int max_len, int window,
   }
   // A wave holds at most kPagesPerWave pages.
   S = max_of(S, (pages + kPagesPerWave * W - 1) / (kPagesPerWave * W));
+  const bool pair = S == 1 && partition_tokens == 0 && L >= kMinSplitContext &&
+                    B <= kMaxPairB && pair_fits(W, G, D);
+  if (byte_cache && !pair && partition_tokens == 0 && L >= kMinSplitContext &&
+      B <= kMaxBalancedB && pairs * pages < (1LL << 31)) {
+    // Balanced mode: ranges of at most kPagesPerWave * W pages, and partial
+    // slots enough that no item spans more of them.
+    p->balanced = true;
+    p->pair = false;
+    p->W = 8;
+    p->S = (int)max_of(kMinBalancedSlots,
+                       (pages + kPagesPerWave * p->W - 1) / (kPagesPerWave * p->W) + 1);
+    p->slots = p->S;
+    return true;
+  }
   if (S > 65535) return false;
+  p->balanced = false;
   p->S = (int)S;
   p->W = W;
-  p->pair = S == 1 && partition_tokens == 0 && L >= kMinSplitContext && B <= kMaxPairB &&
-            pair_fits(W, G, D);
+  p->pair = pair;
   p->slots = p->pair ? 2 : p->S;
   return true;
 }

@@ -130,32 +130,38 @@ def test_workspace_query():
         2 * rnd(2 * 8 * 2 * 4) + rnd(2 * 8 * 2 * 128 * 4) + cnt(2 * 2)
     assert lib.pa_decode_workspace_bytes(2, 8, 2, 128, 100, 0, 33) == (1 << 64) - 1
     assert lib.pa_decode_workspace_bytes(-1, 8, 2, 128, 100, 0, 0) == (1 << 64) - 1
-    # From 1024 tokens the byte-format plan (equal page ranges over the batch)
-    # keeps 16 partial slots per (sequence, query head); the 16-bit plan for
-    # 32 x 8 KV heads is one pass, so the query returns the former.
-    rows = 32 * 32 * 16
+    # From 1024 tokens, 32 sequences x 8 KV heads take pair mode in both
+    # formats (two partial slots per query head: its own and its helper's).
+    rows = 32 * 32 * 2
     assert lib.pa_decode_workspace_bytes(32, 32, 8, 128, 4096, 0, 0) == \
         2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(32 * 8)
+    # Above 64 sequences (no pair mode) the byte-format plan (equal page
+    # ranges over the batch) keeps 16 partial slots per (sequence, query
+    # head); the 16-bit plan is one pass, so the query returns the former.
+    rows = 65 * 32 * 16
+    assert lib.pa_decode_workspace_bytes(65, 32, 8, 128, 4096, 0, 0) == \
+        2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(65 * 8)
     # Longer contexts: more slots, so that no range exceeds 64 pages per wave
     # (65536 tokens = 2048 pages: ceil(2048 / 512) + 1 = 5 < 16, still 16;
     # 2^20 tokens = 32768 pages: 64 + 1 = 65 slots).
     rows = 1 * 8 * 65
     assert lib.pa_decode_workspace_bytes(1, 8, 8, 64, 1 << 20, 0, 0) >= \
         2 * rnd(rows * 4) + rnd(rows * 64 * 4) + cnt(8)
-    # The per-format query: a 16-bit cache takes one split per sequence in
-    # pair mode here (two partial slots per query head: its own and its
-    # helper's), a byte cache the balanced plan's slots.
+    # The per-format query: with 32 sequences both formats take pair mode
+    # (two partial slots per query head).
     rows2 = 32 * 32 * 2
-    assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == \
-        2 * rnd(rows2 * 4) + rnd(rows2 * 128 * 4) + cnt(32 * 8)
+    for fmt in (_lib.PA_BF16, _lib.PA_F8E4M3, _lib.PA_I8):
+        assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, fmt) == \
+            2 * rnd(rows2 * 4) + rnd(rows2 * 128 * 4) + cnt(32 * 8)
     # Above 64 sequences no pair mode: one split, no workspace.
     assert lib.pa_decode_workspace_bytes_for(65, 32, 8, 128, 4096, 0, 0, _lib.PA_BF16) == 0
     # Below 1024 tokens one pass.
     assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 1000, 0, 0, _lib.PA_BF16) == 0
-    rows = 32 * 32 * 16
+    # A byte cache with more than 64 sequences: the balanced plan's slots.
+    rows = 65 * 32 * 16
     for fmt in (_lib.PA_F8E4M3, _lib.PA_I8):
-        assert lib.pa_decode_workspace_bytes_for(32, 32, 8, 128, 4096, 0, 0, fmt) == \
-            2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(32 * 8)
+        assert lib.pa_decode_workspace_bytes_for(65, 32, 8, 128, 4096, 0, 0, fmt) == \
+            2 * rnd(rows * 4) + rnd(rows * 128 * 4) + cnt(65 * 8)
     assert lib.pa_decode_workspace_bytes_for(-1, 8, 2, 128, 100, 0, 0, _lib.PA_BF16) == \
         (1 << 64) - 1
     # Above 1024 sequences only the grid plan applies.

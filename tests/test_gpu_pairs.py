@@ -122,3 +122,84 @@ def test_pair_identity_map(name):
     P.same_output(a, b, P.TOL[wl.act], "identity map vs table")
     err = P.max_abs(P.out_f64(a), _oracle(wl))
     assert err <= P.TOL[wl.act]
+
+
+# Byte caches (E4M3, INT8) take pair mode too where the grid plan has one
+# split per sequence and B <= 64 (more than 256 (sequence, KV head) items,
+# four-wave workgroups); elsewhere they take the balanced plan.
+BYTE_CASES = {
+    "e4m3_b40": lambda: W.decode_workload("pair_e4m3", 111, B=40, Hq=32, Hkv=8, D=128,
+                                          act="bf16", cache="e4m3", ctx_range=(0, 5000)),
+    "e4m3_ring_f16": lambda: W.decode_workload("pair_e4m3_ring", 112, B=36, Hq=32, Hkv=8,
+                                               D=128, act="f16", cache="e4m3", window=2048,
+                                               pos_range=(100, 6000)),
+    "int8_b48": lambda: W.decode_workload("pair_int8", 113, B=48, Hq=32, Hkv=8, D=128,
+                                          act="bf16", cache="int8", ctx_range=(1, 4500)),
+}
+
+
+def _byte_pair_mode(wl):
+    """The plan's workspace is pair mode's: the counters, then two partial
+    slots per (sequence, query head)."""
+    L = int(wl.context_lens.max())
+    fmt = ops._lib.PA_F8E4M3 if wl.cache == "e4m3" else ops._lib.PA_I8
+    rnd = lambda x: (x + 255) // 256 * 256      # noqa: E731
+    rows = wl.B * wl.Hq * 2
+    want = rnd(max(wl.B * wl.Hkv, ops.MIN_COUNTERS) * 4) + 2 * rnd(rows * 4) + rnd(rows * wl.D * 4)
+    return ops.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, L, wl.window, 0, fmt) == want
+
+
+@pytest.mark.parametrize("name", list(BYTE_CASES))
+@pytest.mark.parametrize("append", [False, True])
+def test_pair_decode_byte_cache(name, append):
+    wl = BYTE_CASES[name]()
+    if name == "e4m3_b40" and not append:
+        wl.context_lens[7] = 0          # an empty sequence among the pairs (its new
+        #                                 row then has no position for the fused write)
+    P.say(f"[pairs {wl.cache}] {name} append={append} B={wl.B} pages={_pages(wl)}")
+    assert _byte_pair_mode(wl), "pair mode expected"
+    i8 = wl.cache == "int8"
+    if i8:
+        pools = P.gpu_pools_i8(wl)
+        ks_, vs_, sl = [], [], []
+        for b in range(wl.B):
+            n = wl.cached_k[b].shape[0]
+            if n:
+                pos = np.arange(wl.cached_pos0[b], wl.cached_pos0[b] + n)
+                sl.append(pool.slots_from_table(wl.block_tables[b], pos, wl.BS, wl.window))
+                ks_.append(wl.cached_k[b])
+                vs_.append(wl.cached_v[b])
+        P._gpu_write_i8(wl, pools, np.concatenate(ks_), np.concatenate(vs_), np.concatenate(sl))
+        if not append:
+            new_slots = np.array([pool.slots_from_table(wl.block_tables[b], [wl.new_pos[b]],
+                                                        wl.BS, wl.window)[0]
+                                  for b in range(wl.B)], np.int32)
+            P._gpu_write_i8(wl, pools, wl.new_k, wl.new_v, new_slots)
+        kc, vc, ks, vs = pools
+        extra = dict(key_scales=ks, value_scales=vs)
+    else:
+        kc, vc = P.hip_decode_append_setup(wl) if append else P.hip_decode_setup(wl)
+        extra = {}
+    if append:
+        extra.update(new_key=P._act_tensor(wl.new_k, wl.act),
+                     new_value=P._act_tensor(wl.new_v, wl.act))
+    q = P._act_tensor(wl.query, wl.act)
+    outs = [ops.decode(q, kc, vc, _t(wl.block_tables), _t(wl.context_lens),
+                       int(wl.context_lens.max()), wl.scale, wl.k_scale, wl.v_scale,
+                       wl.window, **extra).clone() for _ in range(2)]
+    torch.cuda.synchronize()
+    if i8:
+        opools = P.oracle_decode_setup_i8(wl)
+        for got, r, what in zip(pools, opools, ("key codes", "value codes", "key scales",
+                                                "value scales")):
+            g = P.scale_bits(got) if got.dtype == torch.float32 else P.pool_bits(got)
+            assert np.array_equal(g, r.view(np.int32) if r.dtype == np.float32 else r), what
+        ref = P.oracle_decode_i8(wl, opools)
+    else:
+        okc, ovc = P.oracle_decode_setup(wl)
+        assert np.array_equal(P.pool_bits(kc), okc), "key pool differs"
+        assert np.array_equal(P.pool_bits(vc), ovc), "value pool differs"
+        ref = P.oracle_decode(wl, okc, ovc)
+    errs = [P.max_abs(P.out_f64(o), ref) for o in outs]
+    P.say(f"    max-abs error of the two calls {[f'{e:.3e}' for e in errs]}")
+    assert max(errs) <= P.TOL[wl.cache]
