@@ -806,18 +806,34 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   int hb = -1, help_lo = 0, help_hi = 0, Lh = 0, ctx_h = 0;  // help job on sequence hb
   if (paired) {
     // Rank the sequences by pages (ties by index), longest first; rank r
-    // pairs with rank B - 1 - r.
+    // pairs with rank B - 1 - r.  Lane j's key, pages then 63 - j, orders
+    // the batch that way with no two keys equal; this sequence's rank is
+    // the count of larger keys (one ballot), and its partner's key the one
+    // with exactly B - 1 - r larger keys, found bit by bit from the top
+    // (one ballot per key bit; a loop over the B lengths with a lane read
+    // per step took ~1 us of every wave's start).
     const int Lx = min(lens_lane, len_cap);
     const int Px = lane < B && Lx > 0 ? (Lx + kPage - 1) / kPage : 0;
-    int rank = 0;
-    for (int j = 0; j < B; ++j) {
-      const int pj = __builtin_amdgcn_readlane(Px, j);
-      rank += (pj > Px) || (pj == Px && j < lane);
-    }
-    const int r = __builtin_amdgcn_readlane(rank, b);
+    const unsigned key = lane < B ? ((unsigned)Px << 6) | (unsigned)(63 - lane) : 0u;
+    const unsigned kb = (unsigned)__builtin_amdgcn_readlane((int)key, b);
+    const int r = (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key > kb));
     const int pr = B - 1 - r;
-    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && rank == pr);
-    const int partner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    const int p_max = (int)(((long long)len_cap + kPage - 1) / kPage);   // >= every Px
+    const int kbits = 32 - __builtin_clz((unsigned)max(p_max, 1)) + 6;
+    unsigned prefix = 0;
+    int above = pr;                        // larger keys still to pass
+    for (int bit = kbits - 1; bit >= 0; --bit) {
+      const unsigned hi = ~((1u << bit) - 1u);
+      const unsigned cand = prefix | (1u << bit);
+      const int n = (int)__builtin_popcountll(
+          __builtin_amdgcn_ballot_w64(lane < B && (key & hi) == cand));
+      if (above < n) {
+        prefix = cand;
+      } else {
+        above -= n;
+      }
+    }
+    const int partner = 63 - (int)(prefix & 63u);
     const int Pp = __builtin_amdgcn_readlane(Px, partner);
     if (r < pr) {
       own_hi = plan::pair_split(P, Pp);

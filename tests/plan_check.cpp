@@ -7,6 +7,7 @@
 //                 up to the length cap; at most 65535 splits;
 //   pair mode     every page of every item is read exactly once (by its own
 //                 workgroup or its one helper), and every job fits a wave;
+//                 the kernel's ballot ranking gives the same ranks and partners;
 //   balanced mode a range spans at most kPagesPerWave * W pages, the ranges
 //                 cover the batch, and no item meets more ranges than it has
 //                 partial slots, for random length mixes up to the cap;
@@ -72,6 +73,32 @@ static void check_grid(int B, int Hkv, int max_len, int window, int part, const 
   }
 }
 
+// The kernel's ranking, restated on the host: lane j's key is its pages then
+// 63 - j; a sequence's rank is the count of larger keys, and its partner's
+// key the one with exactly B - 1 - r larger keys, found bit by bit from the
+// top with one count per bit (the kernel counts with ballots).
+static void kernel_rank(const std::vector<int>& P, int B, int b, int p_max, int* r,
+                        int* partner) {
+  unsigned key[64];
+  for (int l = 0; l < 64; ++l) key[l] = l < B ? ((unsigned)P[l] << 6) | (unsigned)(63 - l) : 0u;
+  int rr = 0;
+  for (int l = 0; l < 64; ++l) rr += key[l] > key[b];
+  int kbits = 6;
+  for (unsigned m = (unsigned)(p_max > 1 ? p_max : 1); m; m >>= 1) ++kbits;
+  unsigned prefix = 0;
+  int above = B - 1 - rr;
+  for (int bit = kbits - 1; bit >= 0; --bit) {
+    const unsigned hi = ~((1u << bit) - 1u);
+    const unsigned cand = prefix | (1u << bit);
+    int n = 0;
+    for (int l = 0; l < B; ++l) n += (key[l] & hi) == cand;
+    if (above < n) prefix = cand;
+    else above -= n;
+  }
+  *r = rr;
+  *partner = 63 - (int)(prefix & 63u);
+}
+
 // Pair mode: rank by pages (ties by index), pair rank r with B - 1 - r, the
 // shorter item's workgroup reads [a, Pl) of the longer one (pair_split), as
 // the kernel computes it from the batch's lengths.  Every page of every item
@@ -90,6 +117,14 @@ static void check_pairs(std::mt19937_64& rng, const Plan& p, int B, long long ca
       for (int j = 0; j < B; ++j) rank[i] += P[j] > P[i] || (P[j] == P[i] && j < i);
     std::vector<int> by_rank(B);
     for (int i = 0; i < B; ++i) by_rank[rank[i]] = i;
+    const int p_max = (int)pages_of(cap);
+    for (int b = 0; b < B; ++b) {
+      int kr, kp;
+      kernel_rank(P, B, b, p_max, &kr, &kp);
+      CHECK(kr == rank[b] && kp == by_rank[B - 1 - rank[b]],
+            "kernel ranking of item %d: rank %d partner %d, want %d %d", b, kr, kp, rank[b],
+            by_rank[B - 1 - rank[b]]);
+    }
     std::vector<long long> read(B, 0);
     std::vector<int> helped_by(B, -1);
     for (int b = 0; b < B; ++b) {
