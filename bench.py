@@ -69,16 +69,26 @@ _KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (comments do not change
+    what is compiled)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel_prefix: str) -> str:
-    """sha256 over the HIP sources a kernel family is built from, to tie
-    recorded counter data to a build of that kernel."""
+    """sha256 over the code (comments stripped) of the HIP sources a kernel
+    family is built from, to tie recorded counter data to a build of that
+    kernel."""
     import hashlib
     d = os.path.join(ROOT, "paged_kv_cache_175_amd", "csrc")
     h = hashlib.sha256()
     for f in _KERNEL_SOURCES[kernel_prefix]:
         h.update(f.encode())
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

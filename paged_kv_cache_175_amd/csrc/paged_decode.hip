@@ -10,9 +10,11 @@
 //
 // Work split, two modes chosen by the host plan.  Grid mode (decode_split):
 // a workgroup of W waves (W = 4 or 8) owns one split of the pages of
-// (sequence b, KV head g); its waves take the split's pages round-robin, so
-// they stream neighbouring pages side by side.  Balanced mode
-// (decode_balanced, E4M3 and INT8 caches): the pages of the whole batch are
+// (sequence b, KV head g) and, in pair mode, also the tail of the sequence
+// its own is paired with; its waves claim the job's pages one at a time
+// from an LDS counter, so they stream neighbouring pages side by side and
+// finish together.  Balanced mode (decode_balanced, E4M3 and INT8 caches
+// where pair mode does not apply): the pages of the whole batch are
 // cut into equal ranges, one per workgroup, whatever the mix of context
 // lengths, and the waves claim a range's pages one at a time.  Either way
 // each wave prefetches its next page into a second register buffer while it
@@ -587,8 +589,8 @@ __device__ __forceinline__ uint32_t encode_elem(uint16_t x, float scale) {
 }
 
 // Store element d of cache row `row` of the page at element offset `page`
-// (non-temporal: nothing in the launch reads it back from memory; measured
-// 1.3 us faster on the Mistral batch).
+// (balanced mode's appended row; non-temporal: nothing in the launch reads
+// it back from memory).
 template <int D, int CF>
 __device__ __forceinline__ void store_row_elem(uint8_t* key_cache, uint8_t* value_cache,
                                                size_t page, int row, int d, uint32_t kq,
@@ -615,10 +617,11 @@ __device__ __forceinline__ void store_row_elem(uint8_t* key_cache, uint8_t* valu
 // An item read by several workgroups (its splits, or its owner and its
 // helper) is merged by the last of them to finish (finish_item).
 //
-// The decoded token's row (append mode) is encoded by the wave that reads
-// its page, from the activations, stored into its cache row and patched
-// into that page's registers: no workgroup barrier, and nothing in the
-// launch depends on the stores landing.
+// The decoded token's row (append mode) is loaded and encoded (as the writer
+// encodes it) into LDS by every workgroup whose job holds its page; the wave
+// that claims that page patches the row into its page registers and writes
+// the lines that hold the row back to the cache whole (compute_page): no
+// extra barrier, and nothing in the launch depends on the stores landing.
 
 // Wave partial of an empty job: the combine skips m = -inf.
 template <int G>

@@ -26,3 +26,11 @@ def test_kernel_source_hashes():
         h = bench.kernel_source_hash(prefix)
         assert len(h) == 64 and h == bench.kernel_source_hash(prefix)
     assert bench.kernel_source_hash("decode_") != bench.kernel_source_hash("prefill_")
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) {  // one\n  return x + 1; /* two\n three */\n}\n"
+    b = "// header\nint f(int x) {\n\n  return x + 1;\n}\n"
+    c = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)

@@ -4,8 +4,9 @@ pa_decode with a caller workspace, both through the C ABI.
 
 Two calls in a row on one GPU, the second with a smaller input, then the
 first again: each output matches pa_decode's on the same inputs and the
-oracle within the output tolerance.  A 16-bit cache (split plan) and an
-E4M3 cache (balanced ranges) both use the scratch.  The two entry points run
+oracle within the output tolerance.  A 16-bit cache (split plan), an
+E4M3 cache (balanced ranges) and an E4M3 batch in pair mode all use the
+scratch.  The two entry points run
 the same kernels with the same plan, but the waves of a workgroup claim
 pages as they go, so the summation order, and the last bits, may differ
 from one launch to the next.
@@ -38,10 +39,17 @@ def _noalloc(wl, kc, vc):
     return out
 
 
-@pytest.mark.parametrize("cache", ["bf16", "e4m3"])
-def test_noalloc_matches_pa_decode_twice(cache):
-    big = W.decode_workload(f"noalloc_big_{cache}", 41, B=6, Hq=32, Hkv=8, D=128, act="bf16",
-                            cache=cache, ctx_range=(3000, 6000))
+@pytest.mark.parametrize("case", ["bf16", "e4m3", "e4m3_pairs"])
+def test_noalloc_matches_pa_decode_twice(case):
+    cache = case.split("_")[0]
+    if case.endswith("pairs"):
+        # 40 sequences x 8 KV heads from 1024 tokens: pair mode (one split per
+        # sequence, short sequences help long ones through the scratch).
+        big = W.decode_workload(f"noalloc_big_{case}", 43, B=40, Hq=32, Hkv=8, D=128,
+                                act="bf16", cache=cache, ctx_range=(1024, 4000))
+    else:
+        big = W.decode_workload(f"noalloc_big_{case}", 41, B=6, Hq=32, Hkv=8, D=128,
+                                act="bf16", cache=cache, ctx_range=(3000, 6000))
     small = W.decode_workload(f"noalloc_small_{cache}", 42, B=3, Hq=8, Hkv=2, D=64, act="bf16",
                               cache=cache, ctx_range=(1100, 2500))
     pools, refs = [], []
