@@ -210,14 +210,20 @@ size_t pa_decode_workspace_bytes_for(int32_t B, int32_t Hq, int32_t Hkv, int32_t
  *                 partial results are merged (max_len = max_context_len,
  *                 capped at window); 0 lets the library choose: one pass
  *                 without workspace below 1024 tokens (max_len); from 1024
- *                 on, for 16-bit caches enough splits for ~2048 resident
- *                 waves, at most one split per page of each of the
- *                 workgroup's waves and at most 16 splits (more if a split
- *                 would exceed 64 pages per wave), and for E4M3 and INT8
- *                 caches (B <= 1024) equal ranges of the whole batch's
- *                 pages, one per workgroup, whatever the mix of context
- *                 lengths (a sequence cut between ranges is merged like the
- *                 splits).  Results do not depend on it beyond rounding.
+ *                 on, enough splits for ~2048 resident waves, at most one
+ *                 split per page of each of the workgroup's waves and at
+ *                 most 16 splits (more if a split would exceed 64 pages
+ *                 per wave); with one split per sequence and B <= 64, pair
+ *                 mode: the workgroup of each shorter sequence of a pair
+ *                 (the batch ranked by length, longest with shortest) also
+ *                 reads the tail of the longer one, and the two partials
+ *                 are merged like splits; E4M3 and INT8 caches (B <= 1024)
+ *                 where pair mode does not apply: equal ranges of the
+ *                 whole batch's pages, one per workgroup, whatever the mix
+ *                 of context lengths (a sequence cut between ranges is
+ *                 merged like the splits).  Results do not depend on the
+ *                 plan beyond rounding (the summation order, which also
+ *                 varies from launch to launch).
  * workspace       device scratch of pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0), 256-byte aligned, kept by
  *                 the caller across calls.  It starts with the counter
