@@ -817,38 +817,47 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // per step took ~1 us of every wave's start).
     const int Lx = min(lens_lane, len_cap);
     const int Px = lane < B && Lx > 0 ? (Lx + kPage - 1) / kPage : 0;
-    const unsigned key = lane < B ? ((unsigned)Px << 6) | (unsigned)(63 - lane) : 0u;
-    const unsigned kb = (unsigned)__builtin_amdgcn_readlane((int)key, b);
-    const int r = (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key > kb));
-    const int pr = B - 1 - r;
-    const int p_max = (int)(((long long)len_cap + kPage - 1) / kPage);   // >= every Px
-    const int kbits = 32 - __builtin_clz((unsigned)max(p_max, 1)) + 6;
-    unsigned prefix = 0;
-    int above = pr;                        // larger keys still to pass
-    for (int bit = kbits - 1; bit >= 0; --bit) {
-      const unsigned hi = ~((1u << bit) - 1u);
-      const unsigned cand = prefix | (1u << bit);
-      const int n = (int)__builtin_popcountll(
-          __builtin_amdgcn_ballot_w64(lane < B && (key & hi) == cand));
-      if (above < n) {
-        prefix = cand;
-      } else {
-        above -= n;
+    // Lengths within 3 pages of the first sequence's: no two differ by the
+    // 2 kMinHelpPages pages a help needs, so nothing is paired (the ranking
+    // below would find the same) and it is skipped.
+    const int P0 = __builtin_amdgcn_readfirstlane(Px);
+    const bool spread = __builtin_amdgcn_ballot_w64(
+        lane < B && (Px > P0 + (plan::kMinHelpPages - 1) ||
+                     Px + (plan::kMinHelpPages - 1) < P0)) != 0;
+    if (spread) {
+      const unsigned key = lane < B ? ((unsigned)Px << 6) | (unsigned)(63 - lane) : 0u;
+      const unsigned kb = (unsigned)__builtin_amdgcn_readlane((int)key, b);
+      const int r = (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key > kb));
+      const int pr = B - 1 - r;
+      const int p_max = (int)(((long long)len_cap + kPage - 1) / kPage);   // >= every Px
+      const int kbits = 32 - __builtin_clz((unsigned)max(p_max, 1)) + 6;
+      unsigned prefix = 0;
+      int above = pr;                        // larger keys still to pass
+      for (int bit = kbits - 1; bit >= 0; --bit) {
+        const unsigned hi = ~((1u << bit) - 1u);
+        const unsigned cand = prefix | (1u << bit);
+        const int n = (int)__builtin_popcountll(
+            __builtin_amdgcn_ballot_w64(lane < B && (key & hi) == cand));
+        if (above < n) {
+          prefix = cand;
+        } else {
+          above -= n;
+        }
       }
-    }
-    const int partner = 63 - (int)(prefix & 63u);
-    const int Pp = __builtin_amdgcn_readlane(Px, partner);
-    if (r < pr) {
-      own_hi = plan::pair_split(P, Pp);
-      own_parts = own_hi < P ? 2 : 1;
-    } else if (r > pr) {
-      const int a = plan::pair_split(Pp, P);
-      if (a < Pp) {
-        hb = partner;
-        help_lo = a;
-        help_hi = Pp;
-        ctx_h = __builtin_amdgcn_readlane(lens_lane, partner);
-        Lh = min(ctx_h, len_cap);
+      const int partner = 63 - (int)(prefix & 63u);
+      const int Pp = __builtin_amdgcn_readlane(Px, partner);
+      if (r < pr) {
+        own_hi = plan::pair_split(P, Pp);
+        own_parts = own_hi < P ? 2 : 1;
+      } else if (r > pr) {
+        const int a = plan::pair_split(Pp, P);
+        if (a < Pp) {
+          hb = partner;
+          help_lo = a;
+          help_hi = Pp;
+          ctx_h = __builtin_amdgcn_readlane(lens_lane, partner);
+          Lh = min(ctx_h, len_cap);
+        }
       }
     }
   } else if (S > 1) {

@@ -109,14 +109,23 @@ static void check_pairs(std::mt19937_64& rng, const Plan& p, int B, long long ca
     std::vector<int> P(B);
     for (int b = 0; b < B; ++b) {
       long long L = trial == 0 ? cap : trial == 1 ? (b % 2 ? cap : 0)
+                  : trial == 2 ? cap - std::uniform_int_distribution<long long>(0, 3 * kBlock)(rng)
                   : std::uniform_int_distribution<long long>(0, cap)(rng);
-      P[b] = (int)pages_of(L);
+      P[b] = (int)pages_of(L < 0 ? 0 : L);
     }
     std::vector<int> rank(B, 0);
     for (int i = 0; i < B; ++i)
       for (int j = 0; j < B; ++j) rank[i] += P[j] > P[i] || (P[j] == P[i] && j < i);
     std::vector<int> by_rank(B);
     for (int i = 0; i < B; ++i) by_rank[rank[i]] = i;
+    // The kernel skips the ranking when every length is within
+    // kMinHelpPages - 1 pages of the first one's: then no pair may help.
+    bool near = true;
+    for (int b = 0; b < B; ++b) near &= std::abs(P[b] - P[0]) <= kMinHelpPages - 1;
+    if (near)
+      for (int i = 0; i < B; ++i)
+        for (int j = 0; j < B; ++j)
+          if (P[i] >= P[j]) CHECK(pair_split(P[i], P[j]) == P[i], "a help within the shortcut");
     const int p_max = (int)pages_of(cap);
     for (int b = 0; b < B; ++b) {
       int kr, kp;
