@@ -21,14 +21,27 @@ from paged_kv_cache_175_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cache,part", [("bf16", 0), ("bf16", 64), ("e4m3", 0)])
-def test_decode_append_graph_replays(cache, part):
-    """bf16 one pass and forced splits; E4M3 over 1024+ tokens takes the
-    balanced plan (equal page ranges, cut sequences merged in the launch)."""
-    wl = W.decode_workload("graph_decode", 91, B=6, Hq=32, Hkv=8, D=128, act="bf16",
-                           cache=cache, ctx_range=(1, 900) if cache == "bf16" else (1, 2500))
+# name: (cache, partition_tokens, B, context range).  bf16 one pass and
+# forced splits; E4M3 over 1024+ tokens with 6 sequences takes the balanced
+# plan (equal page ranges, cut sequences merged in the launch); 32 sequences
+# from 1024 tokens take pair mode (partials of helped sequences merged in the
+# launch) in both formats.
+GRAPH_CASES = {
+    "bf16_one_pass": ("bf16", 0, 6, (1, 900)),
+    "bf16_splits": ("bf16", 64, 6, (1, 900)),
+    "e4m3_balanced": ("e4m3", 0, 6, (1, 2500)),
+    "bf16_pairs": ("bf16", 0, 32, (1024, 4000)),
+    "e4m3_pairs": ("e4m3", 0, 32, (1024, 4000)),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
+def test_decode_append_graph_replays(name):
+    cache, part, B, ctx_range = GRAPH_CASES[name]
+    wl = W.decode_workload("graph_decode", 91, B=B, Hq=32, Hkv=8, D=128, act="bf16",
+                           cache=cache, ctx_range=ctx_range)
     sc = dict(k_scale=wl.k_scale, v_scale=wl.v_scale)
-    P.say(f"[graph] decode append cache={cache} part={part} lens={list(wl.context_lens)}")
+    P.say(f"[graph] decode append {name} lens={list(wl.context_lens)}")
     kc, vc = P.hip_decode_append_setup(wl)
     q = P._act_tensor(wl.query, wl.act)
     nk, nv = P._act_tensor(wl.new_k, wl.act), P._act_tensor(wl.new_v, wl.act)
