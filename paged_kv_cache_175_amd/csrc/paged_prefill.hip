@@ -15,14 +15,15 @@
 // waves owns 64 * NQ consecutive rows; each wave owns NQ tiles of 16 rows.
 // The workgroup walks the sequence's key pages (32 tokens each) up to the last
 // position its rows can see.  Pages of a 16-bit cache go from global memory
-// straight into LDS (global_load_lds_dwordx4, no registers), two pages ahead
-// of the one being computed, through three LDS buffers and one barrier a
-// page.  E4M3 and INT8 pages are widened to the activation format on the
-// way, so they pass through registers, one page ahead, through two buffers.
-// An INT8 page ("libmir-metal 0.2.0, src/native/trace/kv.rs", fn build:
-// per-token/head codes with fp32 scales) also stages its 32 K and 32 V row
-// scales; the K scales multiply the scores and the V scales the P of the V
-// MFMAs (the all-ones tile takes the unscaled P).
+// straight into LDS (global_load_lds_dwordx4, no registers) two at a time:
+// four LDS page buffers hold the pair being computed and the next pair in
+// flight, with one barrier per pair.  E4M3 and INT8 pages are widened to the
+// activation format on the way, so they pass through registers, one page
+// ahead, through two buffers.  An INT8 page ("libmir-metal 0.2.0,
+// src/native/trace/kv.rs", fn build: per-token/head codes with fp32 scales)
+// also stages its 32 K and 32 V row scales; the K scales multiply the scores
+// and the V scales the P of the V MFMAs (the running sum takes the unscaled
+// P).
 //
 // Per wave and page, everything is computed transposed so that the
 // probabilities never leave registers:
@@ -40,10 +41,11 @@
 // LDS pages hold K as [D/8][32] chunks of 8 elements and V as [D][4] chunks
 // (dimension, 8-token group) with the 16-byte chunks of each row
 // XOR-swizzled so that both operand reads are free of bank conflicts.
-// The running sum l of each query comes out of the same MFMAs: one more
-// O^T tile whose V^T rows are all ones gives sum_k P[k][q] in every row, so
-// l is accumulated from the rounded P that also weights V, and is rescaled
-// with O.  The running maximum m is only raised when a new score exceeds it
+// The running sum l of each query is taken from the same rounded P that
+// weights V: each lane adds its eight P values to a per-lane partial sum
+// with four two-element dot products against ones (v_dot2c_f32_bf16 or
+// _f16, exact products, fp32 sums), rescaled with O; the four lanes that
+// hold a query are added up at the end.  The running maximum m is only raised when a new score exceeds it
 // by more than 2^8 (any lane, checked with a ballot), so the cross-lane
 // maximum and the rescale of O run on a few pages only.  Probabilities
 // therefore stay below 2^8, which fp32 accumulation and the 16-bit P operand
@@ -79,9 +81,11 @@ constexpr int BS = 32;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
-// Pages in flight per workgroup on the LDS-direct path (16-bit caches).
-constexpr int kLookahead = 2;
 constexpr float LOG2E_P = 1.4426950408889634f;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedTrans = 0x400;
 // Scores (in log2 units) may exceed the running maximum by this much before
 // the maximum is raised.
 constexpr float kSlack = 8.0f;
@@ -91,6 +95,23 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
 }
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// acc + w.lo + w.hi for two packed values of an activation format: a
+// two-element dot product against ones (the products are exact).
+template <int AF>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc);
+template <>
+__device__ __forceinline__ float add_pair<FMT_BF16>(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<FMT_F16>(uint32_t w, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+}
 
 // Four 16-bit values of an activation format (hardware conversion, round to
 // nearest even).
@@ -110,22 +131,6 @@ struct Vec4<FMT_F16> {
 // functions map a slot back to its cache chunk.
 __device__ __forceinline__ int k_slot(int dc, int t) { return dc * BS + (t ^ (((t >> 3) & 1) << 2)); }
 __device__ __forceinline__ int v_slot(int d, int tq) { return d * 4 + (tq ^ ((d >> 1) & 3)); }
-
-// Wait until at most `later` pages' LDS-direct loads (U per page and wave)
-// are still in flight: the count must be an immediate, so the few possible
-// values are spelled out.
-template <int LA, int U>
-__device__ __forceinline__ void wait_pages(int later) {
-  if (LA > 3 && later >= 3) {
-    wait_vmcnt<3 * U>();
-  } else if (LA > 2 && later == 2) {
-    wait_vmcnt<2 * U>();
-  } else if (later == 1) {
-    wait_vmcnt<U>();
-  } else {
-    wait_vmcnt<0>();
-  }
-}
 
 // Workgroup barrier that does not wait for outstanding global loads (a
 // __syncthreads would drain the LDS-direct loads still in flight for later
@@ -156,15 +161,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // quantised ring in the window path the ring rows' scales (1 for the
   // chunk's own rows, which come from the activations).
   constexpr bool kScaled = kI8 || (WIN && byte_fmt(CF));
-  // Order of the P and V MFMA work of a page: tile-major where its V
-  // operands fit in registers beside everything else (measured: sliding
-  // prefill, D = 128, 2 tiles, 744 -> 779 TFLOP/s), else P first (D >= 96
-  // with 3 or more tiles of a 16-bit or INT8 cache spilled tile-major).
-  constexpr bool kTileMajor = D <= 64 || NQ <= 2 || CF == FMT_E4M3;
-  // LDS-direct staging keeps LA pages in flight (LA + 1 buffers; the page a
-  // wave computes is the oldest).
-  constexpr int LA = kDma ? kLookahead : 1;
-  constexpr int NBUF = kDma ? LA + 1 : 2;
+  // LDS-direct staging works on pairs of pages: the pair being computed
+  // and the next one in flight, four buffers.
+  constexpr int NBUF = kDma ? 4 : 2;
   constexpr int EB = kDma ? 2 : 1;        // cache bytes per element
   constexpr int NCH = PAGE / 8;           // 8-element chunks per page (K or V)
   constexpr int RW = 16 * NQ * kWaves;    // rows per workgroup
@@ -235,25 +234,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // o_acc[NT] is the all-ones tile: every row holds the running sum l.
-  float m_run[NQ];
-  // Tile-major shapes (which have the registers for it) test raw maxima
+  // Per tile: the running maximum m_run, the lane's partial running sum
+  // l_acc (its eight keys of each page), and O^T.  The raw scores are tested
   // against a raw threshold: a raw score above m_thr is more than kSlack
   // above m_run once scaled (m_thr = (m_run + kSlack) / scale; the scale is
   // > 0, checked by the host), which saves a multiply and an add per tile
-  // and page.  The others scale the maxima and test them against m_run.
+  // and page.
+  float m_run[NQ];
   float m_thr[NQ];
-  f32x4 o_acc[NT + 1][NQ];
+  float l_acc[NQ];
+  f32x4 o_acc[NT][NQ];
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
     // A window row can meet pages that lie wholly below its window before
     // its first live key: a finite floor keeps exp2(s - m) at 0 there.
     m_run[t] = WIN ? -1.0e30f : -INFINITY;
     m_thr[t] = -INFINITY;
+    l_acc[t] = 0.f;
 #pragma unroll
-    for (int n = 0; n <= NT; ++n) o_acc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) o_acc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const vec ones = __builtin_convertvector(f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, vec);
 
   // Operand offsets (elements) inside a staged page.  K: chunk row
   // (4s + q4), key row 8 * (col / 4) + 4 * kt + col % 4.  V: head dim
@@ -484,10 +484,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     store_win(0);
     __syncthreads();
   } else if constexpr (kDma) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      if (i < npages) dma_page(phys_of(i), i);
-    wait_pages<LA, UPW>(min(LA, npages) - 1);   // page 0 has landed
+    // The first pair.
+    if (npages > 0) dma_page(phys_of(0), 0);
+    if (npages > 1) dma_page(phys_of(1), 1);
+    wait_vmcnt<0>();
     lds_barrier();
   } else {
     load_regs(phys_of(0));
@@ -501,8 +501,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (WIN) {
       if (p + 1 < npages) load_win(base + BS);
     } else if constexpr (kDma) {
-      // Into the buffer of page p - 1, which every wave has finished.
-      if (p + LA < npages) dma_page(phys_of(p + LA), cur == 0 ? NBUF - 1 : cur - 1);
+      // Page p sits in buffer p mod 4.  At the first page of a pair the next
+      // pair goes into the buffers of the previous pair, which every wave
+      // finished before the last barrier.
+      cur = p & 3;
+      if ((p & 1) == 0) {
+        if (p + 2 < npages) dma_page(phys_of(p + 2), (p + 2) & 3);
+        if (p + 3 < npages) dma_page(phys_of(p + 3), (p + 3) & 3);
+      }
     } else {
       if (p + 1 < npages) load_regs(phys_of(p + 1));
     }
@@ -573,33 +579,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const float m2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], c[0]), c[1]);
           const float m3 = __builtin_elementwise_maximum(c[2], c[3]);
           lmax[t] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, m2), m3);
-          if constexpr (!kTileMajor) lmax[t] *= qk_scale_log2;
         }
         auto raise_max = [&](int t) {
-          const float lm = kTileMajor ? qk_scale_log2 * lmax[t] : lmax[t];
+          const float lm = qk_scale_log2 * lmax[t];
           float cm = fmaxf(lm, shfl_xor_f(lm, 16));
           cm = fmaxf(cm, shfl_xor_f(cm, 32));
           const float m_new = fmaxf(m_run[t], cm);
           const float alpha = m_new == m_run[t] ? 1.f : fast_exp2(m_run[t] - m_new);
 #pragma unroll
-          for (int n = 0; n <= NT; ++n) o_acc[n][t] *= alpha;
+          for (int n = 0; n < NT; ++n) o_acc[n][t] *= alpha;
+          l_acc[t] *= alpha;
           m_run[t] = m_new;
-          if constexpr (kTileMajor) m_thr[t] = (m_new + kSlack) / qk_scale_log2;
+          m_thr[t] = (m_new + kSlack) / qk_scale_log2;
         };
-        if constexpr (kTileMajor) {
-          // One test for all tiles, so that the block after it holds every
-          // tile's exponentials and V MFMAs.
-          bool raise = false;
+        // One test for all tiles, so that the block after it holds every
+        // tile's exponentials and V MFMAs.
+        bool raise = false;
 #pragma unroll
-          for (int t = 0; t < NQ; ++t) raise |= lmax[t] > m_thr[t];
-          if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        for (int t = 0; t < NQ; ++t) raise |= lmax[t] > m_thr[t];
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-            for (int t = 0; t < NQ; ++t) raise_max(t);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < NQ; ++t)
-            if (__builtin_amdgcn_ballot_w64(lmax[t] > m_run[t] + kSlack) != 0) raise_max(t);
+          for (int t = 0; t < NQ; ++t) raise_max(t);
         }
       }
 
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         return __builtin_bit_cast(vec, vw);
       };
       // P of tile t (and, beside the unscaled P, the P that weights V when
-      // the keys carry V scales); l += 1^T P^T from the unscaled P.
+      // the keys carry V scales); the lane's partial l adds the unscaled P.
       auto p_operand = [&](int t) -> vec {
         f32x8 pv;
 #pragma unroll
@@ -628,7 +628,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           for (int r = 0; r < 4; ++r)
             pv[4 * kt + r] = fast_exp2(fmaf(s_acc[kt][t][r], qk_scale_log2, -m_run[t]));
         vec pb = __builtin_convertvector(pv, vec);
-        o_acc[NT][t] = Mfma<AF>::mma(ones, pb, o_acc[NT][t]);
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l_acc[t] = add_pair<AF>(pw[e], l_acc[t]);
         if constexpr (kScaled) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
@@ -640,30 +642,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         return pb;
       };
-      if constexpr (kTileMajor) {
-        // One query tile at a time: a tile's V MFMAs are issued between the
-        // next tile's exponentials, so the wave keeps the matrix core and
-        // the VALU busy together (all V operands stay in registers).
-        vec va[NT];
+      // One query tile at a time; all V operands stay in registers.
+      vec va[NT];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) va[n] = v_operand(n);
+      for (int n = 0; n < NT; ++n) va[n] = v_operand(n);
+      if constexpr (!decltype(masked)::value && !kScaled) {
+        // Software-pipelined over the tiles: tile t's P and tile t - 1's V
+        // MFMAs form one scheduling region, inside which group barriers
+        // interleave them (an MFMA, two exponentials, two other VALU
+        // instructions, ...) so that the matrix core works while the VALU
+        // computes P.  Left to itself the scheduler issues every
+        // exponential of the page first and every V MFMA after them.
+        vec p_prev = p_operand(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 1; t < NQ; ++t) {
+          const vec pb = p_operand(t);
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+            o_acc[n][t - 1] = Mfma<AF>::mma(va[n], p_prev, o_acc[n][t - 1]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedTrans, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          p_prev = pb;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          o_acc[n][NQ - 1] = Mfma<AF>::mma(va[n], p_prev, o_acc[n][NQ - 1]);
+      } else {
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
           const vec pb = p_operand(t);
 #pragma unroll
           for (int n = 0; n < NT; ++n) o_acc[n][t] = Mfma<AF>::mma(va[n], pb, o_acc[n][t]);
-        }
-      } else {
-        // Every tile's P first, then the V MFMAs one V operand at a time:
-        // fewer registers, for the shapes where the tile-major order spills.
-        vec pb[NQ];
-#pragma unroll
-        for (int t = 0; t < NQ; ++t) pb[t] = p_operand(t);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const vec va = v_operand(n);
-#pragma unroll
-          for (int t = 0; t < NQ; ++t) o_acc[n][t] = Mfma<AF>::mma(va, pb[t], o_acc[n][t]);
         }
       }
       };
@@ -676,12 +691,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if constexpr (kDma) {
-      // This wave's share of page p + 1 has landed (the later pages may
-      // still be in flight); the barrier publishes every wave's share and
-      // retires buffer `cur` for reuse.
-      wait_pages<LA, UPW>(max(0, min(LA - 1, npages - 2 - p)));
-      lds_barrier();
-      cur = cur == NBUF - 1 ? 0 : cur + 1;
+      // After the second page of a pair: this wave's share of the next pair
+      // has landed; the barrier publishes every wave's share and retires
+      // the pair just computed for reuse.
+      if ((p & 1) == 1 && p + 1 < npages) {
+        wait_vmcnt<0>();
+        lds_barrier();
+      }
     } else {
       if constexpr (WIN) {
         if (p + 1 < npages) store_win(cur ^ 1);
@@ -694,13 +710,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   if (!wave_live) return;
+  // l of each query: the partial sums of the four lanes that hold it.
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    l_acc[t] += shfl_xor_f(l_acc[t], 16);
+    l_acc[t] += shfl_xor_f(l_acc[t], 32);
+  }
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
     const int r = row0 + 16 * t + col;
     if (r >= rows) continue;
     const int j = r / G;
     const int hq = g * G + r - j * G;
-    const float inv = v_scale / o_acc[NT][t][0];
+    const float inv = v_scale / l_acc[t];
     uint16_t* dst = out + ((size_t)(q_begin + j) * Hq + hq) * D + 4 * q4;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
