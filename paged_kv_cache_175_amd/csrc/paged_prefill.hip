@@ -46,11 +46,12 @@
 // weights V: each lane adds its eight P values to a per-lane partial sum
 // with four two-element dot products against ones (v_dot2c_f32_bf16 or
 // _f16, exact products, fp32 sums), rescaled with O; the four lanes that
-// hold a query are added up at the end.  The running maximum m is only raised when a new score exceeds it
-// by more than 2^8 (any lane, checked with a ballot), so the cross-lane
-// maximum and the rescale of O run on a few pages only.  Probabilities
-// therefore stay below 2^8, which fp32 accumulation and the 16-bit P operand
-// both hold without loss of relative precision.
+// hold a query are added up at the end.  The running maximum m is only
+// raised when a new score exceeds it by more than 2^8 (any lane, checked
+// with a ballot), so the cross-lane maximum and the rescale of O run on a
+// few pages only.  Probabilities therefore stay below 2^8, which fp32
+// accumulation and the 16-bit P operand both hold without loss of relative
+// precision.
 //
 // Rows at or past the context end in a sequence's last page hold stale data.
 // Their scores are always masked (every query sits before the context end),
@@ -62,7 +63,9 @@
 // been written into it yet, since its later tokens would overwrite rows its
 // earlier queries still need.  Query i attends to positions i - W + 1 .. i:
 // those before the chunk come from the ring pages, the chunk's own from its
-// K/V activations, staged into the same LDS layout (16-bit caches).
+// K/V activations, staged through registers into the same LDS layout, one
+// page ahead, two buffers (a byte ring's codes widened on the way, with
+// per-row scales).
 //
 // Workgroup order: workgroups are dispatched to the 8 XCDs round-robin, so
 // the flat workgroup id is remapped to give each XCD a contiguous range of
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // pages together are D / 8 such units, up to UPW per wave (at D = 96 the
   // last two waves have none).
   constexpr int UPW = (D / 8 + kWaves - 1) / kWaves;
-  // Register staging (E4M3): chunks per thread.
+  // Register staging (E4M3, INT8): chunks per thread.
   constexpr int ST = (NCH + kThreads - 1) / kThreads;
   typedef typename Mfma<AF>::vec vec;
 
