@@ -1,0 +1,124 @@
+"""Every prefill kernel instantiation against the oracle: head sizes 64, 96
+and 128, bf16 and f16 activations, a cache in the activation format, E4M3 or
+INT8, causal (``pa_prefill_chunk`` / ``_i8``) and sliding-window
+(``pa_prefill_chunk_window`` / ``_quant``) prefill.
+
+Small shapes with ragged chunks whose rows do not fill a workgroup's row
+tile, contexts and histories that end inside a page, and page ranges of odd
+and even lengths (the 16-bit causal path stages pages in pairs).  Checked:
+the output within the cache format's tolerance, and the pools byte for byte
+against the oracle's writer (the rings position by position through each
+side's table).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paritylib as P
+import test_gpu_window_prefill as WP
+import test_gpu_window_prefill_quant as WQ
+from oracle import cache as o_cache
+from oracle import pool as o_pool
+from paged_kv_cache_175_amd import pool
+from paged_kv_cache_175_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = (64, 96, 128)
+ACTS = ("bf16", "f16")
+CACHES = (None, "e4m3", "int8")   # None: the activation format
+
+
+def _cases():
+    for D in HEAD_DIMS:
+        for act in ACTS:
+            for cache in CACHES:
+                yield f"d{D}_{act}_{cache or act}"
+
+
+def _parse(name):
+    d, act, cache = name.split("_")
+    return int(d[1:]), act, (None if cache == act else cache)
+
+
+@pytest.mark.parametrize("name", list(_cases()))
+def test_causal_prefill_matrix(name):
+    D, act, cache = _parse(name)
+    seed = 700 + HEAD_DIMS.index(D) * 10 + ACTS.index(act) * 3 + CACHES.index(cache)
+    # Two sequences: a 96-token shared prefix (3 pages), chunks of 70 and 33
+    # tokens, 8 query heads over 2 KV heads.
+    wl = W.prefill_workload(f"matrix_{name}", seed, B=2, Hq=8, Hkv=2, D=D, act=act,
+                            prefix_len=96, chunks=[70, 33], cache=cache)
+    P.say(f"[prefill matrix] {name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={D} "
+          f"prefix={wl.prefix_len} chunks={list(wl.chunk_lens)}")
+    if cache == "int8":
+        pools = P.hip_prefill_setup_i8(wl)
+        out = P.hip_prefill_i8(wl, pools)
+        torch.cuda.synchronize()
+        opools = P.oracle_prefill_setup_i8(wl)
+        for got, ref, what in zip(pools, opools, ("key codes", "value codes", "key scales",
+                                                 "value scales")):
+            g = P.scale_bits(got) if got.dtype == torch.float32 else P.pool_bits(got)
+            r = ref.view(np.int32) if ref.dtype == np.float32 else ref
+            assert np.array_equal(g, r), what
+        ref = P.oracle_prefill_i8(wl, opools)
+        tol = P.TOL["int8"]
+    else:
+        kc, vc = P.hip_prefill_setup(wl)
+        out = P.hip_prefill(wl, kc, vc)
+        torch.cuda.synchronize()
+        okc, ovc = P.oracle_prefill_setup(wl)
+        assert np.array_equal(P.pool_bits(kc), okc), "key pool bytes differ"
+        assert np.array_equal(P.pool_bits(vc), ovc), "value pool bytes differ"
+        ref = P.oracle_prefill(wl, okc, ovc)
+        tol = P.TOL[wl.cache]
+    err = P.max_abs(P.out_f64(out), ref)
+    P.say(f"    max-abs error {err:.3e} (tolerance {tol:.0e})")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("name", list(_cases()))
+def test_window_prefill_matrix(name):
+    D, act, cache = _parse(name)
+    seed = 800 + HEAD_DIMS.index(D) * 10 + ACTS.index(act) * 3 + CACHES.index(cache)
+    # Three sequences over a 128-token window: a wrapped ring (history 300),
+    # a partial ring (history 45) and none; chunks of 100, 64 and 33.
+    wl = W.window_prefill_workload(f"wmatrix_{name}", seed, B=3, Hq=8, Hkv=2, D=D, act=act,
+                                   window=128, hist=[300, 45, 0], chunk=[100, 64, 33],
+                                   cache=cache)
+    P.say(f"[window prefill matrix] {name}: B={wl.B} W={wl.window} "
+          f"hist={list(wl.hist_lens)} chunks={list(wl.chunk_lens)}")
+    if cache is None:
+        out, kc, vc, bt = WP.hip_run(wl)
+        ref, okc, ovc = WP.oracle_run(wl)
+        pools, opools = (kc, vc, None, None), (okc, ovc, None, None)
+    else:
+        out, pools, bt = WQ.hip_run(wl)
+        ref, opools = WQ.oracle_run(wl)
+    # The ring after the chunk: every resident position, through each side's
+    # table (the two sides place the ring blocks differently).
+    gk, gv = P.pool_bits(pools[0]), P.pool_bits(pools[1])
+    i8 = cache == "int8"
+    if i8:
+        gks, gvs = P.scale_bits(pools[2]), P.scale_bits(pools[3])
+        oks, ovs = opools[2].view(np.int32), opools[3].view(np.int32)
+    for b in range(wl.B):
+        ctx = int(wl.context_lens[b])
+        for p in range(max(0, ctx - wl.window), ctx):
+            s_h = pool.slots_from_table(bt[b], np.array([p]), wl.BS, wl.window)[0]
+            s_o = o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
+            kh, vh = o_cache.get_row(gk, gv, s_h // wl.BS, s_h % wl.BS)
+            ko, vo = o_cache.get_row(opools[0], opools[1], s_o // wl.BS, s_o % wl.BS)
+            assert np.array_equal(kh, ko) and np.array_equal(vh, vo), (b, p)
+            if i8:
+                assert np.array_equal(gks[s_h // wl.BS, :, s_h % wl.BS],
+                                      oks[s_o // wl.BS, :, s_o % wl.BS]), (b, p)
+                assert np.array_equal(gvs[s_h // wl.BS, :, s_h % wl.BS],
+                                      ovs[s_o // wl.BS, :, s_o % wl.BS]), (b, p)
+    tol = P.TOL[cache or act]
+    err = P.max_abs(P.out_f64(out), ref)
+    P.say(f"    max-abs error {err:.3e} (tolerance {tol:.0e})")
+    assert err <= tol
