@@ -430,7 +430,13 @@ pa_status pa_prefill_chunk_window(void* out, const void* query, const void* key,
  *                 act_dtype: the same as pa_prefill_chunk_window.
  * The ring rows are read at those values; the chunk's own rows (key, value)
  * are the activations as given (they are quantised only when written into
- * the ring after this call).  Other arguments, outputs and errors as
+ * the ring after this call).  Over an E4M3 ring the kernel folds k_scale
+ * and v_scale into the score and output scales and reads the chunk's rows
+ * as key / k_scale and value / v_scale rounded to act_dtype and clamped to
+ * +-448 (the E4M3 range): the same values up to that rounding whenever the
+ * scales cover the chunk (|key| <= 448 * k_scale, |value| <= 448 *
+ * v_scale), as they must for the ring the chunk is written into.  Other
+ * arguments, outputs and errors as
  * pa_prefill_chunk_window; PA_ERR_UNSUPPORTED for another cache_dtype;
  * PA_ERR_INVALID for E4M3 scales that are not finite and > 0, or NULL INT8
  * scale pools.

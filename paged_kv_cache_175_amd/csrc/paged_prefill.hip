@@ -64,8 +64,10 @@
 // earlier queries still need.  Query i attends to positions i - W + 1 .. i:
 // those before the chunk come from the ring pages, the chunk's own from its
 // K/V activations, staged through registers into the same LDS layout, one
-// page ahead, two buffers (a byte ring's codes widened on the way, with
-// per-row scales).
+// page ahead, two buffers (a byte ring's codes widened on the way; an INT8
+// ring's row scales beside the page; over an E4M3 ring the tensor scales
+// fold into the score and output scales and the chunk's rows are divided
+// by them).
 //
 // Workgroup order: workgroups are dispatched to the 8 XCDs round-robin, so
 // the flat workgroup id is remapped to give each XCD a contiguous range of
@@ -73,6 +75,7 @@
 // head's shared prefix pages then run on one XCD, close in time, and hit in
 // its L2.
 
+#include <cfloat>
 #include <type_traits>
 
 #include "common.hpp"
@@ -134,6 +137,16 @@ struct Vec4<FMT_F16> {
   typedef _Float16 type __attribute__((ext_vector_type(4)));
 };
 
+// Eight values of an activation format times m, clamped to +-448 (the E4M3
+// range) and rounded back to the format.
+template <int AF>
+__device__ __forceinline__ u32x4 mul_clamp(u32x4 w, float m) {
+  typedef typename Mfma<AF>::vec v8;
+  f32x8 f = __builtin_convertvector(__builtin_bit_cast(v8, w), f32x8) * m;
+  f = __builtin_elementwise_min(__builtin_elementwise_max(f, (f32x8)(-448.f)), (f32x8)(448.f));
+  return __builtin_bit_cast(u32x4, __builtin_convertvector(f, v8));
+}
+
 // LDS chunk slots (16-byte chunks, in chunk units within one page).  Both
 // maps are involutions on the row index bits they touch, so the same
 // functions map a slot back to its cache chunk.
@@ -158,17 +171,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int B, int MBPS,
     int row_tiles, float qk_scale_log2, float v_scale, const float* __restrict__ key_scales,
     const float* __restrict__ value_scales, const uint16_t* __restrict__ key_act,
-    const uint16_t* __restrict__ value_act, int window, float ring_k_scale,
-    float ring_v_scale) {
+    const uint16_t* __restrict__ value_act, int window, float chunk_k_mul,
+    float chunk_v_mul) {
   constexpr int KS = D / 32;              // k-steps of S^T (32 head dims each)
   constexpr int NT = D / 16;              // 16-dim tiles of O^T
   constexpr int PAGE = BS * D;            // elements of one K (or V) page
   constexpr bool kDma = !byte_fmt(CF) && !WIN;
   constexpr bool kI8 = CF == FMT_I8;
-  // Per-key scales staged beside each page: the INT8 row scales, and for a
-  // quantised ring in the window path the ring rows' scales (1 for the
-  // chunk's own rows, which come from the activations).
-  constexpr bool kScaled = kI8 || (WIN && byte_fmt(CF));
+  // Per-key scales staged beside each page: the INT8 row scales (in the
+  // window path 1 for the chunk's own rows, which come from the
+  // activations).
+  constexpr bool kScaled = kI8;
+  // Window path over an E4M3 ring: the ring's tensor scales fold into the
+  // score and output scales, and the chunk's own rows are staged divided
+  // by them (clamped to the E4M3 range, which holds them whenever the
+  // scales cover the chunk, as they must for the ring it is written to).
+  constexpr bool kFoldWin = WIN && CF == FMT_E4M3;
   // LDS-direct staging works on pairs of pages: the pair being computed
   // and the next one in flight, four buffers.
   constexpr int NBUF = kDma ? 4 : 2;
@@ -371,12 +389,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // pos mod W; the ring has every position from max(0, start - W) on); a
   // row of the chunk from the activations; any other row is zero (never
   // visible to a query).  A quantised ring's codes are widened exactly to
-  // the activation format, and the page's row scales are staged beside it:
-  // the ring's (E4M3: the tensor scales; INT8: each row's own), 1 for the
-  // chunk's rows, 0 for the others.
+  // the activation format.  An INT8 ring's page also stages its row scales
+  // (each ring row's own, 1 for the chunk's rows, 0 for the others); over
+  // an E4M3 ring the chunk's rows are divided by the tensor scales when
+  // they are stored to LDS.
   constexpr int NIT = (BS * (D / 8) + kThreads - 1) / kThreads;
   u32x4 wk[WIN ? NIT : 1], wv[WIN ? NIT : 1];
   float wsc = 0.f;  // threads 0..31: K scale of row tid; 32..63: V scale of row tid - 32
+  bool wch[WIN ? NIT : 1];  // item holds a chunk row (E4M3 ring: divided when stored)
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
   // Eight ring elements of K (or V) starting at element `off` of the cache
   // (16-bit: one 16-byte load; bytes: one 8-byte load, widened).
@@ -403,11 +423,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int pos = base + row;
         const bool is_k = tid < BS;
         if (pos >= ring_lo && pos < first_pos) {
-          if constexpr (kI8) {
-            wsc = (is_k ? key_scales : value_scales)[((size_t)phys * Hkv + g) * BS + row];
-          } else {
-            wsc = is_k ? ring_k_scale : ring_v_scale;
-          }
+          wsc = (is_k ? key_scales : value_scales)[((size_t)phys * Hkv + g) * BS + row];
         } else {
           wsc = pos >= first_pos && pos < ctx ? 1.f : 0.f;
         }
@@ -429,6 +445,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int i = 0; i < NIT; ++i) {
       const int item = tid + i * kThreads;
       u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
+      wch[i] = false;
       if (item < NCH) {
         const int r = item & (BS - 1);
         const int c = item / BS;
@@ -454,6 +471,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const size_t row = ((size_t)(q_begin + pos - first_pos) * Hkv + g) * D + 8 * c;
           kw = *reinterpret_cast<const u32x4*>(key_act + row);
           vw = *reinterpret_cast<const u32x4*>(value_act + row);
+          wch[i] = true;
         }
       }
       wk[i] = kw;
@@ -470,6 +488,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (item < NCH) {
         const int r = item & (BS - 1);
         const int c = item / BS;
+        if constexpr (kFoldWin) {
+          if (!win_native && wch[i]) {
+            wk[i] = mul_clamp<AF>(wk[i], chunk_k_mul);
+            wv[i] = mul_clamp<AF>(wv[i], chunk_v_mul);
+          }
+        }
         *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c, r) * 8]) = wk[i];
         if (win_native) {
           *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(item % D, item / D) * 8]) = wv[i];
@@ -764,18 +788,21 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   const long long per_xcd = (items + kXcds - 1) / kXcds;
   if (per_xcd * kXcds > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // An E4M3 cache's tensor scales fold into the score and output scales
-  // when every key is a cache row; in the window path the chunk's own rows
-  // are not, so there the ring rows carry them as row scales.
-  constexpr bool kFold = CF == FMT_E4M3 && !WIN;
+  // (in the window path the chunk's own rows are staged divided by them).
+  constexpr bool kFold = CF == FMT_E4M3;
   const float qk = a.softmax_scale * (kFold ? a.k_scale : 1.f) * LOG2E_P;
   const float vs = kFold ? a.v_scale : 1.f;
+  // The chunk rows' multipliers of the window path over an E4M3 ring
+  // (1 / scale, capped to a finite value for denormal scales).
+  const float kmul = WIN && kFold ? fminf(1.f / a.k_scale, FLT_MAX) : 1.f;
+  const float vmul = WIN && kFold ? fminf(1.f / a.v_scale, FLT_MAX) : 1.f;
   hipLaunchKernelGGL((prefill_kernel<D, CF, AF, NQ, WIN>), dim3((unsigned)(per_xcd * kXcds)),
                      dim3(kThreads), 0, s, (uint16_t*)a.out, (const uint16_t*)a.query,
                      a.cu_q_lens, (const uint8_t*)a.key_cache, (const uint8_t*)a.value_cache,
                      a.block_tables, a.context_lens, a.Hq, a.Hkv, G, a.B, a.MBPS,
                      (int)row_tiles, qk, vs, a.key_scales, a.value_scales,
                      (const uint16_t*)a.key_act, (const uint16_t*)a.value_act, a.window,
-                     a.k_scale, a.v_scale);
+                     kmul, vmul);
   return hipGetLastError();
 }
 
