@@ -435,7 +435,9 @@ pa_status pa_prefill_chunk_window(void* out, const void* query, const void* key,
  * as key / k_scale and value / v_scale rounded to act_dtype and clamped to
  * +-448 (the E4M3 range): the same values up to that rounding whenever the
  * scales cover the chunk (|key| <= 448 * k_scale, |value| <= 448 *
- * v_scale), as they must for the ring the chunk is written into.  Other
+ * v_scale), as they must for the ring the chunk is written into.  Over an
+ * INT8 ring each ring row is read as its codes times its row scale rounded
+ * to act_dtype (one rounding beyond the exact code * scale).  Other
  * arguments, outputs and errors as
  * pa_prefill_chunk_window; PA_ERR_UNSUPPORTED for another cache_dtype;
  * PA_ERR_INVALID for E4M3 scales that are not finite and > 0, or NULL INT8

@@ -64,10 +64,12 @@
 // earlier queries still need.  Query i attends to positions i - W + 1 .. i:
 // those before the chunk come from the ring pages, the chunk's own from its
 // K/V activations, staged through registers into the same LDS layout, one
-// page ahead, two buffers (a byte ring's codes widened on the way; an INT8
-// ring's row scales beside the page; over an E4M3 ring the tensor scales
+// page ahead, two buffers.  A byte ring's page is held in registers as its
+// raw codes and widened to the activation format when it is stored to LDS;
+// an INT8 ring's rows are staged as their codes times their row scales,
+// rounded to the activation format; over an E4M3 ring the tensor scales
 // fold into the score and output scales and the chunk's rows are divided
-// by them).
+// by them.
 //
 // Workgroup order: workgroups are dispatched to the 8 XCDs round-robin, so
 // the flat workgroup id is remapped to give each XCD a contiguous range of
@@ -106,6 +108,21 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
 }
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Eight INT8 codes times their scales (s[k] for code k), rounded to the
+// activation format.
+template <int AF>
+__device__ __forceinline__ u32x4 i8x8_scaled(u32x2 c, f32x8 s) {
+  f32x8 f;
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f[4 * w + i] = static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(c[w] >> (8 * i))));
+  f *= s;
+  typedef typename Mfma<AF>::vec v8;
+  return __builtin_bit_cast(u32x4, __builtin_convertvector(f, v8));
+}
 
 // acc + w.lo + w.hi for two packed values of an activation format: a
 // two-element dot product against ones (the products are exact).
@@ -178,10 +195,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int PAGE = BS * D;            // elements of one K (or V) page
   constexpr bool kDma = !byte_fmt(CF) && !WIN;
   constexpr bool kI8 = CF == FMT_I8;
-  // Per-key scales staged beside each page: the INT8 row scales (in the
-  // window path 1 for the chunk's own rows, which come from the
-  // activations).
-  constexpr bool kScaled = kI8;
+  // Per-key scales staged beside each page: the INT8 row scales of the
+  // causal path.
+  constexpr bool kScaled = kI8 && !WIN;
+  // Window path over an INT8 ring: each ring row is staged as its codes
+  // times its scales, rounded to the activation format.
+  constexpr bool kWinI8 = WIN && kI8;
+  constexpr bool kWinByte = WIN && byte_fmt(CF);
   // Window path over an E4M3 ring: the ring's tensor scales fold into the
   // score and output scales, and the chunk's own rows are staged divided
   // by them (clamped to the E4M3 range, which holds them whenever the
@@ -389,13 +409,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // pos mod W; the ring has every position from max(0, start - W) on); a
   // row of the chunk from the activations; any other row is zero (never
   // visible to a query).  A quantised ring's codes are widened exactly to
-  // the activation format.  An INT8 ring's page also stages its row scales
-  // (each ring row's own, 1 for the chunk's rows, 0 for the others); over
-  // an E4M3 ring the chunk's rows are divided by the tensor scales when
-  // they are stored to LDS.
+  // the activation format when the page is stored to LDS (held as raw
+  // codes until then).  An INT8 ring's rows are staged as codes times their
+  // row scales, rounded to the activation format; over an E4M3 ring the
+  // chunk's rows are divided by the tensor scales when they are stored.
   constexpr int NIT = (BS * (D / 8) + kThreads - 1) / kThreads;
   u32x4 wk[WIN ? NIT : 1], wv[WIN ? NIT : 1];
-  float wsc = 0.f;  // threads 0..31: K scale of row tid; 32..63: V scale of row tid - 32
+  // A byte ring's native page: raw codes, widened when stored (and an INT8
+  // ring's scales: the K chunk's row, the V chunk's eight rows).
+  u32x2 wkc[kWinByte ? NIT : 1], wvc[kWinByte ? NIT : 1];
+  float wks[kWinI8 ? NIT : 1];
+  f32x4 wvs0[kWinI8 ? NIT : 1], wvs1[kWinI8 ? NIT : 1];
   bool wch[WIN ? NIT : 1];  // item holds a chunk row (E4M3 ring: divided when stored)
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
   // Eight ring elements of K (or V) starting at element `off` of the cache
@@ -417,26 +441,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int ring_blk = (base % window) / BS;
     const int phys = base >= first_pos ? 0 : ident ? b * MBPS + ring_blk : bt[ring_blk];
     const size_t page = (size_t)phys * blk_stride + head_off;
-    if constexpr (kScaled) {
-      if (tid < 2 * BS) {
-        const int row = tid & (BS - 1);
-        const int pos = base + row;
-        const bool is_k = tid < BS;
-        if (pos >= ring_lo && pos < first_pos) {
-          wsc = (is_k ? key_scales : value_scales)[((size_t)phys * Hkv + g) * BS + row];
-        } else {
-          wsc = pos >= first_pos && pos < ctx ? 1.f : 0.f;
-        }
-      }
-    }
     win_native = base + BS <= first_pos;
     if (win_native) {
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         const int item = tid + i * kThreads;
         if (item < NCH) {
-          wk[i] = ring_chunk(key_cache, page + (size_t)item * 8);
-          wv[i] = ring_chunk(value_cache, page + (size_t)item * 8);
+          if constexpr (kWinByte) {
+            wkc[i] = *reinterpret_cast<const u32x2*>(key_cache + page + (size_t)item * 8);
+            wvc[i] = *reinterpret_cast<const u32x2*>(value_cache + page + (size_t)item * 8);
+            if constexpr (kWinI8) {
+              const size_t srow = ((size_t)phys * Hkv + g) * BS;
+              wks[i] = key_scales[srow + (item & (BS - 1))];
+              const f32x4* vsp = reinterpret_cast<const f32x4*>(value_scales + srow + 8 * (item / D));
+              wvs0[i] = vsp[0];
+              wvs1[i] = vsp[1];
+            }
+            // Every staged register is written on both paths, so that no
+            // loaded value has to be copied where the paths join.
+            wk[i] = u32x4{0u, 0u, 0u, 0u};
+            wv[i] = u32x4{0u, 0u, 0u, 0u};
+          } else {
+            wk[i] = ring_chunk(key_cache, page + (size_t)item * 8);
+            wv[i] = ring_chunk(value_cache, page + (size_t)item * 8);
+          }
         }
       }
       return;
@@ -446,12 +474,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int item = tid + i * kThreads;
       u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
       wch[i] = false;
+      if constexpr (kWinByte) {
+        wkc[i] = u32x2{0u, 0u};
+        wvc[i] = u32x2{0u, 0u};
+        if constexpr (kWinI8) {
+          wks[i] = 0.f;
+          wvs0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          wvs1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
       if (item < NCH) {
         const int r = item & (BS - 1);
         const int c = item / BS;
         const int pos = base + r;
         if (pos >= ring_lo && pos < first_pos) {
-          kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
+          if constexpr (kWinI8) {
+            const size_t srow = ((size_t)phys * Hkv + g) * BS + r;
+            kw = i8x8_scaled<AF>(*reinterpret_cast<const u32x2*>(key_cache + page +
+                                                                 (size_t)(c * BS + r) * 8),
+                                 (f32x8)(key_scales[srow]));
+          } else {
+            kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
+          }
           if constexpr (byte_fmt(CF)) {
             u32x2 vq = u32x2{0u, 0u};
 #pragma unroll
@@ -459,7 +503,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
               vq[e >> 2] |= (uint32_t)value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 +
                                                   (r & 7)]
                             << (8 * (e & 3));
-            vw = widen(vq);
+            if constexpr (kWinI8) {
+              vw = i8x8_scaled<AF>(vq, (f32x8)(value_scales[((size_t)phys * Hkv + g) * BS + r]));
+            } else {
+              vw = widen(vq);
+            }
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -494,6 +542,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             wv[i] = mul_clamp<AF>(wv[i], chunk_v_mul);
           }
         }
+        if constexpr (kWinByte) {
+          if (win_native) {
+            if constexpr (kWinI8) {
+              const f32x4 s0 = wvs0[i], s1 = wvs1[i];
+              wk[i] = i8x8_scaled<AF>(wkc[i], (f32x8)(wks[i]));
+              wv[i] = i8x8_scaled<AF>(wvc[i], f32x8{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]});
+            } else {
+              wk[i] = widen(wkc[i]);
+              wv[i] = widen(wvc[i]);
+            }
+          }
+        }
         *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c, r) * 8]) = wk[i];
         if (win_native) {
           *reinterpret_cast<u32x4*>(&v_lds[buf][v_slot(item % D, item / D) * 8]) = wv[i];
@@ -506,10 +566,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
         }
       }
-    }
-    if constexpr (kScaled) {
-      if (tid < BS) ks_lds[buf][tid] = wsc;
-      else if (tid < 2 * BS) vs_lds[buf][tid - BS] = wsc;
     }
   };
 
