@@ -202,6 +202,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // times its scales, rounded to the activation format.
   constexpr bool kWinI8 = WIN && kI8;
   constexpr bool kWinByte = WIN && byte_fmt(CF);
+  // Window path over an E4M3 ring: a ring row on a row-by-row page is
+  // staged as raw codes too and widened when stored.
+  constexpr bool kWinDefer = WIN && CF == FMT_E4M3;
   // Window path over an E4M3 ring: the ring's tensor scales fold into the
   // score and output scales, and the chunk's own rows are staged divided
   // by them (clamped to the E4M3 range, which holds them whenever the
@@ -408,11 +411,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // row before the chunk comes from the ring (its ring page holds rows
   // pos mod W; the ring has every position from max(0, start - W) on); a
   // row of the chunk from the activations; any other row is zero (never
-  // visible to a query).  A quantised ring's codes are widened exactly to
-  // the activation format when the page is stored to LDS (held as raw
-  // codes until then).  An INT8 ring's rows are staged as codes times their
-  // row scales, rounded to the activation format; over an E4M3 ring the
-  // chunk's rows are divided by the tensor scales when they are stored.
+  // visible to a query).  A quantised ring's rows are held as raw codes
+  // and widened when the page is stored to LDS (E4M3 exactly; INT8 as codes
+  // times their row scales, rounded to the activation format), except an
+  // INT8 ring's rows on a row-by-row page, which are scaled in registers
+  // of their own as they arrive.  Over an E4M3 ring the chunk's rows are
+  // divided by the tensor scales when they are stored.
   constexpr int NIT = (BS * (D / 8) + kThreads - 1) / kThreads;
   u32x4 wk[WIN ? NIT : 1], wv[WIN ? NIT : 1];
   // A byte ring's native page: raw codes, widened when stored (and an INT8
@@ -420,7 +424,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   u32x2 wkc[kWinByte ? NIT : 1], wvc[kWinByte ? NIT : 1];
   float wks[kWinI8 ? NIT : 1];
   f32x4 wvs0[kWinI8 ? NIT : 1], wvs1[kWinI8 ? NIT : 1];
-  bool wch[WIN ? NIT : 1];  // item holds a chunk row (E4M3 ring: divided when stored)
+  // Item class: 0 a zero row or a native page, 1 a byte ring's row on a
+  // row-by-row page (E4M3: widened when stored; INT8: scaled while staging,
+  // held apart from the chunk rows' registers), 2 a chunk row (E4M3 ring:
+  // divided when stored).  One variable, so that the branches that set it
+  // store values, not flags in different places.  On a row-by-row page the
+  // chunk rows' loads then write registers that nothing else writes, and
+  // no load is waited for before the page's products (a merge of loaded
+  // and computed values into one register waits for the load).
+  int wcl[WIN ? NIT : 1];
+  // An E4M3 ring's row on a row-by-row page: the K codes in wkc, the V
+  // codes one byte per register (gathered from eight V chunks).
+  uint32_t wvb[kWinDefer ? NIT : 1][8];
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
   // Eight ring elements of K (or V) starting at element `off` of the cache
   // (16-bit: one 16-byte load; bytes: one 8-byte load, widened).
@@ -446,6 +461,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         const int item = tid + i * kThreads;
+        wcl[i] = 0;
         if (item < NCH) {
           if constexpr (kWinByte) {
             wkc[i] = *reinterpret_cast<const u32x2*>(key_cache + page + (size_t)item * 8);
@@ -461,6 +477,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // loaded value has to be copied where the paths join.
             wk[i] = u32x4{0u, 0u, 0u, 0u};
             wv[i] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (kWinDefer) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) wvb[i][e] = 0u;
+            }
           } else {
             wk[i] = ring_chunk(key_cache, page + (size_t)item * 8);
             wv[i] = ring_chunk(value_cache, page + (size_t)item * 8);
@@ -473,10 +493,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int i = 0; i < NIT; ++i) {
       const int item = tid + i * kThreads;
       u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
-      wch[i] = false;
+      wcl[i] = 0;
       if constexpr (kWinByte) {
         wkc[i] = u32x2{0u, 0u};
         wvc[i] = u32x2{0u, 0u};
+        if constexpr (kWinDefer) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wvb[i][e] = 0u;
+        }
         if constexpr (kWinI8) {
           wks[i] = 0.f;
           wvs0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -488,38 +512,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int c = item / BS;
         const int pos = base + r;
         if (pos >= ring_lo && pos < first_pos) {
-          if constexpr (kWinI8) {
-            const size_t srow = ((size_t)phys * Hkv + g) * BS + r;
-            kw = i8x8_scaled<AF>(*reinterpret_cast<const u32x2*>(key_cache + page +
-                                                                 (size_t)(c * BS + r) * 8),
-                                 (f32x8)(key_scales[srow]));
-          } else {
-            kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
-          }
-          if constexpr (byte_fmt(CF)) {
-            u32x2 vq = u32x2{0u, 0u};
+          if constexpr (kWinDefer) {
+            wkc[i] = *reinterpret_cast<const u32x2*>(key_cache + page + (size_t)(c * BS + r) * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              vq[e >> 2] |= (uint32_t)value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 +
-                                                  (r & 7)]
-                            << (8 * (e & 3));
-            if constexpr (kWinI8) {
-              vw = i8x8_scaled<AF>(vq, (f32x8)(value_scales[((size_t)phys * Hkv + g) * BS + r]));
-            } else {
-              vw = widen(vq);
-            }
+              wvb[i][e] = value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 + (r & 7)];
+            wcl[i] = 1;
           } else {
+            if constexpr (kWinI8) {
+              // The INT8 ring row's scaled K and V go into the native
+              // page's scale registers (unused on row-by-row pages), not
+              // into the registers the chunk rows' loads write.
+              const size_t srow = ((size_t)phys * Hkv + g) * BS + r;
+              wvs0[i] = __builtin_bit_cast(
+                  f32x4, i8x8_scaled<AF>(*reinterpret_cast<const u32x2*>(key_cache + page +
+                                                                         (size_t)(c * BS + r) * 8),
+                                         (f32x8)(key_scales[srow])));
+              wcl[i] = 1;
+            } else {
+              kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
+            }
+            if constexpr (byte_fmt(CF)) {
+              u32x2 vq = u32x2{0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const size_t at = page + ((size_t)(r >> 3) * D + 8 * c + 2 * e) * 8 + (r & 7);
-              vw[e] = (uint32_t)vc16[at] | ((uint32_t)vc16[at + 8] << 16);
+              for (int e = 0; e < 8; ++e)
+                vq[e >> 2] |= (uint32_t)value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 +
+                                                    (r & 7)]
+                              << (8 * (e & 3));
+              if constexpr (kWinI8) {
+                wvs1[i] = __builtin_bit_cast(
+                    f32x4, i8x8_scaled<AF>(vq, (f32x8)(value_scales[((size_t)phys * Hkv + g) * BS + r])));
+              } else {
+                vw = widen(vq);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const size_t at = page + ((size_t)(r >> 3) * D + 8 * c + 2 * e) * 8 + (r & 7);
+                vw[e] = (uint32_t)vc16[at] | ((uint32_t)vc16[at + 8] << 16);
+              }
             }
           }
         } else if (pos >= first_pos && pos < ctx) {
           const size_t row = ((size_t)(q_begin + pos - first_pos) * Hkv + g) * D + 8 * c;
           kw = *reinterpret_cast<const u32x4*>(key_act + row);
           vw = *reinterpret_cast<const u32x4*>(value_act + row);
-          wch[i] = true;
+          wcl[i] = 2;
         }
       }
       wk[i] = kw;
@@ -537,7 +575,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int r = item & (BS - 1);
         const int c = item / BS;
         if constexpr (kFoldWin) {
-          if (!win_native && wch[i]) {
+          if (!win_native && wcl[i] == 2) {
             wk[i] = mul_clamp<AF>(wk[i], chunk_k_mul);
             wv[i] = mul_clamp<AF>(wv[i], chunk_v_mul);
           }
@@ -552,6 +590,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
               wk[i] = widen(wkc[i]);
               wv[i] = widen(wvc[i]);
             }
+          } else if (kWinI8 && wcl[i] == 1) {
+            wk[i] = __builtin_bit_cast(u32x4, wvs0[i]);
+            wv[i] = __builtin_bit_cast(u32x4, wvs1[i]);
+          } else if (kWinDefer && wcl[i] == 1) {
+            u32x2 vq;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              vq[h] = wvb[i][4 * h] | (wvb[i][4 * h + 1] << 8) | (wvb[i][4 * h + 2] << 16) |
+                      (wvb[i][4 * h + 3] << 24);
+            wk[i] = widen(wkc[i]);
+            wv[i] = widen(vq);
           }
         }
         *reinterpret_cast<u32x4*>(&k_lds[buf][k_slot(c, r) * 8]) = wk[i];
