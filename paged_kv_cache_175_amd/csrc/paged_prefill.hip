@@ -437,14 +437,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // codes one byte per register (gathered from eight V chunks).
   uint32_t wvb[kWinDefer ? NIT : 1][8];
   const uint16_t* vc16 = reinterpret_cast<const uint16_t*>(value_cache);
-  // Eight ring elements of K (or V) starting at element `off` of the cache
-  // (16-bit: one 16-byte load; bytes: one 8-byte load, widened).
+  // Eight elements of a 16-bit ring's K (or V) starting at element `off`
+  // of the cache: one 16-byte load.
   auto ring_chunk = [&](const uint8_t* cache, size_t off) -> u32x4 {
-    if constexpr (byte_fmt(CF)) {
-      return widen(*reinterpret_cast<const u32x2*>(cache + off));
-    } else {
-      return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(cache) + off);
-    }
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(cache) + off);
   };
   // A page wholly before the chunk is all ring rows, every one written
   // (the ring holds max(0, start - W) .. start - 1, all W rows once
@@ -518,39 +514,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int e = 0; e < 8; ++e)
               wvb[i][e] = value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 + (r & 7)];
             wcl[i] = 1;
+          } else if constexpr (kWinI8) {
+            // The INT8 ring row's scaled K and V go into the native page's
+            // scale registers (unused on row-by-row pages), not into the
+            // registers the chunk rows' loads write.
+            const size_t srow = ((size_t)phys * Hkv + g) * BS + r;
+            wvs0[i] = __builtin_bit_cast(
+                f32x4, i8x8_scaled<AF>(*reinterpret_cast<const u32x2*>(key_cache + page +
+                                                                       (size_t)(c * BS + r) * 8),
+                                       (f32x8)(key_scales[srow])));
+            u32x2 vq = u32x2{0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              vq[e >> 2] |= (uint32_t)value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 +
+                                                  (r & 7)]
+                            << (8 * (e & 3));
+            wvs1[i] = __builtin_bit_cast(f32x4, i8x8_scaled<AF>(vq, (f32x8)(value_scales[srow])));
+            wcl[i] = 1;
           } else {
-            if constexpr (kWinI8) {
-              // The INT8 ring row's scaled K and V go into the native
-              // page's scale registers (unused on row-by-row pages), not
-              // into the registers the chunk rows' loads write.
-              const size_t srow = ((size_t)phys * Hkv + g) * BS + r;
-              wvs0[i] = __builtin_bit_cast(
-                  f32x4, i8x8_scaled<AF>(*reinterpret_cast<const u32x2*>(key_cache + page +
-                                                                         (size_t)(c * BS + r) * 8),
-                                         (f32x8)(key_scales[srow])));
-              wcl[i] = 1;
-            } else {
-              kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
-            }
-            if constexpr (byte_fmt(CF)) {
-              u32x2 vq = u32x2{0u, 0u};
+            kw = ring_chunk(key_cache, page + (size_t)(c * BS + r) * 8);
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                vq[e >> 2] |= (uint32_t)value_cache[page + ((size_t)(r >> 3) * D + 8 * c + e) * 8 +
-                                                    (r & 7)]
-                              << (8 * (e & 3));
-              if constexpr (kWinI8) {
-                wvs1[i] = __builtin_bit_cast(
-                    f32x4, i8x8_scaled<AF>(vq, (f32x8)(value_scales[((size_t)phys * Hkv + g) * BS + r])));
-              } else {
-                vw = widen(vq);
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const size_t at = page + ((size_t)(r >> 3) * D + 8 * c + 2 * e) * 8 + (r & 7);
-                vw[e] = (uint32_t)vc16[at] | ((uint32_t)vc16[at + 8] << 16);
-              }
+            for (int e = 0; e < 4; ++e) {
+              const size_t at = page + ((size_t)(r >> 3) * D + 8 * c + 2 * e) * 8 + (r & 7);
+              vw[e] = (uint32_t)vc16[at] | ((uint32_t)vc16[at + 8] << 16);
             }
           }
         } else if (pos >= first_pos && pos < ctx) {
