@@ -12,11 +12,12 @@
 //
 // A workgroup takes 32 consecutive input tokens of one KV head.  It reads
 // their K and V rows with fully coalesced 16-byte loads into LDS, then writes
-// them out token-fastest: consecutive lanes handle consecutive tokens, so
-// when the tokens fill consecutive rows of a page (a prefill chunk) the K
-// chunks of the [D/8][32][8] page and the V elements of the [4][D][8] page
-// (8-token groups) leave as contiguous runs instead of scattered stores.
-// Decode-time writes (one token per sequence) take the same path.
+// them out: K token-fastest, one 16-byte (8-byte) chunk of the [D/8][32][8]
+// page per store, so consecutive lanes write consecutive rows; V, when 8
+// tokens fill a whole 8-token group of rows of the [4][D][8] page (a
+// prefill chunk), one 16-byte (8-byte) chunk per store, 8 tokens of one
+// dimension gathered from LDS, else element by element.  Decode-time
+// writes (one token per sequence) take the same kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -129,23 +130,64 @@ __global__ __launch_bounds__(kThreads) void cache_write(
       *reinterpret_cast<u32x4*>(key_cache + dst) = kw;
     }
   }
-  // V: single elements, token-fastest within each group of 8 tokens, then
-  // dimension, then group (the page's own order).
-  for (int i = tid; i < kGroup * D; i += kThreads) {
-    const int n = (i / (8 * D)) * 8 + (i & 7);
-    const int d = (i >> 3) % D;
-    const int slot = slot_s[n];
-    if (slot < 0) continue;
-    const int blk = slot / kPage;
-    const int off = slot - blk * kPage;
-    const size_t dst = ((size_t)blk * Hkv + h) * page_elems + v_page_off(off, d, D);
-    const uint16_t x = v_s[n * ROW + d];
-    if constexpr (CF == FMT_E4M3) {
-      value_cache[dst] = static_cast<uint8_t>(e4m3_encode(lo16_to_f32<AF>(x), v_scale));
-    } else if constexpr (CF == FMT_I8) {
-      value_cache[dst] = static_cast<uint8_t>(i8_encode(lo16_to_f32<AF>(x), vsc_s[n]));
+  // V: the page holds 8-token groups, one 16-byte (8-byte) chunk per
+  // (group, dimension).  Where a group's 8 tokens fill 8 consecutive rows
+  // starting at a multiple of 8 (a prefill chunk), a thread gathers the 8
+  // elements of one dimension from LDS and stores the chunk at once;
+  // consecutive threads take consecutive dimensions, so the stores are
+  // contiguous runs.  Other groups (decode rows, a chunk that starts
+  // mid-group) are stored element by element.
+  for (int i = tid; i < (kGroup / 8) * D; i += kThreads) {
+    const int tq = i / D;
+    const int d = i - tq * D;
+    const int n8 = 8 * tq;
+    const int s0 = slot_s[n8];
+    bool whole = s0 >= 0 && (s0 & 7) == 0;
+#pragma unroll
+    for (int j = 1; j < 8; ++j) whole = whole && slot_s[n8 + j] == s0 + j;
+    if (whole) {
+      const int blk = s0 / kPage;
+      const size_t dst = ((size_t)blk * Hkv + h) * page_elems + v_page_off(s0 - blk * kPage, d, D);
+      uint16_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = v_s[(n8 + j) * ROW + d];
+      if constexpr (byte_fmt(CF)) {
+        u32x2 q = u32x2{0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint32_t e;
+          if constexpr (CF == FMT_E4M3) {
+            e = e4m3_encode(lo16_to_f32<AF>(x[j]), v_scale);
+          } else {
+            e = i8_encode(lo16_to_f32<AF>(x[j]), vsc_s[n8 + j]);
+          }
+          q[j >> 2] |= (e & 0xffu) << (8 * (j & 3));
+        }
+        *reinterpret_cast<u32x2*>(value_cache + dst) = q;
+      } else {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (uint32_t)x[2 * k] | ((uint32_t)x[2 * k + 1] << 16);
+        *reinterpret_cast<u32x4*>(value_cache + dst * 2) = w;
+      }
     } else {
-      reinterpret_cast<uint16_t*>(value_cache)[dst] = x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = n8 + j;
+        const int slot = slot_s[n];
+        if (slot < 0) continue;
+        const int blk = slot / kPage;
+        const int off = slot - blk * kPage;
+        const size_t dst = ((size_t)blk * Hkv + h) * page_elems + v_page_off(off, d, D);
+        const uint16_t x = v_s[n * ROW + d];
+        if constexpr (CF == FMT_E4M3) {
+          value_cache[dst] = static_cast<uint8_t>(e4m3_encode(lo16_to_f32<AF>(x), v_scale));
+        } else if constexpr (CF == FMT_I8) {
+          value_cache[dst] = static_cast<uint8_t>(i8_encode(lo16_to_f32<AF>(x), vsc_s[n]));
+        } else {
+          reinterpret_cast<uint16_t*>(value_cache)[dst] = x;
+        }
+      }
     }
   }
 }
