@@ -275,3 +275,29 @@ def max_abs(a: np.ndarray, b: np.ndarray) -> float:
     if np.isnan(d).any():
         return float("nan")
     return float(d.max())
+
+
+def check_window_rings(wl, pools, opools, bt) -> None:
+    """The rings after a window prefill, position by position: every
+    resident position (the last ``window`` of each sequence) through each
+    side's table (the two sides place the ring blocks differently).  ``pools``
+    = (key, value, key scales or None, value scales or None) on the GPU,
+    ``opools`` the oracle's as numpy, ``bt`` the GPU side's block tables."""
+    gk, gv = pool_bits(pools[0]), pool_bits(pools[1])
+    i8 = pools[2] is not None
+    if i8:
+        gks, gvs = scale_bits(pools[2]), scale_bits(pools[3])
+        oks, ovs = opools[2].view(np.int32), opools[3].view(np.int32)
+    for b in range(wl.B):
+        ctx = int(wl.context_lens[b])
+        for p in range(max(0, ctx - wl.window), ctx):
+            s_h = pool.slots_from_table(bt[b], np.array([p]), wl.BS, wl.window)[0]
+            s_o = o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
+            kh, vh = o_cache.get_row(gk, gv, s_h // wl.BS, s_h % wl.BS)
+            ko, vo = o_cache.get_row(opools[0], opools[1], s_o // wl.BS, s_o % wl.BS)
+            assert np.array_equal(kh, ko) and np.array_equal(vh, vo), (b, p)
+            if i8:
+                assert np.array_equal(gks[s_h // wl.BS, :, s_h % wl.BS],
+                                      oks[s_o // wl.BS, :, s_o % wl.BS]), (b, p)
+                assert np.array_equal(gvs[s_h // wl.BS, :, s_h % wl.BS],
+                                      ovs[s_o // wl.BS, :, s_o % wl.BS]), (b, p)

@@ -20,9 +20,6 @@ import torch
 import paritylib as P
 import test_gpu_window_prefill as WP
 import test_gpu_window_prefill_quant as WQ
-from oracle import cache as o_cache
-from oracle import pool as o_pool
-from paged_kv_cache_175_amd import pool
 from paged_kv_cache_175_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -99,25 +96,8 @@ def test_window_prefill_matrix(name):
         out, pools, bt = WQ.hip_run(wl)
         ref, opools = WQ.oracle_run(wl)
     # The ring after the chunk: every resident position, through each side's
-    # table (the two sides place the ring blocks differently).
-    gk, gv = P.pool_bits(pools[0]), P.pool_bits(pools[1])
-    i8 = cache == "int8"
-    if i8:
-        gks, gvs = P.scale_bits(pools[2]), P.scale_bits(pools[3])
-        oks, ovs = opools[2].view(np.int32), opools[3].view(np.int32)
-    for b in range(wl.B):
-        ctx = int(wl.context_lens[b])
-        for p in range(max(0, ctx - wl.window), ctx):
-            s_h = pool.slots_from_table(bt[b], np.array([p]), wl.BS, wl.window)[0]
-            s_o = o_cache.slot_of(wl.block_tables[b], o_pool.ring_index(p, wl.window), wl.BS)
-            kh, vh = o_cache.get_row(gk, gv, s_h // wl.BS, s_h % wl.BS)
-            ko, vo = o_cache.get_row(opools[0], opools[1], s_o // wl.BS, s_o % wl.BS)
-            assert np.array_equal(kh, ko) and np.array_equal(vh, vo), (b, p)
-            if i8:
-                assert np.array_equal(gks[s_h // wl.BS, :, s_h % wl.BS],
-                                      oks[s_o // wl.BS, :, s_o % wl.BS]), (b, p)
-                assert np.array_equal(gvs[s_h // wl.BS, :, s_h % wl.BS],
-                                      ovs[s_o // wl.BS, :, s_o % wl.BS]), (b, p)
+    # table.
+    P.check_window_rings(wl, pools, opools, bt)
     tol = P.TOL[cache or act]
     err = P.max_abs(P.out_f64(out), ref)
     P.say(f"    max-abs error {err:.3e} (tolerance {tol:.0e})")
