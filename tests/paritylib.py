@@ -16,7 +16,6 @@ import sys
 import numpy as np
 import torch
 
-from oracle import attention as o_attn
 from oracle import cache as o_cache
 from oracle import pool as o_pool
 from paged_kv_cache_175_amd import ops, pool
